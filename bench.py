@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-hop KV-cache correction (KVCMAS hot path) on one MI355X.
+
+Workload (one step = one whole hop): a Llama-3.1-8B-shaped shared segment of 32768 tokens,
+32 layers, 8 KV heads x 128 (D = 1024 per K and per V), bf16, corrected against a pool of
+20 anchors stored as rank-32 factors; shift 300 positions; one third of the layers carry a
+source no anchor holds.  Every step re-aligns, scores, gates, weights and applies the delta
+for all layers, keys and values, through kvc_correct_hop.  Inputs are synthetic (seeded
+generator) and resident in HBM before the timed region.
+
+Prints one JSON line: corrected KV tokens/s (all layers), the roofline of the dominant kernel
+(measured with HIP events around each launch on the library's stream) and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "corrected KV tokens/s (all layers) at 8B shape, 32K seg; % HBM/MFMA roofline"
+PEAK_HBM = 8.0e12            # B/s, MI355X HBM3E
+PEAK_MFMA_BF16 = 2.5e15      # flop/s, dense bf16
+# VALU lane-ops/s for the unpacked fp32 instructions this build emits: 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz (the 157.3 TFLOP/s vector figure counts FMA as 2 and packed dual FP32).
+PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name, L, S, D, N, rC, rD, b=2):
+    """Algorithmic HBM bytes, MFMA flops and VALU lane-ops of one launch of `name` (whole hop)."""
+    src = 2 * L * S * D * b                       # K and V source read
+    fac_base = 2 * L * N * (S * rC + D * rC) * b  # base A and B^T, both sides
+    fac_delta = 2 * L * N * (S * rD + D * rD) * b
+    wts = 2 * L * S * N * 4                       # fp32 scores / weights, both sides
+    if name == "score_pages_mfma":
+        return dict(bytes=src + fac_base + wts, flops=4 * L * S * D * N * rC, alu=3 * L * S * D * N)
+    if name == "score_cos_mfma":
+        return dict(bytes=src + 2 * L * N * (S * rC + D * rC) * b + wts, flops=4 * L * S * D * N * rC,
+                    alu=6 * L * S * N * rC)
+    if name == "apply_mfma":
+        return dict(bytes=2 * src + fac_delta + wts, flops=4 * L * S * D * N * rD, alu=0)
+    if name in ("transpose_base", "transpose_delta"):
+        r = rC if name == "transpose_base" else rD
+        return dict(bytes=2 * 2 * L * N * r * D * b, flops=0, alu=0)
+    if name == "softmax":
+        return dict(bytes=2 * wts, flops=0, alu=0)
+    return dict(bytes=0, flops=0, alu=0)
+
+
+def roofline(name, ms, work, traffic=None):
+    t = ms / 1e3
+    cands = [("hbm", work["bytes"] / PEAK_HBM, work["bytes"] / t / 1e9, PEAK_HBM / 1e9, "GB/s"),
+             ("mfma", work["flops"] / PEAK_MFMA_BF16, work["flops"] / t / 1e12, PEAK_MFMA_BF16 / 1e12, "TFLOP/s"),
+             ("alu", work["alu"] / PEAK_VALU_OPS, work["alu"] / t / 1e12, PEAK_VALU_OPS / 1e12, "Tops/s")]
+    bound, _, ach, peak, unit = max(cands, key=lambda c: c[1])
+    return {"kernel": name, "bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic, "ms": round(ms, 4),
+            "algorithmic_bytes": work["bytes"], "mfma_flops": work["flops"], "valu_ops": work["alu"]}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_kv_cache_layer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    v = d.get("kernels", {}).get(kernel)
+    return None if v is None else int(v)
+
+
+def cpu_baseline(data, n_layers):
+    """The fp64 oracle on layer 0 of the same hop (all tokens, keys and values)."""
+    from oracle import kvc_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    S = data.spec.seq_len
+    t0 = time.perf_counter()
+    O.correct_layer(data, 0)
+    dt = time.perf_counter() - t0
+    return {"value": round(S / (dt * n_layers), 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0 of {n_layers}: {S} tokens x (K, V), scores + weights + gate sums + delta in fp64; "
+                      f"{dt:.1f} s, scaled to all layers"}
+
+
+def time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn, ws, steps, warmup, trace=True):
+    for _ in range(warmup):
+        kvc.correct_hop(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, prm_fn(None), workspace=ws)
+    torch.cuda.synchronize()
+    traces = [kvc.KernelTrace(16) for _ in range(steps)] if trace else [None] * steps
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        res = kvc.correct_hop(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, prm_fn(traces[i]), workspace=ws)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    per_kernel = {}
+    for tr in traces:
+        if tr is None:
+            continue
+        for name, t in tr.results():
+            per_kernel.setdefault(name, []).append(t)
+        tr.close()
+    return ms, wall, per_kernel, res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=32, help="smaller values are for quick local runs only")
+    ap.add_argument("--seq-len", type=int, default=32768, help="smaller values are for quick local runs only")
+    ap.add_argument("--mode", choices=["pages", "cos"], default="pages")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second-mode", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs the per-hop correction on one GPU only; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from rank_kv_cache_layer_amd import kvc
+    from rank_kv_cache_layer_amd import workload as W
+
+    mode = W.SCORE_PAGES if args.mode == "pages" else W.SCORE_COS_R
+    sp = W.llama8b_long(n_layers=args.layers, seq_len=args.seq_len, mode=mode)
+    t0 = time.perf_counter()
+    data = W.make_hop(sp)
+    log(f"[bench] generated {sp.name}: L={sp.n_layers} S={sp.seq_len} D={sp.d_model} N={sp.n_anchors} "
+        f"r={sp.rank_base} in {time.perf_counter() - t0:.1f} s")
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kvc.lib()
+    dev = "cuda:0"
+    k = data.k_src.to(dev)
+    v = data.v_src.to(dev)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    pool = kvc.pool_from(data, dev)
+    shp = kvc.shape_of(sp.n_layers, sp.seq_len, sp.n_kv_heads, sp.head_dim)
+
+    def prm_fn(mode_):
+        return lambda tr: kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, mode_, 0, tr)
+
+    ws_bytes = max(kvc.correct_hop_workspace(shp, pool, prm_fn(m)(None)) for m in (W.SCORE_PAGES, W.SCORE_COS_R))
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident on {torch.cuda.get_device_name(0)}; workspace {ws_bytes / 2**20:.0f} MiB")
+
+    ms, wall, per_kernel, res = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode), ws, args.steps,
+                                         args.warmup)
+    flags = res.flags.cpu().tolist()
+    log(f"[bench] {args.mode}: {ms:.3f} ms/hop (wall {wall / args.steps * 1e3:.3f} ms), flags hop={flags[0]} "
+        f"layers={sum(1 for f in flags[1:] if f)} flagged")
+    S, L, D, N, r = sp.seq_len, sp.n_layers, sp.d_model, sp.n_anchors, sp.rank_base
+    kernels = {}
+    for name, ts in per_kernel.items():
+        med = statistics.median(ts)
+        kernels[name] = roofline(name, med, kernel_work(name, L, S, D, N, r, r), measured_traffic(name))
+    dominant = max(kernels.values(), key=lambda x: x["ms"]) if kernels else None
+
+    hop_bytes = 2 * L * S * D * (2 + 2) + 2 * L * N * (2 * r) * (S + D) * 2
+    hop_flops = 8 * L * S * D * N * r
+    hop = {"ms": round(ms, 4), "algorithmic_bytes": hop_bytes, "mfma_flops": hop_flops,
+           "hbm_frac": round(hop_bytes / (ms / 1e3) / PEAK_HBM, 4),
+           "mfma_frac": round(hop_flops / (ms / 1e3) / PEAK_MFMA_BF16, 4)}
+
+    second = None
+    if not args.no_second_mode:
+        m2 = W.SCORE_COS_R if mode == W.SCORE_PAGES else W.SCORE_PAGES
+        ms2, _, pk2, _ = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(m2), ws, max(3, args.steps // 4),
+                                  1)
+        second = {"mode": "cos_r" if m2 == W.SCORE_COS_R else "pages", "ms_per_hop": round(ms2, 4),
+                  "tokens_per_s": round(S / (ms2 / 1e3), 1),
+                  "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
+        log(f"[bench] second mode {second['mode']}: {ms2:.3f} ms/hop")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a bounded sample ...")
+        cpu = cpu_baseline(data, L)
+        log(f"[bench] oracle: {cpu['value']} tokens/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC, "value": round(S / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama8b_hop_{S}tok" if S != 32768 or L != 32 else "llama8b_32k_hop",
+                   "n_layers": L, "seq_len": S, "n_kv_heads": sp.n_kv_heads, "head_dim": sp.head_dim,
+                   "n_anchors": N, "rank": r, "shift": sp.shift, "score_mode": args.mode,
+                   "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
+        "roofline": dominant, "cpu_baseline": cpu,
+        "hop": hop, "kernels": kernels, "second_mode": second,
+        "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

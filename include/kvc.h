@@ -1,0 +1,257 @@
+/*
+ * kvc.h -- C ABI of the MI355X (gfx950) per-hop KV-cache correction library (libkvc.so).
+ *
+ * The library implements the data-parallel hot path of KVCMAS ("KVCMAS: Efficient KV
+ * cache Correction for Shared Context in Multi-Agent Systems", arXiv 2609.34060): for a
+ * shared context segment handed from a source agent i to a target agent j it
+ *   1. re-aligns the cached keys to the target positions (Sec. 2.2; App. A.3
+ *      "Correction Weighting and Positional Alignment"),
+ *   2. scores the segment against the slot's anchor pool stored as rank-r factors
+ *      (Sec. 3.3 Eq. 7),
+ *   3. evaluates the reliability gate (App. A.3 Eq. 9-11),
+ *   4. forms token-wise anchor weights (App. A.3 "Correction Weighting"), and
+ *   5. adds the weighted low-rank delta to the aligned source (Sec. 3.3 Eq. 8, Eq. 12).
+ * It also factorises matrices into rank-r factors for anchor refresh (Eq. 7, App. B.1
+ * "Factorization and Measurement").
+ *
+ * Conventions shared by every call
+ *  - Ownership: the caller owns every buffer.  Device buffers are plain device pointers
+ *    (e.g. from torch tensors); small descriptors are host memory read during the call.
+ *    The library never allocates device memory; calls that need scratch take a workspace
+ *    pointer and size (query with kvc_workspace_size).
+ *  - Streams: all device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Device results are valid after the stream is synchronised.
+ *  - Errors: every call returns a kvc_status.  All validation happens on the host before
+ *    any launch, so a non-OK status has no side effect on device memory.  A human-readable
+ *    reason is available from kvc_last_error() (thread-local).  No call prints, throws
+ *    or exits.
+ *  - Layout: caches are row-major [layer][token][head][dim] with D = n_kv_heads*head_dim
+ *    contiguous; every device pointer must be 16-byte aligned (KVC_E_ALIGN otherwise).
+ *  - Frames: token t of the segment sits at absolute position p + t.  Anchor bases and key
+ *    deltas are stored in the canonical frame, where token t sits at position t.
+ *  - Rotation: rotate-half RoPE; channel c of each head pairs with c + head_dim/2 and turns
+ *    by dp * w_c, w_c = theta^(-2c/head_dim) unless an explicit frequency table is given.
+ *    Angles are evaluated in double precision on the host and passed to the GPU as float.
+ *  - The library is stateless and reentrant.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+#define KVC_MAX_ANCHORS 64
+#define KVC_MAX_HEAD_DIM 256
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_NULL = 1,        /* a required pointer is NULL                               */
+  KVC_E_SHAPE = 2,       /* a size is out of range or inconsistent                   */
+  KVC_E_DTYPE = 3,       /* unsupported dtype or dtype mismatch                      */
+  KVC_E_ALIGN = 4,       /* a device pointer is not 16-byte aligned                  */
+  KVC_E_ALIAS = 5,       /* an output overlaps an input it must not overlap          */
+  KVC_E_WORKSPACE = 6,   /* workspace missing or smaller than kvc_workspace_size()   */
+  KVC_E_HIP = 7,         /* the HIP runtime reported an error at launch              */
+  KVC_E_PARAM = 8,       /* a scalar parameter is out of range                       */
+  KVC_E_UNSUPPORTED = 9  /* valid request this build does not implement              */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Anchor scoring mode.
+ * KVC_SCORE_PAGES: App. A.3 -- token weights from the mean absolute distance between the
+ *   (canonical) source and each anchor's reconstructed base, softmax(-m / temp_weight);
+ *   gate on the Frobenius distance of reconstructed values over the prefix k (Eq. 9),
+ *   g = softmax(-d / temp_gate) (Eq. 10), normalised entropy (Eq. 11), accept iff <= tau.
+ * KVC_SCORE_COS_R: cosine between the source expressed in each anchor's r-dim basis
+ *   (P = Z B^T) and the anchor's own coordinates A; weights softmax(c / temp_weight);
+ *   the hop is flagged when the best segment cosine (values, prefix k) is below tau.   */
+typedef enum { KVC_SCORE_PAGES = 0, KVC_SCORE_COS_R = 1 } kvc_score_mode;
+
+/* Flag bits (0 = accept the correction). */
+#define KVC_FLAG_ENTROPY 1        /* normalised entropy above tau (Eq. 11)                 */
+#define KVC_FLAG_FEW_ANCHORS 2    /* fewer than two compatible anchors (App. A.3)          */
+#define KVC_FLAG_COS_BELOW 4      /* COS_R: best segment cosine below tau                  */
+#define KVC_FLAG_PRED_FLAGGED 8   /* batched chains: the preceding hop was flagged         */
+
+typedef struct {
+  int32_t n_layers;    /* N_l >= 1                                                         */
+  int32_t seq_len;     /* S >= 1, tokens of the shared segment                              */
+  int32_t n_kv_heads;  /* >= 1                                                             */
+  int32_t head_dim;    /* even, <= KVC_MAX_HEAD_DIM; D = n_kv_heads * head_dim              */
+} kvc_shape;
+
+typedef struct {
+  double theta;              /* rotary base (e.g. 10000); used when inv_freq is NULL       */
+  const double* inv_freq;    /* optional host table of head_dim/2 frequencies w_c          */
+} kvc_rope;
+
+/* One slot's anchor pool as seen by one consuming agent (App. A.3: each anchor stores a
+ * base representation and corrections for its consumers; Eq. 7 factors).
+ *  A factors are packed without padding: anchor a owns rows [off_a, off_a + anchor_len[a])
+ *  with off_a = sum_{b<a} anchor_len[b]; arrays are [n_layers][sum(len)][rank].
+ *  B factors are [n_layers][n_anchors][rank][D].
+ *  Key bases and key deltas are canonical-frame.  All factor arrays share `dtype`, which
+ *  must equal the cache dtype.  capacity == 1 bypasses the gate (App. C.3). */
+typedef struct {
+  int32_t n_anchors;          /* 0 .. KVC_MAX_ANCHORS                                       */
+  int32_t rank_base;          /* r_C >= 1                                                   */
+  int32_t rank_delta;         /* r_Delta >= 1                                               */
+  int32_t capacity;           /* pool capacity V (>= n_anchors, or 0 = n_anchors)           */
+  const int32_t* anchor_len;  /* host [n_anchors], each >= 1                                */
+  kvc_dtype dtype;
+  const void* baseA_k;  const void* baseB_k;  const void* baseA_v;  const void* baseB_v;
+  const void* deltaA_k; const void* deltaB_k; const void* deltaA_v; const void* deltaB_v;
+} kvc_pool;
+
+/* Optional per-kernel trace for benchmarking.  The caller creates `capacity` pairs of
+ * hipEvent_t (passed as void*); for every kernel the call launches, the library records
+ * start[i] / stop[i] around it on the call's stream, stores the kernel's id in kernel_id[i]
+ * and increments count (launches beyond capacity are not traced).  Nothing synchronises:
+ * the caller reads elapsed times after synchronising the stream. */
+#define KVC_TRACE_MAX 64
+#define KVC_K_TRANSPOSE_BASE 1
+#define KVC_K_SCORE_PAGES 2
+#define KVC_K_SCORE_COS 3
+#define KVC_K_SCORE_GENERIC 4
+#define KVC_K_GATE 5
+#define KVC_K_SOFTMAX 6
+#define KVC_K_TRANSPOSE_DELTA 7
+#define KVC_K_APPLY 8
+#define KVC_K_APPLY_GENERIC 9
+typedef struct {
+  int32_t capacity;               /* <= KVC_TRACE_MAX                                      */
+  int32_t count;                  /* written by the library                                */
+  int32_t kernel_id[KVC_TRACE_MAX];
+  void* start[KVC_TRACE_MAX];     /* hipEvent_t                                            */
+  void* stop[KVC_TRACE_MAX];      /* hipEvent_t                                            */
+} kvc_trace;
+
+typedef struct {
+  double tau;           /* acceptance threshold (Eq. 11 / best cosine)                      */
+  double temp_gate;     /* Eq. 10 temperature (> 0; the pages use 1)                         */
+  double temp_weight;   /* token-weight temperature (> 0)                                     */
+  int32_t gate_len;     /* comparison prefix k (0 = seq_len), 1 .. seq_len                    */
+  int32_t mode;         /* kvc_score_mode                                                    */
+  int32_t options;      /* bit 0: force the generic (non-MFMA) kernels; other bits 0          */
+  int32_t pad_;
+  kvc_trace* trace;     /* optional kernel trace (NULL = none)                                */
+} kvc_params;
+
+/* Match results.  Rows: index 0 = the hop (Eq. 9 sums over all layers), 1 + l = layer l.
+ *  dist  : device double [1 + n_layers][n_anchors] -- PAGES: d_v of Eq. 9; COS_R: segment
+ *          cosine; NaN for anchors outside the gate set A_k.
+ *  stat  : device double [1 + n_layers] -- PAGES: normalised entropy (NaN if |A_k| < 2);
+ *          COS_R: best segment cosine (NaN if A_k is empty).
+ *  flags : device int32  [1 + n_layers] -- 0 accept, else KVC_FLAG_* bits.
+ *  w_k, w_v : optional device float [n_layers][seq_len][n_anchors] token weights (rows
+ *          >= S_cov and anchors outside the correction set are 0); NULL = not returned.
+ *  s_cov : optional host int32, the covered prefix S_cov = min(S, longest anchor).       */
+typedef struct {
+  double* dist;
+  double* stat;
+  int32_t* flags;
+  float* w_k;
+  float* w_v;
+  int32_t* s_cov;
+} kvc_match_out;
+
+/* Workspace query.  `call` selects the entry point: */
+#define KVC_CALL_MATCH 1
+#define KVC_CALL_APPLY 2
+#define KVC_CALL_CORRECT 3
+
+int32_t kvc_abi_version(void);
+const char* kvc_status_str(kvc_status s);
+const char* kvc_last_error(void);
+
+/* Bytes of workspace `call` (KVC_CALL_MATCH / _APPLY / _CORRECT) needs for this
+ * shape/pool/params; 0 for an invalid request.  params may be NULL (defaults).  The factor
+ * refresh has its own query, kvc_svd_workspace_size. */
+size_t kvc_workspace_size(int32_t call, kvc_shape shape, const kvc_pool* pool,
+                          const kvc_params* params);
+
+/* Key re-alignment (Sec. 2.2, App. A.3): k_out[l,t] = R(pos_to - pos_from) k_in[l,t] for all
+ * layers and tokens.  in_t/out_t may differ (f32 <-> bf16, output rounded to nearest even).
+ * k_in == k_out (in place) is allowed when in_t == out_t; other overlaps give KVC_E_ALIAS.
+ * A zero shift copies bits unchanged. */
+kvc_status kvc_align_rope(const void* k_in, void* k_out, kvc_dtype in_t, kvc_dtype out_t,
+                          kvc_shape shape, int64_t pos_from, int64_t pos_to,
+                          const kvc_rope* rope, void* stream);
+
+/* Anchor matching and reliability gate (Eq. 7, Eq. 9-11, App. A.3 weights): scores the
+ * source segment (keys at start position p_src, values) against `pool`, writes the gate
+ * results and optional token weights to `out`.  Needs workspace KVC_CALL_MATCH. */
+kvc_status kvc_match_anchors(const void* k_src, const void* v_src, kvc_dtype dtype,
+                             kvc_shape shape, int64_t p_src, const kvc_rope* rope,
+                             const kvc_pool* pool, const kvc_params* params,
+                             kvc_match_out* out, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Low-rank delta apply with explicit weights (Eq. 8, Eq. 12 form):
+ *   K_out[t] = R(p_tgt - p_src) K_src[t] + R(p_tgt) sum_a w_k[t,a] A_k,a[t] B_k,a
+ *   V_out[t] = V_src[t]                  + sum_a w_v[t,a] A_v,a[t] B_v,a
+ * for t < s_cov (rows >= s_cov get no delta).  w_k/w_v: device float
+ * [n_layers][seq_len][n_anchors].  Outputs must not overlap the sources (KVC_E_ALIAS): the
+ * source stays the source agent's live cache.  Needs workspace KVC_CALL_APPLY. */
+kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k_out,
+                                   void* v_out, kvc_dtype dtype, kvc_shape shape,
+                                   int64_t p_src, int64_t p_tgt, const kvc_rope* rope,
+                                   const kvc_pool* pool, const float* w_k, const float* w_v,
+                                   int32_t s_cov, void* workspace, size_t ws_bytes,
+                                   void* stream);
+
+/* The whole per-hop correction: match + gate + weights + apply (Sec. 3.3, App. A.3).  The
+ * corrected cache is always written; flags tell the caller to prefill densely instead.
+ * Needs workspace KVC_CALL_CORRECT. */
+kvc_status kvc_correct_hop(const void* k_src, const void* v_src, void* k_out, void* v_out,
+                           kvc_dtype dtype, kvc_shape shape, int64_t p_src, int64_t p_tgt,
+                           const kvc_rope* rope, const kvc_pool* pool,
+                           const kvc_params* params, kvc_match_out* out, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/* One hop of a batch (chained corrections, Eq. 6 and App. A.3 "Cache Materialization"). */
+typedef struct {
+  const void* k_src;   /* ignored when chain_prev >= 0                                     */
+  const void* v_src;
+  void* k_out;
+  void* v_out;
+  int64_t p_src;       /* start position of the source segment                             */
+  int64_t p_tgt;       /* start position in the target agent                               */
+  int32_t chain_prev;  /* index (< this hop's) whose output is this hop's source, or -1    */
+  int32_t pad_;
+  kvc_pool pool;
+  kvc_match_out out;   /* s_cov may be NULL                                                 */
+} kvc_hop_desc;
+
+/* Runs n_hops corrections in dependency order on one stream.  A hop whose predecessor is
+ * flagged is still computed and gets KVC_FLAG_PRED_FLAGGED.  Workspace: the maximum of
+ * kvc_workspace_size(KVC_CALL_CORRECT, ...) over the hops. */
+kvc_status kvc_correct_hops_batched(const kvc_hop_desc* hops, int32_t n_hops, kvc_dtype dtype,
+                                    kvc_shape shape, const kvc_rope* rope,
+                                    const kvc_params* params, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/* Rank-r factorisation of n_mats fp32 matrices z [n_mats][rows][cols] (Eq. 7, App. B.1):
+ * z ~ A B with A = U_r Sigma_r [n_mats][rows][rank] and B = R_r^T [n_mats][rank][cols],
+ * sigma_out [n_mats][rank] (device float).  Randomised subspace iteration with `oversample`
+ * extra columns and `power_iters` power iterations, seeded by `seed`; each component's
+ * sign is fixed so the largest-magnitude entry of its left singular vector is positive.
+ * a_out/b_out dtype out_t.  Workspace: kvc_svd_workspace_size. */
+size_t kvc_svd_workspace_size(int32_t n_mats, int32_t rows, int32_t cols, int32_t rank,
+                              int32_t oversample);
+kvc_status kvc_anchor_refresh_svd(const float* z, int32_t n_mats, int32_t rows, int32_t cols,
+                                  int32_t rank, void* a_out, void* b_out, kvc_dtype out_t,
+                                  float* sigma_out, int32_t oversample, int32_t power_iters,
+                                  uint64_t seed, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H_ */

@@ -1,0 +1,116 @@
+// Reliability gate finalisation (KVCMAS App. A.3 "Reliability Gate", Eq. 9-11).
+//
+// Per-tile fp32 partial sums from the scoring kernels are reduced in double precision in a
+// fixed order (tiles, then layers), so distances, entropies and flags are bit-reproducible.
+//   PAGES:  d_v = sqrt(sum_l sum_{t<k} ||V - A_v B_v||^2)            (Eq. 9)
+//           g = softmax(-d / T)                                       (Eq. 10)
+//           H = -sum g log2 g / log2 |A_k|                            (Eq. 11)
+//           accept iff H <= tau; |A_k| < 2 flags; capacity 1 bypasses (App. C.3)
+//   COS_R:  cos_v = sum <P, A> / sqrt(sum |P|^2 sum |A|^2) over values, prefix k;
+//           flagged when the best cosine is below tau.
+// Row 0 is the hop (sums over all layers); row 1 + l restricts the sums to layer l.
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kMaxLayersGate = 256;
+
+__global__ void __launch_bounds__(1024) gate_finalize(GateArgs p) {
+  extern __shared__ double sh[];            // [3][1 + N_l][N]
+  const int N = p.N, L = p.n_layers;
+  const int rows = 1 + L;
+  const int64_t plane_in = (int64_t)L * p.n_tiles * N;
+  const int planes = p.mode == KVC_SCORE_PAGES ? 1 : 3;
+  // 1) per (layer, anchor): fixed-order sum over tiles
+  for (int i = threadIdx.x; i < L * N; i += blockDim.x) {
+    const int l = i / N, a = i % N;
+    for (int pl = 0; pl < planes; ++pl) {
+      double s = 0.0;
+      if ((p.mask_gate >> a) & 1) {
+        const float* src = p.partials + pl * plane_in + (int64_t)l * p.n_tiles * N + a;
+        for (int t = 0; t < p.n_tiles; ++t) s += (double)src[(int64_t)t * N];
+      }
+      sh[(pl * rows + 1 + l) * N + a] = s;
+    }
+  }
+  __syncthreads();
+  // 2) hop row: fixed-order sum over layers
+  for (int i = threadIdx.x; i < planes * N; i += blockDim.x) {
+    const int pl = i / N, a = i % N;
+    double s = 0.0;
+    for (int l = 0; l < L; ++l) s += sh[(pl * rows + 1 + l) * N + a];
+    sh[(pl * rows + 0) * N + a] = s;
+  }
+  __syncthreads();
+  // 3) one thread per row: decision
+  for (int row = threadIdx.x; row < rows; row += blockDim.x) {
+    int n_gate = 0;
+    for (int a = 0; a < N; ++a) n_gate += (int)((p.mask_gate >> a) & 1);
+    double* dist = p.dist + (int64_t)row * N;
+    int flag = 0;
+    double stat = __builtin_nan("");
+    if (p.mode == KVC_SCORE_PAGES) {
+      double dmin = INFINITY;
+      for (int a = 0; a < N; ++a) {
+        if ((p.mask_gate >> a) & 1) {
+          const double d = sqrt(sh[(0 * rows + row) * N + a]);
+          dist[a] = d;
+          dmin = fmin(dmin, d);
+        } else {
+          dist[a] = __builtin_nan("");
+        }
+      }
+      if (n_gate >= 2) {
+        double z = 0.0;
+        for (int a = 0; a < N; ++a)
+          if ((p.mask_gate >> a) & 1) z += exp(-(dist[a] - dmin) / p.temp_gate);
+        double hsum = 0.0;
+        for (int a = 0; a < N; ++a) {
+          if (!((p.mask_gate >> a) & 1)) continue;
+          const double g = exp(-(dist[a] - dmin) / p.temp_gate) / z;
+          if (g > 0.0) hsum -= g * log2(g);
+        }
+        stat = hsum / log2((double)n_gate);
+      }
+      if (N == 0) flag = KVC_FLAG_FEW_ANCHORS;
+      else if (p.capacity == 1) flag = 0;
+      else if (n_gate < 2) flag = KVC_FLAG_FEW_ANCHORS;
+      else flag = stat > p.tau ? KVC_FLAG_ENTROPY : 0;
+    } else {
+      double best = -INFINITY;
+      for (int a = 0; a < N; ++a) {
+        if ((p.mask_gate >> a) & 1) {
+          const double pa = sh[(0 * rows + row) * N + a];
+          const double pp = sh[(1 * rows + row) * N + a];
+          const double aa = sh[(2 * rows + row) * N + a];
+          const double den = sqrt(pp * aa);
+          const double c = den > 0.0 ? pa / den : 0.0;
+          dist[a] = c;
+          best = fmax(best, c);
+        } else {
+          dist[a] = __builtin_nan("");
+        }
+      }
+      if (n_gate > 0) stat = best;
+      if (N == 0) flag = KVC_FLAG_FEW_ANCHORS;
+      else if (p.capacity == 1) flag = 0;
+      else if (n_gate == 0) flag = KVC_FLAG_FEW_ANCHORS;
+      else flag = best < p.tau ? KVC_FLAG_COS_BELOW : 0;
+    }
+    if (p.pred_flags != nullptr && p.pred_flags[0] != 0) flag |= KVC_FLAG_PRED_FLAGGED;
+    p.stat[row] = stat;
+    p.flags[row] = flag;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t st) {
+  const size_t shmem = sizeof(double) * 3 * (1 + a.n_layers) * (a.N > 0 ? a.N : 1);
+  if (a.n_layers > kMaxLayersGate || shmem > 160 * 1024) return hipErrorInvalidValue;
+  gate_finalize<<<1, 1024, shmem, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,677 @@
+// Host side of libkvc: argument validation, per-hop rotation tables, anchor-set logic,
+// workspace planning and kernel launches behind the C ABI of include/kvc.h.
+//
+// Anchor sets follow KVCMAS (arXiv 2609.34060) App. A.3 "Variable Segment Lengths":
+//   gate set A_k   = anchors whose stored length >= k (k = gate_len, 0 -> S)
+//   coverage S_cov = min(S, longest stored length)
+//   correction set = anchors whose stored length >= S_cov
+// Rows >= S_cov keep the re-aligned source.  Rotation angles are evaluated in double
+// precision here and handed to the kernels as float cos/sin tables.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvc_status fail(kvc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+kvc_status ok() {
+  g_err[0] = 0;
+  return KVC_OK;
+}
+
+size_t esize(kvc_dtype t) { return t == KVC_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+kvc_status check_shape(const kvc_shape& s) {
+  if (s.n_layers < 1 || s.seq_len < 1 || s.n_kv_heads < 1)
+    return fail(KVC_E_SHAPE, "shape: n_layers, seq_len and n_kv_heads must be >= 1 (got %d, %d, %d)", s.n_layers,
+                s.seq_len, s.n_kv_heads);
+  if (s.head_dim < 2 || (s.head_dim & 1) || s.head_dim > KVC_MAX_HEAD_DIM)
+    return fail(KVC_E_SHAPE, "shape: head_dim must be even and in [2, %d] (got %d)", KVC_MAX_HEAD_DIM, s.head_dim);
+  if ((int64_t)s.n_kv_heads * s.head_dim > 65536)
+    return fail(KVC_E_SHAPE, "shape: n_kv_heads * head_dim > 65536");
+  if ((int64_t)s.n_layers > 256) return fail(KVC_E_SHAPE, "shape: n_layers > 256");
+  return KVC_OK;
+}
+
+kvc_status check_dtype(kvc_dtype t, const char* what) {
+  if (t != KVC_F32 && t != KVC_BF16) return fail(KVC_E_DTYPE, "%s: unknown dtype %d", what, (int)t);
+  return KVC_OK;
+}
+
+kvc_status make_tab(RopeTab& tab, int64_t dp, int head_dim, const kvc_rope* rope) {
+  memset(&tab, 0, sizeof tab);
+  tab.active = dp != 0;
+  const int h = head_dim / 2;
+  for (int c = 0; c < h; ++c) {
+    double w;
+    if (rope->inv_freq) {
+      w = rope->inv_freq[c];
+    } else {
+      w = pow(rope->theta, -2.0 * (double)c / (double)head_dim);
+    }
+    if (!std::isfinite(w)) return fail(KVC_E_PARAM, "rope: non-finite frequency at pair %d", c);
+    const double phi = (double)dp * w;
+    tab.cs[c] = (float)cos(phi);
+    tab.sn[c] = (float)sin(phi);
+  }
+  return KVC_OK;
+}
+
+kvc_status check_rope(const kvc_rope* rope) {
+  if (!rope) return fail(KVC_E_NULL, "rope descriptor is NULL");
+  if (!rope->inv_freq && !(rope->theta > 0.0 && std::isfinite(rope->theta)))
+    return fail(KVC_E_PARAM, "rope: theta must be positive and finite when inv_freq is NULL");
+  return KVC_OK;
+}
+
+struct Sets {
+  int k = 0, s_cov = 0;
+  uint64_t gate = 0, corr = 0;
+  int n_gate = 0;
+  std::vector<int> corr_list, use_list;
+};
+
+Sets anchor_sets(const kvc_pool& p, int S, int gate_len) {
+  Sets s;
+  s.k = gate_len == 0 ? S : gate_len;
+  int maxlen = 0;
+  for (int a = 0; a < p.n_anchors; ++a) maxlen = std::max(maxlen, (int)p.anchor_len[a]);
+  s.s_cov = p.n_anchors ? std::min(S, maxlen) : 0;
+  for (int a = 0; a < p.n_anchors; ++a) {
+    const int len = p.anchor_len[a];
+    if (len >= s.k) { s.gate |= 1ull << a; ++s.n_gate; }
+    if (p.n_anchors && len >= s.s_cov) { s.corr |= 1ull << a; s.corr_list.push_back(a); }
+    if ((s.gate | s.corr) >> a & 1) s.use_list.push_back(a);
+  }
+  return s;
+}
+
+kvc_status check_pool(const kvc_pool* p, const kvc_shape& sh, kvc_dtype cache_t, bool need_base, bool need_delta) {
+  if (!p) return fail(KVC_E_NULL, "pool descriptor is NULL");
+  if (p->n_anchors < 0 || p->n_anchors > KVC_MAX_ANCHORS)
+    return fail(KVC_E_SHAPE, "pool: n_anchors must be in [0, %d] (got %d)", KVC_MAX_ANCHORS, p->n_anchors);
+  if (p->rank_base < 1 || p->rank_base > 1024 || p->rank_delta < 1 || p->rank_delta > 1024)
+    return fail(KVC_E_SHAPE, "pool: ranks must be in [1, 1024] (got %d, %d)", p->rank_base, p->rank_delta);
+  if (p->capacity < 0 || (p->capacity > 0 && p->capacity < p->n_anchors))
+    return fail(KVC_E_PARAM, "pool: capacity must be 0 or >= n_anchors");
+  if (p->dtype != cache_t) return fail(KVC_E_DTYPE, "pool dtype %d differs from cache dtype %d", p->dtype, cache_t);
+  if (p->n_anchors == 0) return KVC_OK;
+  if (!p->anchor_len) return fail(KVC_E_NULL, "pool: anchor_len is NULL");
+  int64_t tot = 0;
+  for (int a = 0; a < p->n_anchors; ++a) {
+    if (p->anchor_len[a] < 1) return fail(KVC_E_SHAPE, "pool: anchor_len[%d] = %d < 1", a, p->anchor_len[a]);
+    tot += p->anchor_len[a];
+  }
+  if (tot * std::max(p->rank_base, p->rank_delta) >= (1ll << 40)) return fail(KVC_E_SHAPE, "pool: too many rows");
+  const void* ptrs[8] = {p->baseA_k, p->baseB_k, p->baseA_v, p->baseB_v,
+                         p->deltaA_k, p->deltaB_k, p->deltaA_v, p->deltaB_v};
+  static const char* names[8] = {"baseA_k", "baseB_k", "baseA_v", "baseB_v",
+                                 "deltaA_k", "deltaB_k", "deltaA_v", "deltaB_v"};
+  for (int i = 0; i < 8; ++i) {
+    if ((i < 4 && !need_base) || (i >= 4 && !need_delta)) continue;
+    if (!ptrs[i]) return fail(KVC_E_NULL, "pool: %s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(KVC_E_ALIGN, "pool: %s is not 16-byte aligned", names[i]);
+  }
+  (void)sh;
+  return KVC_OK;
+}
+
+kvc_status check_params(const kvc_params* prm, int S) {
+  if (!prm) return fail(KVC_E_NULL, "params is NULL");
+  if (!std::isfinite(prm->tau)) return fail(KVC_E_PARAM, "params: tau must be finite");
+  if (!(prm->temp_gate > 0.0) || !std::isfinite(prm->temp_gate))
+    return fail(KVC_E_PARAM, "params: temp_gate must be > 0");
+  if (!(prm->temp_weight > 0.0) || !std::isfinite(prm->temp_weight))
+    return fail(KVC_E_PARAM, "params: temp_weight must be > 0");
+  if (prm->gate_len < 0 || prm->gate_len > S) return fail(KVC_E_PARAM, "params: gate_len must be in [0, seq_len]");
+  if (prm->mode != KVC_SCORE_PAGES && prm->mode != KVC_SCORE_COS_R)
+    return fail(KVC_E_PARAM, "params: unknown mode %d", prm->mode);
+  if (prm->options & ~1) return fail(KVC_E_PARAM, "params: unknown option bits 0x%x", prm->options);
+  if (prm->trace) {
+    const kvc_trace* t = prm->trace;
+    if (t->capacity < 0 || t->capacity > KVC_TRACE_MAX || t->count < 0)
+      return fail(KVC_E_PARAM, "params: trace capacity must be in [0, %d]", KVC_TRACE_MAX);
+    for (int i = t->count; i < t->capacity; ++i)
+      if (!t->start[i] || !t->stop[i]) return fail(KVC_E_NULL, "params: trace event %d is NULL", i);
+  }
+  return KVC_OK;
+}
+
+// ---------------------------------------------------------------- path selection
+int32_t D_of(const kvc_shape& s) { return s.n_kv_heads * s.head_dim; }
+bool pow2_rank(int r, int lo) { return r == lo || r == 2 * lo || r == 4 * lo || r == 8 * lo; }
+
+bool mfma_score_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, int n_use) {
+  if (p.dtype != KVC_BF16 || (prm.options & 1)) return false;
+  const int D = D_of(sh);
+  if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 128 || D > 1024) return false;
+  if (prm.mode == KVC_SCORE_PAGES) {
+    if (!(p.rank_base == 16 || pow2_rank(p.rank_base, 16))) return false;
+    const size_t lds = sizeof(float) * (size_t)(D / 128) * 65 * std::max(n_use, 1);
+    return lds <= 150 * 1024;
+  }
+  return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
+}
+
+bool mfma_apply_ok(const kvc_shape& sh, const kvc_pool& p, int options) {
+  if (p.dtype != KVC_BF16 || (options & 1)) return false;
+  const int D = D_of(sh);
+  if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 128) return false;
+  if (!(p.rank_delta == 16 || pow2_rank(p.rank_delta, 16))) return false;
+  const size_t lds = sizeof(float) * 128 * p.n_anchors + 2 * 2 * 128 * (size_t)(p.rank_delta + 8);
+  return lds <= 150 * 1024;
+}
+
+// ------------------------------------------------------------------- workspace
+struct Plan {
+  bool score_mfma = false, apply_mfma = false;
+  int tile = 0, n_tiles = 0, s_work = 0, generic_tt = 0;
+  size_t off_scores = 0, off_partials = 0, off_bt_base = 0, off_bt_delta = 0, total = 0;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* prm, const Sets& s) {
+  Plan pl;
+  const int S = sh.seq_len, D = D_of(sh), L = sh.n_layers, N = std::max(p.n_anchors, 1);
+  kvc_params dflt = {0.3, 1.0, 1.0, 0, KVC_SCORE_PAGES, 0, 0, nullptr};
+  const kvc_params& P = prm ? *prm : dflt;
+  const bool do_match = call == KVC_CALL_MATCH || call == KVC_CALL_CORRECT;
+  const bool do_apply = call == KVC_CALL_APPLY || call == KVC_CALL_CORRECT;
+  size_t off = 0;
+  if (do_match) {
+    const int n_use = (int)s.use_list.size();
+    pl.s_work = s.n_gate ? std::max(s.s_cov, s.k) : s.s_cov;
+    pl.score_mfma = mfma_score_ok(sh, p, P, n_use);
+    if (pl.score_mfma) {
+      pl.tile = P.mode == KVC_SCORE_PAGES ? kPagesTile : kCosTile;
+    } else {
+      pl.generic_tt = std::max(1, 256 / std::max(n_use, 1));
+      pl.tile = pl.generic_tt;
+    }
+    pl.n_tiles = pl.s_work > 0 ? (pl.s_work + pl.tile - 1) / pl.tile : 0;
+    pl.off_scores = off;
+    off += up256(sizeof(float) * 2 * (size_t)L * S * N);
+    pl.off_partials = off;
+    off += up256(sizeof(float) * 3 * (size_t)L * std::max(pl.n_tiles, 1) * N);
+    if (pl.score_mfma && P.mode == KVC_SCORE_PAGES) {
+      pl.off_bt_base = off;
+      off += up256(2 * 2 * (size_t)L * N * D * p.rank_base);
+    }
+  }
+  if (do_apply) {
+    pl.apply_mfma = mfma_apply_ok(sh, p, P.options);
+    if (pl.apply_mfma) {
+      pl.off_bt_delta = off;
+      off += up256(2 * 2 * (size_t)L * N * D * p.rank_delta);
+    }
+  }
+  pl.total = off;
+  return pl;
+}
+
+hipError_t transpose_pair(const void* k, const void* v, uint16_t* dst, int negate, const kvc_shape& sh,
+                          const kvc_pool& p, int r, hipStream_t st) {
+  const size_t per = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * r;
+  const uint16_t* src[2] = {(const uint16_t*)k, (const uint16_t*)v};
+  uint16_t* dsts[2] = {dst, dst + per};
+  const int neg[2] = {negate, negate};
+  return launch_transpose_b(src, dsts, 2, neg, sh.n_layers, p.n_anchors, r, D_of(sh), st);
+}
+
+PoolGeom geom(const kvc_pool& p, const kvc_shape& sh, int r) {
+  PoolGeom g;
+  memset(&g, 0, sizeof g);
+  g.n = p.n_anchors;
+  g.r = r;
+  int64_t tot = 0;
+  for (int a = 0; a < p.n_anchors; ++a) {
+    g.off[a] = (int32_t)tot;
+    g.len[a] = p.anchor_len[a];
+    tot += p.anchor_len[a];
+  }
+  g.a_layer_stride = tot * r;
+  g.b_layer_stride = (int64_t)p.n_anchors * r * D_of(sh);
+  return g;
+}
+
+// Brackets one launch with the caller's trace events (if any).
+struct Tracer {
+  kvc_trace* t;
+  hipStream_t st;
+  int slot = -1;
+  void begin(int id) {
+    slot = -1;
+    if (!t || t->count >= t->capacity || t->count >= KVC_TRACE_MAX) return;
+    slot = t->count++;
+    t->kernel_id[slot] = id;
+    hipEventRecord((hipEvent_t)t->start[slot], st);
+  }
+  void end() {
+    if (slot >= 0) hipEventRecord((hipEvent_t)t->stop[slot], st);
+    slot = -1;
+  }
+};
+
+kvc_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Match: scores -> gate -> weights.  w_out[2] receive the weights (may be workspace).
+kvc_status run_match(const void* k_src, const void* v_src, const kvc_shape& sh, int64_t p_src, const kvc_rope* rope,
+                     const kvc_pool& p, const kvc_params& prm, const Sets& s, const Plan& pl, char* ws,
+                     kvc_match_out* out, float* w_out[2], const int32_t* pred_flags, hipStream_t st) {
+  hipError_t e;
+  Tracer tr{prm.trace, st};
+  const int L = sh.n_layers, S = sh.seq_len, D = D_of(sh);
+  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  float* partials = reinterpret_cast<float*>(ws + pl.off_partials);
+  const int n_use = (int)s.use_list.size();
+  if (n_use > 0 && pl.n_tiles > 0) {
+    ScoreArgs a;
+    memset(&a, 0, sizeof a);
+    a.z[0] = k_src; a.z[1] = v_src;
+    a.A[0] = p.baseA_k; a.A[1] = p.baseA_v;
+    a.B[0] = p.baseB_k; a.B[1] = p.baseB_v;
+    a.scores = scores;
+    a.partials = partials;
+    a.n_layers = L; a.S = S; a.D = D; a.head_dim = sh.head_dim;
+    a.s_cov = s.s_cov; a.k_gate = s.k; a.s_work = pl.s_work; a.n_tiles = pl.n_tiles;
+    a.mask_corr = s.corr; a.mask_gate = s.gate;
+    a.n_use = n_use;
+    for (int i = 0; i < n_use; ++i) a.use[i] = s.use_list[i];
+    a.g = geom(p, sh, p.rank_base);
+    kvc_status st2 = make_tab(a.can, -p_src, sh.head_dim, rope);
+    if (st2 != KVC_OK) return st2;
+    if (pl.score_mfma && prm.mode == KVC_SCORE_PAGES) {
+      uint16_t* bt = reinterpret_cast<uint16_t*>(ws + pl.off_bt_base);
+      tr.begin(KVC_K_TRANSPOSE_BASE);
+      e = transpose_pair(p.baseB_k, p.baseB_v, bt, 1, sh, p, p.rank_base, st);
+      tr.end();
+      if (e != hipSuccess) return hip_fail(e, "transpose base factors");
+      a.Bt[0] = bt;
+      a.Bt[1] = bt + (size_t)L * p.n_anchors * D * p.rank_base;
+      tr.begin(KVC_K_SCORE_PAGES);
+      e = launch_score_pages_mfma(a, st);
+    } else if (pl.score_mfma) {
+      tr.begin(KVC_K_SCORE_COS);
+      e = launch_score_cos_mfma(a, st);
+    } else {
+      tr.begin(KVC_K_SCORE_GENERIC);
+      e = launch_score_generic(a, p.dtype == KVC_BF16, prm.mode, pl.generic_tt, st);
+    }
+    tr.end();
+    if (e != hipSuccess) return hip_fail(e, "score kernel");
+  }
+  GateArgs g;
+  memset(&g, 0, sizeof g);
+  g.partials = partials;
+  g.dist = out->dist; g.stat = out->stat; g.flags = out->flags;
+  g.pred_flags = pred_flags;
+  g.n_layers = L; g.n_tiles = pl.n_tiles; g.N = p.n_anchors; g.mode = prm.mode;
+  g.capacity = p.capacity == 0 ? p.n_anchors : p.capacity;
+  g.mask_gate = s.gate; g.tau = prm.tau; g.temp_gate = prm.temp_gate;
+  tr.begin(KVC_K_GATE);
+  e = launch_gate(g, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "gate kernel");
+  if (p.n_anchors > 0) {
+    SoftmaxArgs m;
+    memset(&m, 0, sizeof m);
+    m.scores = scores;
+    m.w[0] = w_out[0]; m.w[1] = w_out[1];
+    m.n_layers = L; m.S = S; m.N = p.n_anchors; m.s_cov = s.s_cov; m.mode = prm.mode;
+    m.mask_corr = s.corr;
+    m.inv_temp = (float)(1.0 / prm.temp_weight);
+    tr.begin(KVC_K_SOFTMAX);
+    e = launch_softmax(m, st);
+    tr.end();
+    if (e != hipSuccess) return hip_fail(e, "softmax kernel");
+  }
+  if (out->s_cov) *out->s_cov = s.s_cov;
+  return KVC_OK;
+}
+
+kvc_status run_apply(const void* k_src, const void* v_src, void* k_out, void* v_out, const kvc_shape& sh,
+                     int64_t p_src, int64_t p_tgt, const kvc_rope* rope, const kvc_pool& p, const float* w_k,
+                     const float* w_v, int s_cov, const std::vector<int>& corr, const Plan& pl, char* ws,
+                     hipStream_t st, kvc_trace* trace = nullptr) {
+  hipError_t e;
+  Tracer tr{trace, st};
+  ApplyArgs a;
+  memset(&a, 0, sizeof a);
+  const int L = sh.n_layers, D = D_of(sh);
+  a.z[0] = k_src; a.z[1] = v_src;
+  a.out[0] = k_out; a.out[1] = v_out;
+  a.A[0] = p.deltaA_k; a.A[1] = p.deltaA_v;
+  a.B[0] = p.deltaB_k; a.B[1] = p.deltaB_v;
+  a.w[0] = w_k; a.w[1] = w_v;
+  a.n_layers = L; a.S = sh.seq_len; a.D = D; a.head_dim = sh.head_dim; a.s_cov = s_cov;
+  a.n_corr = (int)corr.size();
+  for (int i = 0; i < a.n_corr; ++i) a.corr[i] = corr[i];
+  a.g = geom(p, sh, p.rank_delta);
+  kvc_status s2 = make_tab(a.shift, p_tgt - p_src, sh.head_dim, rope);
+  if (s2 != KVC_OK) return s2;
+  if ((s2 = make_tab(a.tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return s2;
+  if (pl.apply_mfma) {
+    uint16_t* bt = reinterpret_cast<uint16_t*>(ws + pl.off_bt_delta);
+    if (p.n_anchors > 0) {
+      tr.begin(KVC_K_TRANSPOSE_DELTA);
+      e = transpose_pair(p.deltaB_k, p.deltaB_v, bt, 0, sh, p, p.rank_delta, st);
+      tr.end();
+      if (e != hipSuccess) return hip_fail(e, "transpose delta factors");
+    }
+    a.Bt[0] = bt;
+    a.Bt[1] = bt + (size_t)L * p.n_anchors * D * p.rank_delta;
+    tr.begin(KVC_K_APPLY);
+    e = launch_apply_mfma(a, st);
+  } else {
+    tr.begin(KVC_K_APPLY_GENERIC);
+    e = launch_apply_generic(a, p.dtype == KVC_BF16, st);
+  }
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "apply kernel");
+  return KVC_OK;
+}
+
+kvc_status check_cache(const void* k, const void* v, const char* nk, const char* nv) {
+  if (!k) return fail(KVC_E_NULL, "%s is NULL", nk);
+  if (!v) return fail(KVC_E_NULL, "%s is NULL", nv);
+  if (!aligned16(k)) return fail(KVC_E_ALIGN, "%s is not 16-byte aligned", nk);
+  if (!aligned16(v)) return fail(KVC_E_ALIGN, "%s is not 16-byte aligned", nv);
+  return KVC_OK;
+}
+
+kvc_status check_match_out(const kvc_match_out* out, const kvc_shape& sh, const kvc_pool& p) {
+  if (!out) return fail(KVC_E_NULL, "match output descriptor is NULL");
+  if (!out->dist || !out->stat || !out->flags) return fail(KVC_E_NULL, "match output: dist/stat/flags must be set");
+  (void)sh;
+  (void)p;
+  return KVC_OK;
+}
+
+// Full validation of one correct-hop request (no launches).
+struct HopReq {
+  const void *k_src, *v_src;
+  void *k_out, *v_out;
+  int64_t p_src, p_tgt;
+  const kvc_pool* pool;
+  kvc_match_out* out;
+};
+
+kvc_status validate_hop(const HopReq& h, kvc_dtype dt, const kvc_shape& sh, const kvc_rope* rope,
+                        const kvc_params* prm, bool check_src) {
+  kvc_status s;
+  if ((s = check_dtype(dt, "cache")) != KVC_OK) return s;
+  if ((s = check_shape(sh)) != KVC_OK) return s;
+  if ((s = check_rope(rope)) != KVC_OK) return s;
+  if ((s = check_params(prm, sh.seq_len)) != KVC_OK) return s;
+  if ((s = check_pool(h.pool, sh, dt, true, true)) != KVC_OK) return s;
+  if (check_src && (s = check_cache(h.k_src, h.v_src, "k_src", "v_src")) != KVC_OK) return s;
+  if ((s = check_cache(h.k_out, h.v_out, "k_out", "v_out")) != KVC_OK) return s;
+  if ((s = check_match_out(h.out, sh, *h.pool)) != KVC_OK) return s;
+  const size_t bytes = (size_t)sh.n_layers * sh.seq_len * D_of(sh) * esize(dt);
+  if (overlaps(h.k_out, bytes, h.v_out, bytes)) return fail(KVC_E_ALIAS, "k_out overlaps v_out");
+  if (check_src) {
+    const void* srcs[2] = {h.k_src, h.v_src};
+    const void* outs[2] = {h.k_out, h.v_out};
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
+        if (overlaps(outs[i], bytes, srcs[j], bytes))
+          return fail(KVC_E_ALIAS, "output %s overlaps source %s", i ? "v_out" : "k_out", j ? "v_src" : "k_src");
+  }
+  return KVC_OK;
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_str(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_E_NULL: return "null pointer";
+    case KVC_E_SHAPE: return "bad shape";
+    case KVC_E_DTYPE: return "bad dtype";
+    case KVC_E_ALIGN: return "misaligned pointer";
+    case KVC_E_ALIAS: return "output aliases input";
+    case KVC_E_WORKSPACE: return "workspace too small";
+    case KVC_E_HIP: return "HIP runtime error";
+    case KVC_E_PARAM: return "bad parameter";
+    case KVC_E_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* kvc_last_error(void) { return g_err; }
+
+size_t kvc_workspace_size(int32_t call, kvc_shape shape, const kvc_pool* pool, const kvc_params* params) {
+  if (call != KVC_CALL_MATCH && call != KVC_CALL_APPLY && call != KVC_CALL_CORRECT) return 0;
+  if (check_shape(shape) != KVC_OK || !pool || pool->n_anchors < 0 || pool->n_anchors > KVC_MAX_ANCHORS) return 0;
+  if (pool->n_anchors > 0 && !pool->anchor_len) return 0;
+  for (int a = 0; a < pool->n_anchors; ++a)
+    if (pool->anchor_len[a] < 1) return 0;
+  const int gl = params ? params->gate_len : 0;
+  Sets s = anchor_sets(*pool, shape.seq_len, gl);
+  return plan(call, shape, *pool, params, s).total;
+}
+
+kvc_status kvc_align_rope(const void* k_in, void* k_out, kvc_dtype in_t, kvc_dtype out_t, kvc_shape shape,
+                          int64_t pos_from, int64_t pos_to, const kvc_rope* rope, void* stream) {
+  kvc_status s;
+  if ((s = check_dtype(in_t, "in_t")) != KVC_OK) return s;
+  if ((s = check_dtype(out_t, "out_t")) != KVC_OK) return s;
+  if ((s = check_shape(shape)) != KVC_OK) return s;
+  if ((s = check_rope(rope)) != KVC_OK) return s;
+  if (!k_in || !k_out) return fail(KVC_E_NULL, "k_in/k_out is NULL");
+  if (!aligned16(k_in) || !aligned16(k_out)) return fail(KVC_E_ALIGN, "k_in/k_out not 16-byte aligned");
+  const size_t n = (size_t)shape.n_layers * shape.seq_len * D_of(shape);
+  const size_t bi = n * esize(in_t), bo = n * esize(out_t);
+  if (k_in == k_out) {
+    if (in_t != out_t) return fail(KVC_E_ALIAS, "in-place re-alignment needs in_t == out_t");
+  } else if (overlaps(k_in, bi, k_out, bo)) {
+    return fail(KVC_E_ALIAS, "k_out partially overlaps k_in");
+  }
+  RopeTab tab;
+  if ((s = make_tab(tab, pos_to - pos_from, shape.head_dim, rope)) != KVC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (!tab.active && k_in == k_out) return ok();
+  hipError_t e = launch_align(k_in, k_out, in_t == KVC_BF16, out_t == KVC_BF16,
+                              (int64_t)shape.n_layers * shape.seq_len, shape.n_kv_heads, shape.head_dim, tab, st);
+  if (e != hipSuccess) return hip_fail(e, "align kernel");
+  return ok();
+}
+
+kvc_status kvc_match_anchors(const void* k_src, const void* v_src, kvc_dtype dtype, kvc_shape shape, int64_t p_src,
+                             const kvc_rope* rope, const kvc_pool* pool, const kvc_params* params,
+                             kvc_match_out* out, void* workspace, size_t ws_bytes, void* stream) {
+  kvc_status s;
+  if ((s = check_dtype(dtype, "cache")) != KVC_OK) return s;
+  if ((s = check_shape(shape)) != KVC_OK) return s;
+  if ((s = check_rope(rope)) != KVC_OK) return s;
+  if ((s = check_params(params, shape.seq_len)) != KVC_OK) return s;
+  if ((s = check_pool(pool, shape, dtype, true, false)) != KVC_OK) return s;
+  if ((s = check_cache(k_src, v_src, "k_src", "v_src")) != KVC_OK) return s;
+  if ((s = check_match_out(out, shape, *pool)) != KVC_OK) return s;
+  const size_t wbytes = sizeof(float) * (size_t)shape.n_layers * shape.seq_len * pool->n_anchors;
+  if ((out->w_k && !aligned16(out->w_k)) || (out->w_v && !aligned16(out->w_v)))
+    return fail(KVC_E_ALIGN, "w_k/w_v not 16-byte aligned");
+  if (out->w_k && out->w_v && overlaps(out->w_k, wbytes, out->w_v, wbytes))
+    return fail(KVC_E_ALIAS, "w_k overlaps w_v");
+  Sets sets = anchor_sets(*pool, shape.seq_len, params->gate_len);
+  Plan pl = plan(KVC_CALL_MATCH, shape, *pool, params, sets);
+  if (pl.total && (!workspace || ws_bytes < pl.total))
+    return fail(KVC_E_WORKSPACE, "workspace: need %zu bytes, got %zu", pl.total, workspace ? ws_bytes : (size_t)0);
+  if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
+  char* ws = (char*)workspace;
+  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  const size_t plane = (size_t)shape.n_layers * shape.seq_len * std::max(pool->n_anchors, 1);
+  float* w_out[2] = {out->w_k ? out->w_k : scores, out->w_v ? out->w_v : scores + plane};
+  s = run_match(k_src, v_src, shape, p_src, rope, *pool, *params, sets, pl, ws, out, w_out, nullptr,
+                (hipStream_t)stream);
+  return s == KVC_OK ? ok() : s;
+}
+
+kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k_out, void* v_out, kvc_dtype dtype,
+                                   kvc_shape shape, int64_t p_src, int64_t p_tgt, const kvc_rope* rope,
+                                   const kvc_pool* pool, const float* w_k, const float* w_v, int32_t s_cov,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  kvc_status s;
+  if ((s = check_dtype(dtype, "cache")) != KVC_OK) return s;
+  if ((s = check_shape(shape)) != KVC_OK) return s;
+  if ((s = check_rope(rope)) != KVC_OK) return s;
+  if ((s = check_pool(pool, shape, dtype, false, true)) != KVC_OK) return s;
+  if ((s = check_cache(k_src, v_src, "k_src", "v_src")) != KVC_OK) return s;
+  if ((s = check_cache(k_out, v_out, "k_out", "v_out")) != KVC_OK) return s;
+  if (s_cov < 0 || s_cov > shape.seq_len) return fail(KVC_E_PARAM, "s_cov must be in [0, seq_len]");
+  if (pool->n_anchors > 0 && s_cov > 0) {
+    if (!w_k || !w_v) return fail(KVC_E_NULL, "w_k/w_v is NULL");
+    if (!aligned16(w_k) || !aligned16(w_v)) return fail(KVC_E_ALIGN, "w_k/w_v not 16-byte aligned");
+  }
+  const size_t bytes = (size_t)shape.n_layers * shape.seq_len * D_of(shape) * esize(dtype);
+  const void* srcs[2] = {k_src, v_src};
+  const void* outs[2] = {k_out, v_out};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      if (overlaps(outs[i], bytes, srcs[j], bytes))
+        return fail(KVC_E_ALIAS, "output %s overlaps source %s", i ? "v_out" : "k_out", j ? "v_src" : "k_src");
+  if (overlaps(k_out, bytes, v_out, bytes)) return fail(KVC_E_ALIAS, "k_out overlaps v_out");
+  Sets sets;
+  std::vector<int> corr;
+  if (s_cov > 0)
+    for (int a = 0; a < pool->n_anchors; ++a)
+      if (pool->anchor_len[a] >= s_cov) corr.push_back(a);
+  Plan pl = plan(KVC_CALL_APPLY, shape, *pool, nullptr, sets);
+  if (pl.total && (!workspace || ws_bytes < pl.total))
+    return fail(KVC_E_WORKSPACE, "workspace: need %zu bytes, got %zu", pl.total, workspace ? ws_bytes : (size_t)0);
+  if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
+  s = run_apply(k_src, v_src, k_out, v_out, shape, p_src, p_tgt, rope, *pool, w_k, w_v, corr.empty() ? 0 : s_cov,
+                corr, pl, (char*)workspace, (hipStream_t)stream);
+  return s == KVC_OK ? ok() : s;
+}
+
+static kvc_status correct_one(const HopReq& h, kvc_dtype dt, const kvc_shape& sh, const kvc_rope* rope,
+                              const kvc_params* prm, char* ws, size_t ws_bytes, const int32_t* pred_flags,
+                              hipStream_t st) {
+  const kvc_pool& p = *h.pool;
+  Sets sets = anchor_sets(p, sh.seq_len, prm->gate_len);
+  Plan pl = plan(KVC_CALL_CORRECT, sh, p, prm, sets);
+  if (pl.total && (!ws || ws_bytes < pl.total))
+    return fail(KVC_E_WORKSPACE, "workspace: need %zu bytes, got %zu", pl.total, ws ? ws_bytes : (size_t)0);
+  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  const size_t plane = (size_t)sh.n_layers * sh.seq_len * std::max(p.n_anchors, 1);
+  float* w_out[2] = {h.out->w_k ? h.out->w_k : scores, h.out->w_v ? h.out->w_v : scores + plane};
+  kvc_status s = run_match(h.k_src, h.v_src, sh, h.p_src, rope, p, *prm, sets, pl, ws, h.out, w_out, pred_flags, st);
+  if (s != KVC_OK) return s;
+  return run_apply(h.k_src, h.v_src, h.k_out, h.v_out, sh, h.p_src, h.p_tgt, rope, p, w_out[0], w_out[1],
+                   sets.corr_list.empty() ? 0 : sets.s_cov, sets.corr_list, pl, ws, st, prm->trace);
+}
+
+kvc_status kvc_correct_hop(const void* k_src, const void* v_src, void* k_out, void* v_out, kvc_dtype dtype,
+                           kvc_shape shape, int64_t p_src, int64_t p_tgt, const kvc_rope* rope, const kvc_pool* pool,
+                           const kvc_params* params, kvc_match_out* out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  HopReq h{k_src, v_src, k_out, v_out, p_src, p_tgt, pool, out};
+  kvc_status s = validate_hop(h, dtype, shape, rope, params, true);
+  if (s != KVC_OK) return s;
+  if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
+  s = correct_one(h, dtype, shape, rope, params, (char*)workspace, ws_bytes, nullptr, (hipStream_t)stream);
+  return s == KVC_OK ? ok() : s;
+}
+
+kvc_status kvc_correct_hops_batched(const kvc_hop_desc* hops, int32_t n_hops, kvc_dtype dtype, kvc_shape shape,
+                                    const kvc_rope* rope, const kvc_params* params, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  if (n_hops < 0) return fail(KVC_E_PARAM, "n_hops < 0");
+  if (n_hops == 0) return ok();
+  if (!hops) return fail(KVC_E_NULL, "hops is NULL");
+  if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
+  // validate everything before the first launch
+  for (int i = 0; i < n_hops; ++i) {
+    const kvc_hop_desc& d = hops[i];
+    if (d.chain_prev >= i) return fail(KVC_E_PARAM, "hop %d: chain_prev must precede the hop", i);
+    HopReq h{d.chain_prev >= 0 ? hops[d.chain_prev].k_out : d.k_src,
+             d.chain_prev >= 0 ? hops[d.chain_prev].v_out : d.v_src,
+             d.k_out, d.v_out, d.p_src, d.p_tgt, &d.pool, const_cast<kvc_match_out*>(&d.out)};
+    kvc_status s = validate_hop(h, dtype, shape, rope, params, true);
+    if (s != KVC_OK) {
+      char buf[512];
+      snprintf(buf, sizeof buf, "hop %d: %s", i, g_err);
+      return fail(s, "%s", buf);
+    }
+    Sets sets = anchor_sets(d.pool, shape.seq_len, params->gate_len);
+    const size_t need = plan(KVC_CALL_CORRECT, shape, d.pool, params, sets).total;
+    if (need && (!workspace || ws_bytes < need))
+      return fail(KVC_E_WORKSPACE, "hop %d: workspace needs %zu bytes, got %zu", i, need, workspace ? ws_bytes : (size_t)0);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  for (int i = 0; i < n_hops; ++i) {
+    const kvc_hop_desc& d = hops[i];
+    HopReq h{d.chain_prev >= 0 ? hops[d.chain_prev].k_out : d.k_src,
+             d.chain_prev >= 0 ? hops[d.chain_prev].v_out : d.v_src,
+             d.k_out, d.v_out, d.p_src, d.p_tgt, &d.pool, const_cast<kvc_match_out*>(&d.out)};
+    const int32_t* pred = d.chain_prev >= 0 ? hops[d.chain_prev].out.flags : nullptr;
+    kvc_status s = correct_one(h, dtype, shape, rope, params, (char*)workspace, ws_bytes, pred, st);
+    if (s != KVC_OK) return s;
+  }
+  return ok();
+}
+
+size_t kvc_svd_workspace_size(int32_t n_mats, int32_t rows, int32_t cols, int32_t rank, int32_t oversample) {
+  if (n_mats < 1 || rows < 1 || cols < 1 || rank < 1 || oversample < 0) return 0;
+  return svd_workspace_bytes(n_mats, rows, cols, rank, oversample);
+}
+
+kvc_status kvc_anchor_refresh_svd(const float* z, int32_t n_mats, int32_t rows, int32_t cols, int32_t rank,
+                                  void* a_out, void* b_out, kvc_dtype out_t, float* sigma_out, int32_t oversample,
+                                  int32_t power_iters, uint64_t seed, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  kvc_status s;
+  if ((s = check_dtype(out_t, "out_t")) != KVC_OK) return s;
+  if (!z || !a_out || !b_out || !sigma_out) return fail(KVC_E_NULL, "z/a_out/b_out/sigma_out is NULL");
+  if (!aligned16(z) || !aligned16(a_out) || !aligned16(b_out) || !aligned16(sigma_out))
+    return fail(KVC_E_ALIGN, "svd buffers must be 16-byte aligned");
+  if (n_mats < 1 || rows < 1 || cols < 1) return fail(KVC_E_SHAPE, "svd: n_mats, rows, cols must be >= 1");
+  if (rank < 1 || oversample < 0 || rank + oversample > std::min(rows, cols) || rank + oversample > 256)
+    return fail(KVC_E_SHAPE, "svd: need 1 <= rank, rank + oversample <= min(rows, cols, 256)");
+  if (rows % 4 || cols % 4) return fail(KVC_E_SHAPE, "svd: rows and cols must be multiples of 4");
+  if (power_iters < 0 || power_iters > 16) return fail(KVC_E_PARAM, "svd: power_iters must be in [0, 16]");
+  const size_t need = svd_workspace_bytes(n_mats, rows, cols, rank, oversample);
+  if (!workspace || ws_bytes < need) return fail(KVC_E_WORKSPACE, "svd workspace: need %zu bytes", need);
+  if (!aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
+  const size_t zb = (size_t)n_mats * rows * cols * 4;
+  if (overlaps(z, zb, a_out, (size_t)n_mats * rows * rank * esize(out_t)) ||
+      overlaps(z, zb, b_out, (size_t)n_mats * rank * cols * esize(out_t)))
+    return fail(KVC_E_ALIAS, "svd outputs overlap the input");
+  hipError_t e = svd_refresh(z, n_mats, rows, cols, rank, a_out, b_out, out_t == KVC_BF16, sigma_out, oversample,
+                             power_iters, seed, workspace, ws_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "svd refresh");
+  return ok();
+}
+
+}  // extern "C"

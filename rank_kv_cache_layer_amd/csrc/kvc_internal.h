@@ -1,0 +1,135 @@
+// Internal declarations shared by the host side of libkvc and its kernels (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kMaxAnchors = KVC_MAX_ANCHORS;
+constexpr int kMaxHalf = KVC_MAX_HEAD_DIM / 2;
+
+// cos/sin of one per-hop rotation, one entry per rotary pair c (angles evaluated on the host
+// in double precision, rounded to float).  `active` = 0 means the identity (zero shift).
+struct RopeTab {
+  float cs[kMaxHalf];
+  float sn[kMaxHalf];
+  int32_t active;
+};
+
+// Anchor pool geometry as the kernels see it.
+struct PoolGeom {
+  int32_t n;                  // anchors
+  int32_t r;                  // rank of the factor set in use
+  int64_t a_layer_stride;     // elements per layer of the packed A array (sum(len) * r)
+  int64_t b_layer_stride;     // elements per layer of the B array (n * r * D)
+  int32_t off[kMaxAnchors];   // first packed row of each anchor
+  int32_t len[kMaxAnchors];   // stored rows of each anchor
+};
+
+// ----------------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+  return __builtin_bit_cast(uint16_t, b);
+}
+template <typename T> __device__ __forceinline__ float ldf(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ldf<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+template <typename T> __device__ __forceinline__ void stf(T* p, int64_t i, float v);
+template <> __device__ __forceinline__ void stf<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+
+// Maps the hardware block index so that consecutive logical tiles run on the same XCD
+// (blocks are dealt round-robin over the 8 XCDs; each XCD has its own L2).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
+  const int64_t nx = 8;
+  if (nblk < nx) return bid;
+  const int64_t per = nblk / nx, rem = nblk % nx;
+  const int64_t x = bid % nx, i = bid / nx;
+  // first `rem` XCDs own per+1 tiles
+  const int64_t base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + i;
+}
+
+// --------------------------------------------------------------------------- launchers
+// All launchers enqueue on `st` and return hipGetLastError() of the launch.
+
+hipError_t launch_align(const void* in, void* out, int in_bf16, int out_bf16, int64_t n_rows,
+                        int n_heads, int head_dim, const RopeTab& tab, hipStream_t st);
+
+struct ScoreArgs {
+  const void* z[2];          // source K, V   [N_l][S][D]
+  const void* A[2];          // base A (K, V) packed [N_l][sum len][r]
+  const void* B[2];          // base B (K, V) [N_l][N][r][D]  (generic path)
+  const uint16_t* Bt[2];     // base B^T (K, V) [N_l][N][D][r] bf16, negated for PAGES (MFMA)
+  float* scores;             // [2][N_l][S][N]
+  float* partials;           // [3][N_l][n_tiles][N]
+  int32_t n_layers, S, D, head_dim;
+  int32_t s_cov, k_gate, s_work, n_tiles;
+  uint64_t mask_corr, mask_gate;
+  int32_t n_use;             // anchors in corr U gate, ascending
+  int32_t use[kMaxAnchors];
+  PoolGeom g;
+  RopeTab can;               // R(-p_src) for keys
+};
+
+struct SoftmaxArgs {
+  const float* scores;       // [2][N_l][S][N]
+  float* w[2];               // K, V weights [N_l][S][N]
+  int32_t n_layers, S, N, s_cov, mode;
+  uint64_t mask_corr;
+  float inv_temp;
+};
+
+struct ApplyArgs {
+  const void* z[2];          // source K, V
+  void* out[2];              // outputs K, V
+  const void* A[2];          // delta A (K, V) packed
+  const void* B[2];          // delta B (K, V) [N_l][N][r][D] (generic path)
+  const uint16_t* Bt[2];     // delta B^T [N_l][N][D][r] bf16 (MFMA path)
+  const float* w[2];         // weights [N_l][S][N]
+  int32_t n_layers, S, D, head_dim, s_cov;
+  int32_t n_corr;
+  int32_t corr[kMaxAnchors];
+  PoolGeom g;
+  RopeTab shift;             // R(p_tgt - p_src)
+  RopeTab tgt;               // R(p_tgt)
+};
+
+struct GateArgs {
+  const float* partials;     // [3][N_l][n_tiles][N]
+  double* dist;              // [1+N_l][N]
+  double* stat;              // [1+N_l]
+  int32_t* flags;            // [1+N_l]
+  const int32_t* pred_flags; // flags of the preceding hop (row 0 used) or nullptr
+  int32_t n_layers, n_tiles, N, mode, capacity;
+  uint64_t mask_gate;
+  double tau, temp_gate;
+};
+
+hipError_t launch_score_generic(const ScoreArgs& a, int bf16, int mode, int tile_tokens, hipStream_t st);
+hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
+hipError_t launch_apply_generic(const ApplyArgs& a, int bf16, hipStream_t st);
+hipError_t launch_gate(const GateArgs& a, hipStream_t st);
+
+// MFMA (bf16) path
+hipError_t launch_transpose_b(const uint16_t* const* src, uint16_t* const* dst, int n_arrays,
+                              const int* negate, int n_layers, int n_anchors, int r, int D,
+                              hipStream_t st);
+hipError_t launch_score_pages_mfma(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_score_cos_mfma(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t st);
+
+constexpr int kPagesTile = 64;    // tokens per work-group, MFMA PAGES scoring
+constexpr int kCosTile = 64;      // tokens per work-group, MFMA COS_R scoring
+constexpr int kApplyTile = 128;   // tokens per work-group, MFMA apply
+
+// SVD refresh
+hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank, void* a_out,
+                       void* b_out, int out_bf16, float* sigma, int oversample, int power_iters,
+                       uint64_t seed, void* ws, size_t ws_bytes, hipStream_t st);
+size_t svd_workspace_bytes(int n_mats, int rows, int cols, int rank, int oversample);
+
+}  // namespace kvc

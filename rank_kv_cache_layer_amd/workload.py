@@ -30,6 +30,8 @@ from __future__ import annotations
 
 import concurrent.futures as _cf
 import dataclasses
+import mmap
+import multiprocessing
 import os
 from typing import Callable, List, Optional
 
@@ -73,6 +75,7 @@ class HopSpec:
     true_delta_rank: int = 24    # 0 -> plain Gaussian delta factors (tiny workload)
     delta_rms_ratio: float = 0.1
     seed: int = 0
+    source_seed: int = -1        # seed of the source slab (-1 -> seed); a chain shares A0's
 
     @property
     def d_model(self) -> int:
@@ -158,26 +161,24 @@ def _slab(spec: HopSpec, layer: int, side: int, place_keys):
     S, D, N = spec.seq_len, spec.d_model, spec.n_anchors
     rC, rD = spec.rank_base, spec.rank_delta
     seed = spec.seed
+    sseed = spec.seed if spec.source_seed < 0 else spec.source_seed
     lens = spec.lens()
     if spec.scaled:
-        scale = _rng(seed, layer, side, _T_SCALE).uniform(0.5, 2.0, size=D)
+        scale = _rng(sseed, layer, side, _T_SCALE).uniform(0.5, 2.0, size=D)
     else:
         scale = np.ones(D)
     rms_scale = float(np.sqrt(np.mean(scale ** 2)))
     sigma_b = np.sqrt(2.0) * rms_scale
-    e = _rng(seed, layer, side, _T_E).standard_normal((S, D)) * scale[None, :]
+    e = _rng(sseed, layer, side, _T_E).standard_normal((S, D)) * scale[None, :]
+    # the source's rank-r component; a matched layer's anchor 0 holds exactly these factors
+    a_s, b_s = _lowrank(_rng(sseed, layer, side, _T_SRCLR), S, rC, D, sigma_b)
     unrelated = spec.unrelated_layers is not None and layer in spec.unrelated_layers
     base = []
     for a in range(N):
-        base.append(_lowrank(_rng(seed, layer, side, _T_BASE, a), lens[a], rC, D, sigma_b))
-    if unrelated or N == 0:
-        a_s, b_s = _lowrank(_rng(seed, layer, side, _T_SRCLR), S, rC, D, sigma_b)
-    else:
-        a0, b_s = base[0]
-        a_s = np.zeros((S, rC))
-        a_s[: lens[0]] = a0
-        if lens[0] < S:
-            a_s[lens[0]:] = _rng(seed, layer, side, _T_SRCLR).standard_normal((S - lens[0], rC)) * sigma_b
+        if a == 0 and not unrelated:
+            base.append((a_s[: lens[0]].copy(), b_s.copy()))
+        else:
+            base.append(_lowrank(_rng(seed, layer, side, _T_BASE, a), lens[a], rC, D, sigma_b))
     z = e + a_s @ b_s
     rms_src = float(np.sqrt(np.mean(z ** 2)))
     delta = []
@@ -191,43 +192,78 @@ def _slab(spec: HopSpec, layer: int, side: int, place_keys):
     return z, base, delta
 
 
+def _shared_empty(shape, dt: torch.dtype) -> torch.Tensor:
+    """Tensor in an anonymous shared mapping: writes by forked workers are seen by the parent."""
+    n = int(np.prod(shape))
+    es = torch.empty((), dtype=dt).element_size()
+    buf = mmap.mmap(-1, max(n * es, 1))
+    raw = np.frombuffer(buf, dtype=np.uint8, count=n * es)
+    return torch.from_numpy(raw).view(dt).view(shape)
+
+
+_JOB = {}
+
+
+def _one_blas_thread() -> None:
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+    torch.set_num_threads(1)
+
+
+def _fill(layer_side) -> None:
+    spec, place_keys, out, offs, lens = (_JOB[k] for k in ("spec", "place", "out", "offs", "lens"))
+    layer, side = layer_side
+    tag = "kv"[side]
+    z, base, delta = _slab(spec, layer, side, place_keys)
+    out[f"{tag}_src"][layer].copy_(torch.from_numpy(z.astype(np.float32)))
+    for a in range(spec.n_anchors):
+        o, n = offs[a], lens[a]
+        out[f"baseA_{tag}"][layer, o:o + n].copy_(torch.from_numpy(base[a][0].astype(np.float32)))
+        out[f"baseB_{tag}"][layer, a].copy_(torch.from_numpy(base[a][1].astype(np.float32)))
+        out[f"deltaA_{tag}"][layer, o:o + n].copy_(torch.from_numpy(delta[a][0].astype(np.float32)))
+        out[f"deltaB_{tag}"][layer, a].copy_(torch.from_numpy(delta[a][1].astype(np.float32)))
+
+
 def make_hop(spec: HopSpec, place_keys: Optional[Callable] = None, workers: Optional[int] = None) -> HopData:
-    """Build one hop's inputs; bit-identical for a given spec regardless of thread count."""
+    """Build one hop's inputs; bit-identical for a given spec regardless of worker count.
+
+    Large hops are filled by forked worker processes (each (layer, side) slab has its own
+    seeded stream); that path is taken only while no GPU context exists in this process."""
     S, D, N, L = spec.seq_len, spec.d_model, spec.n_anchors, spec.n_layers
     rC, rD = spec.rank_base, spec.rank_delta
     lens = spec.lens()
     offs = list(np.cumsum([0] + lens[:-1])) if N else []
     tot = int(sum(lens))
     dt = _TORCH_DT[spec.dtype]
+    nw = workers or _workers()
+    big = L * S * D >= (1 << 25)
+    use_procs = nw > 1 and big and not torch.cuda.is_initialized()
+    alloc = _shared_empty if use_procs else (lambda shp, d: torch.empty(shp, dtype=d))
     out = {}
     for side, tag in ((0, "k"), (1, "v")):
-        out[f"{tag}_src"] = torch.empty((L, S, D), dtype=dt)
-        out[f"baseA_{tag}"] = torch.empty((L, tot, rC), dtype=dt)
-        out[f"baseB_{tag}"] = torch.empty((L, N, rC, D), dtype=dt)
-        out[f"deltaA_{tag}"] = torch.empty((L, tot, rD), dtype=dt)
-        out[f"deltaB_{tag}"] = torch.empty((L, N, rD, D), dtype=dt)
-
-    def job(layer_side):
-        layer, side = layer_side
-        tag = "kv"[side]
-        z, base, delta = _slab(spec, layer, side, place_keys)
-        out[f"{tag}_src"][layer].copy_(torch.from_numpy(z.astype(np.float32)))
-        for a in range(N):
-            o, n = offs[a], lens[a]
-            out[f"baseA_{tag}"][layer, o:o + n].copy_(torch.from_numpy(base[a][0].astype(np.float32)))
-            out[f"baseB_{tag}"][layer, a].copy_(torch.from_numpy(base[a][1].astype(np.float32)))
-            out[f"deltaA_{tag}"][layer, o:o + n].copy_(torch.from_numpy(delta[a][0].astype(np.float32)))
-            out[f"deltaB_{tag}"][layer, a].copy_(torch.from_numpy(delta[a][1].astype(np.float32)))
-        return None
-
+        out[f"{tag}_src"] = alloc((L, S, D), dt)
+        out[f"baseA_{tag}"] = alloc((L, tot, rC), dt)
+        out[f"baseB_{tag}"] = alloc((L, N, rC, D), dt)
+        out[f"deltaA_{tag}"] = alloc((L, tot, rD), dt)
+        out[f"deltaB_{tag}"] = alloc((L, N, rD, D), dt)
+    _JOB.update(spec=spec, place=place_keys, out=out, offs=offs, lens=lens)
     jobs = [(l, s) for l in range(L) for s in (0, 1)]
-    nw = workers or _workers()
-    if nw == 1:
-        for j in jobs:
-            job(j)
-    else:
-        with _cf.ThreadPoolExecutor(nw) as ex:
-            list(ex.map(job, jobs))
+    try:
+        if nw == 1 or len(jobs) == 1:
+            for j in jobs:
+                _fill(j)
+        elif use_procs:
+            ctx = multiprocessing.get_context("fork")
+            with _cf.ProcessPoolExecutor(min(nw, len(jobs)), mp_context=ctx, initializer=_one_blas_thread) as ex:
+                list(ex.map(_fill, jobs))
+        else:
+            with _cf.ThreadPoolExecutor(nw) as ex:
+                list(ex.map(_fill, jobs))
+    finally:
+        _JOB.clear()
     return HopData(spec=spec, anchor_len=lens, anchor_offset=[int(o) for o in offs], **out)
 
 
@@ -279,21 +315,26 @@ def llama8b_rank128(**kw) -> HopSpec:
 
 def chain_specs(n_requests: int = 8, n_hops: int = 3, seq_len: int = 8192, n_layers: int = 32,
                 n_kv_heads: int = 8, head_dim: int = 128, seed: int = 4, **kw):
-    """Concurrent batch of chains A0 -> A1 -> ... : per hop N ~ U{10..20}, r in {16, 32},
-    shift ~ U{0..1024}; the first source sits at p0 ~ U{0..1024}."""
+    """Concurrent batch of chains A0 -> A1 -> ... : per hop N ~ U{10..20}, shift ~ U{0..1024};
+    per request r in {16, 32} (the base rank of an anchor describes the first agent's source,
+    whose rank-r component every hop's matched anchor holds); the first source sits at
+    p0 ~ U{0..1024}."""
     rng = _rng(seed, _T_MISC)
     reqs = []
+    r0 = int(kw.pop("rank", 0))
     for q in range(n_requests):
         p = int(rng.integers(0, 1025))
         hops = []
+        # every hop's matched anchor is built from the first agent's source (same source seed)
+        src_seed = seed * 1000 + q * 10
+        r = r0 or int(rng.choice([16, 32]))
         for h in range(n_hops):
             n = int(rng.integers(10, 21))
-            r = int(rng.choice([16, 32]))
             s = int(rng.integers(0, 1025))
             spec = HopSpec(name=f"chain_q{q}_h{h}", n_layers=n_layers, seq_len=seq_len,
                            n_kv_heads=n_kv_heads, head_dim=head_dim, n_anchors=n,
                            rank_base=r, rank_delta=r, dtype=BF16, p_src=p, p_tgt=p + s,
-                           tau=0.3, temp_weight=0.1, seed=seed * 1000 + q * 10 + h)
+                           tau=0.3, temp_weight=0.1, seed=src_seed + h, source_seed=src_seed)
             spec = dataclasses.replace(spec, **kw)
             hops.append(spec)
             p = p + s

@@ -1,0 +1,247 @@
+"""GPU parity of the HIP path (called through the C ABI) against the fp64 oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvc_oracle as O
+from rank_kv_cache_layer_amd import kvc
+from rank_kv_cache_layer_amd import workload as W
+
+from hop_helpers import (DEV, assert_gate_equal, assert_outputs_close, assert_weights_close, make, params,
+                         run_gpu, shape)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_hop(spec, options=0, label=""):
+    print(f"[parity] {label or spec.name} dtype={spec.dtype} L={spec.n_layers} S={spec.seq_len} "
+          f"D={spec.d_model} N={spec.n_anchors} r={spec.rank_base}/{spec.rank_delta} mode={spec.mode} "
+          f"opt={options}", flush=True)
+    data = make(spec)
+    ref = O.correct_hop(data)
+    gpu = run_gpu(data, options=options)
+    assert gpu["s_cov"] == ref["s_cov"]
+    assert_outputs_close(gpu, ref, spec.dtype, label)
+    assert_gate_equal(gpu, ref, spec.n_anchors, label, tau=spec.tau)
+    assert_weights_close(gpu, ref, spec.dtype, label)
+    return data, ref, gpu
+
+
+# ------------------------------------------------------------------------- align
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("hd", [64, 128, 96, 6])
+def test_align_rope_matches_oracle(dt, hd):
+    print(f"[parity] align dtype={dt} head_dim={hd}", flush=True)
+    g = torch.Generator().manual_seed(hd)
+    L, S, H = 3, 77, 4
+    x = torch.randn((L, S, H * hd), generator=g).to(dt)
+    out = torch.empty_like(x, device=DEV)
+    kvc.align_rope(x.to(DEV), out, kvc.shape_of(L, S, H, hd), 512, 812)
+    ref = O.round_to(O.rope(x.double().numpy(), 300, hd), "f32" if dt == torch.float32 else "bf16")
+    got = out.double().cpu().numpy()
+    tol = 1e-5 if dt == torch.float32 else 2.0 ** -7
+    assert np.max(np.abs(got - ref)) <= tol * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_align_zero_shift_bit_exact_and_in_place(dt):
+    x = torch.randn((2, 64, 256)).to(dt).to(DEV)
+    y = torch.empty_like(x)
+    kvc.align_rope(x, y, kvc.shape_of(2, 64, 2, 128), 100, 100)
+    assert torch.equal(x, y)
+    z = x.clone()
+    kvc.align_rope(z, z, kvc.shape_of(2, 64, 2, 128), 0, 37)
+    kvc.align_rope(z, z, kvc.shape_of(2, 64, 2, 128), 37, 0)
+    tol = 1e-5 if dt == torch.float32 else 2 * 2.0 ** -7
+    assert (z.float() - x.float()).abs().max().item() <= tol * x.float().abs().max().item()
+
+
+def test_align_dtype_conversion():
+    x = torch.randn((1, 32, 128))
+    y = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=DEV)
+    kvc.align_rope(x.to(DEV), y, kvc.shape_of(1, 32, 1, 128), 5, 5)
+    assert torch.equal(y.cpu(), x.to(torch.bfloat16))
+
+
+# ------------------------------------------------------------------- whole hop
+def test_tiny_fp32_hop():
+    _, ref, gpu = _check_hop(W.tiny(), label="tiny")
+    assert list(gpu["flags"]) == [0, 0, O.FLAG_ENTROPY]
+
+
+def test_tiny_fp32_cosine_mode():
+    _, ref, gpu = _check_hop(W.tiny(mode=W.SCORE_COS_R), label="tiny-cos")
+    assert list(gpu["flags"]) == [0, 0, O.FLAG_COS_BELOW]
+
+
+@pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
+@pytest.mark.parametrize("options", [0, 1])
+def test_llama_shape_reduced_bf16(mode, options):
+    # 8B shape per layer, fewer layers and a ragged token count (several tiles + tail)
+    sp = W.llama8b_hop(n_layers=3, seq_len=1000, mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+    _check_hop(sp, options=options, label=f"llama-reduced-{mode}-{options}")
+
+
+def test_unrelated_layers_flagged_bf16():
+    sp = W.llama8b_long(n_layers=3, seq_len=520, unrelated_layers=[2])
+    _, ref, gpu = _check_hop(sp, label="long-reduced")
+    assert list(gpu["flags"]) == [0, 0, 0, O.FLAG_ENTROPY]
+
+
+@pytest.mark.parametrize("rank", [16, 64, 128])
+def test_ranks_bf16(rank):
+    sp = W.llama8b_hop(n_layers=2, seq_len=300, n_anchors=6, rank_base=rank, rank_delta=rank,
+                       n_kv_heads=4)
+    _check_hop(sp, label=f"rank{rank}")
+
+
+def test_head_dim_64_bf16():
+    sp = W.llama8b_hop(n_layers=2, seq_len=200, n_kv_heads=4, head_dim=64, n_anchors=5)
+    _check_hop(sp, label="hd64")
+
+
+def test_odd_shape_bf16_generic_path():
+    sp = W.llama8b_hop(n_layers=2, seq_len=70, n_kv_heads=3, head_dim=32, n_anchors=3, rank_base=8,
+                       rank_delta=8, true_delta_rank=4)
+    _check_hop(sp, label="odd")
+
+
+def test_partial_coverage_and_gate_prefix():
+    sp = W.llama8b_hop(n_layers=2, seq_len=400, n_kv_heads=2, n_anchors=5,
+                       anchor_len=[330, 400, 250, 400, 390], gate_len=250)
+    data, ref, gpu = _check_hop(sp, label="ragged")
+    assert ref["s_cov"] == 400
+
+
+def test_partial_coverage_short_pool():
+    sp = W.llama8b_hop(n_layers=2, seq_len=400, n_kv_heads=2, n_anchors=4,
+                       anchor_len=[300, 310, 290, 200], gate_len=128)
+    data, ref, gpu = _check_hop(sp, label="short")
+    assert ref["s_cov"] == 310
+    # rows beyond the coverage keep the re-aligned source: values bit-exact, keys to the
+    # rotation's rounding (fp32 on the GPU, fp64 in the oracle)
+    k_al = O.round_to(O.rope(O._np(data.k_src), sp.shift, sp.head_dim), "bf16")
+    assert np.max(np.abs(gpu["k_out"][:, 310:] - k_al[:, 310:])) <= 2.0 ** -8 * np.max(np.abs(k_al))
+    assert np.array_equal(gpu["v_out"][:, 310:], O._np(data.v_src)[:, 310:])
+    # ... and are exactly what the library's own re-alignment call writes
+    al = torch.empty_like(gpu["raw_k"])
+    kvc.align_rope(data.k_src.to(DEV), al, shape(sp), sp.p_src, sp.p_tgt)
+    torch.cuda.synchronize()
+    assert torch.equal(al[:, 310:], gpu["raw_k"][:, 310:])
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_zero_shift_zero_delta_bit_exact(dtype):
+    sp = W.llama8b_hop(n_layers=2, seq_len=200, n_kv_heads=2, n_anchors=3, dtype=dtype, p_src=0, p_tgt=0)
+    data = make(sp)
+    for n in ("deltaA_k", "deltaA_v", "deltaB_k", "deltaB_v"):
+        getattr(data, n).zero_()
+    gpu = run_gpu(data)
+    assert np.array_equal(gpu["k_out"], O._np(data.k_src))
+    assert np.array_equal(gpu["v_out"], O._np(data.v_src))
+
+
+def test_capacity_one_bypass_and_empty_pool():
+    sp = W.llama8b_hop(n_layers=2, seq_len=128, n_kv_heads=2, n_anchors=1, capacity=1)
+    data, ref, gpu = _check_hop(sp, label="cap1")
+    assert np.all(gpu["flags"] == 0)
+    sp0 = W.llama8b_hop(n_layers=2, seq_len=128, n_kv_heads=2, n_anchors=0)
+    data0 = make(sp0)
+    gpu0 = run_gpu(data0)
+    assert np.all(gpu0["flags"] == O.FLAG_FEW_ANCHORS)
+    k_al = O.round_to(O.rope(O._np(data0.k_src), sp0.shift, sp0.head_dim), "bf16")
+    assert np.max(np.abs(gpu0["k_out"] - k_al)) <= 2.0 ** -7 * np.max(np.abs(k_al))
+    assert np.array_equal(gpu0["v_out"], O._np(data0.v_src))
+
+
+def test_identical_anchors_flag_entropy_one():
+    sp = W.llama8b_hop(n_layers=2, seq_len=128, n_kv_heads=2, n_anchors=4)
+    data = make(sp)
+    for n in ("baseA_k", "baseA_v"):
+        t = getattr(data, n)
+        t[:, 128:] = t[:, :128].repeat(1, 3, 1)
+    for n in ("baseB_k", "baseB_v"):
+        t = getattr(data, n)
+        t[:, 1:] = t[:, :1]
+    gpu = run_gpu(data)
+    assert np.all(gpu["flags"] == O.FLAG_ENTROPY)
+    assert np.allclose(gpu["stat"], 1.0, atol=1e-12)
+
+
+def test_repeated_runs_bit_identical():
+    sp = W.llama8b_hop(n_layers=2, seq_len=300, n_kv_heads=4, n_anchors=8)
+    data = make(sp)
+    a = run_gpu(data)
+    b = run_gpu(data)
+    for key in ("k_out", "v_out", "dist", "stat", "flags", "w_k", "w_v"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_match_then_apply_equals_correct_hop():
+    sp = W.llama8b_hop(n_layers=2, seq_len=260, n_kv_heads=4, n_anchors=6)
+    data = make(sp)
+    full = run_gpu(data)
+    k, v = data.k_src.to(DEV), data.v_src.to(DEV)
+    pool = kvc.pool_from(data, DEV)
+    m = kvc.match_anchors(k, v, shape(sp), sp.p_src, pool, params(sp))
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    kvc.apply_lowrank_delta(k, v, ko, vo, shape(sp), sp.p_src, sp.p_tgt, pool, m.w_k, m.w_v, m.s_cov)
+    torch.cuda.synchronize()
+    assert torch.equal(ko, full["raw_k"]) and torch.equal(vo, full["raw_v"])
+    assert np.array_equal(m.flags.cpu().numpy(), full["flags"])
+
+
+def test_apply_explicit_one_hot_weights():
+    # one-hot weights on anchor 2: K_out = R(s) K + R(p_tgt) A_2 B_2, V_out = V + A_2 B_2
+    sp = W.llama8b_hop(n_layers=2, seq_len=192, n_kv_heads=2, n_anchors=4)
+    data = make(sp)
+    k, v = data.k_src.to(DEV), data.v_src.to(DEV)
+    pool = kvc.pool_from(data, DEV)
+    w = torch.zeros((2, 192, 4), dtype=torch.float32, device=DEV)
+    w[..., 2] = 1.0
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    kvc.apply_lowrank_delta(k, v, ko, vo, shape(sp), sp.p_src, sp.p_tgt, pool, w, w, 192)
+    torch.cuda.synchronize()
+    for l in range(2):
+        A, B = O.layer_factors(data, l, "k", "delta", [2])
+        Av, Bv = O.layer_factors(data, l, "v", "delta", [2])
+        exp_k = O.rope(O._np(data.k_src[l]), sp.shift, 128) + O.rope(A[0] @ B[0], sp.p_tgt, 128)
+        exp_v = O._np(data.v_src[l]) + Av[0] @ Bv[0]
+        gk, gv = ko[l].double().cpu().numpy(), vo[l].double().cpu().numpy()
+        assert np.max(np.abs(gk - exp_k)) <= 2.0 ** -7 * np.max(np.abs(exp_k))
+        assert np.max(np.abs(gv - exp_v)) <= 2.0 ** -7 * np.max(np.abs(exp_v))
+
+
+def test_batched_chain_matches_sequential_oracle():
+    reqs = W.chain_specs(n_requests=2, n_hops=3, seq_len=256, n_layers=2, n_kv_heads=2)
+    for hops in reqs:
+        datas = [make(h) for h in hops]
+        shp = shape(hops[0])
+        k0 = datas[0].k_src.to(DEV)
+        v0 = datas[0].v_src.to(DEV)
+        hl = []
+        for i, (h, d) in enumerate(zip(hops, datas)):
+            pool = kvc.pool_from(d, DEV)
+            out = kvc.alloc_match(h.n_layers, h.seq_len, h.n_anchors, DEV)
+            hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
+                              torch.empty_like(v0), h.p_src, h.p_tgt, i - 1, pool, out))
+        kvc.correct_hops_batched(hl, shp, params(hops[0]))
+        torch.cuda.synchronize()
+        # oracle: hop by hop, rounding to bf16 between hops (materialisation)
+        src_k, src_v = datas[0].k_src, datas[0].v_src
+        for i, (h, d) in enumerate(zip(hops, datas)):
+            d = dataclasses.replace(d, k_src=src_k, v_src=src_v)
+            ref = O.correct_hop(d)
+            gk = hl[i].k_out.double().cpu().numpy()
+            gv = hl[i].v_out.double().cpu().numpy()
+            assert np.max(np.abs(gk - ref["k_out"])) <= 2.0 ** -7 * np.max(np.abs(ref["k_out"])) * (i + 1)
+            assert np.max(np.abs(gv - ref["v_out"])) <= 2.0 ** -7 * np.max(np.abs(ref["v_out"])) * (i + 1)
+            flags = hl[i].out.flags.cpu().numpy()
+            pred = i > 0 and hl[i - 1].out.flags[0].item() != 0
+            assert np.array_equal(flags, ref["flags"] | (O.FLAG_ENTROPY * 0 + (8 if pred else 0)))
+            assert np.all(ref["flags"] == 0), "chain workload: every hop should match its anchor 0"
+            # the oracle chains its own materialised (bf16-rounded) output into the next hop
+            src_k = torch.from_numpy(ref["k_out"]).to(torch.bfloat16)
+            src_v = torch.from_numpy(ref["v_out"]).to(torch.bfloat16)
