@@ -115,15 +115,14 @@ typedef struct {
  * and increments count (launches beyond capacity are not traced).  Nothing synchronises:
  * the caller reads elapsed times after synchronising the stream. */
 #define KVC_TRACE_MAX 64
-#define KVC_K_TRANSPOSE_BASE 1
-#define KVC_K_SCORE_PAGES 2
-#define KVC_K_SCORE_COS 3
-#define KVC_K_SCORE_GENERIC 4
-#define KVC_K_GATE 5
-#define KVC_K_SOFTMAX 6
-#define KVC_K_TRANSPOSE_DELTA 7
-#define KVC_K_APPLY 8
-#define KVC_K_APPLY_GENERIC 9
+#define KVC_K_PACK_BASE 1        /* base B factors -> MFMA operand chunks                     */
+#define KVC_K_SCORE_COS 3        /* second-mode scores (bf16 MFMA)                            */
+#define KVC_K_SCORE_GENERIC 4    /* scores, any shape / dtype (VALU)                          */
+#define KVC_K_GATE 5             /* Eq. 9-11 finalisation (fp64)                              */
+#define KVC_K_SOFTMAX 6          /* token weights from materialised scores                    */
+#define KVC_K_PACK_DELTA 7       /* delta B factors -> MFMA operand chunks (keys turned)      */
+#define KVC_K_FUSED 8            /* fused score / weights / apply (bf16 MFMA)                 */
+#define KVC_K_APPLY_GENERIC 9    /* apply, any shape / dtype (VALU)                           */
 typedef struct {
   int32_t capacity;               /* <= KVC_TRACE_MAX                                      */
   int32_t count;                  /* written by the library                                */

@@ -69,9 +69,7 @@ __global__ void __launch_bounds__(256) align_rope_vec8(const Tin* __restrict__ i
     for (int i = 0; i < 8; ++i) {
       const float a = x.get(i), b = y.get(i);
       if (tab.active) {
-        const float c = cs[c0 + i], s = sn[c0 + i];
-        ox[i] = a * c - b * s;
-        oy[i] = a * s + b * c;
+        rot_pair(a, b, cs[c0 + i], sn[c0 + i], ox[i], oy[i]);
       } else {
         ox[i] = a;
         oy[i] = b;
@@ -99,10 +97,7 @@ __global__ void __launch_bounds__(256) align_rope_scalar(const Tin* __restrict__
     const int64_t i0 = row * D + (int64_t)head * head_dim + c;
     const float a = ldf(in, i0), b = ldf(in, i0 + h);
     float x = a, y = b;
-    if (tab.active) {
-      x = a * tab.cs[c] - b * tab.sn[c];
-      y = a * tab.sn[c] + b * tab.cs[c];
-    }
+    if (tab.active) rot_pair(a, b, tab.cs[c], tab.sn[c], x, y);
     stf(out, i0, x);
     stf(out, i0 + h, y);
   }

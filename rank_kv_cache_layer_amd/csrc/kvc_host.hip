@@ -161,34 +161,35 @@ kvc_status check_params(const kvc_params* prm, int S) {
 
 // ---------------------------------------------------------------- path selection
 int32_t D_of(const kvc_shape& s) { return s.n_kv_heads * s.head_dim; }
-bool pow2_rank(int r, int lo) { return r == lo || r == 2 * lo || r == 4 * lo || r == 8 * lo; }
 
-bool mfma_score_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, int n_use) {
+// The fused bf16 MFMA kernel: one work-group holds 64 tokens x all D channels (D / 128 waves,
+// at most 8), head_dim 64 or 128, ranks in steps of 16.
+bool fused_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, bool pages_scores, bool apply) {
   if (p.dtype != KVC_BF16 || (prm.options & 1)) return false;
   const int D = D_of(sh);
   if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 128 || D > 1024) return false;
-  if (prm.mode == KVC_SCORE_PAGES) {
-    if (!(p.rank_base == 16 || pow2_rank(p.rank_base, 16))) return false;
-    const size_t lds = sizeof(float) * (size_t)(D / 128) * 65 * std::max(n_use, 1);
-    return lds <= 150 * 1024;
+  if (pages_scores) {
+    const int r = p.rank_base;
+    if (r != 16 && r != 32 && r != 64 && r != 128) return false;
   }
-  return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
+  if (apply && (p.rank_delta % 16 || p.rank_delta > 256)) return false;
+  return true;
 }
 
-bool mfma_apply_ok(const kvc_shape& sh, const kvc_pool& p, int options) {
-  if (p.dtype != KVC_BF16 || (options & 1)) return false;
+bool cos_mfma_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) {
+  if (p.dtype != KVC_BF16 || (prm.options & 1)) return false;
   const int D = D_of(sh);
-  if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 128) return false;
-  if (!(p.rank_delta == 16 || pow2_rank(p.rank_delta, 16))) return false;
-  const size_t lds = sizeof(float) * 128 * p.n_anchors + 2 * 2 * 128 * (size_t)(p.rank_delta + 8);
-  return lds <= 150 * 1024;
+  if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 128 || D > 1024) return false;
+  return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
 }
 
 // ------------------------------------------------------------------- workspace
 struct Plan {
-  bool score_mfma = false, apply_mfma = false;
+  bool fused_match = false;   // PAGES scores inside the fused kernel
+  bool fused_apply = false;   // apply inside the fused kernel
+  bool cos_mfma = false;
   int tile = 0, n_tiles = 0, s_work = 0, generic_tt = 0;
-  size_t off_scores = 0, off_partials = 0, off_bt_base = 0, off_bt_delta = 0, total = 0;
+  size_t off_scores = 0, off_w = 0, off_partials = 0, off_pack_base = 0, off_pack_delta = 0, total = 0;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -200,45 +201,45 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
   const kvc_params& P = prm ? *prm : dflt;
   const bool do_match = call == KVC_CALL_MATCH || call == KVC_CALL_CORRECT;
   const bool do_apply = call == KVC_CALL_APPLY || call == KVC_CALL_CORRECT;
+  const bool pages = P.mode == KVC_SCORE_PAGES;
   size_t off = 0;
+  if (do_apply) pl.fused_apply = fused_ok(sh, p, P, false, true);
   if (do_match) {
     const int n_use = (int)s.use_list.size();
     pl.s_work = s.n_gate ? std::max(s.s_cov, s.k) : s.s_cov;
-    pl.score_mfma = mfma_score_ok(sh, p, P, n_use);
-    if (pl.score_mfma) {
-      pl.tile = P.mode == KVC_SCORE_PAGES ? kPagesTile : kCosTile;
+    pl.fused_match = pages && fused_ok(sh, p, P, true, false) && (!do_apply || pl.fused_apply);
+    if (pl.fused_match) {
+      pl.tile = kFusedTile;
+      pl.n_tiles = (S + kFusedTile - 1) / kFusedTile;
     } else {
-      pl.generic_tt = std::max(1, 256 / std::max(n_use, 1));
-      pl.tile = pl.generic_tt;
+      pl.cos_mfma = !pages && cos_mfma_ok(sh, p, P);
+      if (pl.cos_mfma) {
+        pl.tile = kCosTile;
+      } else {
+        pl.generic_tt = std::max(1, 256 / std::max(n_use, 1));
+        pl.tile = pl.generic_tt;
+      }
+      pl.n_tiles = pl.s_work > 0 ? (pl.s_work + pl.tile - 1) / pl.tile : 0;
+      pl.off_scores = off;
+      off += up256(sizeof(float) * 2 * (size_t)L * S * N);
+      if (!(do_apply && pl.fused_apply && !pages)) {   // weights are materialised unless fused
+        pl.off_w = off;
+        off += up256(sizeof(float) * 2 * (size_t)L * S * N);
+      }
     }
-    pl.n_tiles = pl.s_work > 0 ? (pl.s_work + pl.tile - 1) / pl.tile : 0;
-    pl.off_scores = off;
-    off += up256(sizeof(float) * 2 * (size_t)L * S * N);
     pl.off_partials = off;
     off += up256(sizeof(float) * 3 * (size_t)L * std::max(pl.n_tiles, 1) * N);
-    if (pl.score_mfma && P.mode == KVC_SCORE_PAGES) {
-      pl.off_bt_base = off;
+    if (pl.fused_match) {
+      pl.off_pack_base = off;
       off += up256(2 * 2 * (size_t)L * N * D * p.rank_base);
     }
   }
-  if (do_apply) {
-    pl.apply_mfma = mfma_apply_ok(sh, p, P.options);
-    if (pl.apply_mfma) {
-      pl.off_bt_delta = off;
-      off += up256(2 * 2 * (size_t)L * N * D * p.rank_delta);
-    }
+  if (do_apply && pl.fused_apply) {
+    pl.off_pack_delta = off;
+    off += up256(2 * 2 * (size_t)L * N * D * p.rank_delta);
   }
   pl.total = off;
   return pl;
-}
-
-hipError_t transpose_pair(const void* k, const void* v, uint16_t* dst, int negate, const kvc_shape& sh,
-                          const kvc_pool& p, int r, hipStream_t st) {
-  const size_t per = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * r;
-  const uint16_t* src[2] = {(const uint16_t*)k, (const uint16_t*)v};
-  uint16_t* dsts[2] = {dst, dst + per};
-  const int neg[2] = {negate, negate};
-  return launch_transpose_b(src, dsts, 2, neg, sh.n_layers, p.n_anchors, r, D_of(sh), st);
 }
 
 PoolGeom geom(const kvc_pool& p, const kvc_shape& sh, int r) {
@@ -279,122 +280,244 @@ kvc_status hip_fail(hipError_t e, const char* what) {
   return fail(KVC_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Match: scores -> gate -> weights.  w_out[2] receive the weights (may be workspace).
-kvc_status run_match(const void* k_src, const void* v_src, const kvc_shape& sh, int64_t p_src, const kvc_rope* rope,
-                     const kvc_pool& p, const kvc_params& prm, const Sets& s, const Plan& pl, char* ws,
-                     kvc_match_out* out, float* w_out[2], const int32_t* pred_flags, hipStream_t st) {
-  hipError_t e;
-  Tracer tr{prm.trace, st};
-  const int L = sh.n_layers, S = sh.seq_len, D = D_of(sh);
-  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
-  float* partials = reinterpret_cast<float*>(ws + pl.off_partials);
-  const int n_use = (int)s.use_list.size();
-  if (n_use > 0 && pl.n_tiles > 0) {
-    ScoreArgs a;
-    memset(&a, 0, sizeof a);
-    a.z[0] = k_src; a.z[1] = v_src;
-    a.A[0] = p.baseA_k; a.A[1] = p.baseA_v;
-    a.B[0] = p.baseB_k; a.B[1] = p.baseB_v;
-    a.scores = scores;
-    a.partials = partials;
-    a.n_layers = L; a.S = S; a.D = D; a.head_dim = sh.head_dim;
-    a.s_cov = s.s_cov; a.k_gate = s.k; a.s_work = pl.s_work; a.n_tiles = pl.n_tiles;
-    a.mask_corr = s.corr; a.mask_gate = s.gate;
-    a.n_use = n_use;
-    for (int i = 0; i < n_use; ++i) a.use[i] = s.use_list[i];
-    a.g = geom(p, sh, p.rank_base);
-    kvc_status st2 = make_tab(a.can, -p_src, sh.head_dim, rope);
-    if (st2 != KVC_OK) return st2;
-    if (pl.score_mfma && prm.mode == KVC_SCORE_PAGES) {
-      uint16_t* bt = reinterpret_cast<uint16_t*>(ws + pl.off_bt_base);
-      tr.begin(KVC_K_TRANSPOSE_BASE);
-      e = transpose_pair(p.baseB_k, p.baseB_v, bt, 1, sh, p, p.rank_base, st);
-      tr.end();
-      if (e != hipSuccess) return hip_fail(e, "transpose base factors");
-      a.Bt[0] = bt;
-      a.Bt[1] = bt + (size_t)L * p.n_anchors * D * p.rank_base;
-      tr.begin(KVC_K_SCORE_PAGES);
-      e = launch_score_pages_mfma(a, st);
-    } else if (pl.score_mfma) {
-      tr.begin(KVC_K_SCORE_COS);
-      e = launch_score_cos_mfma(a, st);
-    } else {
-      tr.begin(KVC_K_SCORE_GENERIC);
-      e = launch_score_generic(a, p.dtype == KVC_BF16, prm.mode, pl.generic_tt, st);
-    }
-    tr.end();
-    if (e != hipSuccess) return hip_fail(e, "score kernel");
+kvc_status fused_tab(FusedTab& ft, int64_t dp, int head_dim, const kvc_rope* rope) {
+  RopeTab t;
+  kvc_status s = make_tab(t, dp, head_dim, rope);
+  if (s != KVC_OK) return s;
+  memset(&ft, 0, sizeof ft);
+  for (int c = 0; c < head_dim / 2 && c < kFusedHalf; ++c) {
+    ft.cs[c] = t.cs[c];
+    ft.sn[c] = t.sn[c];
   }
+  ft.active = t.active;
+  return KVC_OK;
+}
+
+// Packs B factors of both sides into MFMA operand chunks.
+kvc_status pack_pair(const void* bk, const void* bv, uint16_t* dst, int r, int negate, const FusedTab* key_tab,
+                     const kvc_shape& sh, const kvc_pool& p, Tracer& tr, int trace_id, hipStream_t st) {
+  if (p.n_anchors == 0) return KVC_OK;
+  const size_t per = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * r;
+  const uint16_t* src[2] = {(const uint16_t*)bk, (const uint16_t*)bv};
+  uint16_t* dsts[2] = {dst, dst + per};
+  const int neg[2] = {negate, negate};
+  const FusedTab* tabs[2] = {key_tab, nullptr};
+  tr.begin(trace_id);
+  hipError_t e = launch_pack_b(src, dsts, neg, tabs, 2, sh.n_layers, p.n_anchors, r, D_of(sh), sh.head_dim, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "pack factors");
+  return KVC_OK;
+}
+
+// Common fields of the fused kernel's arguments.
+kvc_status fused_args(FusedArgs& f, const void* k_src, const void* v_src, const kvc_shape& sh, int64_t p_src,
+                      int64_t p_tgt, const kvc_rope* rope, const kvc_pool& p, const Sets& s, float inv_temp) {
+  memset(&f, 0, sizeof f);
+  f.z[0] = (const uint16_t*)k_src;
+  f.z[1] = (const uint16_t*)v_src;
+  f.n_layers = sh.n_layers;
+  f.S = sh.seq_len;
+  f.D = D_of(sh);
+  f.n_tiles = (sh.seq_len + kFusedTile - 1) / kFusedTile;
+  f.s_cov = s.corr_list.empty() ? 0 : s.s_cov;
+  f.k_gate = s.k;
+  f.r_b = p.rank_base;
+  f.r_d = p.rank_delta;
+  f.N = p.n_anchors;
+  f.mask_corr = s.corr;
+  f.mask_gate = s.gate;
+  f.n_use = (int)s.use_list.size();
+  for (int i = 0; i < f.n_use; ++i) f.use[i] = (uint8_t)s.use_list[i];
+  f.n_corr = (int)s.corr_list.size();
+  for (int i = 0; i < f.n_corr; ++i) f.corr[i] = (uint8_t)s.corr_list[i];
+  int64_t tot = 0;
+  for (int a = 0; a < p.n_anchors; ++a) {
+    f.off[a] = (int32_t)tot;
+    f.len[a] = p.anchor_len[a];
+    tot += p.anchor_len[a];
+  }
+  f.ab_layer = tot * p.rank_base;
+  f.ad_layer = tot * p.rank_delta;
+  f.inv_temp = inv_temp;
+  kvc_status st;
+  if ((st = fused_tab(f.can, -p_src, sh.head_dim, rope)) != KVC_OK) return st;
+  if ((st = fused_tab(f.shift, p_tgt - p_src, sh.head_dim, rope)) != KVC_OK) return st;
+  return KVC_OK;
+}
+
+kvc_status run_gate(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, const Sets& s, const float* partials,
+                    int n_tiles, kvc_match_out* out, const int32_t* pred_flags, Tracer& tr, hipStream_t st) {
   GateArgs g;
   memset(&g, 0, sizeof g);
   g.partials = partials;
   g.dist = out->dist; g.stat = out->stat; g.flags = out->flags;
   g.pred_flags = pred_flags;
-  g.n_layers = L; g.n_tiles = pl.n_tiles; g.N = p.n_anchors; g.mode = prm.mode;
+  g.n_layers = sh.n_layers; g.n_tiles = n_tiles; g.N = p.n_anchors; g.mode = prm.mode;
   g.capacity = p.capacity == 0 ? p.n_anchors : p.capacity;
   g.mask_gate = s.gate; g.tau = prm.tau; g.temp_gate = prm.temp_gate;
   tr.begin(KVC_K_GATE);
-  e = launch_gate(g, st);
+  hipError_t e = launch_gate(g, st);
   tr.end();
   if (e != hipSuccess) return hip_fail(e, "gate kernel");
-  if (p.n_anchors > 0) {
-    SoftmaxArgs m;
-    memset(&m, 0, sizeof m);
-    m.scores = scores;
-    m.w[0] = w_out[0]; m.w[1] = w_out[1];
-    m.n_layers = L; m.S = S; m.N = p.n_anchors; m.s_cov = s.s_cov; m.mode = prm.mode;
-    m.mask_corr = s.corr;
-    m.inv_temp = (float)(1.0 / prm.temp_weight);
-    tr.begin(KVC_K_SOFTMAX);
-    e = launch_softmax(m, st);
-    tr.end();
-    if (e != hipSuccess) return hip_fail(e, "softmax kernel");
-  }
-  if (out->s_cov) *out->s_cov = s.s_cov;
   return KVC_OK;
 }
 
-kvc_status run_apply(const void* k_src, const void* v_src, void* k_out, void* v_out, const kvc_shape& sh,
-                     int64_t p_src, int64_t p_tgt, const kvc_rope* rope, const kvc_pool& p, const float* w_k,
-                     const float* w_v, int s_cov, const std::vector<int>& corr, const Plan& pl, char* ws,
-                     hipStream_t st, kvc_trace* trace = nullptr) {
+// Materialised scores (second mode, or any shape through the generic kernel) + gate partials.
+kvc_status run_scores(const void* k_src, const void* v_src, const kvc_shape& sh, int64_t p_src, const kvc_rope* rope,
+                      const kvc_pool& p, const kvc_params& prm, const Sets& s, const Plan& pl, char* ws, Tracer& tr,
+                      hipStream_t st) {
+  const int n_use = (int)s.use_list.size();
+  if (n_use == 0 || pl.n_tiles == 0) return KVC_OK;
+  ScoreArgs a;
+  memset(&a, 0, sizeof a);
+  a.z[0] = k_src; a.z[1] = v_src;
+  a.A[0] = p.baseA_k; a.A[1] = p.baseA_v;
+  a.B[0] = p.baseB_k; a.B[1] = p.baseB_v;
+  a.scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  a.partials = reinterpret_cast<float*>(ws + pl.off_partials);
+  a.n_layers = sh.n_layers; a.S = sh.seq_len; a.D = D_of(sh); a.head_dim = sh.head_dim;
+  a.s_cov = s.s_cov; a.k_gate = s.k; a.s_work = pl.s_work; a.n_tiles = pl.n_tiles;
+  a.mask_corr = s.corr; a.mask_gate = s.gate;
+  a.n_use = n_use;
+  for (int i = 0; i < n_use; ++i) a.use[i] = s.use_list[i];
+  a.g = geom(p, sh, p.rank_base);
+  kvc_status s2 = make_tab(a.can, -p_src, sh.head_dim, rope);
+  if (s2 != KVC_OK) return s2;
   hipError_t e;
-  Tracer tr{trace, st};
+  if (pl.cos_mfma) {
+    tr.begin(KVC_K_SCORE_COS);
+    e = launch_score_cos_mfma(a, st);
+  } else {
+    tr.begin(KVC_K_SCORE_GENERIC);
+    e = launch_score_generic(a, p.dtype == KVC_BF16, prm.mode, pl.generic_tt, st);
+  }
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "score kernel");
+  return KVC_OK;
+}
+
+kvc_status run_softmax(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, const Sets& s, const float* scores,
+                       float* const w_out[2], Tracer& tr, hipStream_t st) {
+  if (p.n_anchors == 0) return KVC_OK;
+  SoftmaxArgs m;
+  memset(&m, 0, sizeof m);
+  m.scores = scores;
+  m.w[0] = w_out[0]; m.w[1] = w_out[1];
+  m.n_layers = sh.n_layers; m.S = sh.seq_len; m.N = p.n_anchors; m.s_cov = s.s_cov; m.mode = prm.mode;
+  m.mask_corr = s.corr;
+  m.inv_temp = (float)(1.0 / prm.temp_weight);
+  tr.begin(KVC_K_SOFTMAX);
+  hipError_t e = launch_softmax(m, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "softmax kernel");
+  return KVC_OK;
+}
+
+kvc_status run_apply_generic(const void* k_src, const void* v_src, void* k_out, void* v_out, const kvc_shape& sh,
+                             int64_t p_src, int64_t p_tgt, const kvc_rope* rope, const kvc_pool& p, const float* w_k,
+                             const float* w_v, int s_cov, const std::vector<int>& corr, Tracer& tr, hipStream_t st) {
   ApplyArgs a;
   memset(&a, 0, sizeof a);
-  const int L = sh.n_layers, D = D_of(sh);
   a.z[0] = k_src; a.z[1] = v_src;
   a.out[0] = k_out; a.out[1] = v_out;
   a.A[0] = p.deltaA_k; a.A[1] = p.deltaA_v;
   a.B[0] = p.deltaB_k; a.B[1] = p.deltaB_v;
   a.w[0] = w_k; a.w[1] = w_v;
-  a.n_layers = L; a.S = sh.seq_len; a.D = D; a.head_dim = sh.head_dim; a.s_cov = s_cov;
+  a.n_layers = sh.n_layers; a.S = sh.seq_len; a.D = D_of(sh); a.head_dim = sh.head_dim; a.s_cov = s_cov;
   a.n_corr = (int)corr.size();
   for (int i = 0; i < a.n_corr; ++i) a.corr[i] = corr[i];
   a.g = geom(p, sh, p.rank_delta);
   kvc_status s2 = make_tab(a.shift, p_tgt - p_src, sh.head_dim, rope);
   if (s2 != KVC_OK) return s2;
   if ((s2 = make_tab(a.tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return s2;
-  if (pl.apply_mfma) {
-    uint16_t* bt = reinterpret_cast<uint16_t*>(ws + pl.off_bt_delta);
-    if (p.n_anchors > 0) {
-      tr.begin(KVC_K_TRANSPOSE_DELTA);
-      e = transpose_pair(p.deltaB_k, p.deltaB_v, bt, 0, sh, p, p.rank_delta, st);
-      tr.end();
-      if (e != hipSuccess) return hip_fail(e, "transpose delta factors");
-    }
-    a.Bt[0] = bt;
-    a.Bt[1] = bt + (size_t)L * p.n_anchors * D * p.rank_delta;
-    tr.begin(KVC_K_APPLY);
-    e = launch_apply_mfma(a, st);
-  } else {
-    tr.begin(KVC_K_APPLY_GENERIC);
-    e = launch_apply_generic(a, p.dtype == KVC_BF16, st);
-  }
+  tr.begin(KVC_K_APPLY_GENERIC);
+  hipError_t e = launch_apply_generic(a, p.dtype == KVC_BF16, st);
   tr.end();
   if (e != hipSuccess) return hip_fail(e, "apply kernel");
   return KVC_OK;
 }
+
+// The whole hop (or its match half when k_out == nullptr): every path of the library.
+//   fused PAGES : pack base (+ delta) -> fused kernel (scores, weights, apply) -> gate
+//   second mode : scores -> gate -> fused kernel (weights from scores, apply)
+//   generic     : scores -> gate -> softmax -> generic apply
+kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_out, const kvc_shape& sh, int64_t p_src,
+                   int64_t p_tgt, const kvc_rope* rope, const kvc_pool& p, const kvc_params& prm, const Sets& s,
+                   const Plan& pl, char* ws, kvc_match_out* out, const int32_t* pred_flags, hipStream_t st) {
+  Tracer tr{prm.trace, st};
+  const bool apply = k_out != nullptr;
+  float* partials = reinterpret_cast<float*>(ws + pl.off_partials);
+  const float inv_temp = (float)(1.0 / prm.temp_weight);
+  kvc_status r;
+  if (pl.fused_match) {
+    uint16_t* pb = reinterpret_cast<uint16_t*>(ws + pl.off_pack_base);
+    if ((r = pack_pair(p.baseB_k, p.baseB_v, pb, p.rank_base, 1, nullptr, sh, p, tr, KVC_K_PACK_BASE, st)) != KVC_OK)
+      return r;
+    FusedArgs f;
+    if ((r = fused_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
+    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_base;
+    f.Ab[0] = (const uint16_t*)p.baseA_k; f.Ab[1] = (const uint16_t*)p.baseA_v;
+    f.Bb[0] = pb; f.Bb[1] = pb + per_b;
+    f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
+    f.partials = partials;
+    if (apply) {
+      FusedTab tgt;
+      if ((r = fused_tab(tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return r;
+      uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
+      if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
+        return r;
+      const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_delta;
+      f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
+      f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
+      f.Bd[0] = pd; f.Bd[1] = pd + per_d;
+      f.apply = 1;
+    }
+    tr.begin(KVC_K_FUSED);
+    hipError_t e = launch_fused(f, FUSED_PAGES, sh.head_dim, st);
+    tr.end();
+    if (e != hipSuccess) return hip_fail(e, "fused kernel");
+    if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+    if (out->s_cov) *out->s_cov = s.s_cov;
+    return KVC_OK;
+  }
+  // materialised scores
+  if ((r = run_scores(k_src, v_src, sh, p_src, rope, p, prm, s, pl, ws, tr, st)) != KVC_OK) return r;
+  if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+  const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
+  const size_t plane = (size_t)sh.n_layers * sh.seq_len * std::max(p.n_anchors, 1);
+  if (apply && pl.fused_apply) {
+    // second scoring mode: weights formed from the scores inside the fused kernel
+    FusedArgs f;
+    if ((r = fused_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
+    FusedTab tgt;
+    if ((r = fused_tab(tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return r;
+    uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
+    if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
+      return r;
+    const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_delta;
+    f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
+    f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
+    f.Bd[0] = pd; f.Bd[1] = pd + per_d;
+    f.w_in[0] = scores; f.w_in[1] = scores + plane;
+    f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
+    f.apply = 1;
+    tr.begin(KVC_K_FUSED);
+    hipError_t e = launch_fused(f, FUSED_SCORES, sh.head_dim, st);
+    tr.end();
+    if (e != hipSuccess) return hip_fail(e, "fused kernel");
+  } else {
+    float* wbuf = reinterpret_cast<float*>(ws + pl.off_w);
+    float* w_out[2] = {out->w_k ? out->w_k : wbuf, out->w_v ? out->w_v : wbuf + plane};
+    if ((r = run_softmax(sh, p, prm, s, scores, w_out, tr, st)) != KVC_OK) return r;
+    if (apply &&
+        (r = run_apply_generic(k_src, v_src, k_out, v_out, sh, p_src, p_tgt, rope, p, w_out[0], w_out[1],
+                               s.corr_list.empty() ? 0 : s.s_cov, s.corr_list, tr, st)) != KVC_OK)
+      return r;
+  }
+  if (out->s_cov) *out->s_cov = s.s_cov;
+  return KVC_OK;
+}
+
 
 kvc_status check_cache(const void* k, const void* v, const char* nk, const char* nv) {
   if (!k) return fail(KVC_E_NULL, "%s is NULL", nk);
@@ -528,12 +651,8 @@ kvc_status kvc_match_anchors(const void* k_src, const void* v_src, kvc_dtype dty
   if (pl.total && (!workspace || ws_bytes < pl.total))
     return fail(KVC_E_WORKSPACE, "workspace: need %zu bytes, got %zu", pl.total, workspace ? ws_bytes : (size_t)0);
   if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
-  char* ws = (char*)workspace;
-  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
-  const size_t plane = (size_t)shape.n_layers * shape.seq_len * std::max(pool->n_anchors, 1);
-  float* w_out[2] = {out->w_k ? out->w_k : scores, out->w_v ? out->w_v : scores + plane};
-  s = run_match(k_src, v_src, shape, p_src, rope, *pool, *params, sets, pl, ws, out, w_out, nullptr,
-                (hipStream_t)stream);
+  s = run_hop(k_src, v_src, nullptr, nullptr, shape, p_src, 0, rope, *pool, *params, sets, pl, (char*)workspace, out,
+              nullptr, (hipStream_t)stream);
   return s == KVC_OK ? ok() : s;
 }
 
@@ -561,18 +680,46 @@ kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k
       if (overlaps(outs[i], bytes, srcs[j], bytes))
         return fail(KVC_E_ALIAS, "output %s overlaps source %s", i ? "v_out" : "k_out", j ? "v_src" : "k_src");
   if (overlaps(k_out, bytes, v_out, bytes)) return fail(KVC_E_ALIAS, "k_out overlaps v_out");
+  // correction set of an explicit-weight apply: anchors covering the first s_cov rows
   Sets sets;
-  std::vector<int> corr;
+  sets.k = shape.seq_len;
+  sets.s_cov = s_cov;
   if (s_cov > 0)
     for (int a = 0; a < pool->n_anchors; ++a)
-      if (pool->anchor_len[a] >= s_cov) corr.push_back(a);
+      if (pool->anchor_len[a] >= s_cov) {
+        sets.corr |= 1ull << a;
+        sets.corr_list.push_back(a);
+        sets.use_list.push_back(a);
+      }
   Plan pl = plan(KVC_CALL_APPLY, shape, *pool, nullptr, sets);
   if (pl.total && (!workspace || ws_bytes < pl.total))
     return fail(KVC_E_WORKSPACE, "workspace: need %zu bytes, got %zu", pl.total, workspace ? ws_bytes : (size_t)0);
   if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
-  s = run_apply(k_src, v_src, k_out, v_out, shape, p_src, p_tgt, rope, *pool, w_k, w_v, corr.empty() ? 0 : s_cov,
-                corr, pl, (char*)workspace, (hipStream_t)stream);
-  return s == KVC_OK ? ok() : s;
+  hipStream_t st = (hipStream_t)stream;
+  Tracer tr{nullptr, st};
+  if (pl.fused_apply) {
+    FusedArgs f;
+    if ((s = fused_args(f, k_src, v_src, shape, p_src, p_tgt, rope, *pool, sets, 1.f)) != KVC_OK) return s;
+    FusedTab tgt;
+    if ((s = fused_tab(tgt, p_tgt, shape.head_dim, rope)) != KVC_OK) return s;
+    uint16_t* pd = reinterpret_cast<uint16_t*>((char*)workspace + pl.off_pack_delta);
+    if ((s = pack_pair(pool->deltaB_k, pool->deltaB_v, pd, pool->rank_delta, 0, &tgt, shape, *pool, tr,
+                       KVC_K_PACK_DELTA, st)) != KVC_OK)
+      return s;
+    const size_t per_d = (size_t)shape.n_layers * pool->n_anchors * D_of(shape) * pool->rank_delta;
+    f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
+    f.Ad[0] = (const uint16_t*)pool->deltaA_k; f.Ad[1] = (const uint16_t*)pool->deltaA_v;
+    f.Bd[0] = pd; f.Bd[1] = pd + per_d;
+    f.w_in[0] = w_k; f.w_in[1] = w_v;
+    f.apply = 1;
+    hipError_t e = launch_fused(f, FUSED_GIVEN, shape.head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "fused kernel");
+  } else {
+    s = run_apply_generic(k_src, v_src, k_out, v_out, shape, p_src, p_tgt, rope, *pool, w_k, w_v,
+                          sets.corr_list.empty() ? 0 : s_cov, sets.corr_list, tr, st);
+    if (s != KVC_OK) return s;
+  }
+  return ok();
 }
 
 static kvc_status correct_one(const HopReq& h, kvc_dtype dt, const kvc_shape& sh, const kvc_rope* rope,
@@ -583,13 +730,8 @@ static kvc_status correct_one(const HopReq& h, kvc_dtype dt, const kvc_shape& sh
   Plan pl = plan(KVC_CALL_CORRECT, sh, p, prm, sets);
   if (pl.total && (!ws || ws_bytes < pl.total))
     return fail(KVC_E_WORKSPACE, "workspace: need %zu bytes, got %zu", pl.total, ws ? ws_bytes : (size_t)0);
-  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
-  const size_t plane = (size_t)sh.n_layers * sh.seq_len * std::max(p.n_anchors, 1);
-  float* w_out[2] = {h.out->w_k ? h.out->w_k : scores, h.out->w_v ? h.out->w_v : scores + plane};
-  kvc_status s = run_match(h.k_src, h.v_src, sh, h.p_src, rope, p, *prm, sets, pl, ws, h.out, w_out, pred_flags, st);
-  if (s != KVC_OK) return s;
-  return run_apply(h.k_src, h.v_src, h.k_out, h.v_out, sh, h.p_src, h.p_tgt, rope, p, w_out[0], w_out[1],
-                   sets.corr_list.empty() ? 0 : sets.s_cov, sets.corr_list, pl, ws, st, prm->trace);
+  return run_hop(h.k_src, h.v_src, h.k_out, h.v_out, sh, h.p_src, h.p_tgt, rope, p, *prm, sets, pl, ws, h.out,
+                 pred_flags, st);
 }
 
 kvc_status kvc_correct_hop(const void* k_src, const void* v_src, void* k_out, void* v_out, kvc_dtype dtype,

@@ -41,6 +41,13 @@ template <typename T> __device__ __forceinline__ void stf(T* p, int64_t i, float
 template <> __device__ __forceinline__ void stf<float>(float* p, int64_t i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
 
+// One rotate-half pair turned by the angle whose cosine/sine are (c, s).  Written with explicit
+// fused multiply-adds so every kernel that re-aligns keys rounds identically.
+__device__ __forceinline__ void rot_pair(float x, float y, float c, float s, float& ox, float& oy) {
+  ox = fmaf(x, c, -(y * s));
+  oy = fmaf(x, s, y * c);
+}
+
 // Maps the hardware block index so that consecutive logical tiles run on the same XCD
 // (blocks are dealt round-robin over the 8 XCDs; each XCD has its own L2).
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
@@ -63,7 +70,6 @@ struct ScoreArgs {
   const void* z[2];          // source K, V   [N_l][S][D]
   const void* A[2];          // base A (K, V) packed [N_l][sum len][r]
   const void* B[2];          // base B (K, V) [N_l][N][r][D]  (generic path)
-  const uint16_t* Bt[2];     // base B^T (K, V) [N_l][N][D][r] bf16, negated for PAGES (MFMA)
   float* scores;             // [2][N_l][S][N]
   float* partials;           // [3][N_l][n_tiles][N]
   int32_t n_layers, S, D, head_dim;
@@ -88,7 +94,6 @@ struct ApplyArgs {
   void* out[2];              // outputs K, V
   const void* A[2];          // delta A (K, V) packed
   const void* B[2];          // delta B (K, V) [N_l][N][r][D] (generic path)
-  const uint16_t* Bt[2];     // delta B^T [N_l][N][D][r] bf16 (MFMA path)
   const float* w[2];         // weights [N_l][S][N]
   int32_t n_layers, S, D, head_dim, s_cov;
   int32_t n_corr;
@@ -114,17 +119,58 @@ hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_apply_generic(const ApplyArgs& a, int bf16, hipStream_t st);
 hipError_t launch_gate(const GateArgs& a, hipStream_t st);
 
-// MFMA (bf16) path
-hipError_t launch_transpose_b(const uint16_t* const* src, uint16_t* const* dst, int n_arrays,
-                              const int* negate, int n_layers, int n_anchors, int r, int D,
-                              hipStream_t st);
-hipError_t launch_score_pages_mfma(const ScoreArgs& a, hipStream_t st);
+// second scoring mode, bf16 MFMA
 hipError_t launch_score_cos_mfma(const ScoreArgs& a, hipStream_t st);
-hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t st);
+constexpr int kCosTile = 64;      // tokens per work-group
 
-constexpr int kPagesTile = 64;    // tokens per work-group, MFMA PAGES scoring
-constexpr int kCosTile = 64;      // tokens per work-group, MFMA COS_R scoring
-constexpr int kApplyTile = 128;   // tokens per work-group, MFMA apply
+// ------------------------------------------------------------------ fused hop (bf16)
+// One work-group = 64 tokens x all D channels of one (layer, side); wave w owns channels
+// [128 w, 128 w + 128).  Phase 1 scores the tile (or loads given weights/scores), phase 2
+// forms the token weights, phase 3 applies the weighted low-rank delta with both rotations
+// and the residual folded in.
+constexpr int kFusedTile = 64;
+constexpr int kFusedHalf = 64;    // rotary pairs per head the fused path supports (head_dim <= 128)
+
+enum FusedMode { FUSED_PAGES = 0, FUSED_SCORES = 1, FUSED_GIVEN = 2 };
+
+struct FusedTab {
+  float cs[kFusedHalf];
+  float sn[kFusedHalf];
+  int32_t active;
+};
+
+struct FusedArgs {
+  const uint16_t* z[2];       // source K, V        [N_l][S][D]
+  uint16_t* out[2];           // corrected K, V     [N_l][S][D]        (apply only)
+  const uint16_t* Ab[2];      // base A, packed     [N_l][sum len][r_C]
+  const uint16_t* Bb[2];      // base B^T, MFMA operand chunks, negated   (PAGES)
+  const uint16_t* Ad[2];      // delta A, packed    [N_l][sum len][r_D]
+  const uint16_t* Bd[2];      // delta B^T chunks; key rows turned by R(p_tgt)
+  const float* w_in[2];       // GIVEN: weights, SCORES: cosine scores   [N_l][S][N]
+  float* w_out[2];            // optional weights out                    [N_l][S][N]
+  float* partials;            // PAGES gate sums, value side             [N_l][n_tiles][N]
+  int32_t n_layers, S, D, n_tiles;
+  int32_t s_cov, k_gate, r_b, r_d;
+  int32_t N, n_use, n_corr, apply;
+  int32_t ring_stride;               // LDS row stride of the A staging ring (set by the launcher)
+  uint64_t mask_corr, mask_gate;
+  int64_t ab_layer, ad_layer;       // elements per layer of the packed A arrays
+  int32_t off[kMaxAnchors];         // first packed row of each anchor
+  int32_t len[kMaxAnchors];         // stored rows of each anchor
+  uint8_t use[kMaxAnchors];         // anchors scored (gate U correction set), ascending
+  uint8_t corr[kMaxAnchors];        // correction set, ascending
+  FusedTab can;                     // R(-p_src), keys' canonical frame
+  FusedTab shift;                   // R(p_tgt - p_src), residual of the keys
+  float inv_temp;                   // 1 / temp_weight
+};
+
+// Packs B [N_l][N][r][D] (bf16) into MFMA operand chunks: chunk (l, a, cb, ks) holds, for lane
+// q of a wave, the 8 values B[16 ks + 8 (q / 32) + i][32 cb + q % 32], i = 0..7.  `negate`
+// flips signs; `tab` (may be inactive) turns every row by a rotate-half rotation first.
+hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const int* negate,
+                         const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors,
+                         int r, int D, int head_dim, hipStream_t st);
+hipError_t launch_fused(const FusedArgs& a, int mode, int head_dim, hipStream_t st);
 
 // SVD refresh
 hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank, void* a_out,

@@ -53,8 +53,8 @@ class Pool(C.Structure):
 
 
 TRACE_MAX = 64
-KERNEL_NAMES = {1: "transpose_base", 2: "score_pages_mfma", 3: "score_cos_mfma", 4: "score_generic",
-                5: "gate_finalize", 6: "softmax", 7: "transpose_delta", 8: "apply_mfma", 9: "apply_generic"}
+KERNEL_NAMES = {1: "pack_base", 3: "score_cos_mfma", 4: "score_generic", 5: "gate_finalize", 6: "softmax",
+                7: "pack_delta", 8: "fused_hop", 9: "apply_generic"}
 
 
 class Trace(C.Structure):
