@@ -15,6 +15,7 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -37,24 +38,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(name, L, S, D, N, rC, rD, b=2):
-    """Algorithmic HBM bytes, MFMA flops and VALU lane-ops of one launch of `name` (whole hop)."""
+def kernel_work(name, L, S, D, N, rC, rD, mode="pages", b=2):
+    """Algorithmic HBM bytes, MFMA flops and VALU lane-ops of one launch of `name` (whole hop).
+
+    Bytes count each operand once: the K/V source read, the corrected K/V written, the A and B
+    factors the launch contracts (B in its packed operand form, same size), the fp32 scores a
+    second-mode launch reads.  Flops are the MFMA contractions (2 per multiply-add).  VALU
+    lane-ops are the first-mode epilogue: one |E| add per (token, channel, anchor) on both sides
+    plus one E^2 fma on the value side."""
     src = 2 * L * S * D * b                       # K and V source read
-    fac_base = 2 * L * N * (S * rC + D * rC) * b  # base A and B^T, both sides
+    out = 2 * L * S * D * b                       # corrected K and V written
+    fac_base = 2 * L * N * (S * rC + D * rC) * b  # base A and B, both sides
     fac_delta = 2 * L * N * (S * rD + D * rD) * b
-    wts = 2 * L * S * N * 4                       # fp32 scores / weights, both sides
-    if name == "score_pages_mfma":
-        return dict(bytes=src + fac_base + wts, flops=4 * L * S * D * N * rC, alu=3 * L * S * D * N)
+    scores = 2 * L * S * N * 4
+    if name == "fused_hop" and mode == "pages":
+        return dict(bytes=src + out + fac_base + fac_delta, flops=4 * L * S * D * N * (rC + rD), alu=3 * L * S * D * N)
+    if name == "fused_hop":                       # second mode: weights from materialised scores
+        return dict(bytes=src + out + fac_delta + scores, flops=4 * L * S * D * N * rD, alu=0)
     if name == "score_cos_mfma":
-        return dict(bytes=src + 2 * L * N * (S * rC + D * rC) * b + wts, flops=4 * L * S * D * N * rC,
-                    alu=6 * L * S * N * rC)
-    if name == "apply_mfma":
-        return dict(bytes=2 * src + fac_delta + wts, flops=4 * L * S * D * N * rD, alu=0)
-    if name in ("transpose_base", "transpose_delta"):
-        r = rC if name == "transpose_base" else rD
+        return dict(bytes=src + fac_base + scores, flops=4 * L * S * D * N * rC, alu=6 * L * S * N * rC)
+    if name in ("pack_base", "pack_delta"):
+        r = rC if name == "pack_base" else rD
         return dict(bytes=2 * 2 * L * N * r * D * b, flops=0, alu=0)
-    if name == "softmax":
-        return dict(bytes=2 * wts, flops=0, alu=0)
     return dict(bytes=0, flops=0, alu=0)
 
 
@@ -144,6 +149,7 @@ def main():
     ap.add_argument("--layers", type=int, default=32, help="smaller values are for quick local runs only")
     ap.add_argument("--seq-len", type=int, default=32768, help="smaller values are for quick local runs only")
     ap.add_argument("--mode", choices=["pages", "cos"], default="pages")
+    ap.add_argument("--p-src", type=int, default=512, help="start position of the segment in the source agent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-mode", action="store_true")
     args = ap.parse_args()
@@ -177,6 +183,10 @@ def main():
     ko, vo = torch.empty_like(k), torch.empty_like(v)
     pool = kvc.pool_from(data, dev)
     shp = kvc.shape_of(sp.n_layers, sp.seq_len, sp.n_kv_heads, sp.head_dim)
+    # keys are drawn in the canonical frame; place the segment at start position 512 (target 812)
+    # with the library's own re-alignment, in place
+    kvc.align_rope(k, k, shp, 0, args.p_src)
+    sp = dataclasses.replace(sp, p_src=args.p_src, p_tgt=args.p_src + sp.shift)
 
     def prm_fn(mode_):
         return lambda tr: kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, mode_, 0, tr)
@@ -195,7 +205,7 @@ def main():
     kernels = {}
     for name, ts in per_kernel.items():
         med = statistics.median(ts)
-        kernels[name] = roofline(name, med, kernel_work(name, L, S, D, N, r, r), measured_traffic(name))
+        kernels[name] = roofline(name, med, kernel_work(name, L, S, D, N, r, r, args.mode), measured_traffic(name))
     dominant = max(kernels.values(), key=lambda x: x["ms"]) if kernels else None
 
     hop_bytes = 2 * L * S * D * (2 + 2) + 2 * L * N * (2 * r) * (S + D) * 2
