@@ -123,6 +123,8 @@ typedef struct {
 #define KVC_K_PACK_DELTA 7       /* delta B factors -> MFMA operand chunks (keys turned)      */
 #define KVC_K_FUSED 8            /* fused score / weights / apply (bf16 MFMA)                 */
 #define KVC_K_APPLY_GENERIC 9    /* apply, any shape / dtype (VALU)                           */
+#define KVC_K_SCORE_SPLIT 10     /* first-mode scores, 256 x 256 tiles (bf16 MFMA)            */
+#define KVC_K_APPLY_SPLIT 11     /* token weights + apply, 256 x 256 tiles (bf16 MFMA)        */
 typedef struct {
   int32_t capacity;               /* <= KVC_TRACE_MAX                                      */
   int32_t count;                  /* written by the library                                */
@@ -137,7 +139,8 @@ typedef struct {
   double temp_weight;   /* token-weight temperature (> 0)                                     */
   int32_t gate_len;     /* comparison prefix k (0 = seq_len), 1 .. seq_len                    */
   int32_t mode;         /* kvc_score_mode                                                    */
-  int32_t options;      /* bit 0: force the generic (non-MFMA) kernels; other bits 0          */
+  int32_t options;      /* bit 0: force the generic (non-MFMA) kernels; bit 1: use the
+                           single-pass fused kernel instead of the two-pass one; others 0    */
   int32_t pad_;
   kvc_trace* trace;     /* optional kernel trace (NULL = none)                                */
 } kvc_params;

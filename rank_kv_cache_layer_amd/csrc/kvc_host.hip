@@ -148,7 +148,7 @@ kvc_status check_params(const kvc_params* prm, int S) {
   if (prm->gate_len < 0 || prm->gate_len > S) return fail(KVC_E_PARAM, "params: gate_len must be in [0, seq_len]");
   if (prm->mode != KVC_SCORE_PAGES && prm->mode != KVC_SCORE_COS_R)
     return fail(KVC_E_PARAM, "params: unknown mode %d", prm->mode);
-  if (prm->options & ~1) return fail(KVC_E_PARAM, "params: unknown option bits 0x%x", prm->options);
+  if (prm->options & ~3) return fail(KVC_E_PARAM, "params: unknown option bits 0x%x", prm->options);
   if (prm->trace) {
     const kvc_trace* t = prm->trace;
     if (t->capacity < 0 || t->capacity > KVC_TRACE_MAX || t->count < 0)
@@ -183,13 +183,34 @@ bool cos_mfma_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
   return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
 }
 
+// The two-pass bf16 path: 256-token x 256-channel work-groups (D a multiple of 256), ranks
+// 16/32 for first-mode scores and 16/32/64 for the apply, within the LDS budget.
+constexpr size_t kLdsBudget = 160 * 1024;
+bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, bool pages_scores, bool apply) {
+  if (p.dtype != KVC_BF16 || (prm.options & 3)) return false;
+  const int D = D_of(sh);
+  if ((sh.head_dim != 64 && sh.head_dim != 128) || D % kSplitWidth) return false;
+  if (pages_scores) {
+    if (p.rank_base != 16 && p.rank_base != 32) return false;
+    if (split_score_lds(p.rank_base) + 8 * 1024 > kLdsBudget) return false;
+  }
+  if (apply) {
+    if (p.rank_delta != 16 && p.rank_delta != 32 && p.rank_delta != 64) return false;
+    if (split_apply_lds(p.rank_delta, p.n_anchors) + 2 * 1024 > kLdsBudget) return false;
+  }
+  return true;
+}
+
 // ------------------------------------------------------------------- workspace
 struct Plan {
+  bool split_match = false;   // first-mode scores in the two-pass path
+  bool split_apply = false;   // apply in the two-pass path
   bool fused_match = false;   // PAGES scores inside the fused kernel
   bool fused_apply = false;   // apply inside the fused kernel
   bool cos_mfma = false;
   int tile = 0, n_tiles = 0, s_work = 0, generic_tt = 0;
-  size_t off_scores = 0, off_w = 0, off_partials = 0, off_pack_base = 0, off_pack_delta = 0, total = 0;
+  size_t off_scores = 0, off_w = 0, off_partials = 0, off_pack_base = 0, off_pack_delta = 0, off_mpart = 0;
+  size_t total = 0;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -203,12 +224,27 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
   const bool do_apply = call == KVC_CALL_APPLY || call == KVC_CALL_CORRECT;
   const bool pages = P.mode == KVC_SCORE_PAGES;
   size_t off = 0;
-  if (do_apply) pl.fused_apply = fused_ok(sh, p, P, false, true);
+  if (do_apply) {
+    pl.split_apply = split_ok(sh, p, P, false, true);
+    pl.fused_apply = !pl.split_apply && fused_ok(sh, p, P, false, true);
+  }
   if (do_match) {
     const int n_use = (int)s.use_list.size();
     pl.s_work = s.n_gate ? std::max(s.s_cov, s.k) : s.s_cov;
-    pl.fused_match = pages && fused_ok(sh, p, P, true, false) && (!do_apply || pl.fused_apply);
-    if (pl.fused_match) {
+    pl.split_match = pages && split_ok(sh, p, P, true, do_apply);
+    if (pl.split_match && do_apply && !pl.split_apply) pl.split_match = false;
+    if (do_apply && pages && !pl.split_match && pl.split_apply) {   // keep the pair on one path
+      pl.split_apply = false;
+      pl.fused_apply = fused_ok(sh, p, P, false, true);
+    }
+    pl.fused_match = !pl.split_match && pages && fused_ok(sh, p, P, true, false) && (!do_apply || pl.fused_apply);
+    if (pl.split_match) {
+      const int ntt = (S + kScoreTile - 1) / kScoreTile, nct = D / kSplitWidth;
+      pl.tile = kScoreTile;
+      pl.n_tiles = ntt * nct;
+      pl.off_mpart = off;
+      off += up256(sizeof(float) * (size_t)nct * 2 * L * N * S);
+    } else if (pl.fused_match) {
       pl.tile = kFusedTile;
       pl.n_tiles = (S + kFusedTile - 1) / kFusedTile;
     } else {
@@ -222,19 +258,19 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
       pl.n_tiles = pl.s_work > 0 ? (pl.s_work + pl.tile - 1) / pl.tile : 0;
       pl.off_scores = off;
       off += up256(sizeof(float) * 2 * (size_t)L * S * N);
-      if (!(do_apply && pl.fused_apply && !pages)) {   // weights are materialised unless fused
+      if (!(do_apply && (pl.fused_apply || pl.split_apply) && !pages)) {   // weights materialised unless fused
         pl.off_w = off;
         off += up256(sizeof(float) * 2 * (size_t)L * S * N);
       }
     }
     pl.off_partials = off;
     off += up256(sizeof(float) * 3 * (size_t)L * std::max(pl.n_tiles, 1) * N);
-    if (pl.fused_match) {
+    if (pl.fused_match || pl.split_match) {
       pl.off_pack_base = off;
       off += up256(2 * 2 * (size_t)L * N * D * p.rank_base);
     }
   }
-  if (do_apply && pl.fused_apply) {
+  if (do_apply && (pl.fused_apply || pl.split_apply)) {
     pl.off_pack_delta = off;
     off += up256(2 * 2 * (size_t)L * N * D * p.rank_delta);
   }
@@ -345,6 +381,62 @@ kvc_status fused_args(FusedArgs& f, const void* k_src, const void* v_src, const 
   return KVC_OK;
 }
 
+// Common fields of the two-pass kernels' arguments.
+kvc_status split_args(SplitArgs& f, const void* k_src, const void* v_src, const kvc_shape& sh, int64_t p_src,
+                      int64_t p_tgt, const kvc_rope* rope, const kvc_pool& p, const Sets& s, float inv_temp) {
+  memset(&f, 0, sizeof f);
+  f.z[0] = (const uint16_t*)k_src;
+  f.z[1] = (const uint16_t*)v_src;
+  f.n_layers = sh.n_layers;
+  f.S = sh.seq_len;
+  f.D = D_of(sh);
+  f.ntt = (sh.seq_len + kScoreTile - 1) / kScoreTile;   // set per launch by the kernels
+  f.nct = D_of(sh) / kSplitWidth;
+  f.N = p.n_anchors;
+  f.r_b = p.rank_base;
+  f.r_d = p.rank_delta;
+  f.s_cov = s.corr_list.empty() ? 0 : s.s_cov;
+  f.k_gate = s.k;
+  f.mask_corr = s.corr;
+  f.mask_gate = s.gate;
+  f.n_use = (int)s.use_list.size();
+  for (int i = 0; i < f.n_use; ++i) f.use[i] = (uint8_t)s.use_list[i];
+  f.n_corr = (int)s.corr_list.size();
+  for (int i = 0; i < f.n_corr; ++i) f.corr[i] = (uint8_t)s.corr_list[i];
+  int64_t tot = 0;
+  for (int a = 0; a < p.n_anchors; ++a) {
+    f.off[a] = (int32_t)tot;
+    f.len[a] = p.anchor_len[a];
+    tot += p.anchor_len[a];
+  }
+  f.ab_layer = tot * p.rank_base;
+  f.ad_layer = tot * p.rank_delta;
+  f.inv_temp = inv_temp;
+  f.inv_d = 1.f / (float)D_of(sh);
+  kvc_status st;
+  if ((st = fused_tab(f.can, -p_src, sh.head_dim, rope)) != KVC_OK) return st;
+  if ((st = fused_tab(f.shift, p_tgt - p_src, sh.head_dim, rope)) != KVC_OK) return st;
+  return KVC_OK;
+}
+
+// Packs the delta B factors (key rows turned by R(p_tgt)) and fills the apply fields.
+kvc_status split_apply_fields(SplitArgs& f, void* k_out, void* v_out, const kvc_shape& sh, int64_t p_tgt,
+                              const kvc_rope* rope, const kvc_pool& p, char* ws, const Plan& pl, Tracer& tr,
+                              hipStream_t st) {
+  FusedTab tgt;
+  kvc_status r;
+  if ((r = fused_tab(tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return r;
+  uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
+  if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
+    return r;
+  const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_delta;
+  f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
+  f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
+  f.Bd[0] = pd; f.Bd[1] = pd + per_d;
+  f.apply = 1;
+  return KVC_OK;
+}
+
 kvc_status run_gate(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, const Sets& s, const float* partials,
                     int n_tiles, kvc_match_out* out, const int32_t* pred_flags, Tracer& tr, hipStream_t st) {
   GateArgs g;
@@ -449,6 +541,35 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
   float* partials = reinterpret_cast<float*>(ws + pl.off_partials);
   const float inv_temp = (float)(1.0 / prm.temp_weight);
   kvc_status r;
+  if (pl.split_match) {
+    uint16_t* pb = reinterpret_cast<uint16_t*>(ws + pl.off_pack_base);
+    if ((r = pack_pair(p.baseB_k, p.baseB_v, pb, p.rank_base, 1, nullptr, sh, p, tr, KVC_K_PACK_BASE, st)) != KVC_OK)
+      return r;
+    SplitArgs f;
+    if ((r = split_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
+    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_base;
+    f.Ab[0] = (const uint16_t*)p.baseA_k; f.Ab[1] = (const uint16_t*)p.baseA_v;
+    f.Bb[0] = pb; f.Bb[1] = pb + per_b;
+    f.mpart = reinterpret_cast<float*>(ws + pl.off_mpart);
+    f.partials = partials;
+    f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
+    if (p.n_anchors > 0) {
+      tr.begin(KVC_K_SCORE_SPLIT);
+      hipError_t e = launch_split_score(f, sh.head_dim, st);
+      tr.end();
+      if (e != hipSuccess) return hip_fail(e, "score kernel");
+    }
+    if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+    if (apply && (r = split_apply_fields(f, k_out, v_out, sh, p_tgt, rope, p, ws, pl, tr, st)) != KVC_OK) return r;
+    if (apply || out->w_k || out->w_v) {
+      tr.begin(KVC_K_APPLY_SPLIT);
+      hipError_t e = launch_split_apply(f, SPLIT_W_PARTIALS, sh.head_dim, st);
+      tr.end();
+      if (e != hipSuccess) return hip_fail(e, "apply kernel");
+    }
+    if (out->s_cov) *out->s_cov = s.s_cov;
+    return KVC_OK;
+  }
   if (pl.fused_match) {
     uint16_t* pb = reinterpret_cast<uint16_t*>(ws + pl.off_pack_base);
     if ((r = pack_pair(p.baseB_k, p.baseB_v, pb, p.rank_base, 1, nullptr, sh, p, tr, KVC_K_PACK_BASE, st)) != KVC_OK)
@@ -485,7 +606,18 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
   if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
   const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
   const size_t plane = (size_t)sh.n_layers * sh.seq_len * std::max(p.n_anchors, 1);
-  if (apply && pl.fused_apply) {
+  if (apply && pl.split_apply) {
+    // second scoring mode: weights formed from the scores inside the apply kernel
+    SplitArgs f;
+    if ((r = split_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
+    if ((r = split_apply_fields(f, k_out, v_out, sh, p_tgt, rope, p, ws, pl, tr, st)) != KVC_OK) return r;
+    f.w_in[0] = scores; f.w_in[1] = scores + plane;
+    f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
+    tr.begin(KVC_K_APPLY_SPLIT);
+    hipError_t e = launch_split_apply(f, SPLIT_W_SCORES, sh.head_dim, st);
+    tr.end();
+    if (e != hipSuccess) return hip_fail(e, "apply kernel");
+  } else if (apply && pl.fused_apply) {
     // second scoring mode: weights formed from the scores inside the fused kernel
     FusedArgs f;
     if ((r = fused_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
@@ -697,7 +829,15 @@ kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k
   if (workspace && !aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   Tracer tr{nullptr, st};
-  if (pl.fused_apply) {
+  if (pl.split_apply) {
+    SplitArgs f;
+    if ((s = split_args(f, k_src, v_src, shape, p_src, p_tgt, rope, *pool, sets, 1.f)) != KVC_OK) return s;
+    if ((s = split_apply_fields(f, k_out, v_out, shape, p_tgt, rope, *pool, (char*)workspace, pl, tr, st)) != KVC_OK)
+      return s;
+    f.w_in[0] = w_k; f.w_in[1] = w_v;
+    hipError_t e = launch_split_apply(f, SPLIT_W_GIVEN, shape.head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "apply kernel");
+  } else if (pl.fused_apply) {
     FusedArgs f;
     if ((s = fused_args(f, k_src, v_src, shape, p_src, p_tgt, rope, *pool, sets, 1.f)) != KVC_OK) return s;
     FusedTab tgt;

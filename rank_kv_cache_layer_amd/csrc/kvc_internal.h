@@ -172,6 +172,47 @@ hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const
                          int r, int D, int head_dim, hipStream_t st);
 hipError_t launch_fused(const FusedArgs& a, int mode, int head_dim, hipStream_t st);
 
+// ------------------------------------------------------------ two-pass path (bf16)
+// Score work-group = 256 tokens x 256 channels of one (layer, side), 8 waves of 64 x 128 (one
+// per CU).  Apply work-group = 128 tokens x 256 channels, 4 waves of 64 x 128; two share a CU
+// so one's streaming phases (source in, corrected cache out) overlap the other's MFMA phases.
+constexpr int kScoreTile = 256;
+constexpr int kScoreThreads = 512;
+constexpr int kApplyTile = 128;
+constexpr int kApplyThreads = 256;
+constexpr int kSplitWidth = 256;
+
+enum SplitWMode { SPLIT_W_PARTIALS = 0, SPLIT_W_SCORES = 1, SPLIT_W_GIVEN = 2 };
+
+struct SplitArgs {
+  const uint16_t* z[2];       // source K, V                  [N_l][S][D]
+  uint16_t* out[2];           // corrected K, V               [N_l][S][D]
+  const uint16_t* Ab[2];      // base A, packed               [N_l][sum len][r_C]
+  const uint16_t* Bb[2];      // base B operand chunks, negated
+  const uint16_t* Ad[2];      // delta A, packed              [N_l][sum len][r_D]
+  const uint16_t* Bd[2];      // delta B' operand chunks (key rows turned by R(p_tgt))
+  float* mpart;               // per channel tile |E| sums    [n_ct][2][N_l][N][S]
+  const float* w_in[2];       // given weights / cosine scores [N_l][S][N]
+  float* w_out[2];            // optional weights out          [N_l][S][N]
+  float* partials;            // gate sums, value side         [N_l][n_tt * n_ct][N] (score tiles)
+  int32_t n_layers, S, D, ntt, nct, N, r_b, r_d;   // ntt: token tiles of the launched kernel
+  int32_t s_cov, k_gate, n_use, n_corr, apply, pad_;
+  uint64_t mask_corr, mask_gate;
+  int64_t ab_layer, ad_layer;       // elements per layer of the packed A arrays
+  int32_t off[kMaxAnchors];
+  int32_t len[kMaxAnchors];
+  uint8_t use[kMaxAnchors];
+  uint8_t corr[kMaxAnchors];
+  FusedTab can;                     // R(-p_src)
+  FusedTab shift;                   // R(p_tgt - p_src)
+  float inv_temp, inv_d;            // 1 / temp_weight, 1 / D
+};
+
+hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_split_apply(const SplitArgs& a, int wmode, int head_dim, hipStream_t st);
+size_t split_score_lds(int r_b);                   // dynamic LDS bytes
+size_t split_apply_lds(int r_d, int n_anchors);
+
 // SVD refresh
 hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank, void* a_out,
                        void* b_out, int out_bf16, float* sigma, int oversample, int power_iters,

@@ -110,7 +110,7 @@ def test_correct_hop_validation_codes():
     assert _correct(prm=kvc.params_of(temp_weight=-1.0)) == 8
     assert _correct(prm=kvc.params_of(gate_len=65)) == 8
     assert _correct(prm=kvc.params_of(mode=3)) == 8
-    assert _correct(prm=kvc.params_of(options=2)) == 8
+    assert _correct(prm=kvc.params_of(options=4)) == 8
     assert _correct(prm=kvc.params_of(tau=float("nan"))) == 8
     assert _correct(pool=_pool(n=65)) == 2
     assert _correct(pool=_pool(n=2, lens=[64, 0])) == 2

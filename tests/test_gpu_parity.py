@@ -77,7 +77,7 @@ def test_tiny_fp32_cosine_mode():
 
 
 @pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
-@pytest.mark.parametrize("options", [0, 1])
+@pytest.mark.parametrize("options", [0, 1, 2])   # two-pass MFMA, generic VALU, single-pass fused MFMA
 def test_llama_shape_reduced_bf16(mode, options):
     # 8B shape per layer, fewer layers and a ragged token count (several tiles + tail)
     sp = W.llama8b_hop(n_layers=3, seq_len=1000, mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
