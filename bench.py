@@ -55,6 +55,10 @@ def kernel_work(name, L, S, D, N, rC, rD, mode="pages", b=2):
         return dict(bytes=src + out + fac_base + fac_delta, flops=4 * L * S * D * N * (rC + rD), alu=3 * L * S * D * N)
     if name == "fused_hop":                       # second mode: weights from materialised scores
         return dict(bytes=src + out + fac_delta + scores, flops=4 * L * S * D * N * rD, alu=0)
+    if name == "split_score":                     # first mode: per-token distances + gate sums
+        return dict(bytes=src + fac_base + scores, flops=4 * L * S * D * N * rC, alu=3 * L * S * D * N)
+    if name == "split_apply":                     # token weights from the scores, then the delta
+        return dict(bytes=src + out + fac_delta + scores, flops=4 * L * S * D * N * rD, alu=0)
     if name == "score_cos_mfma":
         return dict(bytes=src + fac_base + scores, flops=4 * L * S * D * N * rC, alu=6 * L * S * N * rC)
     if name in ("pack_base", "pack_delta"):
@@ -96,6 +100,39 @@ def measured_traffic(kernel):
         return None
     v = d.get("kernels", {}).get(kernel)
     return None if v is None else int(v)
+
+
+def measure_peaks(kvc, torch):
+    """Device ceilings from the library's measurement kernels, timed with events on the stream
+    they run on: HBM copy (read + write bytes), bf16 MFMA, LDS reads, unpacked fp32 VALU."""
+    st = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    nb = 1 << 30
+    a = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    t_copy = timed(lambda: kvc.peak_copy(b, a), 10)
+    del a, b
+    blocks = 256 * 8
+    it_m, it_l, it_v = 64, 8192, 65536     # about 7-30 ms per launch at the published peaks
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    t_mfma = timed(lambda: kvc.peak_loop("mfma", sink, blocks, it_m), 3)
+    t_lds = timed(lambda: kvc.peak_loop("lds", sink, blocks, it_l), 3)
+    t_valu = timed(lambda: kvc.peak_loop("valu", sink, blocks, it_v), 3)
+    return {"hbm_copy_GBps": round(2 * nb / t_copy / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(blocks * 4 * it_m * 4 * 32768 / t_mfma / 1e12, 1),
+            "lds_read_bytes_per_clk_per_CU_at_2.4GHz": round(blocks * 256 * it_l * 8 * 16 / t_lds / 256 / 2.4e9, 1),
+            "valu_fp32_Tops": round(blocks * 256 * it_v * 8 / t_valu / 1e12, 2)}
 
 
 def cpu_baseline(data, n_layers):
@@ -196,6 +233,9 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs resident on {torch.cuda.get_device_name(0)}; workspace {ws_bytes / 2**20:.0f} MiB")
 
+    peaks = measure_peaks(kvc, torch)
+    log(f"[bench] measured ceilings: {peaks}")
+
     ms, wall, per_kernel, res = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode), ws, args.steps,
                                          args.warmup)
     flags = res.flags.cpu().tolist()
@@ -239,7 +279,7 @@ def main():
                    "n_anchors": N, "rank": r, "shift": sp.shift, "score_mode": args.mode,
                    "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
         "roofline": dominant, "cpu_baseline": cpu,
-        "hop": hop, "kernels": kernels, "second_mode": second,
+        "hop": hop, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
         "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
     }
     print(json.dumps(out), flush=True)

@@ -124,7 +124,8 @@ typedef struct {
 #define KVC_K_FUSED 8            /* fused score / weights / apply (bf16 MFMA)                 */
 #define KVC_K_APPLY_GENERIC 9    /* apply, any shape / dtype (VALU)                           */
 #define KVC_K_SCORE_SPLIT 10     /* first-mode scores, 256 x 256 tiles (bf16 MFMA)            */
-#define KVC_K_APPLY_SPLIT 11     /* token weights + apply, 256 x 256 tiles (bf16 MFMA)        */
+#define KVC_K_APPLY_SPLIT 11
+#define KVC_K_WEIGHTS_SPLIT 12     /* token weights + apply, 256 x 256 tiles (bf16 MFMA)        */
 typedef struct {
   int32_t capacity;               /* <= KVC_TRACE_MAX                                      */
   int32_t count;                  /* written by the library                                */

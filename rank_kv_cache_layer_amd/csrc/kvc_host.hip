@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "kvc_internal.h"
+#include "kvc_peaks.h"
 
 using namespace kvc;
 
@@ -196,7 +197,7 @@ bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, boo
   }
   if (apply) {
     if (p.rank_delta != 16 && p.rank_delta != 32 && p.rank_delta != 64) return false;
-    if (split_apply_lds(p.rank_delta, p.n_anchors) + 2 * 1024 > kLdsBudget) return false;
+    if (split_apply_lds(p.rank_delta) + 2 * 1024 > kLdsBudget) return false;
   }
   return true;
 }
@@ -210,6 +211,7 @@ struct Plan {
   bool cos_mfma = false;
   int tile = 0, n_tiles = 0, s_work = 0, generic_tt = 0;
   size_t off_scores = 0, off_w = 0, off_partials = 0, off_pack_base = 0, off_pack_delta = 0, off_mpart = 0;
+  size_t off_wa = 0;            // anchor-major token weights of the two-pass path
   size_t total = 0;
 };
 
@@ -273,6 +275,10 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
   if (do_apply && (pl.fused_apply || pl.split_apply)) {
     pl.off_pack_delta = off;
     off += up256(2 * 2 * (size_t)L * N * D * p.rank_delta);
+  }
+  if (pl.split_match || pl.split_apply) {
+    pl.off_wa = off;
+    off += up256(sizeof(float) * 2 * (size_t)L * N * S);
   }
   pl.total = off;
   return pl;
@@ -437,6 +443,25 @@ kvc_status split_apply_fields(SplitArgs& f, void* k_out, void* v_out, const kvc_
   return KVC_OK;
 }
 
+// Anchor-major token weights for the two-pass apply (and the caller's copy, if requested).
+kvc_status run_split_weights(SplitArgs& f, int wmode, char* ws, const Plan& pl, Tracer& tr, hipStream_t st) {
+  f.wa = reinterpret_cast<float*>(ws + pl.off_wa);
+  if (f.n_corr < 1) return KVC_OK;
+  tr.begin(KVC_K_WEIGHTS_SPLIT);
+  hipError_t e = launch_split_weights(f, wmode, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "weights kernel");
+  return KVC_OK;
+}
+
+kvc_status run_split_apply(const SplitArgs& f, const kvc_shape& sh, Tracer& tr, hipStream_t st) {
+  tr.begin(KVC_K_APPLY_SPLIT);
+  hipError_t e = launch_split_apply(f, sh.head_dim, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "apply kernel");
+  return KVC_OK;
+}
+
 kvc_status run_gate(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, const Sets& s, const float* partials,
                     int n_tiles, kvc_match_out* out, const int32_t* pred_flags, Tracer& tr, hipStream_t st) {
   GateArgs g;
@@ -560,12 +585,11 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
       if (e != hipSuccess) return hip_fail(e, "score kernel");
     }
     if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
-    if (apply && (r = split_apply_fields(f, k_out, v_out, sh, p_tgt, rope, p, ws, pl, tr, st)) != KVC_OK) return r;
-    if (apply || out->w_k || out->w_v) {
-      tr.begin(KVC_K_APPLY_SPLIT);
-      hipError_t e = launch_split_apply(f, SPLIT_W_PARTIALS, sh.head_dim, st);
-      tr.end();
-      if (e != hipSuccess) return hip_fail(e, "apply kernel");
+    if (apply || out->w_k || out->w_v)
+      if ((r = run_split_weights(f, SPLIT_W_PARTIALS, ws, pl, tr, st)) != KVC_OK) return r;
+    if (apply) {
+      if ((r = split_apply_fields(f, k_out, v_out, sh, p_tgt, rope, p, ws, pl, tr, st)) != KVC_OK) return r;
+      if ((r = run_split_apply(f, sh, tr, st)) != KVC_OK) return r;
     }
     if (out->s_cov) *out->s_cov = s.s_cov;
     return KVC_OK;
@@ -613,10 +637,8 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
     if ((r = split_apply_fields(f, k_out, v_out, sh, p_tgt, rope, p, ws, pl, tr, st)) != KVC_OK) return r;
     f.w_in[0] = scores; f.w_in[1] = scores + plane;
     f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
-    tr.begin(KVC_K_APPLY_SPLIT);
-    hipError_t e = launch_split_apply(f, SPLIT_W_SCORES, sh.head_dim, st);
-    tr.end();
-    if (e != hipSuccess) return hip_fail(e, "apply kernel");
+    if ((r = run_split_weights(f, SPLIT_W_SCORES, ws, pl, tr, st)) != KVC_OK) return r;
+    if ((r = run_split_apply(f, sh, tr, st)) != KVC_OK) return r;
   } else if (apply && pl.fused_apply) {
     // second scoring mode: weights formed from the scores inside the fused kernel
     FusedArgs f;
@@ -835,8 +857,8 @@ kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k
     if ((s = split_apply_fields(f, k_out, v_out, shape, p_tgt, rope, *pool, (char*)workspace, pl, tr, st)) != KVC_OK)
       return s;
     f.w_in[0] = w_k; f.w_in[1] = w_v;
-    hipError_t e = launch_split_apply(f, SPLIT_W_GIVEN, shape.head_dim, st);
-    if (e != hipSuccess) return hip_fail(e, "apply kernel");
+    if ((s = run_split_weights(f, SPLIT_W_GIVEN, (char*)workspace, pl, tr, st)) != KVC_OK) return s;
+    if ((s = run_split_apply(f, shape, tr, st)) != KVC_OK) return s;
   } else if (pl.fused_apply) {
     FusedArgs f;
     if ((s = fused_args(f, k_src, v_src, shape, p_src, p_tgt, rope, *pool, sets, 1.f)) != KVC_OK) return s;
@@ -954,6 +976,45 @@ kvc_status kvc_anchor_refresh_svd(const float* z, int32_t n_mats, int32_t rows, 
                              power_iters, seed, workspace, ws_bytes, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "svd refresh");
   return ok();
+}
+
+// ------------------------------------------------------------------ measurement kernels
+static kvc_status peak_args(const void* sink, int32_t n_blocks, int32_t iters) {
+  if (!sink) return fail(KVC_E_NULL, "sink is NULL");
+  if (!aligned16(sink)) return fail(KVC_E_ALIGN, "sink not 16-byte aligned");
+  if (n_blocks < 1 || n_blocks > 65536) return fail(KVC_E_SHAPE, "n_blocks must be in [1, 65536]");
+  if (iters < 1 || iters > (1 << 20)) return fail(KVC_E_PARAM, "iters must be in [1, 2^20]");
+  return KVC_OK;
+}
+
+kvc_status kvc_peak_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src) return fail(KVC_E_NULL, "dst/src is NULL");
+  if (!aligned16(dst) || !aligned16(src)) return fail(KVC_E_ALIGN, "dst/src not 16-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(KVC_E_SHAPE, "bytes must be a positive multiple of 16");
+  if (overlaps(dst, bytes, src, bytes)) return fail(KVC_E_ALIAS, "dst overlaps src");
+  hipError_t e = launch_peak_copy(dst, src, bytes, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "copy kernel");
+}
+
+kvc_status kvc_peak_mfma_bf16(float* sink, int32_t n_blocks, int32_t iters, void* stream) {
+  kvc_status s = peak_args(sink, n_blocks, iters);
+  if (s != KVC_OK) return s;
+  hipError_t e = launch_peak_mfma(sink, n_blocks, iters, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "mfma loop");
+}
+
+kvc_status kvc_peak_lds_read(uint32_t* sink, int32_t n_blocks, int32_t iters, void* stream) {
+  kvc_status s = peak_args(sink, n_blocks, iters);
+  if (s != KVC_OK) return s;
+  hipError_t e = launch_peak_lds(sink, n_blocks, iters, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "lds loop");
+}
+
+kvc_status kvc_peak_valu(float* sink, int32_t n_blocks, int32_t iters, void* stream) {
+  kvc_status s = peak_args(sink, n_blocks, iters);
+  if (s != KVC_OK) return s;
+  hipError_t e = launch_peak_valu(sink, n_blocks, iters, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "valu loop");
 }
 
 }  // extern "C"

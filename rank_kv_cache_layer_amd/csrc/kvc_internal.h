@@ -194,6 +194,7 @@ struct SplitArgs {
   float* mpart;               // per channel tile |E| sums    [n_ct][2][N_l][N][S]
   const float* w_in[2];       // given weights / cosine scores [N_l][S][N]
   float* w_out[2];            // optional weights out          [N_l][S][N]
+  float* wa;                  // token weights, anchor-major   [2][N_l][N][S]
   float* partials;            // gate sums, value side         [N_l][n_tt * n_ct][N] (score tiles)
   int32_t n_layers, S, D, ntt, nct, N, r_b, r_d;   // ntt: token tiles of the launched kernel
   int32_t s_cov, k_gate, n_use, n_corr, apply, pad_;
@@ -209,14 +210,21 @@ struct SplitArgs {
 };
 
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st);
-hipError_t launch_split_apply(const SplitArgs& a, int wmode, int head_dim, hipStream_t st);
+hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st);
+hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st);
 size_t split_score_lds(int r_b);                   // dynamic LDS bytes
-size_t split_apply_lds(int r_d, int n_anchors);
+size_t split_apply_lds(int r_d);
 
 // SVD refresh
 hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank, void* a_out,
                        void* b_out, int out_bf16, float* sigma, int oversample, int power_iters,
                        uint64_t seed, void* ws, size_t ws_bytes, hipStream_t st);
 size_t svd_workspace_bytes(int n_mats, int rows, int cols, int rank, int oversample);
+
+// machine-ceiling measurement kernels (kvc_peaks.hip)
+hipError_t launch_peak_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+hipError_t launch_peak_mfma(float* sink, int n_blocks, int iters, hipStream_t st);
+hipError_t launch_peak_lds(uint32_t* sink, int n_blocks, int iters, hipStream_t st);
+hipError_t launch_peak_valu(float* sink, int n_blocks, int iters, hipStream_t st);
 
 }  // namespace kvc

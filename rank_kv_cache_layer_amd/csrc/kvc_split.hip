@@ -55,6 +55,25 @@ __device__ __forceinline__ uint4 scale8(uint4 r, float w) {
 
 // wave-uniform value held in a VGPR (e.g. read from LDS) -> scalar register
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// entry j (wave-uniform) of a table held one entry per lane -> scalar register
+__device__ __forceinline__ int lane_get(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+
+// Anchor slot tables of a work-group, one slot per lane (at most 64 anchors): slot j's anchor,
+// first packed A row and readable row count, fetched once per wave; the pipelined loops pick
+// slot j with a lane read instead of a chain of dependent memory lookups.
+struct Slots {
+  int a, off, lim;
+};
+__device__ __forceinline__ Slots load_slots(const uint8_t* list, int n, const int32_t* off, const int32_t* len,
+                                            int row_cap, int lane) {
+  Slots s{0, 0, 0};
+  if (lane < n) {
+    s.a = list[lane];
+    s.off = off[s.a];
+    s.lim = min(row_cap, len[s.a]);
+  }
+  return s;
+}
 
 // Raw buffer access: a 128-bit descriptor (base, size in bytes) in scalar registers plus a
 // 32-bit per-lane byte offset; loads past the size return 0 and stores past it are dropped,
@@ -262,6 +281,7 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], const uint
 template <int UA, int UB>
 struct Operands {
   uint4 a[UA], b[UB];
+  float w[UA];
 };
 
 // A: buffer over the anchor's first `lim` rows (R bf16 each, rows >= lim read as 0); B: buffer
@@ -283,12 +303,22 @@ struct Stream {
 #pragma unroll
     for (int i = 0; i < UB; ++i) o.b[i] = bload16(B, (uint32_t)(tid + i * NT) * 16u);
   }
-  static __device__ __forceinline__ void commit(const Ops& o, uint16_t* as, uint16_t* bs, int tid, const float* wrow) {
+  // with the token weights of the A rows (buffer over one anchor's weight row, fp32)
+  static __device__ __forceinline__ void issue_w(Ops& o, rsrc_t A, rsrc_t B, rsrc_t W, int t0, int tid) {
+    issue(o, A, B, t0, tid);
+#pragma unroll
+    for (int i = 0; i < UA; ++i) {
+      const int row = (tid + i * NT) / (R / 8);
+      o.w[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(W, (t0 + row) * 4, 0, 0));
+    }
+  }
+  template <bool SCALE>
+  static __device__ __forceinline__ void commit(const Ops& o, uint16_t* as, uint16_t* bs, int tid) {
 #pragma unroll
     for (int i = 0; i < UA; ++i) {
       const int u = tid + i * NT;
       const int row = u / (R / 8), c = u - row * (R / 8);
-      const uint4 x = wrow ? scale8(o.a[i], wrow[row]) : o.a[i];
+      const uint4 x = SCALE ? scale8(o.a[i], o.w[i]) : o.a[i];
       *reinterpret_cast<uint4*>(as + row * RS + c * 8) = x;
     }
 #pragma unroll
@@ -306,8 +336,6 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
   __shared__ float mp[2][2][kST];
   __shared__ float qp[kNW][kMaxAnchors];
   __shared__ float tab[2][kFusedHalf];
-  __shared__ int32_t s_off[kMaxAnchors], s_len[kMaxAnchors];
-  __shared__ uint8_t s_list[kMaxAnchors];
 
   const TileId id = tile_id(p);
   const bool keys = id.side == 0;
@@ -328,11 +356,7 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
     tab[0][i] = p.can.cs[i];
     tab[1][i] = p.can.sn[i];
   }
-  for (int i = tid; i < kMaxAnchors; i += kNT) {
-    s_off[i] = p.off[i];
-    s_len[i] = p.len[i];
-    s_list[i] = list[i];
-  }
+  const Slots sl = load_slots(list, keys ? p.n_corr : p.n_use, p.off, p.len, S, lane);
   __syncthreads();
 
   const uint16_t* Al = p.Ab[id.side] + id.layer * p.ab_layer;
@@ -342,9 +366,10 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
   // so the pipeline below issues and commits unconditionally (no branches around memory ops)
   auto src = [&](int j, typename SM::Ops& o) {
     const bool live = j < nl;
-    const int a = uni(s_list[live ? j : 0]);
-    const int lim = live ? min(S, uni(s_len[a])) : 0;
-    SM::issue(o, make_rsrc(Al + (int64_t)uni(s_off[a]) * R, (uint32_t)lim * R * 2),
+    const int js = live ? j : 0;
+    const int a = lane_get(sl.a, js);
+    const int lim = live ? lane_get(sl.lim, js) : 0;
+    SM::issue(o, make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
                        make_rsrc(Bl + a * bstride, live ? BSZ * 2 : 0), t0, tid);
   };
 
@@ -359,7 +384,7 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
     if (keys && p.can.active) rotate_tile<HD>(z, tab[0], tab[1], hi);
   }
   __syncthreads();   // the staging area overlaps the operand slots
-  SM::commit(o0, As, Bs, tid, nullptr);
+  SM::template commit<false>(o0, As, Bs, tid);
   src(2, o0);
   __syncthreads();
 
@@ -373,7 +398,7 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
     constexpr int buf = decltype(stage)::value;
     asm volatile("; pipeline stage %0" ::"n"(buf));
     const bool live = j < nl;
-    const int a = uni(s_list[live ? j : 0]);
+    const int a = lane_get(sl.a, live ? j : 0);
     const bool want_m = live && ((p.mask_corr >> a) & 1);
     const bool want_q = live && !keys && ((p.mask_gate >> a) & 1) && t0 < p.k_gate;
     if (live) {
@@ -399,7 +424,7 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
     }
     // anchor j + 1 (fetched two steps ago into onext) goes to the other slot; anchor j + 3 is
     // fetched into the freed registers
-    SM::commit(onext, As + (buf ^ 1) * ASZ, Bs + (buf ^ 1) * BSZ, tid, nullptr);
+    SM::template commit<false>(onext, As + (buf ^ 1) * ASZ, Bs + (buf ^ 1) * BSZ, tid);
     src(j + 3, onext);
     __syncthreads();
     if (want_m && tid < kST) {
@@ -424,19 +449,68 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
   }
 }
 
-// ================================================================== pass 2: weights + apply
-// WMODE: SPLIT_W_PARTIALS (first mode: m from the score partials), SPLIT_W_SCORES (second
-// mode: cosines), SPLIT_W_GIVEN (explicit weights).
-template <int HD, int RKD, int WMODE>
+// ================================================================== token weights
+// App. A.3 "Correction Weighting": per token and side, softmax over the correction set of
+// -m / T_w (first mode, m = mean |Z_can - A B| from the per-channel-tile partials) or of
+// cosine / T_w (second mode), or the caller's weights as given; 0 past S_cov.  Written
+// anchor-major (w[side][layer][a][t], the apply kernel's operand order) and, if requested,
+// token-major for the caller (w_out[side][layer][t][a], 0 outside the correction set).
+__global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
+  extern __shared__ float xs[];   // [n_corr][256]
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x * 256 + tid;
+  const int layer = blockIdx.y, side = blockIdx.z;
+  const int S = p.S, N = p.N, L = p.n_layers, nc = p.n_corr;
+  const bool in = t < S, cov = t < p.s_cov;
+  float mx = -INFINITY;
+  for (int j = 0; j < nc; ++j) {
+    const int a = p.corr[j];
+    float x = 0.f;
+    if (cov) {
+      if (wmode == SPLIT_W_PARTIALS) {
+        float m = 0.f;
+        for (int q = 0; q < p.nct; ++q) m += p.mpart[((((int64_t)q * 2 + side) * L + layer) * N + a) * S + t];
+        x = -(m * p.inv_d) * p.inv_temp;
+      } else if (wmode == SPLIT_W_SCORES) {
+        x = p.w_in[side][((int64_t)layer * S + t) * N + a] * p.inv_temp;
+      } else {
+        x = p.w_in[side][((int64_t)layer * S + t) * N + a];
+      }
+    }
+    xs[j * 256 + tid] = x;
+    mx = fmaxf(mx, x);
+  }
+  if (wmode != SPLIT_W_GIVEN) {
+    float sum = 0.f;
+    for (int j = 0; j < nc; ++j) {
+      const float e = expf(xs[j * 256 + tid] - mx);
+      xs[j * 256 + tid] = e;
+      sum += e;
+    }
+    const float inv = 1.f / sum;
+    for (int j = 0; j < nc; ++j) xs[j * 256 + tid] *= inv;
+  }
+  if (!in) return;
+  float* wa = p.wa + ((int64_t)side * L + layer) * N * S;
+  for (int j = 0; j < nc; ++j) wa[(int64_t)p.corr[j] * S + t] = cov ? xs[j * 256 + tid] : 0.f;
+  if (p.w_out[side]) {
+    float* dst = p.w_out[side] + ((int64_t)layer * S + t) * N;
+    for (int a = 0; a < N; ++a) dst[a] = 0.f;
+    for (int j = 0; j < nc; ++j) dst[p.corr[j]] = cov ? xs[j * 256 + tid] : 0.f;
+  }
+}
+
+// ================================================================== pass 2: apply
+// Sec. 3.3 Eq. 8 / App. A.3 Eq. 12: out = R(s) Z + sum_a w_a A_a B'_a, the token weights read
+// anchor-major (split_weights) and folded into the A rows on their way into LDS.
+template <int HD, int RKD>
 __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
-  constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
+  constexpr int kST = kApplyTile, kNT = kApplyThreads;
   using SM = Stream<RKD, kST, kNT>;
   constexpr int R = RKD * 16, RS = R + 8;
   constexpr int ASZ = kST * RS, BSZ = kNCBW * RKD * kC;
-  extern __shared__ __attribute__((aligned(16))) uint16_t dyn[];   // As[2][ASZ], Bs[2][BSZ], w[N][256] fp32
+  extern __shared__ __attribute__((aligned(16))) uint16_t dyn[];   // As[2][ASZ], Bs[2][BSZ] | staging
   __shared__ float tab[2][kFusedHalf];
-  __shared__ int32_t s_off[kMaxAnchors], s_len[kMaxAnchors];
-  __shared__ uint8_t s_corr[kMaxAnchors];
 
   const TileId id = tile_id(p);
   const bool keys = id.side == 0;
@@ -447,98 +521,40 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
   const int d0 = id.cq * kSW + cw * 128;
   uint16_t* As = dyn;
   uint16_t* Bs = dyn + 2 * ASZ;
-  constexpr int kRing = 2 * ASZ + 2 * BSZ > kNW * kStage ? 2 * ASZ + 2 * BSZ : kNW * kStage;
-  float* wsh = reinterpret_cast<float*>(dyn + kRing);   // [N][256], after the ring / staging area
 
   for (int i = tid; i < HD / 2; i += kNT) {
     tab[0][i] = p.shift.cs[i];
     tab[1][i] = p.shift.sn[i];
   }
-  for (int i = tid; i < kMaxAnchors; i += kNT) {
-    s_off[i] = p.off[i];
-    s_len[i] = p.len[i];
-    s_corr[i] = p.corr[i];
-  }
-  __syncthreads();
-  const int nc = (p.apply && t0 < p.s_cov) ? p.n_corr : 0;
-  const uint16_t* Al = p.apply ? p.Ad[id.side] + id.layer * p.ad_layer : nullptr;
-  const uint16_t* Bl = p.apply ? p.Bd[id.side] + (((int64_t)id.layer * N) * NCB + id.cq * kNCBW) * RKD * kC : nullptr;
+  const int nc = (t0 < p.s_cov) ? p.n_corr : 0;
+  const Slots sl = load_slots(p.corr, p.n_corr, p.off, p.len, min(S, p.s_cov), lane);
+  const uint16_t* Al = p.Ad[id.side] + id.layer * p.ad_layer;
+  const uint16_t* Bl = p.Bd[id.side] + (((int64_t)id.layer * N) * NCB + id.cq * kNCBW) * RKD * kC;
+  const float* Wl = p.wa + ((int64_t)id.side * p.n_layers + id.layer) * N * S;
   const int64_t bstride = (int64_t)NCB * RKD * kC;
-  const int lim_cov = min(S, p.s_cov);
   // zero-size descriptors past the correction set (see split_score)
   auto src = [&](int j, typename SM::Ops& o) {
     const bool live = j < nc;
-    const int a = uni(s_corr[live ? j : 0]);
-    const int lim = live ? min(lim_cov, uni(s_len[a])) : 0;
-    SM::issue(o, make_rsrc(Al + (int64_t)uni(s_off[a]) * R, (uint32_t)lim * R * 2),
-                        make_rsrc(Bl + a * bstride, live ? BSZ * 2 : 0), t0, tid);
+    const int js = live ? j : 0;
+    const int a = lane_get(sl.a, js);
+    const int lim = live ? lane_get(sl.lim, js) : 0;
+    SM::issue_w(o, make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
+                make_rsrc(Bl + a * bstride, live ? BSZ * 2 : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
+                t0, tid);
   };
   typename SM::Ops o0, o1;
-  if (p.apply) {
-    src(0, o0);
-    src(1, o1);
-  }
-
-  // ---- token weights of the tile's tokens, anchor-major in LDS
-  if (tid < kST) {
-    const int t = t0 + tid;
-    const bool cov = t < p.s_cov;
-    if (WMODE == SPLIT_W_GIVEN) {
-      const float* src_w = p.w_in[id.side] + ((int64_t)id.layer * S + min(t, S - 1)) * N;
-      for (int ci = 0; ci < p.n_corr; ++ci) {
-        const int a = uni(s_corr[ci]);
-        wsh[a * kST + tid] = cov ? src_w[a] : 0.f;
-      }
-    } else {
-      float mx = -INFINITY;
-      for (int ci = 0; ci < p.n_corr; ++ci) {
-        const int a = uni(s_corr[ci]);
-        float x = 0.f;
-        if (cov) {
-          if (WMODE == SPLIT_W_PARTIALS) {
-            float m = 0.f;
-            for (int q = 0; q < p.nct; ++q)
-              m += p.mpart[((((int64_t)q * 2 + id.side) * p.n_layers + id.layer) * N + a) * S + t];
-            x = -(m * p.inv_d) * p.inv_temp;
-          } else {
-            x = p.w_in[id.side][((int64_t)id.layer * S + t) * N + a] * p.inv_temp;
-          }
-        }
-        wsh[a * kST + tid] = x;
-        mx = fmaxf(mx, x);
-      }
-      float sum = 0.f;
-      for (int ci = 0; ci < p.n_corr; ++ci) {
-        const int a = uni(s_corr[ci]);
-        const float e = expf(wsh[a * kST + tid] - mx);
-        wsh[a * kST + tid] = e;
-        sum += e;
-      }
-      const float inv = 1.f / sum;
-      for (int ci = 0; ci < p.n_corr; ++ci) {
-        const int a = uni(s_corr[ci]);
-        wsh[a * kST + tid] = cov ? wsh[a * kST + tid] * inv : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-  if (p.w_out[id.side] && id.cq == 0) {
-    float* dst = p.w_out[id.side] + (int64_t)id.layer * S * N;
-    for (int i = tid; i < kST * N; i += kNT) {
-      const int tl = i / N, a = i - tl * N;
-      if (t0 + tl < S) dst[(int64_t)t0 * N + i] = ((p.mask_corr >> a) & 1) ? wsh[a * kST + tl] : 0.f;
-    }
-  }
-  if (!p.apply) return;
+  src(0, o0);
+  src(1, o1);
 
   // ---- residual: R(s) K or V
   f32x16 acc[2][4];
   const uint32_t layer_bytes = (uint32_t)S * D * 2;
+  __syncthreads();   // rotation table
   load_tile(acc, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, dyn + wave * kStage,
             lane, col, hi);
   if (keys && p.shift.active) rotate_tile<HD>(acc, tab[0], tab[1], hi);
   __syncthreads();   // the staging area overlaps the operand slots
-  SM::commit(o0, As, Bs, tid, wsh + uni(s_corr[0]) * kST);
+  SM::template commit<true>(o0, As, Bs, tid);
   src(2, o0);
   __syncthreads();
   // the two pipeline stages are instantiated separately (compile-time slot, distinct marker),
@@ -561,8 +577,7 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
         }
       }
     }
-    SM::commit(onext, As + (buf ^ 1) * ASZ, Bs + (buf ^ 1) * BSZ, tid,
-                         wsh + uni(s_corr[j + 1 < nc ? j + 1 : 0]) * kST);
+    SM::template commit<true>(onext, As + (buf ^ 1) * ASZ, Bs + (buf ^ 1) * BSZ, tid);
     src(j + 3, onext);
     __syncthreads();
   };
@@ -600,22 +615,15 @@ hipError_t score_dispatch(const SplitArgs& a, hipStream_t st) {
   }
 }
 
-template <int HD, int WMODE>
-hipError_t apply_dispatch2(const SplitArgs& a, hipStream_t st) {
-  const size_t lds = split_apply_lds(a.r_d, a.N);
+template <int HD>
+hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
+  const size_t lds = split_apply_lds(a.r_d);
   switch (a.r_d) {
-    case 16: return go(split_apply<HD, 1, WMODE>, a, kApplyTile, kApplyThreads, lds, st);
-    case 32: return go(split_apply<HD, 2, WMODE>, a, kApplyTile, kApplyThreads, lds, st);
-    case 64: return go(split_apply<HD, 4, WMODE>, a, kApplyTile, kApplyThreads, lds, st);
+    case 16: return go(split_apply<HD, 1>, a, kApplyTile, kApplyThreads, lds, st);
+    case 32: return go(split_apply<HD, 2>, a, kApplyTile, kApplyThreads, lds, st);
+    case 64: return go(split_apply<HD, 4>, a, kApplyTile, kApplyThreads, lds, st);
     default: return hipErrorInvalidValue;
   }
-}
-
-template <int HD>
-hipError_t apply_dispatch(const SplitArgs& a, int wmode, hipStream_t st) {
-  if (wmode == SPLIT_W_PARTIALS) return apply_dispatch2<HD, SPLIT_W_PARTIALS>(a, st);
-  if (wmode == SPLIT_W_SCORES) return apply_dispatch2<HD, SPLIT_W_SCORES>(a, st);
-  return apply_dispatch2<HD, SPLIT_W_GIVEN>(a, st);
 }
 
 }  // namespace
@@ -628,11 +636,10 @@ size_t split_score_lds(int r_b) {
                   sizeof(uint16_t) * (kScoreThreads / 64) * kStage);
 }
 
-size_t split_apply_lds(int r_d, int n_anchors) {
+size_t split_apply_lds(int r_d) {
   const int RKD = r_d / 16;
   return std::max(sizeof(uint16_t) * 2 * ((size_t)kApplyTile * (r_d + 8) + (size_t)kNCBW * RKD * kC),
-                  sizeof(uint16_t) * (kApplyThreads / 64) * kStage) +
-         sizeof(float) * (size_t)std::max(n_anchors, 1) * kApplyTile;
+                  sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
 }
 
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st) {
@@ -642,11 +649,18 @@ hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_split_apply(const SplitArgs& a, int wmode, int head_dim, hipStream_t st) {
-  if (a.D % kSW || a.N > kMaxAnchors) return hipErrorInvalidValue;
-  if (head_dim == 128) return apply_dispatch<128>(a, wmode, st);
-  if (head_dim == 64) return apply_dispatch<64>(a, wmode, st);
+hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st) {
+  if (a.D % kSW || a.N > kMaxAnchors || !a.wa) return hipErrorInvalidValue;
+  if (head_dim == 128) return apply_dispatch<128>(a, st);
+  if (head_dim == 64) return apply_dispatch<64>(a, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st) {
+  if (a.N > kMaxAnchors || !a.wa || a.n_corr < 1) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.S + 255) / 256), (unsigned)a.n_layers, 2);
+  split_weights<<<grid, 256, sizeof(float) * 256 * (size_t)a.n_corr, st>>>(a, wmode);
+  return hipGetLastError();
 }
 
 }  // namespace kvc

@@ -26,7 +26,8 @@ STATUS = {0: "KVC_OK", 1: "KVC_E_NULL", 2: "KVC_E_SHAPE", 3: "KVC_E_DTYPE", 4: "
 
 EXPORTS = ["kvc_abi_version", "kvc_status_str", "kvc_last_error", "kvc_workspace_size",
            "kvc_align_rope", "kvc_match_anchors", "kvc_apply_lowrank_delta", "kvc_correct_hop",
-           "kvc_correct_hops_batched", "kvc_svd_workspace_size", "kvc_anchor_refresh_svd"]
+           "kvc_correct_hops_batched", "kvc_svd_workspace_size", "kvc_anchor_refresh_svd",
+           "kvc_peak_copy", "kvc_peak_mfma_bf16", "kvc_peak_lds_read", "kvc_peak_valu"]
 
 
 class KvcError(RuntimeError):
@@ -54,7 +55,8 @@ class Pool(C.Structure):
 
 TRACE_MAX = 64
 KERNEL_NAMES = {1: "pack_base", 3: "score_cos_mfma", 4: "score_generic", 5: "gate_finalize", 6: "softmax",
-                7: "pack_delta", 8: "fused_hop", 9: "apply_generic", 10: "split_score", 11: "split_apply"}
+                7: "pack_delta", 8: "fused_hop", 9: "apply_generic", 10: "split_score", 11: "split_apply",
+                12: "split_weights"}
 
 
 class Trace(C.Structure):
@@ -121,6 +123,11 @@ def lib(path: Optional[str] = None):
     L.kvc_anchor_refresh_svd.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                          C.c_void_p, C.c_int, C.c_void_p, C.c_int32, C.c_int32, C.c_uint64,
                                          C.c_void_p, C.c_size_t, C.c_void_p]
+    L.kvc_peak_copy.restype = C.c_int
+    L.kvc_peak_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    for f in (L.kvc_peak_mfma_bf16, L.kvc_peak_lds_read, L.kvc_peak_valu):
+        f.restype = C.c_int
+        f.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
     _lib = L
     return L
 
@@ -382,6 +389,20 @@ def anchor_refresh_svd(z: torch.Tensor, rank: int, out_dtype=torch.float32, over
                                     power_iters, seed, _ptr(ws), ws.numel() if ws is not None else 0,
                                     _stream(stream)))
     return a, b, s
+
+
+def peak_copy(dst: torch.Tensor, src: torch.Tensor, stream=None):
+    """Measurement: dst <- src with the library's streaming copy kernel (same byte size)."""
+    nb = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nb
+    _check(lib().kvc_peak_copy(_ptr(dst), _ptr(src), nb, _stream(stream)))
+
+
+def peak_loop(kind: str, sink: torch.Tensor, n_blocks: int, iters: int, stream=None):
+    """Measurement loops: kind in {"mfma", "lds", "valu"}; sink holds n_blocks * 256 words."""
+    assert sink.numel() >= n_blocks * 256 and sink.element_size() == 4
+    f = {"mfma": lib().kvc_peak_mfma_bf16, "lds": lib().kvc_peak_lds_read, "valu": lib().kvc_peak_valu}[kind]
+    _check(f(_ptr(sink), n_blocks, iters, _stream(stream)))
 
 
 def pool_from(data, device) -> PoolTensors:
