@@ -184,8 +184,8 @@ bool cos_mfma_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
   return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
 }
 
-// The two-pass bf16 path: 256-token x 256-channel work-groups (D a multiple of 256), ranks
-// 16/32 for first-mode scores and 16/32/64 for the apply, within the LDS budget.
+// The two-pass bf16 path: 128-token x 256-channel work-groups (D a multiple of 256), ranks
+// 16/32 (larger ranks would not fit the two-per-CU register budget), within the LDS budget.
 constexpr size_t kLdsBudget = 160 * 1024;
 bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, bool pages_scores, bool apply) {
   if (p.dtype != KVC_BF16 || (prm.options & 3)) return false;
@@ -196,7 +196,7 @@ bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, boo
     if (split_score_lds(p.rank_base) + 8 * 1024 > kLdsBudget) return false;
   }
   if (apply) {
-    if (p.rank_delta != 16 && p.rank_delta != 32 && p.rank_delta != 64) return false;
+    if (p.rank_delta != 16 && p.rank_delta != 32) return false;
     if (split_apply_lds(p.rank_delta) + 2 * 1024 > kLdsBudget) return false;
   }
   return true;

@@ -176,8 +176,8 @@ hipError_t launch_fused(const FusedArgs& a, int mode, int head_dim, hipStream_t 
 // Score work-group = 256 tokens x 256 channels of one (layer, side), 8 waves of 64 x 128 (one
 // per CU).  Apply work-group = 128 tokens x 256 channels, 4 waves of 64 x 128; two share a CU
 // so one's streaming phases (source in, corrected cache out) overlap the other's MFMA phases.
-constexpr int kScoreTile = 256;
-constexpr int kScoreThreads = 512;
+constexpr int kScoreTile = 128;
+constexpr int kScoreThreads = 256;
 constexpr int kApplyTile = 128;
 constexpr int kApplyThreads = 256;
 constexpr int kSplitWidth = 256;

@@ -102,16 +102,30 @@ __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, AUX);
 }
 
+// LDS byte offset of a shared-memory pointer, and typed LDS reads at a byte offset
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_char*)p);
+}
+__device__ __forceinline__ uint4 lds_u4(uint32_t off) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)off);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float lds_f(uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)off);
+}
+
 template <int HD> __device__ __forceinline__ constexpr bool lower_blk(int b) { return ((b * 32) % HD) < HD / 2; }
 template <int HD> __device__ __forceinline__ constexpr int partner_blk(int b) { return b + HD / 64; }
 template <int HD> __device__ __forceinline__ int pair_index(int b, int row) { return (b * 32) % HD + row; }
 
-// Wave-private LDS staging of a 32-token x 128-channel bf16 half tile, rows padded to 132
-// elements (264 bytes: consecutive rows start 2 banks apart, so the accumulator-layout 8-byte
-// accesses of 16 lanes hit 32 distinct banks).  Global traffic goes through it with 16-byte
-// row-contiguous accesses (each token row is 256 contiguous bytes) instead of row-strided
-// 8-byte accesses in accumulator layout.
-constexpr int kStRow = 132;
+// Wave-private LDS staging of a 32-token x 128-channel bf16 half tile, rows padded to 136
+// elements (272 bytes: every row stays 16-byte aligned for the 16-byte accesses, and
+// consecutive rows start 4 banks apart, so the accumulator-layout 8-byte accesses of 16 lanes
+// hit 32 distinct banks).  Global traffic goes through it with 16-byte row-contiguous accesses
+// (each token row is 256 contiguous bytes) instead of row-strided 8-byte accesses in
+// accumulator layout.
+constexpr int kStRow = 136;
 constexpr int kStage = 32 * kStRow;            // elements per wave
 
 // 64 tokens x 128 channels (rows tw0.., channels d0..) of a layer's stored cache, buffer over
@@ -190,28 +204,6 @@ __device__ __forceinline__ void rotate_tile(f32x16 (&z)[2][4], const float* cs, 
   }
 }
 
-__device__ __forceinline__ float abs_sum(const f32x16& e) {
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; j += 4) {
-    s0 += fabsf(e[j]);
-    s1 += fabsf(e[j + 1]);
-    s2 += fabsf(e[j + 2]);
-    s3 += fabsf(e[j + 3]);
-  }
-  return (s0 + s1) + (s2 + s3);
-}
-
-__device__ __forceinline__ float sq_sum(const f32x16& e) {
-  float q0 = 0.f, q1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    q0 = fmaf(e[j], e[j], q0);
-    q1 = fmaf(e[j + 1], e[j + 1], q1);
-  }
-  return q0 + q1;
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -235,104 +227,149 @@ __device__ __forceinline__ TileId tile_id(const SplitArgs& p) {
 }
 
 // ================================================================== pass 1: scores
-// One anchor for a wave: 8 accumulator blocks (2 token x 4 channel), each E = Z_can - A B
-// reduced to per-lane |E| sums and (Q) masked E^2 sums.  The empty asm statement after each
-// block's epilogue "redefines" the A operands, so the compiler cannot hoist later MFMA chains
-// above it (which would need up to 8 live result blocks); the other wave of the SIMD fills
-// the MFMA-to-epilogue latency.
-template <int RK, bool Q>
-__device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], const uint16_t* as, const uint16_t* bs,
-                                             int col, int hi, int lane, float qm0, float qm1, float& ms0,
-                                             float& ms1, float& qs) {
-  constexpr int RS = RK * 16 + 8;
+// One anchor for a wave: 8 accumulator blocks (2 token x 4 channel, channel-block major), each
+// E = Z_can - A B reduced to per-lane |E| sums and (Q) E^2 sums.  Software-pipelined one block
+// deep: the MFMA chain of block b + 1 is issued before the VALU reduction of block b, and the
+// empty asm statement after each reduction "redefines" the A operands, so the compiler cannot
+// hoist the chain of block b + 2 above it (two live result blocks, not eight).
+// `slot`: LDS byte offset of the anchor's slot; `aoff[tb][ks]`: this lane's A fragment offsets
+// inside a slot; `boff`: this lane's offset of its first B chunk inside a slot.
+template <int RK, bool Q, typename RG>
+__device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t slot, const uint32_t (&aoff)[2][RK],
+                                             uint32_t boff, float qm0, float qm1, float& ms0, float& ms1,
+                                             float& qs) {
   bf16x8 av[2][RK];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < RK; ++ks)
-      av[tb][ks] = as_bf8(*reinterpret_cast<const uint4*>(as + (tb * 32 + col) * RS + ks * 16 + 8 * hi));
+    for (int ks = 0; ks < RK; ++ks) av[tb][ks] = as_bf8(lds_u4(slot + aoff[tb][ks]));
+  const uint32_t bs = slot + boff;
+  float m[2] = {0.f, 0.f}, q[2] = {0.f, 0.f};
+  auto chain = [&](const bf16x8* bv, int tb, int db) {
+    f32x16 e = mfma(bv[0], av[tb][0], z[tb][db]);
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    bf16x8 bv[RK];
+    for (int ks = 1; ks < RK; ++ks) e = mfma(bv[ks], av[tb][ks], e);
+    return e;
+  };
+  auto reduce = [&](const f32x16& e, int tb) {
 #pragma unroll
-    for (int ks = 0; ks < RK; ++ks) bv[ks] = as_bf8(*reinterpret_cast<const uint4*>(bs + (db * RK + ks) * kC + lane * 8));
+    for (int j = 0; j < 16; ++j) m[tb] += fabsf(e[j]);
+    if (Q) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      f32x16 e = mfma(bv[0], av[tb][0], z[tb][db]);
-#pragma unroll
-      for (int ks = 1; ks < RK; ++ks) e = mfma(bv[ks], av[tb][ks], e);
-      const float s = abs_sum(e);
-      if (tb == 0) ms0 += s; else ms1 += s;
-      if (Q) qs = fmaf(sq_sum(e), tb == 0 ? qm0 : qm1, qs);
-      if constexpr (RK == 1)
-        asm volatile("" : "+v"(av[0][0]), "+v"(av[1][0]), "+v"(ms0), "+v"(ms1), "+v"(qs));
-      else if constexpr (RK == 2)
-        asm volatile("" : "+v"(av[0][0]), "+v"(av[0][1]), "+v"(av[1][0]), "+v"(av[1][1]), "+v"(ms0), "+v"(ms1),
-                     "+v"(qs));
-      else
-        asm volatile("" : "+v"(av[0][0]), "+v"(av[1][0]), "+v"(ms0), "+v"(ms1), "+v"(qs));
+      for (int j = 0; j < 16; ++j) q[tb] = fmaf(e[j], e[j], q[tb]);
     }
+  };
+  bf16x8 bv[RK];
+#pragma unroll
+  for (int ks = 0; ks < RK; ++ks) bv[ks] = as_bf8(lds_u4(bs + ks * 1024));
+  f32x16 e = chain(bv, 0, 0);
+#pragma unroll
+  for (int b = 1; b <= 8; ++b) {
+    f32x16 en;
+    if (b < 8) {
+      const int db = b >> 1, tb = b & 1;
+      if (tb == 0) {
+#pragma unroll
+        for (int ks = 0; ks < RK; ++ks) bv[ks] = as_bf8(lds_u4(bs + (db * RK + ks) * 1024));
+      }
+      en = chain(bv, tb, db);
+    }
+    reduce(e, (b - 1) & 1);
+    // the q sums are tied too: left free, their FMAs sink and keep every block alive
+    if constexpr (RK == 1)
+      asm volatile("" : "+v"(av[0][0]), "+v"(av[1][0]), "+v"(m[0]), "+v"(m[1]), "+v"(q[0]), "+v"(q[1]));
+    else
+      asm volatile("" : "+v"(av[0][0]), "+v"(av[0][1]), "+v"(av[1][0]), "+v"(av[1][1]), "+v"(m[0]), "+v"(m[1]),
+                   "+v"(q[0]), "+v"(q[1]));
+    e = en;
   }
+  ms0 += m[0];
+  ms1 += m[1];
+  if (Q) qs = fmaf(q[0], qm0, fmaf(q[1], qm1, qs));
 }
 
-// Streams one anchor's operands into LDS: A rows t0 .. t0+127 (rank R, rows >= lim are 0) and
-// the work-group's packed B slice (kNCBW x RK chunks, contiguous).  Thread tid owns RK units
-// of A and 2 RK of B; `issue` loads them into registers, `commit` writes them to a slot.
-template <int UA, int UB>
-struct Operands {
-  uint4 a[UA], b[UB];
-  float w[UA];
-};
+// ------------------------------------------------------------ operand ring (LDS, DMA-filled)
+// Anchor operands stream from memory straight into LDS with buffer->LDS DMA (each lane of a
+// wave instruction moves 16 bytes to LDS base + 16 * lane; lanes past the descriptor's size
+// write zeros), into a ring of kSlots slots: slot j % kSlots holds anchor j's A rows, its B
+// slice and (apply) its token weights.  Anchor j + 2 is fetched while anchor j is consumed; a
+// step waits only for its own slot (vmcnt), then a bare barrier (no release fence, which
+// would drain every DMA in flight).
+constexpr int kSlots = 3;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// A: buffer over the anchor's first `lim` rows (R bf16 each, rows >= lim read as 0); B: buffer
-// over the work-group's packed slice.  With TT tokens and NT threads, A unit u = tid + NT i
-// (i < UA = TT R / 8 / NT) is row u / (R/8), 16-byte column u % (R/8) of the tile; B unit
-// u = tid + NT i (i < UB = 512 RK / NT) is bytes [16 u, 16 u + 16) of the slice.
-template <int RK, int TT, int NT>
-struct Stream {
-  static constexpr int R = RK * 16, RS = R + 8;
-  static constexpr int UA = TT * (R / 8) / NT, UB = kNCBW * RK * 64 / NT;
-  using Ops = Operands<UA, UB>;
-  static __device__ __forceinline__ void issue(Ops& o, rsrc_t A, rsrc_t B, int t0, int tid) {
+// The transfer is issued through inline assembly: the compiler then neither reorders LDS
+// accesses around it nor makes every later LDS read wait for all transfers in flight (it cannot
+// tell ring slots apart); the explicit waits below order each slot's transfer before its reads.
+// LDS address in M0 (wave-uniform), 16 bytes per lane at M0 + 16 * lane.
+// M0 is written only here (nothing else in these kernels uses it).
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory");
+}
+
+
+// s_waitcnt with vmcnt <= N and lgkmcnt = 0 (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] in [15:14]), then the work-group barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
+// Slot layout for rank 16 RK, TT tokens, NW waves: A rows (TT x R bf16, 16-byte units
+// swizzled so the fragment reads of 16 consecutive rows hit distinct banks), the B slice
+// (kNCBW x RK packed 1 KiB chunks), the TT token weights (fp32, apply only).
+template <int RK, int TT, int NW, bool W>
+struct Ring {
+  static constexpr int R = RK * 16;
+  static constexpr int U = R / 8;                       // 16-byte units per A row
+  static constexpr int A_BYTES = TT * R * 2;
+  static constexpr int B_BYTES = kNCBW * RK * 1024;
+  static constexpr int W_BYTES = W ? TT * 4 : 0;
+  static constexpr int SLOT = A_BYTES + B_BYTES + W_BYTES;
+  static constexpr int A_PER_WAVE = A_BYTES / 1024 / NW;
+  static constexpr int B_PER_WAVE = B_BYTES / 1024 / NW;
+  static constexpr int W_LANES = W ? TT / 4 / NW : 0;    // lanes per wave moving weights
+  static constexpr int DMA_PER_WAVE = A_PER_WAVE + B_PER_WAVE + (W ? 1 : 0);
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "ring split");
+  static_assert(!W || (TT % (4 * NW) == 0 && W_LANES <= 64), "weight split");
+
+  // 16-byte unit of A row `row`, column unit `c`, inside the slot
+  static __device__ __forceinline__ int a_unit(int row, int c) { return row * U + (c ^ ((row / (16 / U)) & (U - 1))); }
+
+  // DMA anchor operands into `slot`: A rows t0.. of buffer `Ar` (rows past its size read 0),
+  // B slice of buffer `Br`, weights t0.. of buffer `Wr`.
+  // `slot`: LDS byte offset of the slot (wave-uniform); `wave` must be wave-uniform too
+  static __device__ __forceinline__ void fetch(uint32_t slot, rsrc_t Ar, rsrc_t Br, rsrc_t Wr, int t0, int wave,
+                                               int lane) {
 #pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      const int u = tid + i * NT;
-      const int row = u / (R / 8), c = u - row * (R / 8);
-      o.a[i] = bload16<kStream>(A, (uint32_t)(((t0 + row) * R + c * 8) * 2));
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+      const int u = (wave * A_PER_WAVE + i) * 64 + lane;     // LDS unit this lane fills
+      const int row = u / U, cpos = u % U;
+      const int c = cpos ^ ((row / (16 / U)) & (U - 1));     // global unit stored there
+      dma16(Ar, slot + (wave * A_PER_WAVE + i) * 1024, (uint32_t)(((t0 + row) * R + c * 8) * 2));
     }
 #pragma unroll
-    for (int i = 0; i < UB; ++i) o.b[i] = bload16(B, (uint32_t)(tid + i * NT) * 16u);
-  }
-  // with the token weights of the A rows (buffer over one anchor's weight row, fp32)
-  static __device__ __forceinline__ void issue_w(Ops& o, rsrc_t A, rsrc_t B, rsrc_t W, int t0, int tid) {
-    issue(o, A, B, t0, tid);
-#pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      const int row = (tid + i * NT) / (R / 8);
-      o.w[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(W, (t0 + row) * 4, 0, 0));
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int kc = wave * B_PER_WAVE + i;
+      dma16(Br, slot + A_BYTES + kc * 1024, (uint32_t)(kc * 1024 + lane * 16));
     }
-  }
-  template <bool SCALE>
-  static __device__ __forceinline__ void commit(const Ops& o, uint16_t* as, uint16_t* bs, int tid) {
-#pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      const int u = tid + i * NT;
-      const int row = u / (R / 8), c = u - row * (R / 8);
-      const uint4 x = SCALE ? scale8(o.a[i], o.w[i]) : o.a[i];
-      *reinterpret_cast<uint4*>(as + row * RS + c * 8) = x;
+    if constexpr (W) {
+      if (lane < W_LANES)
+        dma16(Wr, slot + A_BYTES + B_BYTES + wave * W_LANES * 16, (uint32_t)((t0 + (wave * W_LANES + lane) * 4) * 4));
     }
-#pragma unroll
-    for (int i = 0; i < UB; ++i) *reinterpret_cast<uint4*>(bs + (tid + i * NT) * 8) = o.b[i];
   }
 };
 
 template <int HD, int RK>
-__global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
+__global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
   constexpr int kST = kScoreTile, kNT = kScoreThreads, kNW = kNT / 64;
-  using SM = Stream<RK, kST, kNT>;
-  constexpr int R = RK * 16, RS = R + 8;
-  constexpr int ASZ = kST * RS, BSZ = kNCBW * RK * kC;
-  extern __shared__ __attribute__((aligned(16))) uint16_t dyn[];   // As[2][ASZ], Bs[2][BSZ]
+  using RG = Ring<RK, kST, kNW, false>;
+  constexpr int R = RK * 16;
+  extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
   __shared__ float mp[2][2][kST];
   __shared__ float qp[kNW][kMaxAnchors];
   __shared__ float tab[2][kFusedHalf];
@@ -344,8 +381,6 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
   const int D = p.D, S = p.S, N = p.N, NCB = D >> 5;
   const int t0 = id.tt * kST, tw0 = t0 + tw * 64;
   const int d0 = id.cq * kSW + cw * 128;
-  uint16_t* As = dyn;
-  uint16_t* Bs = dyn + 2 * ASZ;
 
   const uint8_t* list = keys ? p.corr : p.use;
   int nl = keys ? p.n_corr : p.n_use;
@@ -357,86 +392,84 @@ __global__ void __launch_bounds__(kScoreThreads) split_score(SplitArgs p) {
     tab[1][i] = p.can.sn[i];
   }
   const Slots sl = load_slots(list, keys ? p.n_corr : p.n_use, p.off, p.len, S, lane);
-  __syncthreads();
 
   const uint16_t* Al = p.Ab[id.side] + id.layer * p.ab_layer;
   const uint16_t* Bl = p.Bb[id.side] + (((int64_t)id.layer * N) * NCB + id.cq * kNCBW) * RK * kC;
   const int64_t bstride = (int64_t)NCB * RK * kC;
-  // past the end of the list the descriptors have size 0: the loads return 0 and fetch nothing,
-  // so the pipeline below issues and commits unconditionally (no branches around memory ops)
-  auto src = [&](int j, typename SM::Ops& o) {
+  // past the end of the list the descriptors have size 0: the DMA writes zeros and fetches
+  // nothing, so every step issues the same number of transfers
+  const uint32_t ring0 = lds_off(ring);
+  const int wv = uni(wave);
+  auto fetch = [&](int j) {
     const bool live = j < nl;
     const int js = live ? j : 0;
     const int a = lane_get(sl.a, js);
     const int lim = live ? lane_get(sl.lim, js) : 0;
-    SM::issue(o, make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
-                       make_rsrc(Bl + a * bstride, live ? BSZ * 2 : 0), t0, tid);
+    RG::fetch(ring0 + (uint32_t)(j % kSlots) * RG::SLOT,
+              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
+              make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(nullptr, 0), t0, wv, lane);
   };
-
-  // two register sets: set j & 1 holds anchor j's operands from two steps before it is used
-  typename SM::Ops o0, o1;
-  src(0, o0);
-  src(1, o1);
-  f32x16 z[2][4];
-  if (nl > 0) {
-    load_tile(z, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, (uint32_t)S * D * 2), tw0, D, d0,
-              dyn + wave * kStage, lane, col, hi);
-    if (keys && p.can.active) rotate_tile<HD>(z, tab[0], tab[1], hi);
-  }
-  __syncthreads();   // the staging area overlaps the operand slots
-  SM::template commit<false>(o0, As, Bs, tid);
-  src(2, o0);
-  __syncthreads();
+  uint32_t aoff[2][RK];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < RK; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
+  const uint32_t boff = RG::A_BYTES + cw * 4 * RK * 1024 + lane * 16;
 
   const float qm0 = (tw0 + col < p.k_gate && tw0 + col < S) ? 1.f : 0.f;
   const float qm1 = (tw0 + 32 + col < p.k_gate && tw0 + 32 + col < S) ? 1.f : 0.f;
   float* mpart = p.mpart + (((int64_t)id.cq * 2 + id.side) * p.n_layers + id.layer) * N * S;
+  auto store_m = [&](int j) {   // partial |E| sums of anchor j (LDS buffer j & 1), both channel halves
+    const int a = lane_get(sl.a, j);
+    if (((p.mask_corr >> a) & 1) && tid < kST) {
+      const int t = t0 + tid;
+      if (t < S) mpart[(int64_t)a * S + t] = mp[j & 1][0][tid] + mp[j & 1][1][tid];
+    }
+  };
 
-  // the two pipeline stages are instantiated separately (compile-time slot, distinct marker),
-  // so the compiler cannot fold them into one body that shares a single register set
-  auto step = [&](auto stage, int j, typename SM::Ops& onext) {
-    constexpr int buf = decltype(stage)::value;
-    asm volatile("; pipeline stage %0" ::"n"(buf));
-    const bool live = j < nl;
-    const int a = lane_get(sl.a, live ? j : 0);
-    const bool want_m = live && ((p.mask_corr >> a) & 1);
-    const bool want_q = live && !keys && ((p.mask_gate >> a) & 1) && t0 < p.k_gate;
-    if (live) {
-      const uint16_t* as = As + buf * ASZ + tw * 64 * RS;
-      const uint16_t* bs = Bs + buf * BSZ + cw * 4 * RK * kC;
+  // value rows also accumulate the gate sums (Eq. 9), masked per anchor afterwards
+  auto run = [&](const f32x16 (&z)[2][4], auto values) {
+    constexpr bool Q = decltype(values)::value;
+#pragma nounroll
+    for (int j = 0; j < nl; ++j) {
+      wait_vm_barrier<RG::DMA_PER_WAVE>();   // anchor j landed for every wave; slot (j + 2) % 3 is free
+      if (j > 0) store_m(j - 1);
+      fetch(j + 2);
+      const int a = lane_get(sl.a, j);
+      const uint32_t slot = ring0 + (uint32_t)(j % kSlots) * RG::SLOT;
       float ms0 = 0.f, ms1 = 0.f, qs = 0.f;
-      if (want_q)
-        score_anchor<RK, true>(z, as, bs, col, hi, lane, qm0, qm1, ms0, ms1, qs);
-      else
-        score_anchor<RK, false>(z, as, bs, col, hi, lane, qm0, qm1, ms0, ms1, qs);
-      if (want_m) {
+      score_anchor<RK, Q, RG>(z, slot, aoff, boff, qm0, qm1, ms0, ms1, qs);
+      if ((p.mask_corr >> a) & 1) {
         ms0 += __shfl_xor(ms0, 32);
         ms1 += __shfl_xor(ms1, 32);
         if (hi == 0) {
-          mp[buf][cw][tw * 64 + col] = ms0;
-          mp[buf][cw][tw * 64 + 32 + col] = ms1;
+          mp[j & 1][cw][tw * 64 + col] = ms0;
+          mp[j & 1][cw][tw * 64 + 32 + col] = ms1;
         }
       }
-      if (want_q) {
+      if (Q && ((p.mask_gate >> a) & 1)) {
         qs = wave_sum(qs);
         if (lane == 0) qp[wave][a] = qs;
       }
     }
-    // anchor j + 1 (fetched two steps ago into onext) goes to the other slot; anchor j + 3 is
-    // fetched into the freed registers
-    SM::template commit<false>(onext, As + (buf ^ 1) * ASZ, Bs + (buf ^ 1) * BSZ, tid);
-    src(j + 3, onext);
-    __syncthreads();
-    if (want_m && tid < kST) {
-      const int t = t0 + tid;
-      if (t < S) mpart[(int64_t)a * S + t] = mp[buf][0][tid] + mp[buf][1][tid];
-    }
   };
-  for (int j = 0; j < nl; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, o1);
-    step(std::integral_constant<int, 1>{}, j + 1, o0);
+  if (nl > 0) {
+    f32x16 z[2][4];
+    fetch(0);
+    __syncthreads();   // rotation table
+    // staging (wave-private) in the ring past slot 0, free until anchor 1 is fetched
+    load_tile(z, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, (uint32_t)S * D * 2), tw0, D, d0,
+              reinterpret_cast<uint16_t*>(ring + RG::SLOT) + wave * kStage, lane, col, hi);
+    if (keys && p.can.active) rotate_tile<HD>(z, tab[0], tab[1], hi);
+    wait_vm_barrier<63>();   // every wave is done with the staging area
+    fetch(1);
+    if (keys)
+      run(z, std::false_type{});
+    else
+      run(z, std::true_type{});
   }
-  __syncthreads();
+  wait_vm_barrier<0>();   // also drains the trailing (empty) transfers
+  if (nl > 0) store_m(nl - 1);
   if (!keys && p.partials) {
     float* part = p.partials + ((int64_t)id.layer * p.ntt * p.nct + (int64_t)id.tt * p.nct + id.cq) * N;
     for (int a = tid; a < N; a += kNT) {
@@ -502,14 +535,13 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
 
 // ================================================================== pass 2: apply
 // Sec. 3.3 Eq. 8 / App. A.3 Eq. 12: out = R(s) Z + sum_a w_a A_a B'_a, the token weights read
-// anchor-major (split_weights) and folded into the A rows on their way into LDS.
+// anchor-major (split_weights) and folded into the A fragments after they leave LDS.
 template <int HD, int RKD>
 __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
-  constexpr int kST = kApplyTile, kNT = kApplyThreads;
-  using SM = Stream<RKD, kST, kNT>;
-  constexpr int R = RKD * 16, RS = R + 8;
-  constexpr int ASZ = kST * RS, BSZ = kNCBW * RKD * kC;
-  extern __shared__ __attribute__((aligned(16))) uint16_t dyn[];   // As[2][ASZ], Bs[2][BSZ] | staging
+  constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
+  using RG = Ring<RKD, kST, kNW, true>;
+  constexpr int R = RKD * 16;
+  extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
   __shared__ float tab[2][kFusedHalf];
 
   const TileId id = tile_id(p);
@@ -519,8 +551,6 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
   const int D = p.D, S = p.S, N = p.N, NCB = D >> 5;
   const int t0 = id.tt * kST, tw0 = t0 + tw * 64;
   const int d0 = id.cq * kSW + cw * 128;
-  uint16_t* As = dyn;
-  uint16_t* Bs = dyn + 2 * ASZ;
 
   for (int i = tid; i < HD / 2; i += kNT) {
     tab[0][i] = p.shift.cs[i];
@@ -533,62 +563,58 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
   const float* Wl = p.wa + ((int64_t)id.side * p.n_layers + id.layer) * N * S;
   const int64_t bstride = (int64_t)NCB * RKD * kC;
   // zero-size descriptors past the correction set (see split_score)
-  auto src = [&](int j, typename SM::Ops& o) {
+  const uint32_t ring0 = lds_off(ring);
+  const int wv = uni(wave);
+  auto fetch = [&](int j) {
     const bool live = j < nc;
     const int js = live ? j : 0;
     const int a = lane_get(sl.a, js);
     const int lim = live ? lane_get(sl.lim, js) : 0;
-    SM::issue_w(o, make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
-                make_rsrc(Bl + a * bstride, live ? BSZ * 2 : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
-                t0, tid);
+    RG::fetch(ring0 + (uint32_t)(j % kSlots) * RG::SLOT,
+              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
+              make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
+              t0, wv, lane);
   };
-  typename SM::Ops o0, o1;
-  src(0, o0);
-  src(1, o1);
+  uint32_t aoff[2][RKD];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < RKD; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
+  const uint32_t boff = RG::A_BYTES + cw * 4 * RKD * 1024 + lane * 16;
+  const uint32_t woff = RG::A_BYTES + RG::B_BYTES + (tw * 64 + col) * 4;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(ring + RG::SLOT) + wave * kStage;
 
-  // ---- residual: R(s) K or V
+  if (nc > 0) fetch(0);
+  __syncthreads();   // rotation table
+  // ---- residual: R(s) K or V (staging in the ring past slot 0, free until anchor 1 is fetched)
   f32x16 acc[2][4];
   const uint32_t layer_bytes = (uint32_t)S * D * 2;
-  __syncthreads();   // rotation table
-  load_tile(acc, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, dyn + wave * kStage,
-            lane, col, hi);
+  load_tile(acc, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, stage, lane, col, hi);
   if (keys && p.shift.active) rotate_tile<HD>(acc, tab[0], tab[1], hi);
-  __syncthreads();   // the staging area overlaps the operand slots
-  SM::template commit<true>(o0, As, Bs, tid);
-  src(2, o0);
-  __syncthreads();
-  // the two pipeline stages are instantiated separately (compile-time slot, distinct marker),
-  // so the compiler cannot fold them into one body that shares a single register set
-  auto step = [&](auto stage, int j, typename SM::Ops& onext) {
-    constexpr int buf = decltype(stage)::value;
-    asm volatile("; pipeline stage %0" ::"n"(buf));
-    if (j < nc) {
-      const uint16_t* as = As + buf * ASZ + tw * 64 * RS;
-      const uint16_t* bs = Bs + buf * BSZ + cw * 4 * RKD * kC;
+  if (nc > 0) {
+    wait_vm_barrier<63>();   // every wave is done with the staging area
+    fetch(1);
+  }
+#pragma nounroll
+  for (int j = 0; j < nc; ++j) {
+    wait_vm_barrier<RG::DMA_PER_WAVE>();   // anchor j landed for every wave; slot (j + 2) % 3 is free
+    fetch(j + 2);
+    const uint32_t slot = ring0 + (uint32_t)(j % kSlots) * RG::SLOT;
+    const float w0 = lds_f(slot + woff), w1 = lds_f(slot + woff + 128);
 #pragma unroll
-      for (int ks = 0; ks < RKD; ++ks) {
-        const bf16x8 a0 = as_bf8(*reinterpret_cast<const uint4*>(as + col * RS + ks * 16 + 8 * hi));
-        const bf16x8 a1 = as_bf8(*reinterpret_cast<const uint4*>(as + (32 + col) * RS + ks * 16 + 8 * hi));
+    for (int ks = 0; ks < RKD; ++ks) {
+      const bf16x8 a0 = as_bf8(scale8(lds_u4(slot + aoff[0][ks]), w0));
+      const bf16x8 a1 = as_bf8(scale8(lds_u4(slot + aoff[1][ks]), w1));
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8 b = as_bf8(*reinterpret_cast<const uint4*>(bs + (db * RKD + ks) * kC + lane * 8));
-          acc[0][db] = mfma(b, a0, acc[0][db]);
-          acc[1][db] = mfma(b, a1, acc[1][db]);
-        }
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 b = as_bf8(lds_u4(slot + boff + (db * RKD + ks) * 1024));
+        acc[0][db] = mfma(b, a0, acc[0][db]);
+        acc[1][db] = mfma(b, a1, acc[1][db]);
       }
     }
-    SM::template commit<true>(onext, As + (buf ^ 1) * ASZ, Bs + (buf ^ 1) * BSZ, tid);
-    src(j + 3, onext);
-    __syncthreads();
-  };
-  for (int j = 0; j < nc; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, o1);
-    step(std::integral_constant<int, 1>{}, j + 1, o0);
   }
-
-  // the last step ended with a barrier: the operand slots are free for the output staging
-  store_tile(acc, make_rsrc(p.out[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, dyn + wave * kStage,
-             lane, col, hi);
+  wait_vm_barrier<0>();   // trailing (empty) transfers drained, every wave past its last reads
+  store_tile(acc, make_rsrc(p.out[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, stage, lane, col, hi);
 }
 
 template <typename K>
@@ -610,7 +636,6 @@ hipError_t score_dispatch(const SplitArgs& a, hipStream_t st) {
   switch (a.r_b) {
     case 16: return go(split_score<HD, 1>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
     case 32: return go(split_score<HD, 2>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
-    case 64: return go(split_score<HD, 4>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -621,25 +646,21 @@ hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
   switch (a.r_d) {
     case 16: return go(split_apply<HD, 1>, a, kApplyTile, kApplyThreads, lds, st);
     case 32: return go(split_apply<HD, 2>, a, kApplyTile, kApplyThreads, lds, st);
-    case 64: return go(split_apply<HD, 4>, a, kApplyTile, kApplyThreads, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-// dynamic LDS: two operand slots (A rows + packed B slice) or the 8 waves' staging areas,
-// whichever is larger, then (apply) the token weights
+// dynamic LDS: the operand ring, or slot 0 plus the waves' staging areas, whichever is larger
 size_t split_score_lds(int r_b) {
-  const int RK = r_b / 16;
-  return std::max(sizeof(uint16_t) * 2 * ((size_t)kScoreTile * (r_b + 8) + (size_t)kNCBW * RK * kC),
-                  sizeof(uint16_t) * (kScoreThreads / 64) * kStage);
+  const size_t slot = (size_t)kScoreTile * r_b * 2 + (size_t)kNCBW * (r_b / 16) * 1024;
+  return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kScoreThreads / 64) * kStage);
 }
 
 size_t split_apply_lds(int r_d) {
-  const int RKD = r_d / 16;
-  return std::max(sizeof(uint16_t) * 2 * ((size_t)kApplyTile * (r_d + 8) + (size_t)kNCBW * RKD * kC),
-                  sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
+  const size_t slot = (size_t)kApplyTile * r_d * 2 + (size_t)kNCBW * (r_d / 16) * 1024 + (size_t)kApplyTile * 4;
+  return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
 }
 
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st) {
