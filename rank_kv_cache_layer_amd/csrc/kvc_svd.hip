@@ -1,16 +1,488 @@
-// Rank-r factor refresh (KVCMAS Eq. 7, App. B.1 "Factorization and Measurement").
+// Rank-r factor refresh (KVCMAS Sec. 3.3 Eq. 7, App. B.1 "Factorization and Measurement"):
+// Z ~ A B with A = U_r Sigma_r and B = R_r^T, for a batch of fp32 matrices Z [rows][cols].
+//
+// The pages name no method; this is randomised subspace iteration (Halko, Martinsson & Tropp,
+// "Finding structure with randomness", SIAM Review 2011, Alg. 4.4) with a Gaussian sketch of
+// l = rank + oversample columns and `power_iters` power iterations, every intermediate basis
+// re-orthonormalised by CholeskyQR2 (Fukaya et al. 2014) with a fp64 Gram matrix.  Directions
+// whose Cholesky pivot vanishes (rank-deficient sketches, e.g. an exactly rank-r Z) are dropped
+// (their basis columns set to zero).  The small problem is solved as the symmetric
+// eigenproblem of the l x l Gram matrix of Bsk = Q^T Z (fp64) by parallel cyclic Jacobi
+// (Golub & Van Loan, Matrix Computations, Sec. 8.5): Bsk Bsk^T = W Lambda W^T, sigma = sqrt(lambda),
+// A = Q W_r Sigma_r, B = Sigma_r^-1 W_r^T Bsk.  Each component is signed so that the
+// largest-magnitude entry of its left singular vector (column of A) is positive.
+//
+// Kernels: sketch (counter-based Gaussian draws), a batched tiled GEMM for every product
+// (VALU FMA in fp32 or fp64; the refresh is off the time-to-first-token path), Cholesky with
+// pivot dropping + triangular inverse, Jacobi, top-r selection, sign fix.
+#include <math.h>
+
 #include "kvc_internal.h"
 
 namespace kvc {
+namespace {
 
-size_t svd_workspace_bytes(int n_mats, int rows, int cols, int rank, int oversample) {
-  (void)n_mats; (void)rows; (void)cols; (void)rank; (void)oversample;
-  return 256;
+typedef uint16_t bf16_bits;
+
+// ------------------------------------------------------------------ counter-based sketch
+// splitmix64 finaliser (Steele, Lea & Flood, "Fast splittable pseudorandom number generators",
+// OOPSLA 2014), applied to (seed, element index); two 32-bit halves -> Box-Muller normal.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
 }
 
-hipError_t svd_refresh(const float*, int, int, int, int, void*, void*, int, float*, int, int, uint64_t, void*, size_t,
-                       hipStream_t) {
-  return hipErrorNotSupported;
+__global__ void __launch_bounds__(256) sketch(float* om, int64_t count, uint64_t seed) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const uint64_t r = splitmix64(seed ^ splitmix64((uint64_t)i));
+  const double u1 = ((double)(uint32_t)(r >> 32) + 1.0) * (1.0 / 4294967296.0);   // (0, 1]
+  const double u2 = (double)(uint32_t)r * (1.0 / 4294967296.0);                    // [0, 1)
+  om[i] = (float)(sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2));
+}
+
+// ------------------------------------------------------------------ batched tiled GEMM
+// C[b] (M x N) = opA(A[b]) (M x K) * opB(B[b]) (K x N), products and sums in ACC.
+// opA[i][k] = TRA ? A[k * lda + i] : A[i * lda + k]; opB[k][j] = TRB ? B[j * ldb + k] : B[k * ldb + j].
+// 64 x 64 tile per work-group of 256 threads (4 x 4 outputs each), K in steps of 16 through LDS;
+// every tail is bounds-checked.
+template <typename T> __device__ __forceinline__ double to_d(T x) { return (double)x; }
+template <typename T> __device__ __forceinline__ T from_acc(double x);
+template <> __device__ __forceinline__ float from_acc<float>(double x) { return (float)x; }
+template <> __device__ __forceinline__ double from_acc<double>(double x) { return x; }
+template <> __device__ __forceinline__ bf16_bits from_acc<bf16_bits>(double x) {
+  return __builtin_bit_cast(bf16_bits, (__bf16)(float)x);
+}
+
+template <typename TA, typename TB, typename TC, typename ACC, bool TRA, bool TRB>
+__global__ void __launch_bounds__(256) gemm(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ C,
+                                            int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA,
+                                            int64_t sB, int64_t sC) {
+  __shared__ ACC As[16][64 + 1];
+  __shared__ ACC Bs[16][64 + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  ACC acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = (ACC)0;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      int i, k;
+      if (TRA) { i = e & 63; k = e >> 6; } else { i = e >> 4; k = e & 15; }
+      const int gi = i0 + i, gk = k0 + k;
+      ACC x = (ACC)0;
+      if (gi < M && gk < K) x = (ACC)(TRA ? A[(int64_t)gk * lda + gi] : A[(int64_t)gi * lda + gk]);
+      As[k][i] = x;
+      int j, kb;
+      if (TRB) { j = e >> 4; kb = e & 15; } else { j = e & 63; kb = e >> 6; }
+      const int gj = j0 + j, gkb = k0 + kb;
+      ACC y = (ACC)0;
+      if (gj < N && gkb < K) y = (ACC)(TRB ? B[(int64_t)gj * ldb + gkb] : B[(int64_t)gkb * ldb + gj]);
+      Bs[kb][j] = y;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      ACC a[4], b[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = As[k][ty * 4 + r];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[c] = Bs[k][tx * 4 + c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fma(a[r], b[c], acc[r][c]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gi = i0 + ty * 4 + r;
+    if (gi >= M) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int gj = j0 + tx * 4 + c;
+      if (gj < N) C[(int64_t)gi * ldc + gj] = from_acc<TC>((double)acc[r][c]);
+    }
+  }
+}
+
+template <typename TA, typename TB, typename TC, typename ACC, bool TRA, bool TRB>
+hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
+                    int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
+  gemm<TA, TB, TC, ACC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ Cholesky with dropping
+// In: G [l][l] (symmetric positive semi-definite Gram matrix, fp64).  Out: Li [l][l] = L^-1
+// with G ~ L L^T, rows and columns of dropped pivots zero, so that Y Li^T has orthonormal or
+// zero columns.  A pivot is dropped when it falls below `rel_tol` times the largest diagonal
+// entry of G.  One work-group per matrix; G is overwritten by L.
+__global__ void __launch_bounds__(1024) chol_inv(double* G, double* Li, int l, double rel_tol) {
+  __shared__ double diag_max;
+  __shared__ double piv;
+  __shared__ int dead[256];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  G += (int64_t)blockIdx.x * l * l;
+  Li += (int64_t)blockIdx.x * l * l;
+  if (tid == 0) {
+    double m = 0.0;
+    for (int i = 0; i < l; ++i) m = fmax(m, G[(int64_t)i * l + i]);
+    diag_max = m;
+  }
+  __syncthreads();
+  const double tol = rel_tol * diag_max;
+  for (int k = 0; k < l; ++k) {
+    if (tid == 0) {
+      const double d = G[(int64_t)k * l + k];
+      const bool drop = !(d > tol);
+      dead[k] = drop;
+      piv = drop ? 0.0 : sqrt(d);
+      G[(int64_t)k * l + k] = drop ? 1.0 : sqrt(d);
+    }
+    __syncthreads();
+    const double p = piv;
+    for (int i = k + 1 + tid; i < l; i += nt) G[(int64_t)i * l + k] = p > 0.0 ? G[(int64_t)i * l + k] / p : 0.0;
+    __syncthreads();
+    // trailing update of the lower triangle: G[i][j] -= L[i][k] L[j][k], k < j <= i
+    const int rem = l - k - 1;
+    for (int e = tid; e < rem * rem; e += nt) {
+      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
+      if (j <= i) G[(int64_t)i * l + j] -= G[(int64_t)i * l + k] * G[(int64_t)j * l + k];
+    }
+    __syncthreads();
+  }
+  // Li = L^-1 by forward substitution, one column per thread
+  for (int c = tid; c < l; c += nt) {
+    for (int i = 0; i < c; ++i) Li[(int64_t)i * l + c] = 0.0;
+    if (dead[c]) {
+      for (int i = c; i < l; ++i) Li[(int64_t)i * l + c] = 0.0;
+      continue;
+    }
+    Li[(int64_t)c * l + c] = 1.0 / G[(int64_t)c * l + c];
+    for (int i = c + 1; i < l; ++i) {
+      double s = 0.0;
+      for (int k = c; k < i; ++k) s += G[(int64_t)i * l + k] * Li[(int64_t)k * l + c];
+      Li[(int64_t)i * l + c] = dead[i] ? 0.0 : -s / G[(int64_t)i * l + i];
+    }
+  }
+  __syncthreads();
+  // dropped directions contribute nothing: zero their rows
+  for (int e = tid; e < l * l; e += nt)
+    if (dead[e / l]) Li[e] = 0.0;
+}
+
+// ------------------------------------------------------------------ Jacobi eigensolver
+// Symmetric A [l][l] (fp64, overwritten; its diagonal ends as the eigenvalues) and V [l][l]
+// (out: eigenvectors as columns).  Parallel cyclic Jacobi with round-robin pairing: each round
+// rotates l/2 disjoint index pairs, (c, s) from Golub & Van Loan's symmetric 2x2 Schur step,
+// A <- J^T A J, V <- V J.  Sweeps until the off-diagonal mass is below tol^2 of the total, or
+// max_sweeps.  One work-group per matrix.
+__global__ void __launch_bounds__(1024) jacobi(double* A, double* V, int l, int max_sweeps, double tol) {
+  __shared__ double cs[128], sn[128];
+  __shared__ int pp[128], qq[128];
+  __shared__ double red[2][32];
+  __shared__ int done;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 31, warp = tid >> 5;
+  A += (int64_t)blockIdx.x * l * l;
+  V += (int64_t)blockIdx.x * l * l;
+  for (int e = tid; e < l * l; e += nt) V[e] = (e / l == e % l) ? 1.0 : 0.0;
+  const int lp = (l + 1) & ~1, half = lp / 2;
+  __syncthreads();
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    // convergence test
+    double off = 0.0, tot = 0.0;
+    for (int e = tid; e < l * l; e += nt) {
+      const double x = A[e] * A[e];
+      tot += x;
+      if (e / l != e % l) off += x;
+    }
+    for (int o = 16; o >= 1; o >>= 1) {
+      off += __shfl_xor(off, o, 32);
+      tot += __shfl_xor(tot, o, 32);
+    }
+    if (lane == 0) {
+      red[0][warp] = off;
+      red[1][warp] = tot;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double o = 0.0, t = 0.0;
+      for (int w = 0; w < (nt + 31) / 32; ++w) {
+        o += red[0][w];
+        t += red[1][w];
+      }
+      done = !(o > tol * tol * t);
+    }
+    __syncthreads();
+    if (done) break;
+    for (int round = 0; round < lp - 1; ++round) {
+      if (tid < half) {
+        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (lp - 1); };
+        int p = pos(tid), q = pos(lp - 1 - tid);
+        if (p > q) { const int t = p; p = q; q = t; }
+        double c = 1.0, s = 0.0;
+        if (q < l) {
+          const double apq = A[(int64_t)p * l + q];
+          if (apq != 0.0) {
+            const double tau = (A[(int64_t)q * l + q] - A[(int64_t)p * l + p]) / (2.0 * apq);
+            const double t = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau)) : -1.0 / (-tau + sqrt(1.0 + tau * tau));
+            c = 1.0 / sqrt(1.0 + t * t);
+            s = t * c;
+          }
+        }
+        pp[tid] = p;
+        qq[tid] = q < l ? q : p;
+        cs[tid] = c;
+        sn[tid] = q < l ? s : 0.0;
+      }
+      __syncthreads();
+      for (int e = tid; e < half * l; e += nt) {   // rows: A <- J^T A
+        const int k = e / l, j = e % l, p = pp[k], q = qq[k];
+        if (p == q) continue;
+        const double c = cs[k], s = sn[k], x = A[(int64_t)p * l + j], y = A[(int64_t)q * l + j];
+        A[(int64_t)p * l + j] = c * x - s * y;
+        A[(int64_t)q * l + j] = s * x + c * y;
+      }
+      __syncthreads();
+      for (int e = tid; e < half * l; e += nt) {   // columns: A <- A J, V <- V J
+        const int k = e / l, i = e % l, p = pp[k], q = qq[k];
+        if (p == q) continue;
+        const double c = cs[k], s = sn[k];
+        const double x = A[(int64_t)i * l + p], y = A[(int64_t)i * l + q];
+        A[(int64_t)i * l + p] = c * x - s * y;
+        A[(int64_t)i * l + q] = s * x + c * y;
+        const double vx = V[(int64_t)i * l + p], vy = V[(int64_t)i * l + q];
+        V[(int64_t)i * l + p] = c * vx - s * vy;
+        V[(int64_t)i * l + q] = s * vx + c * vy;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-r selection
+// From the eigenpairs (diag of E, columns of V) of matrix b: sigma_i = sqrt(lambda_(i)) for the
+// r largest eigenvalues in descending order (ties by index), M1 = V_r Sigma_r [l][r] and
+// M2 = Sigma_r^-1 V_r^T [r][l] (zero rows for sigma = 0).
+__global__ void __launch_bounds__(256) select_top(const double* E, const double* V, float* sigma, double* M1,
+                                                  double* M2, int l, int r) {
+  __shared__ int order[256];
+  __shared__ double sig[256];
+  const int tid = threadIdx.x;
+  E += (int64_t)blockIdx.x * l * l;
+  V += (int64_t)blockIdx.x * l * l;
+  M1 += (int64_t)blockIdx.x * l * r;
+  M2 += (int64_t)blockIdx.x * r * l;
+  sigma += (int64_t)blockIdx.x * r;
+  for (int i = tid; i < l; i += blockDim.x) {
+    const double li = E[(int64_t)i * l + i];
+    int rank = 0;
+    for (int j = 0; j < l; ++j) {
+      const double lj = E[(int64_t)j * l + j];
+      rank += (lj > li) || (lj == li && j < i);
+    }
+    if (rank < r) {
+      order[rank] = i;
+      sig[rank] = sqrt(fmax(li, 0.0));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < r; i += blockDim.x) sigma[i] = (float)sig[i];
+  for (int e = tid; e < l * r; e += blockDim.x) {
+    const int row = e / r, c = e % r;
+    M1[e] = V[(int64_t)row * l + order[c]] * sig[c];
+  }
+  for (int e = tid; e < r * l; e += blockDim.x) {
+    const int c = e / l, col = e % l;
+    M2[e] = sig[c] > 0.0 ? V[(int64_t)col * l + order[c]] / sig[c] : 0.0;
+  }
+}
+
+// ------------------------------------------------------------------ sign convention
+// Component c of matrix b: if the largest-magnitude entry of A[:, c] (first on ties) is
+// negative, negate A[:, c] and B[c, :].  One work-group per (component, matrix).
+template <typename T>
+__global__ void __launch_bounds__(256) fix_signs(T* Aout, T* Bout, int rows, int cols, int r) {
+  __shared__ double bv[256];
+  __shared__ int bi[256];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  Aout += (int64_t)blockIdx.y * rows * r;
+  Bout += (int64_t)blockIdx.y * r * cols;
+  double best = -1.0;
+  int bidx = 0;
+  double bval = 0.0;
+  for (int i = tid; i < rows; i += 256) {
+    double x;
+    if constexpr (sizeof(T) == 2) x = (double)__builtin_bit_cast(__bf16, (uint16_t)Aout[(int64_t)i * r + c]);
+    else x = (double)Aout[(int64_t)i * r + c];
+    if (fabs(x) > best) { best = fabs(x); bidx = i; bval = x; }
+  }
+  bv[tid] = best;
+  bi[tid] = bidx;
+  __shared__ double sval[256];
+  sval[tid] = bval;
+  __syncthreads();
+  for (int o = 128; o >= 1; o >>= 1) {
+    if (tid < o) {
+      const bool take = bv[tid + o] > bv[tid] || (bv[tid + o] == bv[tid] && bi[tid + o] < bi[tid]);
+      if (take) {
+        bv[tid] = bv[tid + o];
+        bi[tid] = bi[tid + o];
+        sval[tid] = sval[tid + o];
+      }
+    }
+    __syncthreads();
+  }
+  if (!(sval[0] < 0.0)) return;
+  for (int i = tid; i < rows; i += 256) {
+    T& x = Aout[(int64_t)i * r + c];
+    if constexpr (sizeof(T) == 2) x = (T)(x ^ 0x8000u);
+    else x = -x;
+  }
+  for (int j = tid; j < cols; j += 256) {
+    T& x = Bout[(int64_t)c * cols + j];
+    if constexpr (sizeof(T) == 2) x = (T)(x ^ 0x8000u);
+    else x = -x;
+  }
+}
+
+// ------------------------------------------------------------------ workspace layout
+struct SvdWs {
+  size_t om, y0, y1, w0, w1, g, li, bsk, g2, v, m1, m2, total;
+};
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
+  const size_t b = (size_t)n_mats, m = rows, n = cols, l = (size_t)rank + oversample, r = rank;
+  SvdWs w;
+  size_t o = 0;
+  w.om = o;  o += al(b * n * l * 4);
+  w.y0 = o;  o += al(b * m * l * 4);
+  w.y1 = o;  o += al(b * m * l * 4);
+  w.w0 = o;  o += al(b * n * l * 4);
+  w.w1 = o;  o += al(b * n * l * 4);
+  w.g = o;   o += al(b * l * l * 8);
+  w.li = o;  o += al(b * l * l * 8);
+  w.bsk = o; o += al(b * l * n * 8);
+  w.g2 = o;  o += al(b * l * l * 8);
+  w.v = o;   o += al(b * l * l * 8);
+  w.m1 = o;  o += al(b * l * r * 8);
+  w.m2 = o;  o += al(b * r * l * 8);
+  w.total = o;
+  return w;
+}
+
+// Y [b][rows][l] (fp32) <- orthonormal (or zero) columns spanning it: CholeskyQR2 with dropping.
+// `tmp` receives the intermediate pass.
+hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, int l, hipStream_t st) {
+  hipError_t e;
+  float* src = Y;
+  float* dst = tmp;
+  for (int pass = 0; pass < 2; ++pass) {
+    // G = Y^T Y (fp64)
+    if ((e = run_gemm<float, float, double, double, true, false>(src, src, G, l, l, rows, l, l, l, (int64_t)rows * l,
+                                                                  (int64_t)rows * l, (int64_t)l * l, b, st)))
+      return e;
+    chol_inv<<<b, 1024, 0, st>>>(G, Li, l, pass == 0 ? 1e-12 : 1e-10);
+    if ((e = hipGetLastError())) return e;
+    // dst = src Li^T
+    if ((e = run_gemm<float, double, float, double, false, true>(src, Li, dst, rows, l, l, l, l, l, (int64_t)rows * l,
+                                                                  (int64_t)l * l, (int64_t)rows * l, b, st)))
+      return e;
+    float* t = src;
+    src = dst;
+    dst = t;
+  }
+  return hipSuccess;   // two passes: the result is back in Y
+}
+
+}  // namespace
+
+size_t svd_workspace_bytes(int n_mats, int rows, int cols, int rank, int oversample) {
+  return layout(n_mats, rows, cols, rank, oversample).total;
+}
+
+hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank, void* a_out, void* b_out,
+                       int out_bf16, float* sigma_out, int oversample, int power_iters, uint64_t seed, void* ws,
+                       size_t ws_bytes, hipStream_t st) {
+  const SvdWs L = layout(n_mats, rows, cols, rank, oversample);
+  if (ws_bytes < L.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  float* om = reinterpret_cast<float*>(base + L.om);
+  float* y0 = reinterpret_cast<float*>(base + L.y0);
+  float* y1 = reinterpret_cast<float*>(base + L.y1);
+  float* w0 = reinterpret_cast<float*>(base + L.w0);
+  float* w1 = reinterpret_cast<float*>(base + L.w1);
+  double* G = reinterpret_cast<double*>(base + L.g);
+  double* Li = reinterpret_cast<double*>(base + L.li);
+  double* bsk = reinterpret_cast<double*>(base + L.bsk);
+  double* g2 = reinterpret_cast<double*>(base + L.g2);
+  double* V = reinterpret_cast<double*>(base + L.v);
+  double* m1 = reinterpret_cast<double*>(base + L.m1);
+  double* m2 = reinterpret_cast<double*>(base + L.m2);
+  const int m = rows, n = cols, l = rank + oversample, r = rank, b = n_mats;
+  const int64_t sZ = (int64_t)m * n, sY = (int64_t)m * l, sW = (int64_t)n * l, sLL = (int64_t)l * l;
+  hipError_t e;
+
+  // Omega [b][n][l] ~ N(0, 1)
+  const int64_t cnt = (int64_t)b * n * l;
+  sketch<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(om, cnt, seed);
+  if ((e = hipGetLastError())) return e;
+  // Y = Z Omega, orthonormalised
+  if ((e = run_gemm<float, float, float, float, false, false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+  if ((e = orth(y0, y1, G, Li, b, m, l, st))) return e;
+  for (int it = 0; it < power_iters; ++it) {
+    // W = Z^T Y, orthonormalised; Y = Z W, orthonormalised
+    if ((e = run_gemm<float, float, float, float, true, false>(z, y0, w0, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
+    if ((e = orth(w0, w1, G, Li, b, n, l, st))) return e;
+    if ((e = run_gemm<float, float, float, float, false, false>(z, w0, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+    if ((e = orth(y0, y1, G, Li, b, m, l, st))) return e;
+  }
+  // Bsk = Q^T Z (fp64), its Gram Bsk Bsk^T, eigenpairs
+  if ((e = run_gemm<float, float, double, double, true, false>(y0, z, bsk, l, n, m, l, n, n, sY, sZ, (int64_t)l * n, b,
+                                                                st)))
+    return e;
+  if ((e = run_gemm<double, double, double, double, false, true>(bsk, bsk, g2, l, l, n, n, n, l, (int64_t)l * n,
+                                                                  (int64_t)l * n, sLL, b, st)))
+    return e;
+  jacobi<<<b, 1024, 0, st>>>(g2, V, l, 40, 1e-13);
+  if ((e = hipGetLastError())) return e;
+  select_top<<<b, 256, 0, st>>>(g2, V, sigma_out, m1, m2, l, r);
+  if ((e = hipGetLastError())) return e;
+  // A = Q (W_r Sigma_r), B = (Sigma_r^-1 W_r^T) Bsk, then the sign convention
+  if (out_bf16) {
+    bf16_bits* A = static_cast<bf16_bits*>(a_out);
+    bf16_bits* Bo = static_cast<bf16_bits*>(b_out);
+    if ((e = run_gemm<float, double, bf16_bits, double, false, false>(y0, m1, A, m, r, l, l, r, r, sY, (int64_t)l * r,
+                                                                       (int64_t)m * r, b, st)))
+      return e;
+    if ((e = run_gemm<double, double, bf16_bits, double, false, false>(m2, bsk, Bo, r, n, l, l, n, n, (int64_t)r * l,
+                                                                        (int64_t)l * n, (int64_t)r * n, b, st)))
+      return e;
+    fix_signs<bf16_bits><<<dim3(r, b), 256, 0, st>>>(A, Bo, m, n, r);
+  } else {
+    float* A = static_cast<float*>(a_out);
+    float* Bo = static_cast<float*>(b_out);
+    if ((e = run_gemm<float, double, float, double, false, false>(y0, m1, A, m, r, l, l, r, r, sY, (int64_t)l * r,
+                                                                   (int64_t)m * r, b, st)))
+      return e;
+    if ((e = run_gemm<double, double, float, double, false, false>(m2, bsk, Bo, r, n, l, l, n, n, (int64_t)r * l,
+                                                                    (int64_t)l * n, (int64_t)r * n, b, st)))
+      return e;
+    fix_signs<float><<<dim3(r, b), 256, 0, st>>>(A, Bo, m, n, r);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace kvc

@@ -1,0 +1,122 @@
+"""GPU anchor refresh (Eq. 7 factorisation, App. B.1) through the C ABI, against the fp64 oracle
+and the closed forms that pin it: Eckart-Young optimum of the i^-1.5 spectrum, exact rank-r
+reconstruction, orthonormal right factors, singular values, sign convention, and the Eq. 12
+round trip (a delta factorised by the refresh and applied by the library reproduces the
+target cache)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvc_oracle as O
+from rank_kv_cache_layer_amd import kvc
+from rank_kv_cache_layer_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _svd(z, rank, p=32, q=3, seed=7, out=torch.float32):
+    print(f"[svd] n={z.shape[0]} {z.shape[1]}x{z.shape[2]} rank={rank} p={p} q={q} out={out}", flush=True)
+    a, b, s = kvc.anchor_refresh_svd(z.to(DEV).contiguous(), rank, out_dtype=out, oversample=p, power_iters=q,
+                                     seed=seed)
+    torch.cuda.synchronize()
+    return a.double().cpu().numpy(), b.double().cpu().numpy(), s.double().cpu().numpy()
+
+
+def test_eckart_young_at_the_refresh_shape():
+    # 4096 x 1024 per layer and side, sigma_i = i^-1.5: the optimal rank-128 relative error is
+    # 4.979e-3 (closed form); the refresh must come within (1 + 1e-3) of it
+    z = W.decaying_matrices(2, 4096, 1024, seed=11)
+    a, b, s = _svd(z, 128)
+    sig = W.singular_values(1024)
+    opt = np.sqrt((sig[128:] ** 2).sum() / (sig ** 2).sum())
+    assert opt == pytest.approx(4.979e-3, rel=2e-4)
+    for m in range(2):
+        zm = z[m].double().numpy()
+        err = np.linalg.norm(zm - a[m] @ b[m]) / np.linalg.norm(zm)
+        assert err <= (1 + 1e-3) * opt, (m, err / opt)
+        ref_s = np.linalg.svd(zm, compute_uv=False)[:128]
+        assert np.max(np.abs(s[m][:64] - ref_s[:64]) / ref_s[:64]) <= 1e-4
+        assert np.max(np.abs(b[m] @ b[m].T - np.eye(128))) <= 1e-5
+
+
+@pytest.mark.parametrize("rows,cols,rank,p", [(300, 200, 16, 8), (256, 1024, 24, 16), (1000, 96, 8, 4)])
+def test_exact_rank_r_is_reconstructed(rows, cols, rank, p):
+    g = torch.Generator().manual_seed(rows + cols)
+    z = (torch.randn((3, rows, rank), generator=g, dtype=torch.float64)
+         @ torch.randn((3, rank, cols), generator=g, dtype=torch.float64)).float()
+    a, b, s = _svd(z, rank, p=p, q=1)
+    for m in range(3):
+        zm = z[m].double().numpy()
+        assert np.linalg.norm(a[m] @ b[m] - zm) / np.linalg.norm(zm) <= 1e-5
+        ref_s = np.linalg.svd(zm, compute_uv=False)[:rank]
+        assert np.allclose(s[m], ref_s, rtol=1e-4)
+
+
+def test_matches_oracle_factorisation_and_sign_convention():
+    z = W.decaying_matrices(2, 512, 384, seed=3)
+    a, b, s = _svd(z, 32, p=32, q=4)
+    for m in range(2):
+        A, B, S = O.truncated_svd(z[m].double().numpy(), 32)
+        assert np.max(np.abs(s[m] - S) / S) <= 1e-4
+        assert np.max(np.abs(a[m] @ b[m] - A @ B)) <= 1e-4 * np.max(np.abs(A @ B))
+        u = a[m] / s[m][None, :]
+        idx = np.argmax(np.abs(u), axis=0)
+        assert np.all(u[idx, np.arange(32)] > 0)
+        # the oracle's components, same sign convention: compare factor by factor
+        assert np.max(np.abs(a[m][:, :16] - A[:, :16])) <= 1e-3 * np.max(np.abs(A))
+
+
+def test_bf16_outputs():
+    z = W.decaying_matrices(1, 512, 256, seed=4)
+    a32, b32, s32 = _svd(z, 32)
+    a16, b16, s16 = _svd(z, 32, out=torch.bfloat16)
+    assert np.array_equal(s16, s32)
+    ref = a32[0] @ b32[0]
+    assert np.max(np.abs(a16[0] @ b16[0] - ref)) <= 2.0 ** -7 * 4 * np.max(np.abs(ref))
+
+
+def test_rank_deficient_sketch_and_zero_matrix():
+    # sketch wider than the rank of z: dropped directions give zero factors, never NaN
+    z = torch.zeros((1, 128, 64))
+    z[0, :, :3] = torch.randn((128, 3))
+    a, b, s = _svd(z, 8, p=8, q=2)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b)) and np.all(np.isfinite(s))
+    assert np.allclose(a[0] @ b[0], z[0].double().numpy(), atol=1e-5)
+    assert np.all(s[0][3:] <= 1e-5 * s[0][0])
+    a0, b0, s0 = _svd(torch.zeros((1, 64, 64)), 4, p=4, q=1)
+    assert np.all(s0 == 0) and np.all(a0 == 0) and np.all(np.isfinite(b0))
+
+
+def test_eq12_round_trip_through_the_library():
+    # Delta = C_j - Align(C_i) of an exactly rank-r pair, factorised on the GPU (keys in the
+    # canonical frame), then applied with one-hot weights: reproduces C_j (Eq. 12)
+    L, S, H, hd, r = 2, 256, 2, 64, 8
+    D = H * hd
+    g = torch.Generator().manual_seed(5)
+    ci_k = torch.randn((L, S, D), generator=g, dtype=torch.float64)
+    ci_v = torch.randn((L, S, D), generator=g, dtype=torch.float64)
+    dk = torch.randn((L, S, r), generator=g, dtype=torch.float64) @ torch.randn((L, r, D), generator=g,
+                                                                                 dtype=torch.float64) * 0.1
+    dv = torch.randn((L, S, r), generator=g, dtype=torch.float64) @ torch.randn((L, r, D), generator=g,
+                                                                                 dtype=torch.float64) * 0.1
+    p_src, p_tgt = 40, 97
+    fr = O.inv_freq(hd)
+    cj_k = O.rope(ci_k.numpy(), p_tgt - p_src, hd, fr) + O.rope(dk.numpy(), p_tgt, hd, fr)
+    cj_v = ci_v.numpy() + dv.numpy()
+    obs_k = np.stack([O.observed_delta(cj_k[l], ci_k[l].numpy(), p_src, p_tgt, hd, True) for l in range(L)])
+    obs_v = np.stack([O.observed_delta(cj_v[l], ci_v[l].numpy(), p_src, p_tgt, hd, False) for l in range(L)])
+    ak, bk, _ = _svd(torch.from_numpy(obs_k).float(), r, p=8, q=1)
+    av, bv, _ = _svd(torch.from_numpy(obs_v).float(), r, p=8, q=1)
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).float().to(DEV)
+    pool = kvc.PoolTensors([S], r, r, f32(np.zeros((L, S, r))), f32(np.zeros((L, 1, r, D))),
+                           f32(np.zeros((L, S, r))), f32(np.zeros((L, 1, r, D))),
+                           f32(ak), f32(bk[:, None]), f32(av), f32(bv[:, None]))
+    w = torch.ones((L, S, 1), device=DEV)
+    k_src, v_src = f32(ci_k.numpy()), f32(ci_v.numpy())
+    ko, vo = torch.empty_like(k_src), torch.empty_like(v_src)
+    kvc.apply_lowrank_delta(k_src, v_src, ko, vo, kvc.shape_of(L, S, H, hd), p_src, p_tgt, pool, w, w, S)
+    torch.cuda.synchronize()
+    for got, want in ((ko, cj_k), (vo, cj_v)):
+        err = np.max(np.abs(got.double().cpu().numpy() - want))
+        assert err <= 1e-4 * np.max(np.abs(want)), err
