@@ -135,6 +135,75 @@ def measure_peaks(kvc, torch):
             "valu_fp32_Tops": round(blocks * 256 * it_v * 8 / t_valu / 1e12, 2)}
 
 
+def measure_refresh(kvc, torch, n_mats=64, rows=4096, cols=1024, rank=128, p=32, q=3, reps=3):
+    """Anchor refresh at its configuration: 32 layers x (K, V) fp32 deltas of 4096 x 1024 with a
+    decaying spectrum, rank 128 (oversample 32, 3 power iterations).  Inputs are generated on
+    the device (Gaussian factors with i^-1.5 column scales), resident before timing."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    sc = torch.arange(1, cols + 1, device="cuda", dtype=torch.float32) ** -1.5
+    z = torch.empty((n_mats, rows, cols), device="cuda")
+    for m in range(n_mats):
+        a = torch.randn((rows, cols), device="cuda", generator=g) * sc[None, :]
+        z[m] = a @ (torch.randn((cols, cols), device="cuda", generator=g) / cols ** 0.5)
+    ws = torch.empty((kvc.svd_workspace_size(n_mats, rows, cols, rank, p),), dtype=torch.uint8, device="cuda")
+    kvc.anchor_refresh_svd(z, rank, oversample=p, power_iters=q, workspace=ws)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        kvc.anchor_refresh_svd(z, rank, oversample=p, power_iters=q, workspace=ws)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    l = rank + p
+    flops = n_mats * 2.0 * rows * cols * l * (2 * q + 2)          # sketch, power iterations, Q^T Z
+    return {"workload": f"{n_mats} x {rows}x{cols} fp32, rank {rank}, oversample {p}, {q} power iterations",
+            "ms": round(ms, 3), "matrices_per_s": round(n_mats / (ms / 1e3), 1),
+            "gemm_flops": int(flops), "achieved_TFLOPs": round(flops / (ms / 1e3) / 1e12, 2),
+            "peak_fp32_vector_TFLOPs": 157.3}
+
+
+def measure_chain(kvc, torch, W, n_requests=2, n_hops=3, steps=3):
+    """Concurrent chains (A0 -> A1 -> A2 -> A3) at the 8B shape, 8192 tokens per request,
+    pools of 10-20 anchors at rank 16 or 32, through kvc_correct_hops_batched (one call for all
+    requests' hops).  Tokens/s counts every hop's corrected segment."""
+    import dataclasses as _dc
+    reqs = W.chain_specs(n_requests=n_requests, n_hops=n_hops)
+    h0 = reqs[0][0]
+    shp = kvc.shape_of(h0.n_layers, h0.seq_len, h0.n_kv_heads, h0.head_dim)
+    hl = []
+    for hops in reqs:
+        base = len(hl)
+        for i, h in enumerate(hops):
+            # drawn in the canonical frame; the first source's keys are placed at p_src on the device
+            d = W.make_hop(_dc.replace(h, p_src=0, p_tgt=h.p_tgt - h.p_src))
+            pool = kvc.pool_from(d, "cuda")
+            if i == 0:
+                k0, v0 = d.k_src.to("cuda"), d.v_src.to("cuda")
+                kvc.align_rope(k0, k0, shp, 0, h.p_src)
+            out = kvc.alloc_match(h.n_layers, h.seq_len, h.n_anchors, "cuda", want_weights=False)
+            hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
+                              torch.empty_like(v0), h.p_src, h.p_tgt, base + i - 1 if i else -1, pool, out))
+            del d
+    prm = kvc.params_of(h0.tau, h0.temp_gate, h0.temp_weight, h0.gate_len, h0.mode, 0, None)
+    kvc.correct_hops_batched(hl, shp, prm)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        kvc.correct_hops_batched(hl, shp, prm)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    toks = sum(h.seq_len for hops in reqs for h in hops)
+    return {"workload": f"{n_requests} requests x {n_hops} chained hops, 32 layers x 8192 tokens, 8x128 KV heads, "
+                        f"bf16, pools of 10-20 anchors at rank 16/32",
+            "ms": round(ms, 3), "tokens_per_s": round(toks / (ms / 1e3), 1),
+            "flags": [int(h.out.flags[0].item()) for h in hl]}
+
+
 def cpu_baseline(data, n_layers):
     """The fp64 oracle on layer 0 of the same hop (all tokens, keys and values)."""
     from oracle import kvc_oracle as O
@@ -189,6 +258,7 @@ def main():
     ap.add_argument("--p-src", type=int, default=512, help="start position of the segment in the source agent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-mode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the refresh and chained-batch sections")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -264,6 +334,17 @@ def main():
                   "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
         log(f"[bench] second mode {second['mode']}: {ms2:.3f} ms/hop")
 
+    refresh = chain = None
+    if not args.no_extra:
+        log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
+        refresh = measure_refresh(kvc, torch)
+        log(f"[bench] refresh: {refresh['ms']} ms, {refresh['achieved_TFLOPs']} TFLOP/s")
+        del k, v, ko, vo, pool, ws
+        torch.cuda.empty_cache()
+        log("[bench] chained batch (2 requests x 3 hops, 8192 tokens) ...")
+        chain = measure_chain(kvc, torch, W)
+        log(f"[bench] chain: {chain['ms']} ms, {chain['tokens_per_s']} tokens/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample ...")
@@ -280,6 +361,7 @@ def main():
                    "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
         "roofline": dominant, "cpu_baseline": cpu,
         "hop": hop, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
+        "refresh": refresh, "chained_batch": chain,
         "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
     }
     print(json.dumps(out), flush=True)
