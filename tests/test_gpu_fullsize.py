@@ -1,0 +1,69 @@
+"""Parity at full size, in the launch configuration the benchmark times: the 32768-token
+Llama-3.1-8B-shaped hop (32 layers, 8 x 128 KV heads, 20 anchors at rank 32, keys at start
+position 512, shift 300, one third of the layers unrelated) and the 4096-token hop corrected
+with 10 anchors at rank 128.  The GPU runs the whole hop; the oracle computes sampled layers
+completely for the gate and sampled tokens of those layers for weights and outputs (the
+oracle takes them one by one, so any sample is exact), and the hop-level gate row is checked
+through the property that ties it to the per-layer rows (Eq. 9 sums the layers' squared
+distances)."""
+import numpy as np
+import pytest
+
+from oracle import kvc_oracle as O
+from rank_kv_cache_layer_amd import workload as W
+
+from hop_helpers import TOL_BF16, W_ATOL, make, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(S, seed):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 63, 64, 127, 128, 129, 255, 256, S // 2, S - 129, S - 128, S - 2, S - 1]
+    return np.unique(np.concatenate([np.array([e for e in edges if 0 <= e < S]), rng.integers(0, S, 200)]))
+
+
+def _check_sampled(spec, layers, seed):
+    print(f"[fullsize] {spec.name} L={spec.n_layers} S={spec.seq_len} N={spec.n_anchors} "
+          f"r={spec.rank_base} layers={layers}", flush=True)
+    data = make(spec)
+    gpu = run_gpu(data)
+    rows = _sample_rows(spec.seq_len, seed)
+    N = spec.n_anchors
+    per = []
+    for l in layers:
+        ref = O.correct_layer(data, l, rows=rows)
+        per.append(ref)
+        for side in ("k", "v"):
+            want = O.round_to(ref[f"{side}_out"], "bf16")
+            got = gpu[f"{side}_out"][l][rows]
+            bound = TOL_BF16 * np.max(np.abs(want))
+            assert np.max(np.abs(got - want)) <= bound, (spec.name, l, side)
+            wg = gpu[f"w_{side}"][l][rows][:, :N]
+            assert np.max(np.abs(wg - ref[f"w_{side}"])) <= W_ATOL[W.BF16], (spec.name, l, side)
+        # per-layer gate row: distances and the decision, bit-exact flags
+        d, h, f = O.gate_decide_pages(np.asarray(ref["q"]), spec.tau, spec.temp_gate, spec.cap(), N)
+        assert np.allclose(gpu["dist"][1 + l][:N], d, rtol=1e-4), (spec.name, l)
+        assert gpu["flags"][1 + l] == f, (spec.name, l, gpu["flags"][1 + l], f)
+        assert abs(gpu["stat"][1 + l] - h) < 2e-3
+        assert abs(h - spec.tau) >= 0.05, "oracle statistic within 0.05 of tau"
+    # hop row: d_hop^2 = sum over layers of d_layer^2, decided by the same rule
+    d_hop = gpu["dist"][0][:N]
+    assert np.allclose(d_hop ** 2, np.sum(gpu["dist"][1:, :N] ** 2, axis=0), rtol=1e-5)
+    d, h, f = O.gate_decide_pages(d_hop.astype(np.float64) ** 2, spec.tau, spec.temp_gate, spec.cap(), N)
+    assert gpu["flags"][0] == f
+    return gpu
+
+
+@pytest.mark.timeout(900)
+def test_32k_hop_sampled():
+    spec = W.llama8b_long(p_src=512, p_tgt=812)
+    gpu = _check_sampled(spec, layers=[0, 2, 17, 31], seed=1)
+    # layers with a source no anchor holds are flagged, the others accepted
+    assert [int(x) for x in gpu["flags"][1:]] == [O.FLAG_ENTROPY if l % 3 == 2 else 0 for l in range(32)]
+
+
+@pytest.mark.timeout(900)
+def test_rank128_hop_sampled():
+    spec = W.llama8b_rank128()
+    _check_sampled(spec, layers=[0, 13, 31], seed=2)
