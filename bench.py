@@ -135,7 +135,7 @@ def measure_peaks(kvc, torch):
             "valu_fp32_Tops": round(blocks * 256 * it_v * 8 / t_valu / 1e12, 2)}
 
 
-def measure_refresh(kvc, torch, n_mats=64, rows=4096, cols=1024, rank=128, p=32, q=3, reps=3):
+def measure_refresh(kvc, torch, n_mats=64, rows=4096, cols=1024, rank=128, p=32, q=3, reps=3, oracle=True):
     """Anchor refresh at its configuration: 32 layers x (K, V) fp32 deltas of 4096 x 1024 with a
     decaying spectrum, rank 128 (oversample 32, 3 power iterations).  Inputs are generated on
     the device (Gaussian factors with i^-1.5 column scales), resident before timing."""
@@ -158,10 +158,20 @@ def measure_refresh(kvc, torch, n_mats=64, rows=4096, cols=1024, rank=128, p=32,
     ms = e0.elapsed_time(e1) / reps
     l = rank + p
     flops = n_mats * 2.0 * rows * cols * l * (2 * q + 2)          # sketch, power iterations, Q^T Z
-    return {"workload": f"{n_mats} x {rows}x{cols} fp32, rank {rank}, oversample {p}, {q} power iterations",
-            "ms": round(ms, 3), "matrices_per_s": round(n_mats / (ms / 1e3), 1),
-            "gemm_flops": int(flops), "achieved_TFLOPs": round(flops / (ms / 1e3) / 1e12, 2),
-            "peak_fp32_vector_TFLOPs": 157.3}
+    out = {"workload": f"{n_mats} x {rows}x{cols} fp32, rank {rank}, oversample {p}, {q} power iterations",
+           "ms": round(ms, 3), "matrices_per_s": round(n_mats / (ms / 1e3), 1),
+           "gemm_flops": int(flops), "achieved_TFLOPs": round(flops / (ms / 1e3) / 1e12, 2),
+           "peak_fp32_vector_TFLOPs": 157.3}
+    if oracle:
+        # the oracle's factorisation (exact fp64 SVD) of one of the same matrices
+        from oracle import kvc_oracle as O
+        zm = z[0].double().cpu().numpy()
+        t0 = time.perf_counter()
+        O.truncated_svd(zm, rank)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(1.0 / dt, 3), "unit": "matrices/s", "kind": "oracle",
+                               "sample": f"1 of the {n_mats} matrices, fp64 SVD, {dt:.2f} s"}
+    return out
 
 
 def measure_chain(kvc, torch, W, n_requests=2, n_hops=3, steps=3):
@@ -337,7 +347,7 @@ def main():
     refresh = chain = None
     if not args.no_extra:
         log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
-        refresh = measure_refresh(kvc, torch)
+        refresh = measure_refresh(kvc, torch, oracle=not args.no_cpu_baseline)
         log(f"[bench] refresh: {refresh['ms']} ms, {refresh['achieved_TFLOPs']} TFLOP/s")
         del k, v, ko, vo, pool, ws
         torch.cuda.empty_cache()

@@ -124,6 +124,131 @@ hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ fp32 GEMM on matrix cores
+// C[b] (M x N, fp32) = opA(A[b]) (M x K) * B[b] (K x N, row-major), fp32 products and sums on
+// v_mfma_f32_32x32x2_f32: 128 x 128 tile per work-group of 4 waves (64 x 64 each, 2 x 2 blocks),
+// K in chunks of 16 through double-buffered LDS (next chunk loaded into registers while the
+// current one is multiplied).  opA = A (row-major, lda) or, with TRA, A^T (A stored K x M).
+// Requires lda, ldb, ldc and the batch strides to be multiples of 4 (16-byte vector loads);
+// tails in M, N, K are bounds-checked.
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float4 ld4_guard(const float* p, int64_t base, int avail) {
+  if (avail >= 4) return *reinterpret_cast<const float4*>(p + base);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (avail > 0) v.x = p[base];
+  if (avail > 1) v.y = p[base + 1];
+  if (avail > 2) v.z = p[base + 2];
+  return v;
+}
+
+template <bool TRA>
+__global__ void __launch_bounds__(256) gemm_f32_mfma(const float* __restrict__ A, const float* __restrict__ B,
+                                                     float* __restrict__ C, int M, int N, int K, int64_t lda,
+                                                     int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC) {
+  __shared__ __attribute__((aligned(16))) float As[2][16][128 + 4];   // [buffer][k][m]
+  __shared__ __attribute__((aligned(16))) float Bs[2][16][128 + 4];   // [buffer][k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  float4 ra[2], rb[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u;
+      if (TRA) {   // A stored [k][m]: 16 rows of 32 float4 along m
+        const int k = idx >> 5, m4 = (idx & 31) * 4;
+        ra[u] = (k0 + k < K) ? ld4_guard(A, (int64_t)(k0 + k) * lda + i0 + m4, M - i0 - m4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {     // A stored [m][k]: 128 rows of 4 float4 along k
+        const int m = idx >> 2, k4 = (idx & 3) * 4;
+        ra[u] = (i0 + m < M) ? ld4_guard(A, (int64_t)(i0 + m) * lda + k0 + k4, K - k0 - k4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      const int k = idx >> 5, n4 = (idx & 31) * 4;
+      rb[u] = (k0 + k < K) ? ld4_guard(B, (int64_t)(k0 + k) * ldb + j0 + n4, N - j0 - n4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u;
+      if (TRA) {
+        const int k = idx >> 5, m4 = (idx & 31) * 4;
+        *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[u];
+      } else {
+        const int m = idx >> 2, k4 = (idx & 3) * 4;
+        As[buf][k4 + 0][m] = ra[u].x;
+        As[buf][k4 + 1][m] = ra[u].y;
+        As[buf][k4 + 2][m] = ra[u].z;
+        As[buf][k4 + 3][m] = ra[u].w;
+      }
+      const int k = idx >> 5, n4 = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = rb[u];
+    }
+  };
+  f32x16v acc[2][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[tb][db][j] = 0.f;
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const bool more = k0 + 16 < K;
+    if (more) load(k0 + 16);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = 2 * kk + kh;
+      float a[2], b[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) a[tb] = As[buf][k][wm * 64 + tb * 32 + l32];
+#pragma unroll
+      for (int db = 0; db < 2; ++db) b[db] = Bs[buf][k][wn * 64 + db * 32 + l32];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          acc[tb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tb], b[db], acc[tb][db], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int j = j0 + wn * 64 + db * 32 + l32;
+      if (j >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + wm * 64 + tb * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (i < M) C[(int64_t)i * ldc + j] = acc[tb][db][r];
+      }
+    }
+}
+
+// fp32 products: matrix cores when every leading dimension allows 16-byte loads, else VALU
+template <bool TRA>
+hipError_t gemm_f32(const float* A, const float* B, float* C, int M, int N, int K, int64_t lda, int64_t ldb,
+                    int64_t ldc, int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st) {
+  if (lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0) {
+    const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128), (unsigned)batch);
+    gemm_f32_mfma<TRA><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+    return hipGetLastError();
+  }
+  return run_gemm<float, float, float, float, TRA, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, st);
+}
+
 // ------------------------------------------------------------------ Cholesky with dropping
 // In: G [l][l] (symmetric positive semi-definite Gram matrix, fp64).  Out: Li [l][l] = L^-1
 // with G ~ L L^T, rows and columns of dropped pivots zero, so that Y Li^T has orthonormal or
@@ -440,13 +565,13 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   sketch<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(om, cnt, seed);
   if ((e = hipGetLastError())) return e;
   // Y = Z Omega, orthonormalised
-  if ((e = run_gemm<float, float, float, float, false, false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+  if ((e = gemm_f32<false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
   if ((e = orth(y0, y1, G, Li, b, m, l, st))) return e;
   for (int it = 0; it < power_iters; ++it) {
     // W = Z^T Y, orthonormalised; Y = Z W, orthonormalised
-    if ((e = run_gemm<float, float, float, float, true, false>(z, y0, w0, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
+    if ((e = gemm_f32<true>(z, y0, w0, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
     if ((e = orth(w0, w1, G, Li, b, n, l, st))) return e;
-    if ((e = run_gemm<float, float, float, float, false, false>(z, w0, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+    if ((e = gemm_f32<false>(z, w0, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
     if ((e = orth(y0, y1, G, Li, b, m, l, st))) return e;
   }
   // Bsk = Q^T Z (fp64), its Gram Bsk Bsk^T, eigenpairs
