@@ -397,12 +397,129 @@ __global__ void __launch_bounds__(1024) jacobi(double* A, double* V, int l, int 
   }
 }
 
+// Same eigenproblem with the matrix resident in LDS as its packed lower triangle (index
+// i (i + 1) / 2 + j, j <= i; fp64), for l up to kJacobiLdsMax.  A round rotates the l/2
+// disjoint pairs at once: each 2 x 2 block between two pairs P, Q (stored once, P <= Q) becomes
+// J_P^T B J_Q, a diagonal block diag(a'_pp, a'_qq) with a'_pq = 0.  The eigenvectors accumulate
+// in VT [l][l] (global, row k = eigenvector k), V <- V J applied to rows p, q of VT.  An odd l
+// is padded with a zero row that is never rotated.
+constexpr int kJacobiLdsMax = 192;
+__device__ __forceinline__ int tri(int i, int j) { return i >= j ? i * (i + 1) / 2 + j : j * (j + 1) / 2 + i; }
+
+__global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l, int max_sweeps, double tol) {
+  extern __shared__ double T[];   // packed lower triangle, lp (lp + 1) / 2 entries
+  __shared__ double cs[kJacobiLdsMax / 2], sn[kJacobiLdsMax / 2];
+  __shared__ int pp[kJacobiLdsMax / 2], qq[kJacobiLdsMax / 2];
+  __shared__ double red[2][32];
+  __shared__ int done;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 31, warp = tid >> 5;
+  A += (int64_t)blockIdx.x * l * l;
+  VT += (int64_t)blockIdx.x * l * l;
+  const int lp = (l + 1) & ~1, half = lp / 2, ntri = lp * (lp + 1) / 2;
+  for (int e = tid; e < ntri; e += nt) {
+    int i = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+    while (i * (i + 1) / 2 > e) --i;
+    while ((i + 1) * (i + 2) / 2 <= e) ++i;
+    const int j = e - i * (i + 1) / 2;
+    T[e] = (i < l && j < l) ? A[(int64_t)i * l + j] : 0.0;
+  }
+  for (int e = tid; e < l * l; e += nt) VT[e] = (e / l == e % l) ? 1.0 : 0.0;
+  const int nblk = half * (half + 1) / 2;
+  __syncthreads();
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (int e = tid; e < ntri; e += nt) {
+      int i = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+      while (i * (i + 1) / 2 > e) --i;
+      while ((i + 1) * (i + 2) / 2 <= e) ++i;
+      const int j = e - i * (i + 1) / 2;
+      const double x = T[e] * T[e];
+      if (i == j) tot += x;
+      else { off += 2.0 * x; tot += 2.0 * x; }
+    }
+    for (int o = 16; o >= 1; o >>= 1) {
+      off += __shfl_xor(off, o, 32);
+      tot += __shfl_xor(tot, o, 32);
+    }
+    if (lane == 0) {
+      red[0][warp] = off;
+      red[1][warp] = tot;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double o = 0.0, t = 0.0;
+      for (int w = 0; w < (nt + 31) / 32; ++w) {
+        o += red[0][w];
+        t += red[1][w];
+      }
+      done = !(o > tol * tol * t);
+    }
+    __syncthreads();
+    if (done) break;
+    for (int round = 0; round < lp - 1; ++round) {
+      if (tid < half) {
+        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (lp - 1); };
+        int p = pos(tid), q = pos(lp - 1 - tid);
+        if (p > q) { const int t = p; p = q; q = t; }
+        double c = 1.0, s = 0.0;
+        if (q < l) {
+          const double apq = T[tri(q, p)];
+          if (apq != 0.0) {
+            const double tau = (T[tri(q, q)] - T[tri(p, p)]) / (2.0 * apq);
+            const double t = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau)) : -1.0 / (-tau + sqrt(1.0 + tau * tau));
+            c = 1.0 / sqrt(1.0 + t * t);
+            s = t * c;
+          }
+        }
+        pp[tid] = p;
+        qq[tid] = q;
+        cs[tid] = c;
+        sn[tid] = s;
+      }
+      __syncthreads();
+      for (int e = tid; e < nblk; e += nt) {   // block (K1, K2), K1 <= K2
+        int k1 = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+        while (k1 * (k1 + 1) / 2 > e) --k1;
+        while ((k1 + 1) * (k1 + 2) / 2 <= e) ++k1;
+        const int k2 = e - k1 * (k1 + 1) / 2;   // k2 <= k1
+        const int p1 = pp[k1], q1 = qq[k1], p2 = pp[k2], q2 = qq[k2];
+        const double c1 = cs[k1], s1 = sn[k1], c2 = cs[k2], s2 = sn[k2];
+        if (k1 == k2) {
+          const double app = T[tri(p1, p1)], aqq = T[tri(q1, q1)], apq = T[tri(q1, p1)];
+          T[tri(p1, p1)] = c1 * c1 * app - 2.0 * c1 * s1 * apq + s1 * s1 * aqq;
+          T[tri(q1, q1)] = s1 * s1 * app + 2.0 * c1 * s1 * apq + c1 * c1 * aqq;
+          T[tri(q1, p1)] = 0.0;
+        } else {
+          // B rows {p1, q1}, columns {p2, q2}; B' = J1^T B J2
+          const double b00 = T[tri(p1, p2)], b01 = T[tri(p1, q2)], b10 = T[tri(q1, p2)], b11 = T[tri(q1, q2)];
+          const double r00 = c1 * b00 - s1 * b10, r01 = c1 * b01 - s1 * b11;
+          const double r10 = s1 * b00 + c1 * b10, r11 = s1 * b01 + c1 * b11;
+          T[tri(p1, p2)] = c2 * r00 - s2 * r01;
+          T[tri(p1, q2)] = s2 * r00 + c2 * r01;
+          T[tri(q1, p2)] = c2 * r10 - s2 * r11;
+          T[tri(q1, q2)] = s2 * r10 + c2 * r11;
+        }
+      }
+      for (int e = tid; e < half * l; e += nt) {   // V <- V J: rows p, q of VT
+        const int k = e / l, i = e % l, p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const double c = cs[k], s = sn[k];
+        const double x = VT[(int64_t)p * l + i], y = VT[(int64_t)q * l + i];
+        VT[(int64_t)p * l + i] = c * x - s * y;
+        VT[(int64_t)q * l + i] = s * x + c * y;
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < l; i += nt) A[(int64_t)i * l + i] = T[tri(i, i)];
+}
+
 // ------------------------------------------------------------------ top-r selection
 // From the eigenpairs (diag of E, columns of V) of matrix b: sigma_i = sqrt(lambda_(i)) for the
 // r largest eigenvalues in descending order (ties by index), M1 = V_r Sigma_r [l][r] and
 // M2 = Sigma_r^-1 V_r^T [r][l] (zero rows for sigma = 0).
 __global__ void __launch_bounds__(256) select_top(const double* E, const double* V, float* sigma, double* M1,
-                                                  double* M2, int l, int r) {
+                                                  double* M2, int l, int r, int v_transposed) {
   __shared__ int order[256];
   __shared__ double sig[256];
   const int tid = threadIdx.x;
@@ -427,11 +544,12 @@ __global__ void __launch_bounds__(256) select_top(const double* E, const double*
   for (int i = tid; i < r; i += blockDim.x) sigma[i] = (float)sig[i];
   for (int e = tid; e < l * r; e += blockDim.x) {
     const int row = e / r, c = e % r;
-    M1[e] = V[(int64_t)row * l + order[c]] * sig[c];
+    M1[e] = (v_transposed ? V[(int64_t)order[c] * l + row] : V[(int64_t)row * l + order[c]]) * sig[c];
   }
   for (int e = tid; e < r * l; e += blockDim.x) {
     const int c = e / l, col = e % l;
-    M2[e] = sig[c] > 0.0 ? V[(int64_t)col * l + order[c]] / sig[c] : 0.0;
+    const double vv = v_transposed ? V[(int64_t)order[c] * l + col] : V[(int64_t)col * l + order[c]];
+    M2[e] = sig[c] > 0.0 ? vv / sig[c] : 0.0;
   }
 }
 
@@ -581,9 +699,20 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   if ((e = run_gemm<double, double, double, double, false, true>(bsk, bsk, g2, l, l, n, n, n, l, (int64_t)l * n,
                                                                   (int64_t)l * n, sLL, b, st)))
     return e;
-  jacobi<<<b, 1024, 0, st>>>(g2, V, l, 40, 1e-13);
+  const int lp = (l + 1) & ~1;
+  const size_t tri_bytes = sizeof(double) * (size_t)lp * (lp + 1) / 2;
+  const bool in_lds = lp <= kJacobiLdsMax;
+  if (in_lds) {
+    if (tri_bytes > 64 * 1024 &&
+        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_lds), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)tri_bytes)))
+      return e;
+    jacobi_lds<<<b, 1024, tri_bytes, st>>>(g2, V, l, 40, 1e-13);
+  } else {
+    jacobi<<<b, 1024, 0, st>>>(g2, V, l, 40, 1e-13);
+  }
   if ((e = hipGetLastError())) return e;
-  select_top<<<b, 256, 0, st>>>(g2, V, sigma_out, m1, m2, l, r);
+  select_top<<<b, 256, 0, st>>>(g2, V, sigma_out, m1, m2, l, r, in_lds ? 1 : 0);
   if ((e = hipGetLastError())) return e;
   // A = Q (W_r Sigma_r), B = (Sigma_r^-1 W_r^T) Bsk, then the sign convention
   if (out_bf16) {
