@@ -308,6 +308,71 @@ __global__ void __launch_bounds__(1024) chol_inv(double* G, double* Li, int l, d
     if (dead[e / l]) Li[e] = 0.0;
 }
 
+// Same factorisation and inverse with L resident in LDS as its packed lower triangle (fp64),
+// for l up to kJacobiLdsMax: right-looking Cholesky with dropping, then the in-place inverse of
+// the lower-triangular factor column by column from the right (X_jj = 1 / L_jj, then
+// X[i][j] = -X_jj sum_{k=j+1..i} X[i][k] L[k][j]); a dropped pivot gets X_jj = 0, which zeroes
+// its row and column of the inverse.  Li is written in full (upper triangle zero).
+__global__ void __launch_bounds__(1024) chol_inv_lds(const double* G, double* Li, int l, double rel_tol) {
+  extern __shared__ double T[];   // packed lower triangle, l (l + 1) / 2 entries
+  __shared__ double col[256];
+  __shared__ double diag_max;
+  __shared__ int dead[256];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  G += (int64_t)blockIdx.x * l * l;
+  Li += (int64_t)blockIdx.x * l * l;
+  const int ntri = l * (l + 1) / 2;
+  for (int i = 0; i < l; ++i)
+    for (int j = tid; j <= i; j += nt) T[i * (i + 1) / 2 + j] = G[(int64_t)i * l + j];
+  __syncthreads();
+  if (tid == 0) {
+    double m = 0.0;
+    for (int i = 0; i < l; ++i) m = fmax(m, T[i * (i + 1) / 2 + i]);
+    diag_max = m;
+  }
+  __syncthreads();
+  const double tol = rel_tol * diag_max;
+  for (int k = 0; k < l; ++k) {
+    const double d = T[k * (k + 1) / 2 + k];   // every thread: the same value
+    const bool drop = !(d > tol);
+    const double piv = drop ? 0.0 : sqrt(d);
+    __syncthreads();
+    if (tid == 0) {
+      dead[k] = drop;
+      T[k * (k + 1) / 2 + k] = drop ? 1.0 : piv;
+    }
+    for (int i = k + 1 + tid; i < l; i += nt) {
+      double& x = T[i * (i + 1) / 2 + k];
+      x = drop ? 0.0 : x / piv;
+    }
+    __syncthreads();
+    const int rem = l - k - 1;
+    for (int e = tid; e < rem * rem; e += nt) {
+      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
+      if (j <= i) T[i * (i + 1) / 2 + j] -= T[i * (i + 1) / 2 + k] * T[j * (j + 1) / 2 + k];
+    }
+    __syncthreads();
+  }
+  // in-place inverse, columns from the right
+  for (int j = l - 1; j >= 0; --j) {
+    const double xjj = dead[j] ? 0.0 : 1.0 / T[j * (j + 1) / 2 + j];
+    for (int i = j + 1 + tid; i < l; i += nt) col[i] = T[i * (i + 1) / 2 + j];
+    __syncthreads();
+    for (int i = j + 1 + tid; i < l; i += nt) {
+      double s = 0.0;
+      for (int k = j + 1; k <= i; ++k) s += T[i * (i + 1) / 2 + k] * col[k];
+      T[i * (i + 1) / 2 + j] = -s * xjj;
+    }
+    if (tid == 0) T[j * (j + 1) / 2 + j] = xjj;
+    __syncthreads();
+  }
+  for (int e = tid; e < l * l; e += nt) {
+    const int i = e / l, j = e % l;
+    Li[e] = j <= i ? T[i * (i + 1) / 2 + j] : 0.0;
+  }
+  (void)ntri;
+}
+
 // ------------------------------------------------------------------ Jacobi eigensolver
 // Symmetric A [l][l] (fp64, overwritten; its diagonal ends as the eigenvalues) and V [l][l]
 // (out: eigenvectors as columns).  Parallel cyclic Jacobi with round-robin pairing: each round
@@ -637,7 +702,17 @@ hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, in
     if ((e = run_gemm<float, float, double, double, true, false>(src, src, G, l, l, rows, l, l, l, (int64_t)rows * l,
                                                                   (int64_t)rows * l, (int64_t)l * l, b, st)))
       return e;
-    chol_inv<<<b, 1024, 0, st>>>(G, Li, l, pass == 0 ? 1e-12 : 1e-10);
+    const double tolr = pass == 0 ? 1e-12 : 1e-10;
+    const size_t tri_bytes = sizeof(double) * (size_t)l * (l + 1) / 2;
+    if (l <= kJacobiLdsMax) {
+      if (tri_bytes > 64 * 1024 &&
+          (e = hipFuncSetAttribute(reinterpret_cast<const void*>(chol_inv_lds),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)tri_bytes)))
+        return e;
+      chol_inv_lds<<<b, 1024, tri_bytes, st>>>(G, Li, l, tolr);
+    } else {
+      chol_inv<<<b, 1024, 0, st>>>(G, Li, l, tolr);
+    }
     if ((e = hipGetLastError())) return e;
     // dst = src Li^T
     if ((e = run_gemm<float, double, float, double, false, true>(src, Li, dst, rows, l, l, l, l, l, (int64_t)rows * l,
