@@ -1,7 +1,10 @@
 // Reliability gate finalisation (KVCMAS App. A.3 "Reliability Gate", Eq. 9-11).
 //
 // Per-tile fp32 partial sums from the scoring kernels are reduced in double precision in a
-// fixed order (tiles, then layers), so distances, entropies and flags are bit-reproducible.
+// fixed order (per layer: strided thread sums over the tiles, a fixed shuffle tree per wave,
+// the waves in order; then the layers in order), so distances, entropies and flags are
+// bit-reproducible.  One work-group per layer does the tile sums (`gate_layer_sums`); a single
+// work-group then forms the hop row and the decisions (`gate_finalize`).
 //   PAGES:  d_v = sqrt(sum_l sum_{t<k} ||V - A_v B_v||^2)            (Eq. 9)
 //           g = softmax(-d / T)                                       (Eq. 10)
 //           H = -sum g log2 g / log2 |A_k|                            (Eq. 11)
@@ -16,23 +19,41 @@ namespace {
 
 constexpr int kMaxLayersGate = 256;
 
+// gsum [3][1 + N_l][N] (row 1 + l): layer l's sums over all tiles, fp64
+__global__ void __launch_bounds__(1024) gate_layer_sums(GateArgs p) {
+  __shared__ double wsum[16][kMaxAnchors];
+  const int N = p.N, L = p.n_layers, l = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int64_t plane_in = (int64_t)L * p.n_tiles * N;
+  const int planes = p.mode == KVC_SCORE_PAGES ? 1 : 3;
+  for (int pl = 0; pl < planes; ++pl) {
+    const float* src = p.partials + pl * plane_in + (int64_t)l * p.n_tiles * N;
+    for (int a = 0; a < N; ++a) {
+      double s = 0.0;
+      if ((p.mask_gate >> a) & 1)
+        for (int t = tid; t < p.n_tiles; t += blockDim.x) s += (double)src[(int64_t)t * N + a];
+      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0) wsum[wave][a] = s;
+    }
+    __syncthreads();
+    for (int a = tid; a < N; a += blockDim.x) {
+      double s = 0.0;
+      for (int w = 0; w < nw; ++w) s += wsum[w][a];
+      p.gsum[((int64_t)pl * (1 + L) + 1 + l) * N + a] = s;
+    }
+    __syncthreads();
+  }
+}
+
 __global__ void __launch_bounds__(1024) gate_finalize(GateArgs p) {
   extern __shared__ double sh[];            // [3][1 + N_l][N]
   const int N = p.N, L = p.n_layers;
   const int rows = 1 + L;
-  const int64_t plane_in = (int64_t)L * p.n_tiles * N;
   const int planes = p.mode == KVC_SCORE_PAGES ? 1 : 3;
-  // 1) per (layer, anchor): fixed-order sum over tiles
-  for (int i = threadIdx.x; i < L * N; i += blockDim.x) {
-    const int l = i / N, a = i % N;
-    for (int pl = 0; pl < planes; ++pl) {
-      double s = 0.0;
-      if ((p.mask_gate >> a) & 1) {
-        const float* src = p.partials + pl * plane_in + (int64_t)l * p.n_tiles * N + a;
-        for (int t = 0; t < p.n_tiles; ++t) s += (double)src[(int64_t)t * N];
-      }
-      sh[(pl * rows + 1 + l) * N + a] = s;
-    }
+  // 1) per (layer, anchor) sums from gate_layer_sums
+  for (int i = threadIdx.x; i < planes * L * N; i += blockDim.x) {
+    const int pl = i / (L * N), l = (i / N) % L, a = i % N;
+    sh[(pl * rows + 1 + l) * N + a] = p.gsum[((int64_t)pl * rows + 1 + l) * N + a];
   }
   __syncthreads();
   // 2) hop row: fixed-order sum over layers
@@ -108,7 +129,12 @@ __global__ void __launch_bounds__(1024) gate_finalize(GateArgs p) {
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t st) {
   const size_t shmem = sizeof(double) * 3 * (1 + a.n_layers) * (a.N > 0 ? a.N : 1);
-  if (a.n_layers > kMaxLayersGate || shmem > 160 * 1024) return hipErrorInvalidValue;
+  if (a.n_layers > kMaxLayersGate || shmem > 160 * 1024 || a.N > kMaxAnchors || !a.gsum) return hipErrorInvalidValue;
+  if (a.n_layers > 0) {
+    gate_layer_sums<<<a.n_layers, 1024, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   gate_finalize<<<1, 1024, shmem, st>>>(a);
   return hipGetLastError();
 }

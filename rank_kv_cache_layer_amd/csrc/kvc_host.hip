@@ -212,6 +212,7 @@ struct Plan {
   int tile = 0, n_tiles = 0, s_work = 0, generic_tt = 0;
   size_t off_scores = 0, off_w = 0, off_partials = 0, off_pack_base = 0, off_pack_delta = 0, off_mpart = 0;
   size_t off_wa = 0;            // anchor-major token weights of the two-pass path
+  size_t off_gsum = 0;          // per-layer gate sums (fp64)
   size_t total = 0;
 };
 
@@ -267,6 +268,8 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
     }
     pl.off_partials = off;
     off += up256(sizeof(float) * 3 * (size_t)L * std::max(pl.n_tiles, 1) * N);
+    pl.off_gsum = off;
+    off += up256(sizeof(double) * 3 * (size_t)(1 + L) * N);
     if (pl.fused_match || pl.split_match) {
       pl.off_pack_base = off;
       off += up256(2 * 2 * (size_t)L * N * D * p.rank_base);
@@ -463,10 +466,12 @@ kvc_status run_split_apply(const SplitArgs& f, const kvc_shape& sh, Tracer& tr, 
 }
 
 kvc_status run_gate(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, const Sets& s, const float* partials,
-                    int n_tiles, kvc_match_out* out, const int32_t* pred_flags, Tracer& tr, hipStream_t st) {
+                    double* gsum, int n_tiles, kvc_match_out* out, const int32_t* pred_flags, Tracer& tr,
+                    hipStream_t st) {
   GateArgs g;
   memset(&g, 0, sizeof g);
   g.partials = partials;
+  g.gsum = gsum;
   g.dist = out->dist; g.stat = out->stat; g.flags = out->flags;
   g.pred_flags = pred_flags;
   g.n_layers = sh.n_layers; g.n_tiles = n_tiles; g.N = p.n_anchors; g.mode = prm.mode;
@@ -584,7 +589,7 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
       tr.end();
       if (e != hipSuccess) return hip_fail(e, "score kernel");
     }
-    if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+    if ((r = run_gate(sh, p, prm, s, partials, reinterpret_cast<double*>(ws + pl.off_gsum), pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
     if (apply || out->w_k || out->w_v)
       if ((r = run_split_weights(f, SPLIT_W_PARTIALS, ws, pl, tr, st)) != KVC_OK) return r;
     if (apply) {
@@ -621,13 +626,13 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
     hipError_t e = launch_fused(f, FUSED_PAGES, sh.head_dim, st);
     tr.end();
     if (e != hipSuccess) return hip_fail(e, "fused kernel");
-    if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+    if ((r = run_gate(sh, p, prm, s, partials, reinterpret_cast<double*>(ws + pl.off_gsum), pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
     if (out->s_cov) *out->s_cov = s.s_cov;
     return KVC_OK;
   }
   // materialised scores
   if ((r = run_scores(k_src, v_src, sh, p_src, rope, p, prm, s, pl, ws, tr, st)) != KVC_OK) return r;
-  if ((r = run_gate(sh, p, prm, s, partials, pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+  if ((r = run_gate(sh, p, prm, s, partials, reinterpret_cast<double*>(ws + pl.off_gsum), pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
   const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
   const size_t plane = (size_t)sh.n_layers * sh.seq_len * std::max(p.n_anchors, 1);
   if (apply && pl.split_apply) {

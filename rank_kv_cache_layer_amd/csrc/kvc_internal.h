@@ -105,6 +105,7 @@ struct ApplyArgs {
 
 struct GateArgs {
   const float* partials;     // [3][N_l][n_tiles][N]
+  double* gsum;              // [3][1+N_l][N] per-layer sums (workspace)
   double* dist;              // [1+N_l][N]
   double* stat;              // [1+N_l]
   int32_t* flags;            // [1+N_l]
