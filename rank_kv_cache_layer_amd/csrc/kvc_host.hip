@@ -397,6 +397,8 @@ kvc_status split_args(SplitArgs& f, const void* k_src, const void* v_src, const 
   f.z[0] = (const uint16_t*)k_src;
   f.z[1] = (const uint16_t*)v_src;
   f.n_layers = sh.n_layers;
+  f.layer0 = 0;
+  f.n_grp = sh.n_layers;
   f.S = sh.seq_len;
   f.D = D_of(sh);
   f.ntt = (sh.seq_len + kScoreTile - 1) / kScoreTile;   // set per launch by the kernels

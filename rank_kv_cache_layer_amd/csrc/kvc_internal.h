@@ -208,6 +208,7 @@ struct SplitArgs {
   FusedTab can;                     // R(-p_src)
   FusedTab shift;                   // R(p_tgt - p_src)
   float inv_temp, inv_d;            // 1 / temp_weight, 1 / D
+  int32_t layer0, n_grp;            // layers [layer0, layer0 + n_grp) in this launch
 };
 
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st);

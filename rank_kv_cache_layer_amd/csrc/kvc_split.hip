@@ -204,25 +204,52 @@ __device__ __forceinline__ void rotate_tile(f32x16 (&z)[2][4], const float* cs, 
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane sums on the VALU (DPP and the gfx950 lane swap), no LDS round trips.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+// sum over the 64 lanes, complete in lane 63: within quads, within rows of 16 (rotations by
+// 4 and 8), then row 0 into row 1, row 2 into row 3, and row 1 into rows 2 and 3
+__device__ __forceinline__ float wave_sum63(float v) {
+  v += dpp<0xB1>(v);          // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);          // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);         // row_ror:4
+  v += dpp<0x128>(v);         // row_ror:8
+  v += dpp<0x142, 0xa>(v);    // row_bcast:15
+  v += dpp<0x143, 0xc>(v);    // row_bcast:31
   return v;
+}
+// v + (v of lane ^ 32)
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
 // Tile decode: the channel tile is the fastest index so the channel tiles of one token tile
 // run side by side on one XCD (they share the anchors' A rows through its L2), then token
-// tiles, layers, sides.
+// tiles, layers, sides.  With `side_first` the side is the fastest index instead: the scoring
+// pass then keeps key tiles (|E| sums only) and value tiles (|E| and E^2 sums, twice the
+// vector work) side by side on every CU, so the matrix and vector units are loaded evenly.
 struct TileId {
   int cq, tt, layer, side;
 };
+template <bool side_first = false>
 __device__ __forceinline__ TileId tile_id(const SplitArgs& p) {
-  const int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
   TileId t;
+  if constexpr (side_first) {
+    t.side = (int)(lb & 1);
+    lb >>= 1;
+    t.cq = (int)(lb % p.nct);
+    t.tt = (int)((lb / p.nct) % p.ntt);
+    t.layer = p.layer0 + (int)((lb / ((int64_t)p.nct * p.ntt)) % p.n_grp);
+    return t;
+  }
   t.cq = (int)(lb % p.nct);
   t.tt = (int)((lb / p.nct) % p.ntt);
-  t.layer = (int)((lb / ((int64_t)p.nct * p.ntt)) % p.n_layers);
-  t.side = (int)(lb / ((int64_t)p.nct * p.ntt * p.n_layers));
+  t.layer = p.layer0 + (int)((lb / ((int64_t)p.nct * p.ntt)) % p.n_grp);
+  t.side = (int)(lb / ((int64_t)p.nct * p.ntt * p.n_grp));
   return t;
 }
 
@@ -259,9 +286,14 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t s
       for (int j = 0; j < 16; ++j) q[tb] = fmaf(e[j], e[j], q[tb]);
     }
   };
-  bf16x8 bv[RK];
+  // B fragments of channel block db (bv) and db + 1 (bn): each block's are read from LDS two
+  // result blocks before their first use
+  bf16x8 bv[RK], bn[RK];
 #pragma unroll
-  for (int ks = 0; ks < RK; ++ks) bv[ks] = as_bf8(lds_u4(bs + ks * 1024));
+  for (int ks = 0; ks < RK; ++ks) {
+    bv[ks] = as_bf8(lds_u4(bs + ks * 1024));
+    bn[ks] = as_bf8(lds_u4(bs + (RK + ks) * 1024));
+  }
   f32x16 e = chain(bv, 0, 0);
 #pragma unroll
   for (int b = 1; b <= 8; ++b) {
@@ -270,9 +302,13 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t s
       const int db = b >> 1, tb = b & 1;
       if (tb == 0) {
 #pragma unroll
-        for (int ks = 0; ks < RK; ++ks) bv[ks] = as_bf8(lds_u4(bs + (db * RK + ks) * 1024));
+        for (int ks = 0; ks < RK; ++ks) bv[ks] = bn[ks];
       }
       en = chain(bv, tb, db);
+      if (tb == 0 && db < 3) {
+#pragma unroll
+        for (int ks = 0; ks < RK; ++ks) bn[ks] = as_bf8(lds_u4(bs + ((db + 1) * RK + ks) * 1024));
+      }
     }
     reduce(e, (b - 1) & 1);
     // the q sums are tied too: left free, their FMAs sink and keep every block alive
@@ -374,7 +410,7 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
   __shared__ float qp[kNW][kMaxAnchors];
   __shared__ float tab[2][kFusedHalf];
 
-  const TileId id = tile_id(p);
+  const TileId id = tile_id<true>(p);
   const bool keys = id.side == 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int tw = wave >> 1, cw = wave & 1;
@@ -436,20 +472,22 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
       if (j > 0) store_m(j - 1);
       fetch(j + 2);
       const int a = lane_get(sl.a, j);
-      const uint32_t slot = ring0 + (uint32_t)(j % kSlots) * RG::SLOT;
+      // through a lane read the base is opaque: each operand address is then one add to it
+      // plus an immediate offset, not a re-derivation of j % kSlots per access
+      const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));
       float ms0 = 0.f, ms1 = 0.f, qs = 0.f;
       score_anchor<RK, Q, RG>(z, slot, aoff, boff, qm0, qm1, ms0, ms1, qs);
       if ((p.mask_corr >> a) & 1) {
-        ms0 += __shfl_xor(ms0, 32);
-        ms1 += __shfl_xor(ms1, 32);
+        ms0 = xor32_sum(ms0);
+        ms1 = xor32_sum(ms1);
         if (hi == 0) {
           mp[j & 1][cw][tw * 64 + col] = ms0;
           mp[j & 1][cw][tw * 64 + 32 + col] = ms1;
         }
       }
       if (Q && ((p.mask_gate >> a) & 1)) {
-        qs = wave_sum(qs);
-        if (lane == 0) qp[wave][a] = qs;
+        qs = wave_sum63(qs);
+        if (lane == 63) qp[wave][a] = qs;
       }
     }
   };
@@ -492,7 +530,7 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
   extern __shared__ float xs[];   // [n_corr][256]
   const int tid = threadIdx.x;
   const int t = blockIdx.x * 256 + tid;
-  const int layer = blockIdx.y, side = blockIdx.z;
+  const int layer = p.layer0 + blockIdx.y, side = blockIdx.z;
   const int S = p.S, N = p.N, L = p.n_layers, nc = p.n_corr;
   const bool in = t < S, cov = t < p.s_cov;
   float mx = -INFINITY;
@@ -544,7 +582,7 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
   extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
   __shared__ float tab[2][kFusedHalf];
 
-  const TileId id = tile_id(p);
+  const TileId id = tile_id<true>(p);
   const bool keys = id.side == 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int tw = wave >> 1, cw = wave & 1;
@@ -599,17 +637,29 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
   for (int j = 0; j < nc; ++j) {
     wait_vm_barrier<RG::DMA_PER_WAVE>();   // anchor j landed for every wave; slot (j + 2) % 3 is free
     fetch(j + 2);
-    const uint32_t slot = ring0 + (uint32_t)(j % kSlots) * RG::SLOT;
+    const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));   // opaque base
+    // every operand of the anchor is read from LDS first (one latency per step), then scaled
+    // and contracted
     const float w0 = lds_f(slot + woff), w1 = lds_f(slot + woff + 128);
+    uint4 ar[2][RKD];
+    bf16x8 bb[4][RKD];
 #pragma unroll
     for (int ks = 0; ks < RKD; ++ks) {
-      const bf16x8 a0 = as_bf8(scale8(lds_u4(slot + aoff[0][ks]), w0));
-      const bf16x8 a1 = as_bf8(scale8(lds_u4(slot + aoff[1][ks]), w1));
+      ar[0][ks] = lds_u4(slot + aoff[0][ks]);
+      ar[1][ks] = lds_u4(slot + aoff[1][ks]);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ks = 0; ks < RKD; ++ks) bb[db][ks] = as_bf8(lds_u4(slot + boff + (db * RKD + ks) * 1024));
+#pragma unroll
+    for (int ks = 0; ks < RKD; ++ks) {
+      const bf16x8 a0 = as_bf8(scale8(ar[0][ks], w0));
+      const bf16x8 a1 = as_bf8(scale8(ar[1][ks], w1));
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 b = as_bf8(lds_u4(slot + boff + (db * RKD + ks) * 1024));
-        acc[0][db] = mfma(b, a0, acc[0][db]);
-        acc[1][db] = mfma(b, a1, acc[1][db]);
+        acc[0][db] = mfma(bb[db][ks], a0, acc[0][db]);
+        acc[1][db] = mfma(bb[db][ks], a1, acc[1][db]);
       }
     }
   }
@@ -626,7 +676,7 @@ hipError_t go(K kernel, const SplitArgs& args, int tile, int threads, size_t shm
   }
   SplitArgs a = args;
   a.ntt = (a.S + tile - 1) / tile;
-  const int64_t nblk = (int64_t)a.nct * a.ntt * a.n_layers * 2;
+  const int64_t nblk = (int64_t)a.nct * a.ntt * a.n_grp * 2;
   kernel<<<dim3((unsigned)nblk), dim3(threads), shmem, st>>>(a);
   return hipGetLastError();
 }
@@ -679,7 +729,7 @@ hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st) 
 
 hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st) {
   if (a.N > kMaxAnchors || !a.wa || a.n_corr < 1) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((a.S + 255) / 256), (unsigned)a.n_layers, 2);
+  const dim3 grid((unsigned)((a.S + 255) / 256), (unsigned)a.n_grp, 2);
   split_weights<<<grid, 256, sizeof(float) * 256 * (size_t)a.n_corr, st>>>(a, wmode);
   return hipGetLastError();
 }
