@@ -309,68 +309,75 @@ __global__ void __launch_bounds__(1024) chol_inv(double* G, double* Li, int l, d
 }
 
 // Same factorisation and inverse with L resident in LDS as its packed lower triangle (fp64),
-// for l up to kJacobiLdsMax: right-looking Cholesky with dropping, then the in-place inverse of
-// the lower-triangular factor column by column from the right (X_jj = 1 / L_jj, then
-// X[i][j] = -X_jj sum_{k=j+1..i} X[i][k] L[k][j]); a dropped pivot gets X_jj = 0, which zeroes
-// its row and column of the inverse.  Li is written in full (upper triangle zero).
+// for l up to kJacobiLdsMax.  Right-looking Cholesky with dropping: step k takes the pivot,
+// scales column k (kept in `col`) and updates the trailing lower triangle row by row (one wave
+// per row, lanes along the row).  Then the inverse X = L^-1 in place by forward elimination of
+// [L | I]: step k divides row k of X (columns <= k) by L_kk and subtracts L_ik times it from
+// every later row i, so each step is one parallel rank-1 update; row i's X entries take the
+// places of L entries already used (column c of L is last read at step c).  A dropped pivot
+// gets X_kk = 0 and a zero column below it, which zeroes its row and column of the inverse.
+// Li is written in full (upper triangle zero).
 __global__ void __launch_bounds__(1024) chol_inv_lds(const double* G, double* Li, int l, double rel_tol) {
-  extern __shared__ double T[];   // packed lower triangle, l (l + 1) / 2 entries
+  extern __shared__ double T[];   // packed lower triangle: entry (i, j), j <= i, at ro[i] + j
   __shared__ double col[256];
   __shared__ double diag_max;
+  __shared__ int ro[256];
   __shared__ int dead[256];
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = blockDim.x, wave = tid >> 6, lane = tid & 63, nw = nt >> 6;
   G += (int64_t)blockIdx.x * l * l;
   Li += (int64_t)blockIdx.x * l * l;
-  const int ntri = l * (l + 1) / 2;
-  for (int i = 0; i < l; ++i)
-    for (int j = tid; j <= i; j += nt) T[i * (i + 1) / 2 + j] = G[(int64_t)i * l + j];
+  for (int i = tid; i < l; i += nt) ro[i] = i * (i + 1) / 2;
+  for (int i = wave; i < l; i += nw)
+    for (int j = lane; j <= i; j += 64) T[i * (i + 1) / 2 + j] = G[(int64_t)i * l + j];
   __syncthreads();
   if (tid == 0) {
     double m = 0.0;
-    for (int i = 0; i < l; ++i) m = fmax(m, T[i * (i + 1) / 2 + i]);
+    for (int i = 0; i < l; ++i) m = fmax(m, T[ro[i] + i]);
     diag_max = m;
   }
   __syncthreads();
   const double tol = rel_tol * diag_max;
   for (int k = 0; k < l; ++k) {
-    const double d = T[k * (k + 1) / 2 + k];   // every thread: the same value
+    const double d = T[ro[k] + k];   // every thread: the same value
     const bool drop = !(d > tol);
     const double piv = drop ? 0.0 : sqrt(d);
-    __syncthreads();
+    for (int i = k + 1 + tid; i < l; i += nt) {
+      const double x = drop ? 0.0 : T[ro[i] + k] / piv;
+      T[ro[i] + k] = x;
+      col[i] = x;
+    }
+    __syncthreads();   // column k complete; every thread has read the pivot
     if (tid == 0) {
       dead[k] = drop;
-      T[k * (k + 1) / 2 + k] = drop ? 1.0 : piv;
+      T[ro[k] + k] = drop ? 1.0 : piv;
     }
-    for (int i = k + 1 + tid; i < l; i += nt) {
-      double& x = T[i * (i + 1) / 2 + k];
-      x = drop ? 0.0 : x / piv;
-    }
-    __syncthreads();
-    const int rem = l - k - 1;
-    for (int e = tid; e < rem * rem; e += nt) {
-      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
-      if (j <= i) T[i * (i + 1) / 2 + j] -= T[i * (i + 1) / 2 + k] * T[j * (j + 1) / 2 + k];
+    for (int i = k + 1 + wave; i < l; i += nw) {
+      const double ci = col[i];
+      const int r = ro[i];
+      for (int j = k + 1 + lane; j <= i; j += 64) T[r + j] -= ci * col[j];
     }
     __syncthreads();
   }
-  // in-place inverse, columns from the right
-  for (int j = l - 1; j >= 0; --j) {
-    const double xjj = dead[j] ? 0.0 : 1.0 / T[j * (j + 1) / 2 + j];
-    for (int i = j + 1 + tid; i < l; i += nt) col[i] = T[i * (i + 1) / 2 + j];
-    __syncthreads();
-    for (int i = j + 1 + tid; i < l; i += nt) {
-      double s = 0.0;
-      for (int k = j + 1; k <= i; ++k) s += T[i * (i + 1) / 2 + k] * col[k];
-      T[i * (i + 1) / 2 + j] = -s * xjj;
+  // inverse by forward elimination
+  for (int k = 0; k < l; ++k) {
+    const double xkk = dead[k] ? 0.0 : 1.0 / T[ro[k] + k];   // every thread: the same value
+    const int rk = ro[k];
+    for (int c = tid; c < k; c += nt) T[rk + c] *= xkk;
+    for (int i = k + 1 + tid; i < l; i += nt) col[i] = T[ro[i] + k];   // L_ik, about to be replaced
+    __syncthreads();   // row k of X final (but X_kk); every thread has read L_kk
+    if (tid == 0) T[rk + k] = xkk;
+    for (int i = k + 1 + wave; i < l; i += nw) {
+      const double li = col[i];
+      const int r = ro[i];
+      for (int c = lane; c < k; c += 64) T[r + c] -= li * T[rk + c];
+      if (lane == 0) T[r + k] = -li * xkk;
     }
-    if (tid == 0) T[j * (j + 1) / 2 + j] = xjj;
     __syncthreads();
   }
-  for (int e = tid; e < l * l; e += nt) {
-    const int i = e / l, j = e % l;
-    Li[e] = j <= i ? T[i * (i + 1) / 2 + j] : 0.0;
+  for (int i = wave; i < l; i += nw) {
+    const int r = ro[i];
+    for (int j = lane; j < l; j += 64) Li[(int64_t)i * l + j] = j <= i ? T[r + j] : 0.0;
   }
-  (void)ntri;
 }
 
 // ------------------------------------------------------------------ Jacobi eigensolver
