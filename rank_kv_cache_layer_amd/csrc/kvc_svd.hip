@@ -17,6 +17,8 @@
 // pivot dropping + triangular inverse, Jacobi, top-r selection, sign fix.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -116,11 +118,116 @@ __global__ void __launch_bounds__(256) gemm(const TA* __restrict__ A, const TB* 
   }
 }
 
+// ------------------------------------------------------------------ fp64 GEMM on matrix cores
+// C[b] (M x N) = opA(A[b]) (M x K) * opB(B[b]) (K x N) with fp64 products and sums on
+// v_mfma_f64_16x16x4_f64 (inputs widened to fp64 as they are loaded, so fp32 products are
+// exact).  A work-group of 4 waves owns a 32 x 32 tile of C (2 x 2 blocks of 16 x 16); K goes
+// in groups of 16, group g to wave g % 4, and the waves' partial tiles are added in wave order
+// at the end.  Inside a group, step s (4 MFMA k-slices) takes k = 4 (l / 16) + s in lane l:
+// the same order for both operands, so the sum is unchanged, and a lane's 4 k of a row-major
+// operand are contiguous (one vector load).  Element v of a block's result in lane l is
+// (4 v + l / 16, l % 16).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct Vec4;
+template <> struct Vec4<float> { typedef float4 type; };
+template <> struct Vec4<double> { typedef double4 type; };
+
+// 4 consecutive elements p[0..3] of a row (k < K guarded per element at the tail)
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, int k, int K, double (&x)[4]) {
+  if (k + 3 < K && (reinterpret_cast<uintptr_t>(p) % sizeof(typename Vec4<T>::type)) == 0) {
+    const typename Vec4<T>::type v = *reinterpret_cast<const typename Vec4<T>::type*>(p);
+    x[0] = (double)v.x; x[1] = (double)v.y; x[2] = (double)v.z; x[3] = (double)v.w;
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] = k + s < K ? to_d(p[s]) : 0.0;
+  }
+}
+
+template <typename TA, typename TB, typename TC, bool TRA, bool TRB>
+__global__ void __launch_bounds__(256) gemm_f64(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ C,
+                                                int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA,
+                                                int64_t sB, int64_t sC) {
+  __shared__ double red[3][16][64];   // partial tiles of waves 1..3
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  const int ia[2] = {i0 + r16, i0 + 16 + r16}, jb[2] = {j0 + r16, j0 + 16 + r16};
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc[t][u] = (f64x4){0.0, 0.0, 0.0, 0.0};
+  const int n_groups = (K + 15) / 16;
+#pragma unroll 2
+  for (int g = wave; g < n_groups; g += 4) {
+    const int k = g * 16 + 4 * kq;   // this lane's k at step 0; k + s at step s
+    double a[2][4], b[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool in_a = ia[t] < M, in_b = jb[t] < N;
+      if (TRA) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[t][s] = in_a && k + s < K ? to_d(A[(int64_t)(k + s) * lda + ia[t]]) : 0.0;
+      } else if (in_a) {
+        load4(A + (int64_t)ia[t] * lda + k, k, K, a[t]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[t][s] = 0.0;
+      }
+      if (!TRB) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[t][s] = in_b && k + s < K ? to_d(B[(int64_t)(k + s) * ldb + jb[t]]) : 0.0;
+      } else if (in_b) {
+        load4(B + (int64_t)jb[t] * ldb + k, k, K, b[t]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[t][s] = 0.0;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[t][u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t][s], b[u][s], acc[t][u], 0, 0, 0);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave - 1][(t * 2 + u) * 4 + v][lane] = acc[t][u][v];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        double x = acc[t][u][v];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) x += red[w][(t * 2 + u) * 4 + v][lane];
+        const int i = i0 + 16 * t + 4 * v + kq, j = j0 + 16 * u + r16;
+        if (i < M && j < N) C[(int64_t)i * ldc + j] = from_acc<TC>(x);
+      }
+}
+
 template <typename TA, typename TB, typename TC, typename ACC, bool TRA, bool TRB>
 hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
                     int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
-  gemm<TA, TB, TC, ACC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+  if constexpr (std::is_same<ACC, double>::value) {
+    const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32), (unsigned)batch);
+    gemm_f64<TA, TB, TC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+  } else {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
+    gemm<TA, TB, TC, ACC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+  }
   return hipGetLastError();
 }
 
