@@ -1,9 +1,9 @@
 // Two-pass per-hop correction for gfx950 (CDNA4), bf16 caches, tiled for operand reuse:
 // every work-group covers 128 tokens x 256 channels of one (layer, side) with 4 waves, wave
 // (tw, cw) owning tokens [64 tw, 64 tw + 64) and channels [128 cw, 128 cw + 128) of the tile;
-// two work-groups share a CU.  Anchor factors stream through double-buffered LDS slots shared
-// by the waves, so each anchor's A rows are read once per 256 channels and its B slice once
-// per 128 tokens.
+// two scoring or three apply work-groups share a CU.  Anchor factors stream through LDS slots
+// shared by the waves, so each anchor's A rows are read once per 256 channels and its B slice
+// once per 128 tokens.
 //
 // KVCMAS (arXiv 2609.34060):
 //  * split_score: App. A.3 "Correction Weighting and Positional Alignment" -- per token, side
@@ -327,11 +327,13 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t s
 // ------------------------------------------------------------ operand ring (LDS, DMA-filled)
 // Anchor operands stream from memory straight into LDS with buffer->LDS DMA (each lane of a
 // wave instruction moves 16 bytes to LDS base + 16 * lane; lanes past the descriptor's size
-// write zeros), into a ring of kSlots slots: slot j % kSlots holds anchor j's A rows, its B
-// slice and (apply) its token weights.  Anchor j + 2 is fetched while anchor j is consumed; a
-// step waits only for its own slot (vmcnt), then a bare barrier (no release fence, which
-// would drain every DMA in flight).
-constexpr int kSlots = 3;
+// write zeros), into a ring of slots: slot j % (slots) holds anchor j's A rows, its B slice and
+// (apply) its token weights.  The scoring pass has three slots and fetches anchor j + 2 while
+// anchor j is consumed; the apply pass has two and fetches anchor j + 1.  A step waits only for
+// its own slot (vmcnt), then a bare barrier (no release fence, which would drain every DMA in
+// flight).
+constexpr int kSlots = 3;        // scoring pass
+constexpr int kApplySlots = 2;   // apply pass (three work-groups per CU)
 typedef __attribute__((address_space(3))) void lds_void;
 
 // The transfer is issued through inline assembly: the compiler then neither reorders LDS
@@ -574,8 +576,11 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
 // ================================================================== pass 2: apply
 // Sec. 3.3 Eq. 8 / App. A.3 Eq. 12: out = R(s) Z + sum_a w_a A_a B'_a, the token weights read
 // anchor-major (split_weights) and folded into the A fragments after they leave LDS.
+// Three work-groups share a CU (at most 168 VGPRs per lane, a two-slot ring of ~49 KB): the
+// extra waves cover the tile's load and store phases and the operand waits, which pays more
+// than a third slot or operands held in registers across a step.
 template <int HD, int RKD>
-__global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
+__global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
   using RG = Ring<RKD, kST, kNW, true>;
   constexpr int R = RKD * 16;
@@ -608,7 +613,7 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
     const int js = live ? j : 0;
     const int a = lane_get(sl.a, js);
     const int lim = live ? lane_get(sl.lim, js) : 0;
-    RG::fetch(ring0 + (uint32_t)(j % kSlots) * RG::SLOT,
+    RG::fetch(ring0 + (uint32_t)(j % kApplySlots) * RG::SLOT,
               make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
               make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
               t0, wv, lane);
@@ -620,46 +625,35 @@ __global__ void __launch_bounds__(kApplyThreads, 2) split_apply(SplitArgs p) {
     for (int ks = 0; ks < RKD; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
   const uint32_t boff = RG::A_BYTES + cw * 4 * RKD * 1024 + lane * 16;
   const uint32_t woff = RG::A_BYTES + RG::B_BYTES + (tw * 64 + col) * 4;
-  uint16_t* stage = reinterpret_cast<uint16_t*>(ring + RG::SLOT) + wave * kStage;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(ring) + wave * kStage;   // over the ring, before anchor 0
 
-  if (nc > 0) fetch(0);
   __syncthreads();   // rotation table
-  // ---- residual: R(s) K or V (staging in the ring past slot 0, free until anchor 1 is fetched)
+  // ---- residual: R(s) K or V
   f32x16 acc[2][4];
   const uint32_t layer_bytes = (uint32_t)S * D * 2;
   load_tile(acc, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, stage, lane, col, hi);
   if (keys && p.shift.active) rotate_tile<HD>(acc, tab[0], tab[1], hi);
   if (nc > 0) {
     wait_vm_barrier<63>();   // every wave is done with the staging area
-    fetch(1);
+    fetch(0);
   }
 #pragma nounroll
   for (int j = 0; j < nc; ++j) {
-    wait_vm_barrier<RG::DMA_PER_WAVE>();   // anchor j landed for every wave; slot (j + 2) % 3 is free
-    fetch(j + 2);
-    const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));   // opaque base
-    // every operand of the anchor is read from LDS first (one latency per step), then scaled
-    // and contracted
+    // anchor j landed for every wave, and every wave is past step j - 1, the last reader of
+    // the other slot, which now takes anchor j + 1
+    wait_vm_barrier<0>();
+    fetch(j + 1);
+    const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kApplySlots) * RG::SLOT));   // opaque base
     const float w0 = lds_f(slot + woff), w1 = lds_f(slot + woff + 128);
-    uint4 ar[2][RKD];
-    bf16x8 bb[4][RKD];
 #pragma unroll
     for (int ks = 0; ks < RKD; ++ks) {
-      ar[0][ks] = lds_u4(slot + aoff[0][ks]);
-      ar[1][ks] = lds_u4(slot + aoff[1][ks]);
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int ks = 0; ks < RKD; ++ks) bb[db][ks] = as_bf8(lds_u4(slot + boff + (db * RKD + ks) * 1024));
-#pragma unroll
-    for (int ks = 0; ks < RKD; ++ks) {
-      const bf16x8 a0 = as_bf8(scale8(ar[0][ks], w0));
-      const bf16x8 a1 = as_bf8(scale8(ar[1][ks], w1));
+      const bf16x8 a0 = as_bf8(scale8(lds_u4(slot + aoff[0][ks]), w0));
+      const bf16x8 a1 = as_bf8(scale8(lds_u4(slot + aoff[1][ks]), w1));
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        acc[0][db] = mfma(bb[db][ks], a0, acc[0][db]);
-        acc[1][db] = mfma(bb[db][ks], a1, acc[1][db]);
+        const bf16x8 b = as_bf8(lds_u4(slot + boff + (db * RKD + ks) * 1024));
+        acc[0][db] = mfma(b, a0, acc[0][db]);
+        acc[1][db] = mfma(b, a1, acc[1][db]);
       }
     }
   }
@@ -702,7 +696,9 @@ hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// dynamic LDS: the operand ring, or slot 0 plus the waves' staging areas, whichever is larger
+// dynamic LDS: the operand ring, or the waves' staging areas (scoring: past slot 0, which is
+// filled during the tile load; apply: from the start, before anchor 0 is fetched), whichever
+// is larger
 size_t split_score_lds(int r_b) {
   const size_t slot = (size_t)kScoreTile * r_b * 2 + (size_t)kNCBW * (r_b / 16) * 1024;
   return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kScoreThreads / 64) * kStage);
@@ -710,7 +706,7 @@ size_t split_score_lds(int r_b) {
 
 size_t split_apply_lds(int r_d) {
   const size_t slot = (size_t)kApplyTile * r_d * 2 + (size_t)kNCBW * (r_d / 16) * 1024 + (size_t)kApplyTile * 4;
-  return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
+  return std::max((size_t)kApplySlots * slot, sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
 }
 
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st) {
