@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 #define KVC_MAX_ANCHORS 64
 #define KVC_MAX_HEAD_DIM 256
 
@@ -93,9 +93,15 @@ typedef struct {
 
 /* One slot's anchor pool as seen by one consuming agent (App. A.3: each anchor stores a
  * base representation and corrections for its consumers; Eq. 7 factors).
- *  A factors are packed without padding: anchor a owns rows [off_a, off_a + anchor_len[a])
- *  with off_a = sum_{b<a} anchor_len[b]; arrays are [n_layers][sum(len)][rank].
+ *  A factors, slot_rows == 0: packed without padding: anchor a owns rows
+ *  [off_a, off_a + anchor_len[a]) with off_a = sum_{b<a} anchor_len[b]; arrays are
+ *  [n_layers][sum(len)][rank].  slot_rows > 0: fixed-capacity slots (a pool arena, see
+ *  kvc_pool_insert): anchor a owns rows [a * slot_rows, a * slot_rows + anchor_len[a]) and
+ *  arrays are [n_layers][n_anchors * slot_rows][rank]; every anchor_len[a] <= slot_rows.
  *  B factors are [n_layers][n_anchors][rank][D].
+ *  live (host, optional): anchors with live[a] == 0 take no part in the call (an empty arena
+ *  slot, or an anchor holding no correction for this consumer); their length and factors are
+ *  not read.  NULL = every anchor live.
  *  Key bases and key deltas are canonical-frame.  All factor arrays share `dtype`, which
  *  must equal the cache dtype.  capacity == 1 bypasses the gate (App. C.3). */
 typedef struct {
@@ -107,6 +113,9 @@ typedef struct {
   kvc_dtype dtype;
   const void* baseA_k;  const void* baseB_k;  const void* baseA_v;  const void* baseB_v;
   const void* deltaA_k; const void* deltaB_k; const void* deltaA_v; const void* deltaB_v;
+  int32_t slot_rows;          /* 0 = packed A rows; > 0 = fixed-capacity slots (above)         */
+  int32_t pad_;
+  const uint8_t* live;        /* host [n_anchors] or NULL                                      */
 } kvc_pool;
 
 /* Optional per-kernel trace for benchmarking.  The caller creates `capacity` pairs of
@@ -253,6 +262,76 @@ kvc_status kvc_anchor_refresh_svd(const float* z, int32_t n_mats, int32_t rows, 
                                   float* sigma_out, int32_t oversample, int32_t power_iters,
                                   uint64_t seed, void* workspace, size_t ws_bytes,
                                   void* stream);
+
+/* ---------------------------------------------------------------- pool updates
+ * KVCMAS App. A.3 "Cache Materialization and Pool Updates": after a dense fallback at the
+ * edge i -> j, the observed correction Delta = C_j - Align(C_i) (Eq. 12) and the source cache
+ * are factorised (Eq. 7) and inserted as a new anchor; accepted corrections are not
+ * reinserted; when the pool is full, the least frequently used anchor among the five oldest
+ * is evicted.  The pool's anchors live in a caller-owned arena: a kvc_pool with
+ * slot_rows > 0 and n_anchors = its capacity, read through kvc_pool_view's live mask. */
+
+/* Eq. 12 in fp32, per layer and side, for the factorisation: any output may be NULL.
+ *  k_base  = R(-p_src) K_src (the canonical-frame source keys)      needs k_src
+ *  v_base  = V_src                                                  needs v_src
+ *  k_delta = R(-p_tgt) (K_tgt - R(p_tgt - p_src) K_src), formed as R(-p_tgt) K_tgt - R(-p_src) K_src
+ *                                                                   needs k_src, k_tgt
+ *  v_delta = V_tgt - V_src                                          needs v_src, v_tgt
+ * Inputs [n_layers][seq_len][D] of dtype; outputs fp32, same layout, 16-byte aligned, not
+ * overlapping any input or each other.  Enqueued on `stream`; no allocation. */
+kvc_status kvc_observed_delta(const void* k_src, const void* v_src, const void* k_tgt, const void* v_tgt,
+                              kvc_dtype dtype, kvc_shape shape, int64_t p_src, int64_t p_tgt,
+                              const kvc_rope* rope, float* k_base, float* v_base, float* k_delta,
+                              float* v_delta, void* stream);
+
+#define KVC_POOL_EVICT_WINDOW 5   /* eviction looks at the five oldest anchors (App. A.3) */
+
+/* Host-side bookkeeping of one shared-context slot's pool (caller-allocated, plain data).
+ * Arena slot a is empty when stamp[a] == 0; otherwise it holds one anchor inserted at the
+ * stamp-th insertion, with `len` rows and the correction for `consumer`. */
+typedef struct {
+  int32_t capacity;                   /* V, 1 .. KVC_MAX_ANCHORS                          */
+  int32_t n_held;
+  int64_t clock;                      /* insertions so far                                */
+  int64_t stamp[KVC_MAX_ANCHORS];     /* insertion order, 0 = empty                       */
+  int64_t uses[KVC_MAX_ANCHORS];      /* accepted hops whose correction set held it       */
+  int32_t len[KVC_MAX_ANCHORS];       /* stored rows                                      */
+  int32_t consumer[KVC_MAX_ANCHORS];  /* consuming agent whose correction it stores       */
+} kvc_pool_state;
+
+kvc_status kvc_pool_state_init(kvc_pool_state* st, int32_t capacity);
+
+/* Records one hop into `consumer` over a segment of seg_len rows, after its gate decision.
+ *  flagged == 0 (accepted correction): nothing is inserted; every anchor of the consumer's
+ *    correction set (its anchors covering min(seg_len, its longest anchor) rows) gains a use;
+ *    *slot_out = *evicted_out = -1.
+ *  flagged != 0 (dense fallback): a slot for the new anchor: the lowest empty slot, or, when
+ *    the pool is full, among the KVC_POOL_EVICT_WINDOW oldest anchors the one with the fewest
+ *    uses (ties: the oldest), which is evicted (*evicted_out).  The slot is stamped with
+ *    seg_len rows and `consumer`; the caller then fills it with kvc_pool_insert.
+ * Host only, no GPU work.  Errors leave the state unchanged. */
+kvc_status kvc_pool_record_hop(kvc_pool_state* st, int32_t consumer, int32_t seg_len, int32_t flagged,
+                               int32_t* slot_out, int32_t* evicted_out);
+
+/* The consumer's view of the arena, for the kvc_pool descriptor of its match / correct calls:
+ * anchor_len_out[a] and live_out[a] for a < capacity (live = the slot holds an anchor with a
+ * correction for `consumer`).  Returns the number of live anchors, or -1 on bad arguments. */
+int32_t kvc_pool_view(const kvc_pool_state* st, int32_t consumer, int32_t* anchor_len_out, uint8_t* live_out);
+
+/* Fills arena slot `slot` with a new anchor after a dense fallback (App. A.3, Eq. 12, Eq. 7):
+ * the canonical source (R(-p_src) K_src, V_src) factorised at rank_base and the observed
+ * correction (kvc_observed_delta) at rank_delta, both by kvc_anchor_refresh_svd's method
+ * (`oversample`, `power_iters`, seeds derived from `seed`), written into the arena's factor
+ * arrays (which this call writes through their const pointers): A rows
+ * [slot * slot_rows, slot * slot_rows + seq_len) of every layer and B entry `slot`.
+ * Caches are arena->dtype; arena->slot_rows >= seq_len.  Workspace:
+ * kvc_pool_insert_workspace_size (fp32 source and correction of one side, factor staging and
+ * the factorisation's own).  Enqueued on `stream`; no allocation. */
+size_t kvc_pool_insert_workspace_size(kvc_shape shape, const kvc_pool* arena, int32_t oversample);
+kvc_status kvc_pool_insert(const void* k_src, const void* v_src, const void* k_tgt, const void* v_tgt,
+                           kvc_shape shape, int64_t p_src, int64_t p_tgt, const kvc_rope* rope,
+                           const kvc_pool* arena, int32_t slot, int32_t oversample, int32_t power_iters,
+                           uint64_t seed, void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -94,16 +94,34 @@ struct Sets {
   std::vector<int> corr_list, use_list;
 };
 
+bool is_live(const kvc_pool& p, int a) { return !p.live || p.live[a] != 0; }
+
+// A-row offset and length of every anchor, and rows per layer of the A arrays
+int64_t anchor_rows(const kvc_pool& p, int32_t* off, int32_t* len) {
+  int64_t tot = 0;
+  for (int a = 0; a < p.n_anchors; ++a) {
+    off[a] = p.slot_rows > 0 ? a * p.slot_rows : (int32_t)tot;
+    len[a] = is_live(p, a) ? p.anchor_len[a] : 0;
+    tot += p.slot_rows > 0 ? p.slot_rows : p.anchor_len[a];
+  }
+  return tot;
+}
+
 Sets anchor_sets(const kvc_pool& p, int S, int gate_len) {
   Sets s;
   s.k = gate_len == 0 ? S : gate_len;
-  int maxlen = 0;
-  for (int a = 0; a < p.n_anchors; ++a) maxlen = std::max(maxlen, (int)p.anchor_len[a]);
-  s.s_cov = p.n_anchors ? std::min(S, maxlen) : 0;
+  int maxlen = 0, n_live = 0;
+  for (int a = 0; a < p.n_anchors; ++a)
+    if (is_live(p, a)) {
+      maxlen = std::max(maxlen, (int)p.anchor_len[a]);
+      ++n_live;
+    }
+  s.s_cov = n_live ? std::min(S, maxlen) : 0;
   for (int a = 0; a < p.n_anchors; ++a) {
+    if (!is_live(p, a)) continue;
     const int len = p.anchor_len[a];
     if (len >= s.k) { s.gate |= 1ull << a; ++s.n_gate; }
-    if (p.n_anchors && len >= s.s_cov) { s.corr |= 1ull << a; s.corr_list.push_back(a); }
+    if (len >= s.s_cov) { s.corr |= 1ull << a; s.corr_list.push_back(a); }
     if ((s.gate | s.corr) >> a & 1) s.use_list.push_back(a);
   }
   return s;
@@ -120,10 +138,17 @@ kvc_status check_pool(const kvc_pool* p, const kvc_shape& sh, kvc_dtype cache_t,
   if (p->dtype != cache_t) return fail(KVC_E_DTYPE, "pool dtype %d differs from cache dtype %d", p->dtype, cache_t);
   if (p->n_anchors == 0) return KVC_OK;
   if (!p->anchor_len) return fail(KVC_E_NULL, "pool: anchor_len is NULL");
+  if (p->slot_rows < 0) return fail(KVC_E_SHAPE, "pool: slot_rows = %d < 0", p->slot_rows);
   int64_t tot = 0;
   for (int a = 0; a < p->n_anchors; ++a) {
+    if (!is_live(*p, a) && p->slot_rows > 0) {   // an empty or foreign slot: its length is not read
+      tot += p->slot_rows;
+      continue;
+    }
     if (p->anchor_len[a] < 1) return fail(KVC_E_SHAPE, "pool: anchor_len[%d] = %d < 1", a, p->anchor_len[a]);
-    tot += p->anchor_len[a];
+    if (p->slot_rows > 0 && p->anchor_len[a] > p->slot_rows)
+      return fail(KVC_E_SHAPE, "pool: anchor_len[%d] = %d exceeds slot_rows = %d", a, p->anchor_len[a], p->slot_rows);
+    tot += p->slot_rows > 0 ? p->slot_rows : p->anchor_len[a];
   }
   if (tot * std::max(p->rank_base, p->rank_delta) >= (1ll << 40)) return fail(KVC_E_SHAPE, "pool: too many rows");
   const void* ptrs[8] = {p->baseA_k, p->baseB_k, p->baseA_v, p->baseB_v,
@@ -292,12 +317,7 @@ PoolGeom geom(const kvc_pool& p, const kvc_shape& sh, int r) {
   memset(&g, 0, sizeof g);
   g.n = p.n_anchors;
   g.r = r;
-  int64_t tot = 0;
-  for (int a = 0; a < p.n_anchors; ++a) {
-    g.off[a] = (int32_t)tot;
-    g.len[a] = p.anchor_len[a];
-    tot += p.anchor_len[a];
-  }
+  const int64_t tot = anchor_rows(p, g.off, g.len);
   g.a_layer_stride = tot * r;
   g.b_layer_stride = (int64_t)p.n_anchors * r * D_of(sh);
   return g;
@@ -375,12 +395,7 @@ kvc_status fused_args(FusedArgs& f, const void* k_src, const void* v_src, const 
   for (int i = 0; i < f.n_use; ++i) f.use[i] = (uint8_t)s.use_list[i];
   f.n_corr = (int)s.corr_list.size();
   for (int i = 0; i < f.n_corr; ++i) f.corr[i] = (uint8_t)s.corr_list[i];
-  int64_t tot = 0;
-  for (int a = 0; a < p.n_anchors; ++a) {
-    f.off[a] = (int32_t)tot;
-    f.len[a] = p.anchor_len[a];
-    tot += p.anchor_len[a];
-  }
+  const int64_t tot = anchor_rows(p, f.off, f.len);
   f.ab_layer = tot * p.rank_base;
   f.ad_layer = tot * p.rank_delta;
   f.inv_temp = inv_temp;
@@ -414,12 +429,7 @@ kvc_status split_args(SplitArgs& f, const void* k_src, const void* v_src, const 
   for (int i = 0; i < f.n_use; ++i) f.use[i] = (uint8_t)s.use_list[i];
   f.n_corr = (int)s.corr_list.size();
   for (int i = 0; i < f.n_corr; ++i) f.corr[i] = (uint8_t)s.corr_list[i];
-  int64_t tot = 0;
-  for (int a = 0; a < p.n_anchors; ++a) {
-    f.off[a] = (int32_t)tot;
-    f.len[a] = p.anchor_len[a];
-    tot += p.anchor_len[a];
-  }
+  const int64_t tot = anchor_rows(p, f.off, f.len);
   f.ab_layer = tot * p.rank_base;
   f.ad_layer = tot * p.rank_delta;
   f.inv_temp = inv_temp;
@@ -759,7 +769,7 @@ size_t kvc_workspace_size(int32_t call, kvc_shape shape, const kvc_pool* pool, c
   if (check_shape(shape) != KVC_OK || !pool || pool->n_anchors < 0 || pool->n_anchors > KVC_MAX_ANCHORS) return 0;
   if (pool->n_anchors > 0 && !pool->anchor_len) return 0;
   for (int a = 0; a < pool->n_anchors; ++a)
-    if (pool->anchor_len[a] < 1) return 0;
+    if (is_live(*pool, a) && pool->anchor_len[a] < 1) return 0;
   const int gl = params ? params->gate_len : 0;
   Sets s = anchor_sets(*pool, shape.seq_len, gl);
   return plan(call, shape, *pool, params, s).total;
@@ -847,7 +857,7 @@ kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k
   sets.s_cov = s_cov;
   if (s_cov > 0)
     for (int a = 0; a < pool->n_anchors; ++a)
-      if (pool->anchor_len[a] >= s_cov) {
+      if (is_live(*pool, a) && pool->anchor_len[a] >= s_cov) {
         sets.corr |= 1ull << a;
         sets.corr_list.push_back(a);
         sets.use_list.push_back(a);
@@ -982,6 +992,202 @@ kvc_status kvc_anchor_refresh_svd(const float* z, int32_t n_mats, int32_t rows, 
   hipError_t e = svd_refresh(z, n_mats, rows, cols, rank, a_out, b_out, out_t == KVC_BF16, sigma_out, oversample,
                              power_iters, seed, workspace, ws_bytes, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "svd refresh");
+  return ok();
+}
+
+// ------------------------------------------------------------------ pool updates (App. A.3)
+kvc_status kvc_observed_delta(const void* k_src, const void* v_src, const void* k_tgt, const void* v_tgt,
+                              kvc_dtype dtype, kvc_shape shape, int64_t p_src, int64_t p_tgt, const kvc_rope* rope,
+                              float* k_base, float* v_base, float* k_delta, float* v_delta, void* stream) {
+  kvc_status s;
+  if ((s = check_dtype(dtype, "cache")) != KVC_OK) return s;
+  if ((s = check_shape(shape)) != KVC_OK) return s;
+  if ((s = check_rope(rope)) != KVC_OK) return s;
+  if ((k_base || k_delta) && !k_src) return fail(KVC_E_NULL, "k_src is NULL");
+  if ((v_base || v_delta) && !v_src) return fail(KVC_E_NULL, "v_src is NULL");
+  if (k_delta && !k_tgt) return fail(KVC_E_NULL, "k_tgt is NULL");
+  if (v_delta && !v_tgt) return fail(KVC_E_NULL, "v_tgt is NULL");
+  const void* ins[4] = {k_src, v_src, k_tgt, v_tgt};
+  float* outs[4] = {k_base, v_base, k_delta, v_delta};
+  const size_t n = (size_t)shape.n_layers * shape.seq_len * D_of(shape);
+  for (int i = 0; i < 4; ++i) {
+    if ((ins[i] && !aligned16(ins[i])) || (outs[i] && !aligned16(outs[i])))
+      return fail(KVC_E_ALIGN, "observed delta: buffers must be 16-byte aligned");
+    for (int j = 0; j < 4; ++j) {
+      if (outs[i] && ins[j] && overlaps(outs[i], n * 4, ins[j], n * esize(dtype)))
+        return fail(KVC_E_ALIAS, "observed delta: output %d overlaps input %d", i, j);
+      if (j != i && outs[i] && outs[j] && overlaps(outs[i], n * 4, outs[j], n * 4))
+        return fail(KVC_E_ALIAS, "observed delta: outputs %d and %d overlap", i, j);
+    }
+  }
+  RopeTab can_src, can_tgt, ident;
+  if ((s = make_tab(can_src, -p_src, shape.head_dim, rope)) != KVC_OK) return s;
+  if ((s = make_tab(can_tgt, -p_tgt, shape.head_dim, rope)) != KVC_OK) return s;
+  if ((s = make_tab(ident, 0, shape.head_dim, rope)) != KVC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t rows = (int64_t)shape.n_layers * shape.seq_len;
+  const int bf = dtype == KVC_BF16;
+  hipError_t e = hipSuccess;
+  if (k_base && e == hipSuccess) e = launch_align(k_src, k_base, bf, 0, rows, shape.n_kv_heads, shape.head_dim, can_src, st);
+  if (v_base && e == hipSuccess) e = launch_align(v_src, v_base, bf, 0, rows, shape.n_kv_heads, shape.head_dim, ident, st);
+  if (k_delta && e == hipSuccess)
+    e = launch_observed_delta(k_tgt, k_src, bf, k_delta, rows, shape.n_kv_heads, shape.head_dim, can_tgt, can_src, st);
+  if (v_delta && e == hipSuccess)
+    e = launch_observed_delta(v_tgt, v_src, bf, v_delta, rows, shape.n_kv_heads, shape.head_dim, ident, ident, st);
+  if (e != hipSuccess) return hip_fail(e, "observed delta kernels");
+  return ok();
+}
+
+kvc_status kvc_pool_state_init(kvc_pool_state* st, int32_t capacity) {
+  if (!st) return fail(KVC_E_NULL, "pool state is NULL");
+  if (capacity < 1 || capacity > KVC_MAX_ANCHORS)
+    return fail(KVC_E_PARAM, "pool capacity must be in [1, %d] (got %d)", KVC_MAX_ANCHORS, capacity);
+  memset(st, 0, sizeof *st);
+  st->capacity = capacity;
+  return ok();
+}
+
+kvc_status kvc_pool_record_hop(kvc_pool_state* st, int32_t consumer, int32_t seg_len, int32_t flagged,
+                               int32_t* slot_out, int32_t* evicted_out) {
+  if (!st || !slot_out || !evicted_out) return fail(KVC_E_NULL, "pool state / slot_out / evicted_out is NULL");
+  if (st->capacity < 1 || st->capacity > KVC_MAX_ANCHORS) return fail(KVC_E_PARAM, "pool state not initialised");
+  if (seg_len < 1) return fail(KVC_E_SHAPE, "seg_len must be >= 1");
+  *slot_out = -1;
+  *evicted_out = -1;
+  const int V = st->capacity;
+  if (!flagged) {
+    // the consumer's correction set: its anchors covering min(S, longest) rows
+    int longest = 0;
+    for (int a = 0; a < V; ++a)
+      if (st->stamp[a] && st->consumer[a] == consumer) longest = std::max(longest, (int)st->len[a]);
+    const int s_cov = std::min(seg_len, longest);
+    for (int a = 0; a < V; ++a)
+      if (st->stamp[a] && st->consumer[a] == consumer && s_cov > 0 && st->len[a] >= s_cov) ++st->uses[a];
+    return ok();
+  }
+  int slot = -1;
+  for (int a = 0; a < V && slot < 0; ++a)
+    if (!st->stamp[a]) slot = a;
+  if (slot < 0) {
+    // full: the KVC_POOL_EVICT_WINDOW oldest anchors, then the fewest uses, ties to the oldest
+    int order[KVC_MAX_ANCHORS];
+    for (int a = 0; a < V; ++a) order[a] = a;
+    std::sort(order, order + V, [&](int x, int y) { return st->stamp[x] < st->stamp[y]; });
+    const int w = std::min(V, (int)KVC_POOL_EVICT_WINDOW);
+    slot = order[0];
+    for (int i = 1; i < w; ++i)
+      if (st->uses[order[i]] < st->uses[slot]) slot = order[i];
+    *evicted_out = slot;
+  } else {
+    ++st->n_held;
+  }
+  st->stamp[slot] = ++st->clock;
+  st->uses[slot] = 0;
+  st->len[slot] = seg_len;
+  st->consumer[slot] = consumer;
+  *slot_out = slot;
+  return ok();
+}
+
+int32_t kvc_pool_view(const kvc_pool_state* st, int32_t consumer, int32_t* anchor_len_out, uint8_t* live_out) {
+  if (!st || !anchor_len_out || !live_out || st->capacity < 1 || st->capacity > KVC_MAX_ANCHORS) return -1;
+  int n = 0;
+  for (int a = 0; a < st->capacity; ++a) {
+    const bool mine = st->stamp[a] != 0 && st->consumer[a] == consumer;
+    live_out[a] = mine ? 1 : 0;
+    anchor_len_out[a] = mine ? st->len[a] : 0;
+    n += mine;
+  }
+  return n;
+}
+
+namespace {
+struct InsertWs {
+  size_t z, d, a, b, sig, svd, total;
+};
+InsertWs insert_layout(const kvc_shape& sh, const kvc_pool& p, int oversample) {
+  InsertWs w;
+  const size_t L = sh.n_layers, S = sh.seq_len, D = D_of(sh), es = esize(p.dtype);
+  const int rmax = std::max(p.rank_base, p.rank_delta);
+  size_t off = 0;
+  w.z = off; off += up256(L * S * D * 4);
+  w.d = off; off += up256(L * S * D * 4);
+  w.a = off; off += up256(L * S * rmax * es);
+  w.b = off; off += up256(L * rmax * D * es);
+  w.sig = off; off += up256(L * rmax * 4);
+  w.svd = off;
+  off += std::max(svd_workspace_bytes(sh.n_layers, sh.seq_len, D_of(sh), p.rank_base, oversample),
+                  svd_workspace_bytes(sh.n_layers, sh.seq_len, D_of(sh), p.rank_delta, oversample));
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t kvc_pool_insert_workspace_size(kvc_shape shape, const kvc_pool* arena, int32_t oversample) {
+  if (check_shape(shape) != KVC_OK || !arena || arena->rank_base < 1 || arena->rank_delta < 1 || oversample < 0)
+    return 0;
+  if (arena->dtype != KVC_F32 && arena->dtype != KVC_BF16) return 0;
+  return insert_layout(shape, *arena, oversample).total;
+}
+
+kvc_status kvc_pool_insert(const void* k_src, const void* v_src, const void* k_tgt, const void* v_tgt,
+                           kvc_shape shape, int64_t p_src, int64_t p_tgt, const kvc_rope* rope, const kvc_pool* arena,
+                           int32_t slot, int32_t oversample, int32_t power_iters, uint64_t seed, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  kvc_status s;
+  if ((s = check_shape(shape)) != KVC_OK) return s;
+  if ((s = check_rope(rope)) != KVC_OK) return s;
+  if (!arena) return fail(KVC_E_NULL, "arena is NULL");
+  if ((s = check_dtype(arena->dtype, "arena")) != KVC_OK) return s;
+  if (!k_src || !v_src || !k_tgt || !v_tgt) return fail(KVC_E_NULL, "k_src/v_src/k_tgt/v_tgt is NULL");
+  const void* fac[8] = {arena->baseA_k, arena->baseB_k, arena->baseA_v, arena->baseB_v,
+                        arena->deltaA_k, arena->deltaB_k, arena->deltaA_v, arena->deltaB_v};
+  for (int i = 0; i < 8; ++i)
+    if (!fac[i]) return fail(KVC_E_NULL, "arena factor array %d is NULL", i);
+  if (arena->slot_rows < shape.seq_len)
+    return fail(KVC_E_SHAPE, "arena slot_rows = %d is below seq_len = %d", arena->slot_rows, shape.seq_len);
+  if (arena->n_anchors < 1 || arena->n_anchors > KVC_MAX_ANCHORS)
+    return fail(KVC_E_SHAPE, "arena n_anchors must be in [1, %d]", KVC_MAX_ANCHORS);
+  if (slot < 0 || slot >= arena->n_anchors) return fail(KVC_E_PARAM, "slot %d outside [0, %d)", slot, arena->n_anchors);
+  const int D = D_of(shape), S = shape.seq_len, L = shape.n_layers;
+  const int rmax = std::max(arena->rank_base, arena->rank_delta);
+  if (arena->rank_base < 1 || arena->rank_delta < 1 || oversample < 0 || rmax + oversample > std::min(S, D) ||
+      rmax + oversample > 256)
+    return fail(KVC_E_SHAPE, "insert: need ranks >= 1 and rank + oversample <= min(seq_len, D, 256)");
+  if (S % 4 || D % 4) return fail(KVC_E_SHAPE, "insert: seq_len and D must be multiples of 4");
+  if (power_iters < 0 || power_iters > 16) return fail(KVC_E_PARAM, "insert: power_iters must be in [0, 16]");
+  const InsertWs w = insert_layout(shape, *arena, oversample);
+  if (!workspace || ws_bytes < w.total) return fail(KVC_E_WORKSPACE, "insert workspace: need %zu bytes", w.total);
+  if (!aligned16(workspace)) return fail(KVC_E_ALIGN, "workspace not 16-byte aligned");
+  char* ws = (char*)workspace;
+  float* z = (float*)(ws + w.z);
+  float* d = (float*)(ws + w.d);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t es = esize(arena->dtype);
+  const size_t V = arena->n_anchors, R = arena->slot_rows;
+  for (int side = 0; side < 2; ++side) {
+    const bool keys = side == 0;
+    if ((s = kvc_observed_delta(keys ? k_src : nullptr, keys ? nullptr : v_src, keys ? k_tgt : nullptr,
+                                keys ? nullptr : v_tgt, arena->dtype, shape, p_src, p_tgt, rope, keys ? z : nullptr,
+                                keys ? nullptr : z, keys ? d : nullptr, keys ? nullptr : d, stream)) != KVC_OK)
+      return s;
+    for (int which = 0; which < 2; ++which) {   // 0: base (source), 1: correction
+      const int r = which ? arena->rank_delta : arena->rank_base;
+      void* A = (void*)(which ? (keys ? arena->deltaA_k : arena->deltaA_v) : (keys ? arena->baseA_k : arena->baseA_v));
+      void* B = (void*)(which ? (keys ? arena->deltaB_k : arena->deltaB_v) : (keys ? arena->baseB_k : arena->baseB_v));
+      hipError_t e = svd_refresh(which ? d : z, L, S, D, r, ws + w.a, ws + w.b, arena->dtype == KVC_BF16,
+                                 (float*)(ws + w.sig), oversample, power_iters, seed * 4 + side * 2 + which,
+                                 ws + w.svd, w.total - w.svd, st);
+      if (e != hipSuccess) return hip_fail(e, "insert factorisation");
+      // A: layer l's rows go to [slot * slot_rows, + S) of the layer's block; B: anchor `slot`
+      e = hipMemcpy2DAsync((char*)A + (size_t)slot * R * r * es, V * R * r * es, ws + w.a, (size_t)S * r * es,
+                           (size_t)S * r * es, L, hipMemcpyDeviceToDevice, st);
+      if (e == hipSuccess)
+        e = hipMemcpy2DAsync((char*)B + (size_t)slot * r * D * es, V * r * D * es, ws + w.b, (size_t)r * D * es,
+                             (size_t)r * D * es, L, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "insert copy into the arena");
+    }
+  }
   return ok();
 }
 

@@ -65,6 +65,9 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
 
 hipError_t launch_align(const void* in, void* out, int in_bf16, int out_bf16, int64_t n_rows,
                         int n_heads, int head_dim, const RopeTab& tab, hipStream_t st);
+// out (fp32) = R(tt) tgt - R(ts) src per rotate-half pair (Eq. 12's observed correction)
+hipError_t launch_observed_delta(const void* tgt, const void* src, int bf16, float* out, int64_t n_rows,
+                                 int n_heads, int head_dim, const RopeTab& tt, const RopeTab& ts, hipStream_t st);
 
 struct ScoreArgs {
   const void* z[2];          // source K, V   [N_l][S][D]

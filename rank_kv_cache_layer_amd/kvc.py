@@ -27,7 +27,10 @@ STATUS = {0: "KVC_OK", 1: "KVC_E_NULL", 2: "KVC_E_SHAPE", 3: "KVC_E_DTYPE", 4: "
 EXPORTS = ["kvc_abi_version", "kvc_status_str", "kvc_last_error", "kvc_workspace_size",
            "kvc_align_rope", "kvc_match_anchors", "kvc_apply_lowrank_delta", "kvc_correct_hop",
            "kvc_correct_hops_batched", "kvc_svd_workspace_size", "kvc_anchor_refresh_svd",
-           "kvc_peak_copy", "kvc_peak_mfma_bf16", "kvc_peak_lds_read", "kvc_peak_valu"]
+           "kvc_peak_copy", "kvc_peak_mfma_bf16", "kvc_peak_lds_read", "kvc_peak_valu",
+           "kvc_observed_delta", "kvc_pool_state_init", "kvc_pool_record_hop", "kvc_pool_view",
+           "kvc_pool_insert_workspace_size", "kvc_pool_insert"]
+POOL_EVICT_WINDOW = 5
 
 
 class KvcError(RuntimeError):
@@ -50,7 +53,14 @@ class Pool(C.Structure):
                 ("capacity", C.c_int32), ("anchor_len", C.POINTER(C.c_int32)), ("dtype", C.c_int32),
                 ("baseA_k", C.c_void_p), ("baseB_k", C.c_void_p), ("baseA_v", C.c_void_p),
                 ("baseB_v", C.c_void_p), ("deltaA_k", C.c_void_p), ("deltaB_k", C.c_void_p),
-                ("deltaA_v", C.c_void_p), ("deltaB_v", C.c_void_p)]
+                ("deltaA_v", C.c_void_p), ("deltaB_v", C.c_void_p), ("slot_rows", C.c_int32),
+                ("pad_", C.c_int32), ("live", C.POINTER(C.c_uint8))]
+
+
+class PoolStateC(C.Structure):
+    _fields_ = [("capacity", C.c_int32), ("n_held", C.c_int32), ("clock", C.c_int64),
+                ("stamp", C.c_int64 * MAX_ANCHORS), ("uses", C.c_int64 * MAX_ANCHORS),
+                ("len", C.c_int32 * MAX_ANCHORS), ("consumer", C.c_int32 * MAX_ANCHORS)]
 
 
 TRACE_MAX = 64
@@ -123,6 +133,22 @@ def lib(path: Optional[str] = None):
     L.kvc_anchor_refresh_svd.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                          C.c_void_p, C.c_int, C.c_void_p, C.c_int32, C.c_int32, C.c_uint64,
                                          C.c_void_p, C.c_size_t, C.c_void_p]
+    L.kvc_observed_delta.restype = C.c_int
+    L.kvc_observed_delta.argtypes = [C.c_void_p] * 4 + [C.c_int, Shape, C.c_int64, C.c_int64, C.POINTER(Rope)] + \
+        [C.c_void_p] * 5
+    L.kvc_pool_state_init.restype = C.c_int
+    L.kvc_pool_state_init.argtypes = [C.POINTER(PoolStateC), C.c_int32]
+    L.kvc_pool_record_hop.restype = C.c_int
+    L.kvc_pool_record_hop.argtypes = [C.POINTER(PoolStateC), C.c_int32, C.c_int32, C.c_int32,
+                                      C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+    L.kvc_pool_view.restype = C.c_int32
+    L.kvc_pool_view.argtypes = [C.POINTER(PoolStateC), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_uint8)]
+    L.kvc_pool_insert_workspace_size.restype = C.c_size_t
+    L.kvc_pool_insert_workspace_size.argtypes = [Shape, C.POINTER(Pool), C.c_int32]
+    L.kvc_pool_insert.restype = C.c_int
+    L.kvc_pool_insert.argtypes = [C.c_void_p] * 4 + [Shape, C.c_int64, C.c_int64, C.POINTER(Rope), C.POINTER(Pool),
+                                                     C.c_int32, C.c_int32, C.c_int32, C.c_uint64, C.c_void_p,
+                                                     C.c_size_t, C.c_void_p]
     L.kvc_peak_copy.restype = C.c_int
     L.kvc_peak_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     for f in (L.kvc_peak_mfma_bf16, L.kvc_peak_lds_read, L.kvc_peak_valu):
@@ -181,15 +207,21 @@ class PoolTensors:
     deltaA_v: torch.Tensor
     deltaB_v: torch.Tensor
     capacity: int = 0
+    slot_rows: int = 0                      # > 0: fixed-capacity arena slots
+    live: Optional[Sequence[int]] = None    # per-anchor mask, None = all live
 
     def c(self):
         n = len(self.anchor_len)
         lens = (C.c_int32 * max(n, 1))(*self.anchor_len)
+        live = None
+        if self.live is not None:
+            live = (C.c_uint8 * max(n, 1))(*[1 if x else 0 for x in self.live])
         p = Pool(n, self.rank_base, self.rank_delta, self.capacity, C.cast(lens, C.POINTER(C.c_int32)),
                  _dt(self.baseA_k), _ptr(self.baseA_k), _ptr(self.baseB_k), _ptr(self.baseA_v),
                  _ptr(self.baseB_v), _ptr(self.deltaA_k), _ptr(self.deltaB_k), _ptr(self.deltaA_v),
-                 _ptr(self.deltaB_v))
-        return p, lens
+                 _ptr(self.deltaB_v), self.slot_rows, 0,
+                 C.cast(live, C.POINTER(C.c_uint8)) if live is not None else None)
+        return p, (lens, live)
 
 
 def params_of(tau=0.3, temp_gate=1.0, temp_weight=0.1, gate_len=0, mode=SCORE_PAGES, options=0,
@@ -413,3 +445,55 @@ def pool_from(data, device) -> PoolTensors:
                        baseA_k=t(data.baseA_k), baseB_k=t(data.baseB_k), baseA_v=t(data.baseA_v),
                        baseB_v=t(data.baseB_v), deltaA_k=t(data.deltaA_k), deltaB_k=t(data.deltaB_k),
                        deltaA_v=t(data.deltaA_v), deltaB_v=t(data.deltaB_v), capacity=sp.capacity)
+
+
+# ------------------------------------------------------------------ pool updates (App. A.3)
+def observed_delta(k_src, v_src, k_tgt, v_tgt, shape: Shape, p_src: int, p_tgt: int, k_base=None, v_base=None,
+                   k_delta=None, v_delta=None, theta=10000.0, stream=None):
+    """Eq. 12 in fp32 (kvc_observed_delta): canonical source and observed correction per side."""
+    rope, _keep = rope_of(theta)
+    t = next(x for x in (k_src, v_src, k_tgt, v_tgt) if x is not None)
+    _check(lib().kvc_observed_delta(_ptr(k_src), _ptr(v_src), _ptr(k_tgt), _ptr(v_tgt), _dt(t), shape, p_src, p_tgt,
+                                    C.byref(rope), _ptr(k_base), _ptr(v_base), _ptr(k_delta), _ptr(v_delta),
+                                    _stream(stream)))
+
+
+class PoolState:
+    """Host bookkeeping of one slot's pool (kvc_pool_state): insert on fallback, LFU eviction."""
+
+    def __init__(self, capacity: int):
+        self.c = PoolStateC()
+        _check(lib().kvc_pool_state_init(C.byref(self.c), capacity))
+
+    def record_hop(self, consumer: int, seg_len: int, flagged: bool):
+        slot, ev = C.c_int32(), C.c_int32()
+        _check(lib().kvc_pool_record_hop(C.byref(self.c), consumer, seg_len, 1 if flagged else 0, C.byref(slot),
+                                         C.byref(ev)))
+        return slot.value, ev.value
+
+    def view(self, consumer: int):
+        n = self.c.capacity
+        lens = (C.c_int32 * MAX_ANCHORS)()
+        live = (C.c_uint8 * MAX_ANCHORS)()
+        k = lib().kvc_pool_view(C.byref(self.c), consumer, lens, live)
+        if k < 0:
+            raise KvcError(8, "pool view: bad arguments")
+        return list(lens[:n]), [int(x) for x in live[:n]]
+
+
+def pool_insert_workspace(shape: Shape, arena: PoolTensors, oversample: int) -> int:
+    p, _keep = arena.c()
+    return int(lib().kvc_pool_insert_workspace_size(shape, C.byref(p), oversample))
+
+
+def pool_insert(k_src, v_src, k_tgt, v_tgt, shape: Shape, p_src: int, p_tgt: int, arena: PoolTensors, slot: int,
+                oversample: int = 16, power_iters: int = 2, seed: int = 0, theta=10000.0, workspace=None,
+                stream=None):
+    """Fills arena slot `slot` from a dense fallback (kvc_pool_insert)."""
+    rope, _k1 = rope_of(theta)
+    p, _k2 = arena.c()
+    need = int(lib().kvc_pool_insert_workspace_size(shape, C.byref(p), oversample))
+    ws = _ws(need, k_src.device, workspace)
+    _check(lib().kvc_pool_insert(_ptr(k_src), _ptr(v_src), _ptr(k_tgt), _ptr(v_tgt), shape, p_src, p_tgt,
+                                 C.byref(rope), C.byref(p), slot, oversample, power_iters, seed, _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)))

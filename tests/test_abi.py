@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for name in header_functions():
         assert hasattr(L, name), name
     assert sorted(header_functions()) == sorted(kvc.EXPORTS)
-    assert L.kvc_abi_version() == 1
+    assert L.kvc_abi_version() == 2
 
 
 def test_status_strings():
