@@ -17,8 +17,29 @@
 namespace kvc {
 namespace {
 
-// out (fp32) = R(tt) tgt - R(ts) src per rotate-half pair, 8 pairs per thread (or 1 when
-// head_dim / 2 is not a multiple of 8); an inactive table is the identity (values).
+// 8 consecutive elements as fp32, one 16-byte (bf16) or two 16-byte (fp32) loads
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// out (fp32) = R(tt) tgt - R(ts) src per rotate-half pair; an inactive table is the identity
+// (values).  VEC = 8: each thread owns pairs c0..c0+7 of one head of one row and moves them
+// with 16-byte accesses (head_dim / 2 a multiple of 8); VEC = 1: one pair per thread.
 template <typename T, int VEC>
 __global__ void __launch_bounds__(256) observed_delta(const T* __restrict__ tgt, const T* __restrict__ src,
                                                       float* __restrict__ out, int64_t n_units, int n_heads,
@@ -40,15 +61,31 @@ __global__ void __launch_bounds__(256) observed_delta(const T* __restrict__ tgt,
     const int head = rem / per_head;
     const int c0 = (rem - head * per_head) * VEC;
     const int64_t base = row * D + (int64_t)head * head_dim + c0;
+    float xt[VEC], yt[VEC], xs[VEC], ys[VEC];
+    if constexpr (VEC == 8) {
+      load8(tgt + base, xt);
+      load8(tgt + base + h, yt);
+      load8(src + base, xs);
+      load8(src + base + h, ys);
+    } else {
+      xt[0] = ldf(tgt, base); yt[0] = ldf(tgt, base + h);
+      xs[0] = ldf(src, base); ys[0] = ldf(src, base + h);
+    }
+    float ox[VEC], oy[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      const float xt = ldf(tgt, base + i), yt = ldf(tgt, base + h + i);
-      const float xs = ldf(src, base + i), ys = ldf(src, base + h + i);
-      float at = xt, bt = yt, as = xs, bs = ys;
-      if (tt.active) rot_pair(xt, yt, ct[c0 + i], st_[c0 + i], at, bt);
-      if (ts.active) rot_pair(xs, ys, cs[c0 + i], ss[c0 + i], as, bs);
-      out[base + i] = at - as;
-      out[base + h + i] = bt - bs;
+      float at = xt[i], bt = yt[i], as = xs[i], bs = ys[i];
+      if (tt.active) rot_pair(xt[i], yt[i], ct[c0 + i], st_[c0 + i], at, bt);
+      if (ts.active) rot_pair(xs[i], ys[i], cs[c0 + i], ss[c0 + i], as, bs);
+      ox[i] = at - as;
+      oy[i] = bt - bs;
+    }
+    if constexpr (VEC == 8) {
+      store8(out + base, ox);
+      store8(out + base + h, oy);
+    } else {
+      out[base] = ox[0];
+      out[base + h] = oy[0];
     }
   }
 }
