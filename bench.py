@@ -238,6 +238,42 @@ def measure_pool_insert(kvc, torch, L=32, S=4096, H=8, hd=128, r=32, V=20, p=16,
     return out
 
 
+def measure_pf_delta(kvc, torch, L=32, S=32768, H=8, hd=128, r=8, reps=10):
+    """App. A.2: a recurring relation's correction, profiled once and stored at rank 8, reused
+    with weight 1 and re-alignment and no matching (kvc_apply_lowrank_delta with one anchor),
+    at the 32K-token 8B shape.  HBM-bound: source and output of K and V, the rank-8 factors and
+    the given weights.  Inputs generated on the device, resident before timing."""
+    D = H * hd
+    g = torch.Generator(device="cuda").manual_seed(9)
+    k, v = (torch.randn((L, S, D), device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+    mk = lambda *sh: (torch.randn(sh, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+    pool = kvc.PoolTensors([S], 16, r, mk(L, S, 16), mk(L, 1, 16, D), mk(L, S, 16), mk(L, 1, 16, D),
+                           mk(L, S, r), mk(L, 1, r, D), mk(L, S, r), mk(L, 1, r, D))
+    w = torch.ones((L, S, 1), dtype=torch.float32, device="cuda")
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    shp = kvc.shape_of(L, S, H, hd)
+    ws = torch.empty((max(kvc.workspace_size(kvc.CALL_APPLY, shp, pool), 16),), dtype=torch.uint8, device="cuda")
+    run = lambda tr=None: kvc.apply_lowrank_delta(k, v, ko, vo, shp, 512, 812, pool, w, w, S, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * L * S * D * 2 * 2 + 2 * L * (S * r + r * D) * 2 + 2 * L * S * 4
+    out = {"workload": f"rank-{r} correction with weight 1 (no matching), {L} layers x {S} tokens x {H}x{hd} bf16",
+           "ms": round(ms, 4), "tokens_per_s": round(S / (ms / 1e3), 1), "bound": "hbm",
+           "algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms / 1e3) / 1e9, 1), "peak_GBps": 8000.0,
+           "frac": round(nbytes / (ms / 1e3) / 8e12, 4)}
+    del k, v, ko, vo, pool, w, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_chain(kvc, torch, W, n_requests=2, n_hops=3, steps=3):
     """Concurrent chains (A0 -> A1 -> A2 -> A3) at the 8B shape, 8192 tokens per request,
     pools of 10-20 anchors at rank 16 or 32, through kvc_correct_hops_batched (one call for all
@@ -408,7 +444,7 @@ def main():
                   "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
         log(f"[bench] second mode {second['mode']}: {ms2:.3f} ms/hop")
 
-    refresh = chain = pool_ins = None
+    refresh = chain = pool_ins = pf = None
     if not args.no_extra:
         log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
         refresh = measure_refresh(kvc, torch, oracle=not args.no_cpu_baseline)
@@ -418,6 +454,9 @@ def main():
         log("[bench] chained batch (2 requests x 3 hops, 8192 tokens) ...")
         chain = measure_chain(kvc, torch, W)
         log(f"[bench] chain: {chain['ms']} ms, {chain['tokens_per_s']} tokens/s")
+        log("[bench] preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens) ...")
+        pf = measure_pf_delta(kvc, torch)
+        log(f"[bench] pf delta: {pf['ms']} ms, {pf['achieved_GBps']} GB/s")
         log("[bench] pool update after a fallback (32 layers x 4096 tokens, rank 32) ...")
         pool_ins = measure_pool_insert(kvc, torch, oracle=not args.no_cpu_baseline)
         log(f"[bench] pool insert: {pool_ins['ms']} ms; Eq. 12 kernels {pool_ins['eq12_kernels']}")
@@ -438,7 +477,7 @@ def main():
                    "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
         "roofline": dominant, "cpu_baseline": cpu,
         "hop": hop, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
-        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins,
+        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf,
         "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
     }
     print(json.dumps(out), flush=True)

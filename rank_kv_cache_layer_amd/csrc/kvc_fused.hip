@@ -555,7 +555,7 @@ __global__ void __launch_bounds__(256) pack_b(PackArgs p) {
   __shared__ float cs[kFusedHalf], sn[kFusedHalf];
   for (int i = threadIdx.x; i < p.head_dim / 2; i += blockDim.x) { cs[i] = p.tab.cs[i]; sn[i] = p.tab.sn[i]; }
   __syncthreads();
-  const int RK = p.r >> 4, NCB = p.D >> 5, D = p.D, hd = p.head_dim, h = hd >> 1;
+  const int RK = (p.r + 15) >> 4, NCB = p.D >> 5, D = p.D, hd = p.head_dim, h = hd >> 1;   // ranks padded to 16
   const int64_t per_mat = (int64_t)NCB * RK * 64;
   const int64_t per_arr = per_mat * p.n_layers * p.n_anchors;
   const int64_t total = per_arr * p.n_arrays;
@@ -576,10 +576,11 @@ __global__ void __launch_bounds__(256) pack_b(PackArgs p) {
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = bf2f(B[(int64_t)(k0 + i) * D + d]);
+      const bool in = k0 + i < p.r;   // rows past the rank pack as zeros
+      const float x = in ? bf2f(B[(int64_t)(k0 + i) * D + d]) : 0.f;
       float val = x;
       if (rot) {
-        const float y = bf2f(B[(int64_t)(k0 + i) * D + partner]);
+        const float y = in ? bf2f(B[(int64_t)(k0 + i) * D + partner]) : 0.f;
         float lo, up;
         if (c < h) {
           rot_pair(x, y, cs[c], sn[c], lo, up);
@@ -630,7 +631,7 @@ hipError_t fused_dispatch(const FusedArgs& a, int mode, hipStream_t st) {
 hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const int* negate,
                          const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors, int r, int D,
                          int head_dim, hipStream_t st) {
-  if (n_arrays < 1 || n_arrays > 4 || (r & 15) || (D & 31) || n_anchors < 1 || head_dim > 2 * kFusedHalf)
+  if (n_arrays < 1 || n_arrays > 4 || r < 1 || (D & 31) || n_anchors < 1 || head_dim > 2 * kFusedHalf)
     return hipErrorInvalidValue;
   PackArgs a;
   memset(&a, 0, sizeof a);
@@ -642,7 +643,7 @@ hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const
     if (tabs[i]) a.tab = *tabs[i];   // at most one distinct rotation per launch
   }
   a.n_arrays = n_arrays; a.n_layers = n_layers; a.n_anchors = n_anchors; a.r = r; a.D = D; a.head_dim = head_dim;
-  const int64_t units = (int64_t)n_arrays * n_layers * n_anchors * (D / 32) * (r / 16) * 64;
+  const int64_t units = (int64_t)n_arrays * n_layers * n_anchors * (D / 32) * ((r + 15) / 16) * 64;
   int64_t blocks = (units + 255) / 256;
   if (blocks > 1 << 20) blocks = 1 << 20;
   pack_b<<<(unsigned)blocks, 256, 0, st>>>(a);

@@ -210,7 +210,8 @@ bool cos_mfma_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
 }
 
 // The two-pass bf16 path: 128-token x 256-channel work-groups (D a multiple of 256), ranks
-// 16/32 (larger ranks would not fit the two-per-CU register budget), within the LDS budget.
+// 16/32 (larger ranks would not fit the register budget; the apply also takes rank 8, padded
+// to the MFMA's 16 on chip), within the LDS budget.
 constexpr size_t kLdsBudget = 160 * 1024;
 bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, bool pages_scores, bool apply) {
   if (p.dtype != KVC_BF16 || (prm.options & 3)) return false;
@@ -221,7 +222,7 @@ bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, boo
     if (split_score_lds(p.rank_base) + 8 * 1024 > kLdsBudget) return false;
   }
   if (apply) {
-    if (p.rank_delta != 16 && p.rank_delta != 32) return false;
+    if (p.rank_delta != 8 && p.rank_delta != 16 && p.rank_delta != 32) return false;
     if (split_apply_lds(p.rank_delta) + 2 * 1024 > kLdsBudget) return false;
   }
   return true;
@@ -242,6 +243,8 @@ struct Plan {
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+// packed B operands hold ranks in slices of 16 (rows past the rank are zero)
+size_t rpad16(int r) { return (size_t)((r + 15) & ~15); }
 
 Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* prm, const Sets& s) {
   Plan pl;
@@ -297,12 +300,12 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
     off += up256(sizeof(double) * 3 * (size_t)(1 + L) * N);
     if (pl.fused_match || pl.split_match) {
       pl.off_pack_base = off;
-      off += up256(2 * 2 * (size_t)L * N * D * p.rank_base);
+      off += up256(2 * 2 * (size_t)L * N * D * rpad16(p.rank_base));
     }
   }
   if (do_apply && (pl.fused_apply || pl.split_apply)) {
     pl.off_pack_delta = off;
-    off += up256(2 * 2 * (size_t)L * N * D * p.rank_delta);
+    off += up256(2 * 2 * (size_t)L * N * D * rpad16(p.rank_delta));
   }
   if (pl.split_match || pl.split_apply) {
     pl.off_wa = off;
@@ -362,7 +365,7 @@ kvc_status fused_tab(FusedTab& ft, int64_t dp, int head_dim, const kvc_rope* rop
 kvc_status pack_pair(const void* bk, const void* bv, uint16_t* dst, int r, int negate, const FusedTab* key_tab,
                      const kvc_shape& sh, const kvc_pool& p, Tracer& tr, int trace_id, hipStream_t st) {
   if (p.n_anchors == 0) return KVC_OK;
-  const size_t per = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * r;
+  const size_t per = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(r);
   const uint16_t* src[2] = {(const uint16_t*)bk, (const uint16_t*)bv};
   uint16_t* dsts[2] = {dst, dst + per};
   const int neg[2] = {negate, negate};
@@ -450,7 +453,7 @@ kvc_status split_apply_fields(SplitArgs& f, void* k_out, void* v_out, const kvc_
   uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
   if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
     return r;
-  const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_delta;
+  const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(p.rank_delta);
   f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
   f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
   f.Bd[0] = pd; f.Bd[1] = pd + per_d;
@@ -589,7 +592,7 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
       return r;
     SplitArgs f;
     if ((r = split_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
-    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_base;
+    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(p.rank_base);
     f.Ab[0] = (const uint16_t*)p.baseA_k; f.Ab[1] = (const uint16_t*)p.baseA_v;
     f.Bb[0] = pb; f.Bb[1] = pb + per_b;
     f.mpart = reinterpret_cast<float*>(ws + pl.off_mpart);
@@ -617,7 +620,7 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
       return r;
     FusedArgs f;
     if ((r = fused_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
-    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_base;
+    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(p.rank_base);
     f.Ab[0] = (const uint16_t*)p.baseA_k; f.Ab[1] = (const uint16_t*)p.baseA_v;
     f.Bb[0] = pb; f.Bb[1] = pb + per_b;
     f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
@@ -628,7 +631,7 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
       uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
       if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
         return r;
-      const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_delta;
+      const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(p.rank_delta);
       f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
       f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
       f.Bd[0] = pd; f.Bd[1] = pd + per_d;
@@ -665,7 +668,7 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
     uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
     if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
       return r;
-    const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * p.rank_delta;
+    const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(p.rank_delta);
     f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
     f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
     f.Bd[0] = pd; f.Bd[1] = pd + per_d;
@@ -885,7 +888,7 @@ kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k
     if ((s = pack_pair(pool->deltaB_k, pool->deltaB_v, pd, pool->rank_delta, 0, &tgt, shape, *pool, tr,
                        KVC_K_PACK_DELTA, st)) != KVC_OK)
       return s;
-    const size_t per_d = (size_t)shape.n_layers * pool->n_anchors * D_of(shape) * pool->rank_delta;
+    const size_t per_d = (size_t)shape.n_layers * pool->n_anchors * D_of(shape) * rpad16(pool->rank_delta);
     f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
     f.Ad[0] = (const uint16_t*)pool->deltaA_k; f.Ad[1] = (const uint16_t*)pool->deltaA_v;
     f.Bd[0] = pd; f.Bd[1] = pd + per_d;

@@ -359,10 +359,12 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // Slot layout for rank 16 RK, TT tokens, NW waves: A rows (TT x R bf16, 16-byte units
 // swizzled so the fragment reads of 16 consecutive rows hit distinct banks), the B slice
-// (kNCBW x RK packed 1 KiB chunks), the TT token weights (fp32, apply only).
-template <int RK, int TT, int NW, bool W>
+// (kNCBW x RK packed 1 KiB chunks), the TT token weights (fp32, apply only).  RA = the rank
+// of the A rows in memory (<= R): the units of an LDS row past it are filled with zeros.
+template <int RK, int TT, int NW, bool W, int RA = RK * 16>
 struct Ring {
   static constexpr int R = RK * 16;
+  static_assert(RA % 8 == 0 && RA <= R, "A row rank");
   static constexpr int U = R / 8;                       // 16-byte units per A row
   static constexpr int A_BYTES = TT * R * 2;
   static constexpr int B_BYTES = kNCBW * RK * 1024;
@@ -388,7 +390,9 @@ struct Ring {
       const int u = (wave * A_PER_WAVE + i) * 64 + lane;     // LDS unit this lane fills
       const int row = u / U, cpos = u % U;
       const int c = cpos ^ ((row / (16 / U)) & (U - 1));     // global unit stored there
-      dma16(Ar, slot + (wave * A_PER_WAVE + i) * 1024, (uint32_t)(((t0 + row) * R + c * 8) * 2));
+      // units past the stored rank read out of range: the transfer writes zeros there
+      const uint32_t voff = c * 8 < RA ? (uint32_t)(((t0 + row) * RA + c * 8) * 2) : 0x80000000u;
+      dma16(Ar, slot + (wave * A_PER_WAVE + i) * 1024, voff);
     }
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) {
@@ -579,11 +583,10 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
 // Three work-groups share a CU (at most 168 VGPRs per lane, a two-slot ring of ~49 KB): the
 // extra waves cover the tile's load and store phases and the operand waits, which pays more
 // than a third slot or operands held in registers across a step.
-template <int HD, int RKD>
+template <int HD, int RKD, int RA>
 __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
-  using RG = Ring<RKD, kST, kNW, true>;
-  constexpr int R = RKD * 16;
+  using RG = Ring<RKD, kST, kNW, true, RA>;
   extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
   __shared__ float tab[2][kFusedHalf];
 
@@ -614,7 +617,7 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
     const int a = lane_get(sl.a, js);
     const int lim = live ? lane_get(sl.lim, js) : 0;
     RG::fetch(ring0 + (uint32_t)(j % kApplySlots) * RG::SLOT,
-              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
+              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * RA, (uint32_t)lim * RA * 2),
               make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
               t0, wv, lane);
   };
@@ -688,8 +691,9 @@ template <int HD>
 hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
   const size_t lds = split_apply_lds(a.r_d);
   switch (a.r_d) {
-    case 16: return go(split_apply<HD, 1>, a, kApplyTile, kApplyThreads, lds, st);
-    case 32: return go(split_apply<HD, 2>, a, kApplyTile, kApplyThreads, lds, st);
+    case 8: return go(split_apply<HD, 1, 8>, a, kApplyTile, kApplyThreads, lds, st);
+    case 16: return go(split_apply<HD, 1, 16>, a, kApplyTile, kApplyThreads, lds, st);
+    case 32: return go(split_apply<HD, 2, 32>, a, kApplyTile, kApplyThreads, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -705,7 +709,8 @@ size_t split_score_lds(int r_b) {
 }
 
 size_t split_apply_lds(int r_d) {
-  const size_t slot = (size_t)kApplyTile * r_d * 2 + (size_t)kNCBW * (r_d / 16) * 1024 + (size_t)kApplyTile * 4;
+  const int rp = (r_d + 15) & ~15;   // on chip the rank is padded to 16
+  const size_t slot = (size_t)kApplyTile * rp * 2 + (size_t)kNCBW * (rp / 16) * 1024 + (size_t)kApplyTile * 4;
   return std::max((size_t)kApplySlots * slot, sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
 }
 

@@ -97,6 +97,34 @@ def test_ranks_bf16(rank):
     _check_hop(sp, label=f"rank{rank}")
 
 
+def test_rank8_delta_two_pass_bf16():
+    # rank-8 corrections on the two-pass apply (padded to the MFMA's 16 on chip)
+    sp = W.llama8b_hop(n_layers=2, seq_len=300, n_anchors=6, rank_base=16, rank_delta=8, n_kv_heads=2)
+    _check_hop(sp, label="rank-delta-8")
+
+
+def test_preconstructed_rank8_delta_weight_one():
+    # App. A.2: a recurring relation's correction, profiled once at rank 8, reused with weight 1
+    # and re-alignment and no matching: K_out = R(s) K + R(p_tgt) A B, V_out = V + A B
+    sp = W.llama8b_hop(n_layers=2, seq_len=520, n_kv_heads=2, n_anchors=1, rank_base=16, rank_delta=8)
+    print(f"[parity] pf-delta L=2 S=520 D={sp.d_model} r=8", flush=True)
+    data = make(sp)
+    k, v = data.k_src.to(DEV), data.v_src.to(DEV)
+    pool = kvc.pool_from(data, DEV)
+    w = torch.ones((2, 520, 1), dtype=torch.float32, device=DEV)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    kvc.apply_lowrank_delta(k, v, ko, vo, shape(sp), sp.p_src, sp.p_tgt, pool, w, w, 520)
+    torch.cuda.synchronize()
+    for l in range(2):
+        A, B = O.layer_factors(data, l, "k", "delta", [0])
+        Av, Bv = O.layer_factors(data, l, "v", "delta", [0])
+        exp_k = O.rope(O._np(data.k_src[l]), sp.shift, 128) + O.rope(A[0] @ B[0], sp.p_tgt, 128)
+        exp_v = O._np(data.v_src[l]) + Av[0] @ Bv[0]
+        gk, gv = ko[l].double().cpu().numpy(), vo[l].double().cpu().numpy()
+        assert np.max(np.abs(gk - exp_k)) <= 2.0 ** -7 * np.max(np.abs(exp_k))
+        assert np.max(np.abs(gv - exp_v)) <= 2.0 ** -7 * np.max(np.abs(exp_v))
+
+
 def test_head_dim_64_bf16():
     sp = W.llama8b_hop(n_layers=2, seq_len=200, n_kv_heads=4, head_dim=64, n_anchors=5)
     _check_hop(sp, label="hd64")
