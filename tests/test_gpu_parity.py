@@ -273,3 +273,33 @@ def test_batched_chain_matches_sequential_oracle():
             # the oracle chains its own materialised (bf16-rounded) output into the next hop
             src_k = torch.from_numpy(ref["k_out"]).to(torch.bfloat16)
             src_v = torch.from_numpy(ref["v_out"]).to(torch.bfloat16)
+
+
+def test_fan_in_ragged_pools_in_one_batched_call():
+    # App. B.1 "Workflow Structures": at fan-in each incoming segment keeps its own source cache
+    # and is corrected separately; App. A.3 "Variable Segment Lengths": ragged anchors, gate set
+    # (length >= k) and correction set (covering the longest covered prefix) differ
+    S = 256
+    segs = [dict(anchor_len=[S, S, S, S], p_src=40, p_tgt=700, seed=21),
+            dict(anchor_len=[S, 180, S, 90, S], p_src=900, p_tgt=956, seed=22),
+            dict(anchor_len=[200, 160, 200], p_src=3, p_tgt=1212, seed=23)]
+    specs = [W.llama8b_hop(n_layers=2, seq_len=S, n_kv_heads=2, n_anchors=len(g["anchor_len"]), **g) for g in segs]
+    datas = [make(sp) for sp in specs]
+    print(f"[parity] fan-in: {len(specs)} segments, pools {[g['anchor_len'] for g in segs]}", flush=True)
+    hl = []
+    for sp, d in zip(specs, datas):
+        k, v = d.k_src.to(DEV), d.v_src.to(DEV)
+        hl.append(kvc.Hop(k, v, torch.empty_like(k), torch.empty_like(v), sp.p_src, sp.p_tgt, -1,
+                          kvc.pool_from(d, DEV), kvc.alloc_match(sp.n_layers, S, sp.n_anchors, DEV)))
+    kvc.correct_hops_batched(hl, shape(specs[0]), params(specs[0]))
+    torch.cuda.synchronize()
+    for i, (sp, d, h) in enumerate(zip(specs, datas, hl)):
+        ref = O.correct_hop(d)
+        gpu = dict(k_out=h.k_out.double().cpu().numpy(), v_out=h.v_out.double().cpu().numpy())
+        assert_outputs_close(gpu, ref, sp.dtype, f"fan-in segment {i}")
+        assert np.array_equal(h.out.flags.cpu().numpy(), ref["flags"]), i
+    # the third segment: no anchor covers it, so its tail keeps the re-aligned source and the
+    # gate (no anchor of length >= k) falls back
+    assert O.correct_hop(datas[2])["s_cov"] == 200
+    assert hl[2].out.flags[0].item() & O.FLAG_FEW_ANCHORS
+
