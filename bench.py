@@ -274,6 +274,25 @@ def measure_pf_delta(kvc, torch, L=32, S=32768, H=8, hd=128, r=8, reps=10):
     return out
 
 
+def measure_study(torch, L=8, S=4096, D=1024, rank=32):
+    """Sec. 3.2 / Fig. 3(b) analogue on synthetic exact caches (each agent adds a rank-24
+    deviation with 1% full-rank noise to the trajectory so far): per-agent normalised error of
+    chained (Eq. 6, exact first agent) and reference-based (Eq. 4) correction at rank 32, run with
+    the library's factorisation and apply."""
+    from rank_kv_cache_layer_amd import study
+    from rank_kv_cache_layer_amd import workload as W
+    ref, agents = W.chain_study_caches(n_layers=L, seq_len=S, d=D, device="cuda")
+    t0 = time.perf_counter()
+    res = study.chain_vs_reference(ref, agents, rank)
+    dt = time.perf_counter() - t0
+    del ref, agents
+    torch.cuda.empty_cache()
+    return {"workload": f"4 agents A0 -> A3, {L} layers x {S} x {D} fp32, per-agent deviation rank 24 + 1% noise, "
+                        f"correction rank {rank}",
+            "error_chained": [round(x, 5) for x in res["chained"]],
+            "error_non_chained": [round(x, 5) for x in res["non_chained"]], "wall_s": round(dt, 3)}
+
+
 def measure_chain(kvc, torch, W, n_requests=2, n_hops=3, steps=3):
     """Concurrent chains (A0 -> A1 -> A2 -> A3) at the 8B shape, 8192 tokens per request,
     pools of 10-20 anchors at rank 16 or 32, through kvc_correct_hops_batched (one call for all
@@ -444,7 +463,7 @@ def main():
                   "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
         log(f"[bench] second mode {second['mode']}: {ms2:.3f} ms/hop")
 
-    refresh = chain = pool_ins = pf = None
+    refresh = chain = pool_ins = pf = study_out = None
     if not args.no_extra:
         log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
         refresh = measure_refresh(kvc, torch, oracle=not args.no_cpu_baseline)
@@ -457,6 +476,9 @@ def main():
         log("[bench] preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens) ...")
         pf = measure_pf_delta(kvc, torch)
         log(f"[bench] pf delta: {pf['ms']} ms, {pf['achieved_GBps']} GB/s")
+        log("[bench] chained vs non-chained correction error along A0 -> A3 (8 layers x 4096 x 1024) ...")
+        study_out = measure_study(torch)
+        log(f"[bench] study: {study_out}")
         log("[bench] pool update after a fallback (32 layers x 4096 tokens, rank 32) ...")
         pool_ins = measure_pool_insert(kvc, torch, oracle=not args.no_cpu_baseline)
         log(f"[bench] pool insert: {pool_ins['ms']} ms; Eq. 12 kernels {pool_ins['eq12_kernels']}")
@@ -477,7 +499,7 @@ def main():
                    "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
         "roofline": dominant, "cpu_baseline": cpu,
         "hop": hop, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
-        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf,
+        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf, "chain_study": study_out,
         "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
     }
     print(json.dumps(out), flush=True)

@@ -362,3 +362,25 @@ def decaying_matrices(n_mats: int, rows: int, cols: int, seed: int = 5, power: f
 
 def singular_values(n: int, power: float = 1.5) -> np.ndarray:
     return np.arange(1, n + 1, dtype=np.float64) ** (-power)
+
+
+def chain_study_caches(n_layers: int = 2, seq_len: int = 256, d: int = 256, n_agents: int = 4,
+                       hop_rank: int = 24, hop_rms: float = 0.1, noise: float = 0.01, seed: int = 6,
+                       device: str = "cpu"):
+    """Exact caches of one side of a segment along A0 -> A1 -> ... (synthetic stand-in for the
+    caches of Fig. 3(b)): a context-free reference C_ref, and C_k = C_ref + sum_{m <= k} E_m where
+    each agent adds its own deviation E_m (rank hop_rank, rms hop_rms x rms(C_ref), plus a full
+    rank component of rms noise x rms(E_m)).  Returns (C_ref, [C_0 .. C_{n-1}]) as fp32 tensors
+    [n_layers][seq_len][d] on `device`."""
+    rng = _rng(seed, _T_MISC, 77)
+    ref = rng.standard_normal((n_layers, seq_len, d))
+    caches, acc = [], ref.copy()
+    for _ in range(n_agents):
+        u = rng.standard_normal((n_layers, seq_len, hop_rank))
+        w = np.stack([_orthonormal_rows(rng, hop_rank, d) for _ in range(n_layers)])
+        e = np.einsum("lsr,lrd->lsd", u, w) * (hop_rms * np.sqrt(d / hop_rank))
+        e += rng.standard_normal(e.shape) * noise * hop_rms
+        acc = acc + e
+        caches.append(acc.copy())
+    t = lambda x: torch.from_numpy(x).float().to(device)
+    return t(ref), [t(c) for c in caches]
