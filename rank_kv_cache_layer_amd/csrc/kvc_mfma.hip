@@ -38,13 +38,14 @@ template <int HD> __device__ __forceinline__ int rot_index(int b, int row) { ret
 
 // ---------------------------------------------------------- COS_R scoring (MFMA)
 // Work-group = 64 tokens of one (layer, side), 4 waves.  The canonical source tile is staged
-// once in LDS as bf16; each wave takes whole anchors and contracts P = B_a Z^T over D with
-// B read in its stored [r][D] layout, then forms per-token cosines with A_a.
-template <int HD, int RB>
+// once in LDS as bf16; each wave takes ANCH anchors per pass and contracts P = B_a Z^T over D
+// with B read in its stored [r][D] layout, then forms per-token cosines with A_a.  The staged
+// tile fills the LDS of a CU, so one wave runs per SIMD and may hold up to 512 VGPRs: more
+// anchors per pass share each source fragment read and give the matrix core independent work.
+template <int HD, int RB, int ANCH>
 __global__ void __launch_bounds__(256) score_cos_mfma(ScoreArgs p) {
   extern __shared__ uint16_t zs[];            // [64][D + 8]
   __shared__ float cs_s[64], sn_s[64];
-  constexpr int ANCH = RB == 1 ? 2 : 1;       // anchors per pass per wave
   const int64_t lb = logical_block();
   const int tile = (int)(lb % p.n_tiles);
   const int layer = (int)((lb / p.n_tiles) % p.n_layers);
@@ -197,12 +198,29 @@ hipError_t allow_lds(K kernel, size_t bytes) {
     kern<<<grid, block, shmem, st>>>(__VA_ARGS__);                     \
   } while (0)
 
+// rank 32: anchors per wave and pass among 2, 3, 5, whichever needs the fewest anchor-passes
+// per wave for n_use anchors over 4 waves (ties to the smaller)
+int cos_anch(int n_use) {
+  int best = 2, cost = 1 << 30;
+  for (int c : {2, 3, 5}) {
+    const int passes = (n_use + 4 * c - 1) / (4 * c);
+    if (passes * c < cost) { cost = passes * c; best = c; }
+  }
+  return best;
+}
+
 template <int HD>
 hipError_t cos_dispatch(const ScoreArgs& a, dim3 grid, size_t shmem, hipStream_t st) {
   switch (a.g.r / 32) {
-    case 1: KVC_LAUNCH((score_cos_mfma<HD, 1>), grid, 256, shmem, st, a); break;
-    case 2: KVC_LAUNCH((score_cos_mfma<HD, 2>), grid, 256, shmem, st, a); break;
-    case 4: KVC_LAUNCH((score_cos_mfma<HD, 4>), grid, 256, shmem, st, a); break;
+    case 1:
+      switch (cos_anch(a.n_use)) {
+        case 5: KVC_LAUNCH((score_cos_mfma<HD, 1, 5>), grid, 256, shmem, st, a); break;
+        case 3: KVC_LAUNCH((score_cos_mfma<HD, 1, 3>), grid, 256, shmem, st, a); break;
+        default: KVC_LAUNCH((score_cos_mfma<HD, 1, 2>), grid, 256, shmem, st, a); break;
+      }
+      break;
+    case 2: KVC_LAUNCH((score_cos_mfma<HD, 2, 1>), grid, 256, shmem, st, a); break;
+    case 4: KVC_LAUNCH((score_cos_mfma<HD, 4, 1>), grid, 256, shmem, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
