@@ -16,7 +16,6 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
-import hashlib
 import json
 import os
 import statistics
@@ -80,17 +79,10 @@ def roofline(name, ms, work, traffic=None):
             "algorithmic_bytes": work["bytes"], "mfma_flops": work["flops"], "valu_ops": work["alu"]}
 
 
-def source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "rank_kv_cache_layer_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel's
+    current source."""
+    from rank_kv_cache_layer_amd.profsum import kernel_source_hash
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -98,10 +90,10 @@ def measured_traffic(kernel):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("source_hash") != source_hash():
-        return None
     v = d.get("kernels", {}).get(kernel)
-    return None if v is None else int(v)
+    if not isinstance(v, dict) or v.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return int(v["bytes"])
 
 
 def measure_peaks(kvc, torch):

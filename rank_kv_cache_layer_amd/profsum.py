@@ -11,12 +11,13 @@ HBM traffic per dispatch = counter KiB x 1024 x calibration, where the calibrati
 counter is taken from the library's streaming copy kernel in the same run, whose true traffic
 is known (bytes read = bytes written = its size): calibration = true bytes / counted bytes.
 
-Outputs: a markdown summary (--out) and, with --traffic, a JSON table {kernel: HBM bytes per
-launch} tagged with a hash of the kernel sources, which bench.py reports as `traffic` only
-while the sources are unchanged.
+Outputs: a markdown summary (--out) and, with --traffic, a JSON table {kernel: {HBM bytes per
+launch, hash of the kernel's defining source and the internal header}}, which bench.py reports
+as `traffic` only while that kernel's source is unchanged.
 
 Usage: python -m rank_kv_cache_layer_amd.profsum --kt D --fetch D --write D [--sq D]
-           [--bench F] --copy-bytes N --cmd "..." --out profiles/X.md [--traffic profiles/traffic.json]
+           [--bench F] --copy-bytes N --cmd "..." --out profiles/X.md
+           [--traffic profiles/traffic.json [--merge]]
 """
 from __future__ import annotations
 
@@ -39,12 +40,20 @@ def short_name(k: str) -> str:
     return k.split("::")[-1].strip()
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
+_KERNEL_DEF = re.compile(r"__global__\s+void\s+__launch_bounds__\([^)]*\)\s+(\w+)\s*\(")
+
+
+def kernel_source_hash(name: str) -> str:
+    """Hash of the shared internal header and of the source file(s) that define kernel `name`
+    (none for runtime or torch kernels), so a counter figure goes stale only when that
+    kernel's own source changes."""
     csrc = os.path.join(PKG, "csrc")
+    h = hashlib.sha256(open(os.path.join(csrc, "kvc_internal.h"), "rb").read())
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+        if f.endswith(".hip"):
+            text = open(os.path.join(csrc, f), "rb").read()
+            if name in _KERNEL_DEF.findall(text.decode()):
+                h.update(f.encode() + text)
     return h.hexdigest()[:16]
 
 
@@ -77,6 +86,8 @@ def main():
     ap.add_argument("--title", default="per-hop correction, 32768-token Llama-3.1-8B-shaped hop")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic")
+    ap.add_argument("--merge", action="store_true",
+                    help="keep the traffic table's entries for kernels this run did not launch")
     a = ap.parse_args()
 
     ks = kernel_stats(a.kt)
@@ -108,7 +119,7 @@ def main():
         f = statistics.median(fe[name]["FETCH_SIZE"]) * 1024 * cal_f if name in fe else None
         w = statistics.median(wr[name]["WRITE_SIZE"]) * 1024 * cal_w if name in wr else None
         if f is not None and w is not None:
-            traffic[name] = int(f + w)
+            traffic[name] = {"bytes": int(f + w), "source_hash": kernel_source_hash(name)}
         alg = algo.get(name, {}).get("algorithmic_bytes")
         fmt = lambda x: "" if x is None else f"{x / 1e9:.3f}"
         lines.append(f"| {name} | {calls} | {avg_ns / 1e6:.4f} | {pct:.1f} | {fmt(f)} | {fmt(w)} | {fmt(alg)} |")
@@ -125,8 +136,11 @@ def main():
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     open(a.out, "w").write("\n".join(lines) + "\n")
     if a.traffic:
-        json.dump({"source_hash": source_hash(), "calibration": {"fetch": cal_f, "write": cal_w},
-                   "kernels": traffic}, open(a.traffic, "w"), indent=1)
+        if a.merge and os.path.exists(a.traffic):
+            old = json.load(open(a.traffic)).get("kernels", {})
+            traffic = {**{k: v for k, v in old.items() if isinstance(v, dict)}, **traffic}
+        json.dump({"calibration": {"fetch": cal_f, "write": cal_w}, "kernels": traffic}, open(a.traffic, "w"),
+                  indent=1)
         open(a.traffic, "a").write("\n")
 
 
