@@ -368,6 +368,63 @@ def time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn, ws, steps, warmup,
     return ms, wall, per_kernel, res
 
 
+def measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool, prm, reps=20, warmup=5):
+    """One hop timed repetition by repetition: `warmup` untimed calls, then `reps` calls each
+    bracketed by its own events, with the 256 MB Infinity Cache flushed in between by a 512 MiB
+    fill outside the bracket; median, p10 and p90 for the fused call (kvc_correct_hop) and for
+    the unfused sequence (kvc_match_anchors, which writes the token weights to memory, then
+    kvc_apply_lowrank_delta; the re-alignment is fused into both), and the standalone key
+    re-alignment (kvc_align_rope) as an HBM stream."""
+    import numpy as np
+    dev = k.device
+    st = torch.cuda.current_stream()
+    L, S, D = shp.n_layers, shp.seq_len, shp.n_kv_heads * shp.head_dim
+    N = len(pool.anchor_len)
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+    m = kvc.alloc_match(L, S, N, dev, want_weights=True)
+    ws_c = torch.empty((max(kvc.correct_hop_workspace(shp, pool, prm), 1),), dtype=torch.uint8, device=dev)
+    ws_m = torch.empty((max(kvc.workspace_size(kvc.CALL_MATCH, shp, pool, prm), 1),), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty((max(kvc.workspace_size(kvc.CALL_APPLY, shp, pool), 1),), dtype=torch.uint8, device=dev)
+
+    def fused():
+        kvc.correct_hop(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, prm, workspace=ws_c)
+
+    def unfused():
+        kvc.match_anchors(k, v, shp, sp.p_src, pool, prm, out=m, workspace=ws_m)
+        kvc.apply_lowrank_delta(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, m.w_k, m.w_v, m.s_cov, workspace=ws_a)
+
+    def align():
+        kvc.align_rope(k, ko, shp, sp.p_src, sp.p_tgt)
+
+    def reps_of(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(reps):
+            flush.fill_(i & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = np.array([a.elapsed_time(b) for a, b in evs])
+        return {"median_ms": round(float(np.median(ts)), 4), "p10_ms": round(float(np.percentile(ts, 10)), 4),
+                "p90_ms": round(float(np.percentile(ts, 90)), 4)}
+
+    out = {"reps": reps, "warmup": warmup, "flush_bytes": flush.numel(), "fused": reps_of(fused),
+           "match_then_apply": reps_of(unfused)}
+    al = reps_of(align)
+    al["bytes"] = 2 * L * S * D * k.element_size()
+    al["achieved_GBps"] = round(al["bytes"] / (al["median_ms"] / 1e3) / 1e9, 1)
+    out["align_rope_keys"] = al
+    out["fused_tokens_per_s"] = round(S / (out["fused"]["median_ms"] / 1e3), 1)
+    out["unfused_over_fused"] = round(out["match_then_apply"]["median_ms"] / out["fused"]["median_ms"], 3)
+    del flush, ws_c, ws_m, ws_a, m
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -445,6 +502,9 @@ def main():
            "hbm_frac": round(hop_bytes / (ms / 1e3) / PEAK_HBM, 4),
            "mfma_frac": round(hop_flops / (ms / 1e3) / PEAK_MFMA_BF16, 4)}
 
+    protocol = measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode)(None))
+    log(f"[bench] per-repetition protocol (cache flushed): {protocol}")
+
     second = None
     if not args.no_second_mode:
         m2 = W.SCORE_COS_R if mode == W.SCORE_PAGES else W.SCORE_PAGES
@@ -490,7 +550,7 @@ def main():
                    "n_anchors": N, "rank": r, "shift": sp.shift, "score_mode": args.mode,
                    "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
         "roofline": dominant, "cpu_baseline": cpu,
-        "hop": hop, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
+        "hop": hop, "protocol": protocol, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
         "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf, "chain_study": study_out,
         "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
     }

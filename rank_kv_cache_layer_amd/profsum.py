@@ -31,6 +31,8 @@ import statistics
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+HOT = ("split_score", "split_apply", "score_cos_mfma", "fused_hop")
+N_SE, N_SIMD = 32, 1024   # MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
 
 
 def short_name(k: str) -> str:
@@ -125,9 +127,22 @@ def main():
         lines.append(f"| {name} | {calls} | {avg_ns / 1e6:.4f} | {pct:.1f} | {fmt(f)} | {fmt(w)} | {fmt(alg)} |")
     if sq:
         lines += ["", "SQ counters (per dispatch, median):", "", "| kernel | counter | value |", "|---|---|---|"]
-        for name in ("split_score", "split_apply", "score_cos_mfma", "fused_hop"):
+        for name in HOT:
             for c, v in sorted(sq.get(name, {}).items()):
                 lines.append(f"| {name} | {c} | {statistics.median(v):.0f} |")
+        derived = []
+        for name in HOT:
+            c = sq.get(name, {})
+            if name in ks and "SQ_BUSY_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                dur = ks[name][1] / 1e9
+                clk = statistics.median(c["SQ_BUSY_CYCLES"]) / N_SE / dur
+                busy = statistics.median(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / (N_SIMD * clk * dur)
+                derived.append(f"| {name} | {clk / 1e9:.2f} | {busy:.3f} |")
+        if derived:
+            lines += ["", f"Derived: shader clock = SQ_BUSY_CYCLES / {N_SE} shader engines / average duration; "
+                          f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (matrix-core cycles summed over SIMDs) / "
+                          f"({N_SIMD} SIMDs x clock x duration).", "",
+                      "| kernel | clock GHz | MFMA busy |", "|---|---|---|", *derived]
     if bench:
         lines += ["", f"bench.py line of the same workload: {bench['ms_per_step']} ms/hop, {bench['value']} tokens/s; "
                       f"dominant kernel {bench['roofline']['kernel']}: {bench['roofline']['achieved']} "
