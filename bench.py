@@ -285,28 +285,30 @@ def measure_study(torch, L=8, S=4096, D=1024, rank=32):
             "error_non_chained": [round(x, 5) for x in res["non_chained"]], "wall_s": round(dt, 3)}
 
 
-def measure_chain(kvc, torch, W, n_requests=2, n_hops=3, steps=3):
-    """Concurrent chains (A0 -> A1 -> A2 -> A3) at the 8B shape, 8192 tokens per request,
-    pools of 10-20 anchors at rank 16 or 32, through kvc_correct_hops_batched (one call for all
-    requests' hops).  Tokens/s counts every hop's corrected segment."""
-    import dataclasses as _dc
+def measure_chain(kvc, torch, W, n_requests=8, n_hops=3, steps=3):
+    """Concurrent chains (A0 -> A1 -> A2 -> A3) at the 8B shape, 8192 tokens per request: the
+    seeded chain specification (per hop 10-20 anchors, rank 16 or 32, positions) with factors and
+    first sources drawn on the device (N(0, 1) sources, factors N(0, 0.2^2), bf16), since the
+    time does not depend on the values; all requests' hops in one kvc_correct_hops_batched
+    call.  Tokens/s counts every hop's corrected segment."""
     reqs = W.chain_specs(n_requests=n_requests, n_hops=n_hops)
     h0 = reqs[0][0]
-    shp = kvc.shape_of(h0.n_layers, h0.seq_len, h0.n_kv_heads, h0.head_dim)
+    L, S, D = h0.n_layers, h0.seq_len, h0.n_kv_heads * h0.head_dim
+    shp = kvc.shape_of(L, S, h0.n_kv_heads, h0.head_dim)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    rnd = lambda *sh, sc=1.0: (torch.randn(sh, device="cuda", generator=g) * sc).to(torch.bfloat16)
     hl = []
     for hops in reqs:
         base = len(hl)
+        k0, v0 = rnd(L, S, D), rnd(L, S, D)
         for i, h in enumerate(hops):
-            # drawn in the canonical frame; the first source's keys are placed at p_src on the device
-            d = W.make_hop(_dc.replace(h, p_src=0, p_tgt=h.p_tgt - h.p_src))
-            pool = kvc.pool_from(d, "cuda")
-            if i == 0:
-                k0, v0 = d.k_src.to("cuda"), d.v_src.to("cuda")
-                kvc.align_rope(k0, k0, shp, 0, h.p_src)
-            out = kvc.alloc_match(h.n_layers, h.seq_len, h.n_anchors, "cuda", want_weights=False)
+            N, r = h.n_anchors, h.rank_base
+            f = lambda rr: (rnd(L, N * S, rr, sc=0.2), rnd(L, N, rr, D, sc=0.2))
+            (bAk, bBk), (bAv, bBv), (dAk, dBk), (dAv, dBv) = f(r), f(r), f(h.rank_delta), f(h.rank_delta)
+            pool = kvc.PoolTensors([S] * N, r, h.rank_delta, bAk, bBk, bAv, bBv, dAk, dBk, dAv, dBv)
+            out = kvc.alloc_match(L, S, N, "cuda", want_weights=False)
             hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
                               torch.empty_like(v0), h.p_src, h.p_tgt, base + i - 1 if i else -1, pool, out))
-            del d
     prm = kvc.params_of(h0.tau, h0.temp_gate, h0.temp_weight, h0.gate_len, h0.mode, 0, None)
     kvc.correct_hops_batched(hl, shp, prm)
     torch.cuda.synchronize()
@@ -319,10 +321,19 @@ def measure_chain(kvc, torch, W, n_requests=2, n_hops=3, steps=3):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     toks = sum(h.seq_len for hops in reqs for h in hops)
-    return {"workload": f"{n_requests} requests x {n_hops} chained hops, 32 layers x 8192 tokens, 8x128 KV heads, "
-                        f"bf16, pools of 10-20 anchors at rank 16/32",
-            "ms": round(ms, 3), "tokens_per_s": round(toks / (ms / 1e3), 1),
-            "flags": [int(h.out.flags[0].item()) for h in hl]}
+    nbytes = sum(int(t.numel()) * 2 for h in hl for t in (h.k_out, h.v_out))
+    nbytes += sum(int(t.numel()) * 2 for h in hl if h.k_src is not None for t in (h.k_src, h.v_src))
+    nbytes += sum(int(t.numel()) * 2 for h in hl for t in (h.pool.baseA_k, h.pool.baseB_k, h.pool.baseA_v,
+                                                            h.pool.baseB_v, h.pool.deltaA_k, h.pool.deltaB_k,
+                                                            h.pool.deltaA_v, h.pool.deltaB_v))
+    out = {"workload": f"{n_requests} requests x {n_hops} chained hops, {L} layers x {S} tokens, "
+                       f"{h0.n_kv_heads}x{h0.head_dim} KV heads, bf16, pools of 10-20 anchors at rank 16/32 "
+                       f"(seeded chain specification, values drawn on the device)",
+           "ms": round(ms, 3), "tokens_per_s": round(toks / (ms / 1e3), 1),
+           "algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms / 1e3) / 1e9, 1)}
+    del hl
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(data, n_layers):
@@ -522,7 +533,7 @@ def main():
         log(f"[bench] refresh: {refresh['ms']} ms, {refresh['achieved_TFLOPs']} TFLOP/s")
         del k, v, ko, vo, pool, ws
         torch.cuda.empty_cache()
-        log("[bench] chained batch (2 requests x 3 hops, 8192 tokens) ...")
+        log("[bench] chained batch (8 requests x 3 hops, 8192 tokens) ...")
         chain = measure_chain(kvc, torch, W)
         log(f"[bench] chain: {chain['ms']} ms, {chain['tokens_per_s']} tokens/s")
         log("[bench] preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens) ...")
