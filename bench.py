@@ -60,10 +60,10 @@ def kernel_work(name, L, S, D, N, rC, rD, mode="pages", b=2):
         return dict(bytes=src + fac_base + scores, flops=4 * L * S * D * N * rC, alu=3 * L * S * D * N)
     if name == "split_apply":                     # token weights from the scores, then the delta
         return dict(bytes=src + out + fac_delta + scores, flops=4 * L * S * D * N * rD, alu=0)
-    if name == "score_cos_mfma":
+    if name in ("score_cos_mfma", "score_cos_gemm"):
         return dict(bytes=src + fac_base + scores, flops=4 * L * S * D * N * rC, alu=6 * L * S * N * rC)
-    if name in ("pack_base", "pack_delta"):
-        r = rC if name == "pack_base" else rD
+    if name in ("pack_base", "pack_delta", "pack_cos"):
+        r = rD if name == "pack_delta" else rC
         return dict(bytes=2 * 2 * L * N * r * D * b, flops=0, alu=0)
     return dict(bytes=0, flops=0, alu=0)
 

@@ -132,9 +132,11 @@ typedef struct {
 #define KVC_K_PACK_DELTA 7       /* delta B factors -> MFMA operand chunks (keys turned)      */
 #define KVC_K_FUSED 8            /* fused score / weights / apply (bf16 MFMA)                 */
 #define KVC_K_APPLY_GENERIC 9    /* apply, any shape / dtype (VALU)                           */
-#define KVC_K_SCORE_SPLIT 10     /* first-mode scores, 256 x 256 tiles (bf16 MFMA)            */
-#define KVC_K_APPLY_SPLIT 11
-#define KVC_K_WEIGHTS_SPLIT 12     /* token weights + apply, 256 x 256 tiles (bf16 MFMA)        */
+#define KVC_K_SCORE_SPLIT 10     /* first-mode scores, 128 x 256 tiles (bf16 MFMA)            */
+#define KVC_K_APPLY_SPLIT 11     /* weighted delta + residual, 128 x 256 tiles (bf16 MFMA)    */
+#define KVC_K_WEIGHTS_SPLIT 12   /* token weights, anchor-major, for the two-pass apply       */
+#define KVC_K_SCORE_COS_GEMM 13  /* second-mode scores as one GEMM per layer-side (bf16 MFMA) */
+#define KVC_K_PACK_COS 14        /* base B rows -> second-mode GEMM operand (keys turned)     */
 typedef struct {
   int32_t capacity;               /* <= KVC_TRACE_MAX                                      */
   int32_t count;                  /* written by the library                                */

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 
-SOURCES = ["kvc_align.hip", "kvc_generic.hip", "kvc_gate.hip", "kvc_mfma.hip", "kvc_fused.hip", "kvc_split.hip",
+SOURCES = ["kvc_align.hip", "kvc_generic.hip", "kvc_gate.hip", "kvc_mfma.hip", "kvc_cosg.hip", "kvc_fused.hip", "kvc_split.hip",
            "kvc_svd.hip",
            "kvc_peaks.hip", "kvc_pool.hip", "kvc_host.hip"]
 

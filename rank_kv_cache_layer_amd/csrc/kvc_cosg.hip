@@ -1,0 +1,291 @@
+// Second scoring mode as one bf16 GEMM per (layer, side) for gfx950 (CDNA4): the projection
+// of the canonical source on every scored anchor's basis, P = Z_can B^T (the Eq. 7 factor B
+// of KVCMAS, arXiv 2609.34060, Sec. 3.3), with tokens as one GEMM dimension, (anchor, rank)
+// as the other and the channels as the contraction; then, per token and anchor, the cosine of
+// P with the anchor coordinates A, and over the prefix k the value-side sums of the segment
+// cosine that the gate reads (App. A.3 "Reliability Gate", second mode).
+//
+// The key re-alignment to the canonical frame is folded into the packed operand: with
+// Z_can = R Z (R = R(-p_src), rotate-half pairs), P = Z_can B^T = Z (R^T B)^T, so the kernel
+// contracts the stored keys with B' = R^T B, each row of B turned by +p_src.  Values use B as
+// stored.
+//
+// Work-group: 128 tokens x all scored anchors (passes of 20) of one (layer, side), 8 waves.
+// Wave (tw, ag) owns tokens [64 tw, 64 tw + 64) and anchors [5 ag, 5 ag + 5) of the pass, i.e.
+// a 64 x 160 block of P in 160 accumulator registers.  The contraction runs over 32-channel
+// chunks: each chunk's source rows (128 x 64 B) and packed B' rows (20 x 32 x 64 B) are copied
+// from memory straight into a three-slot LDS ring by buffer->LDS transfers two chunks ahead.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16, operand A = 32 rank rows of B' x 16 channels, operand B =
+// 32 tokens x 16 channels; result register j of lane l holds rank row 8 (j / 4) + 4 (l / 32)
+// + j % 4 and token l % 32, so the cosine's sums over the rank stay in the lane (plus one
+// exchange with lane l ^ 32).
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kTok = kCosGemmTile;   // tokens per work-group
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAnch = 5;             // anchors per wave and pass
+constexpr int kPass = 4 * kAnch;     // anchors per pass (four anchor groups)
+constexpr int kKc = 32;              // channels per chunk
+constexpr int kRowB = kKc * 2;       // bytes per LDS row (token or rank row of one chunk)
+constexpr int kZBytes = kTok * kRowB;                 // 8 KiB
+constexpr int kBBytes = kPass * 32 * kRowB;           // 40 KiB
+constexpr int kSlot = kZBytes + kBBytes;              // 48 KiB
+constexpr int kRing = 3;
+constexpr int kZDma = kZBytes / 1024 / kWaves;        // 1 transfer per wave
+constexpr int kBDma = kBBytes / 1024 / kWaves;        // 5 transfers per wave
+constexpr int kDmaPerWave = kZDma + kBDma;
+static_assert(kZBytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "ring split");
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit data, gfx9 family
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16-byte unit of row `row`, logical unit c (0..3) of a 64-byte LDS row: units XOR-swizzled by
+// row / 4, so the fragment reads of 16 consecutive rows (same logical unit) hit distinct banks.
+__device__ __forceinline__ int unit_of(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+
+// buffer->LDS transfer of 16 bytes per lane to LDS M0 + 16 * lane (lanes past the descriptor's
+// size write zeros).  Inline assembly so the compiler neither reorders LDS accesses around it
+// nor waits for every transfer in flight before later LDS reads; the ring's explicit waits
+// order each slot.  M0 is written only here.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory");
+}
+
+// s_waitcnt vmcnt <= N, lgkmcnt = 0 (gfx9 encoding), then the work-group barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_char*)p);
+}
+__device__ __forceinline__ bf16x8 lds_frag(uint32_t off) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)off);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// --------------------------------------------------------------------- operand packing
+// B' rows of the scored anchors, in scoring order u, chunked by 32 channels:
+// dst[side][layer][chunk][u][k][32] bf16 (each row 64 contiguous bytes).  Key rows are turned
+// by the transpose of the canonical rotation (cs, sn of R(-p_src)): b'_c = b_c cs + b_{c+h} sn,
+// b'_{c+h} = b_{c+h} cs - b_c sn.  One thread per (side, layer, u, k, rotary pair).
+__global__ void __launch_bounds__(256) pack_cos(CosGemmArgs p, uint16_t* __restrict__ dst) {
+  const int D = p.D, h = p.head_dim / 2, r = 32;
+  const int pairs = D / 2;
+  const int64_t per_row = pairs;
+  const int64_t rows = (int64_t)2 * p.n_layers * p.n_use * r;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * per_row) return;
+  const int pr = (int)(i % per_row);
+  int64_t row = i / per_row;
+  const int k = (int)(row % r);
+  row /= r;
+  const int u = (int)(row % p.n_use);
+  row /= p.n_use;
+  const int layer = (int)(row % p.n_layers);
+  const int side = (int)(row / p.n_layers);
+  const int head = pr / h, c = pr % h;
+  const int dl = head * p.head_dim + c, du = dl + h;
+  const int a = p.use[u];
+  const uint16_t* b = p.B[side] + (int64_t)layer * p.b_layer_stride + ((int64_t)a * r + k) * D;
+  float x = bf2f(b[dl]), y = bf2f(b[du]);
+  if (side == 0 && p.can.active) {
+    const float cs = p.can.cs[c], sn = p.can.sn[c];
+    const float ox = fmaf(x, cs, y * sn), oy = fmaf(y, cs, -(x * sn));
+    x = ox;
+    y = oy;
+  }
+  const int nkc = D / kKc;
+  uint16_t* o = dst + ((((int64_t)side * p.n_layers + layer) * nkc) * p.n_use) * r * kKc;
+  o[(((int64_t)(dl / kKc) * p.n_use + u) * r + k) * kKc + dl % kKc] = f2bf(x);
+  o[(((int64_t)(du / kKc) * p.n_use + u) * r + k) * kKc + du % kKc] = f2bf(y);
+}
+
+// --------------------------------------------------------------------- the GEMM and cosines
+__global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];   // kRing x kSlot
+  const int nwg = (p.n_tiles * kCosTile + kTok - 1) / kTok;   // token range of the scored tiles
+  const int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int tt = (int)(lb % nwg);
+  const int layer = (int)((lb / nwg) % p.n_layers);
+  const int side = (int)(lb / ((int64_t)nwg * p.n_layers));
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
+  const int tw = wave >> 2, ag = wave & 3;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int D = p.D, S = p.S, nkc = D / kKc, r = 32;
+  const int t0 = tt * kTok;
+  const uint32_t ring0 = lds_off(ring);
+
+  const uint16_t* zl = p.z[side] + (int64_t)layer * S * D;
+  const rsrc_t zr = make_rsrc(zl, (uint32_t)S * D * 2);
+  const uint16_t* bside = p.packed + (((int64_t)side * p.n_layers + layer) * nkc) * p.n_use * r * kKc;
+
+  // fragment offsets inside a slot: token rows (operand B) and rank rows (operand A)
+  uint32_t zoff[2][2], boff[kAnch][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) zoff[tb][s] = unit_of(tw * 64 + tb * 32 + col, s * 2 + hi) * 16;
+#pragma unroll
+  for (int x = 0; x < kAnch; ++x)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) boff[x][s] = kZBytes + unit_of((ag * kAnch + x) * 32 + col, s * 2 + hi) * 16;
+
+  for (int u0 = 0; u0 < p.n_use; u0 += kPass) {
+    const int np = min(kPass, p.n_use - u0);
+    // chunk kc of this pass into slot kc % kRing; past the last chunk the descriptors have
+    // size 0 (zeros written, nothing fetched), so every step issues the same transfers
+    auto fetch = [&](int kc) {
+      const bool live = kc < nkc;
+      const uint32_t slot = ring0 + (uint32_t)(kc % kRing) * kSlot;
+      const rsrc_t zs = live ? zr : make_rsrc(zl, 0);
+#pragma unroll
+      for (int i = 0; i < kZDma; ++i) {
+        const int unit = (wv * kZDma + i) * 64 + lane;
+        const int row = unit >> 2, c = (unit & 3) ^ ((row >> 2) & 3);
+        dma16(zs, slot + (uint32_t)(wv * kZDma + i) * 1024,
+              (uint32_t)(((int64_t)(t0 + row) * D + kc * kKc + c * 8) * 2));
+      }
+      const uint16_t* bc = bside + ((int64_t)(live ? kc : 0) * p.n_use + u0) * r * kKc;
+      const rsrc_t bs = make_rsrc(bc, live ? (uint32_t)np * r * kRowB : 0u);
+#pragma unroll
+      for (int i = 0; i < kBDma; ++i) {
+        const int unit = (wv * kBDma + i) * 64 + lane;
+        const int row = unit >> 2, c = (unit & 3) ^ ((row >> 2) & 3);
+        dma16(bs, slot + kZBytes + (uint32_t)(wv * kBDma + i) * 1024, (uint32_t)(row * kRowB + c * 16));
+      }
+    };
+
+    f32x16 acc[kAnch][2];
+#pragma unroll
+    for (int x = 0; x < kAnch; ++x)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[x][tb][j] = 0.f;
+
+    fetch(0);
+    fetch(1);
+#pragma nounroll
+    for (int kc = 0; kc < nkc; ++kc) {
+      wait_vm_barrier<kDmaPerWave>();   // chunk kc landed everywhere; slot (kc + 2) % 3 is free
+      fetch(kc + 2);
+      const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ring0 + (uint32_t)(kc % kRing) * kSlot));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 z0 = lds_frag(slot + zoff[0][s]), z1 = lds_frag(slot + zoff[1][s]);
+#pragma unroll
+        for (int x = 0; x < kAnch; ++x) {
+          const bf16x8 bx = lds_frag(slot + boff[x][s]);
+          acc[x][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx, z0, acc[x][0], 0, 0, 0);
+          acc[x][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx, z1, acc[x][1], 0, 0, 0);
+        }
+      }
+    }
+    wait_vm_barrier<0>();   // trailing (empty) transfers drained; every wave past the last chunk
+
+    // cosines of P with A per token, and the value-side gate sums over the prefix
+#pragma unroll
+    for (int x = 0; x < kAnch; ++x) {
+      const int u = u0 + ag * kAnch + x;
+      if (u >= p.n_use) break;
+      const int a = p.use[u];
+      const int alen = p.len[a];
+      const uint16_t* Aa = p.A[side] + layer * p.a_layer_stride + (int64_t)p.off[a] * r;
+      const bool gate = side == 1 && ((p.mask_gate >> a) & 1);
+      float gnum = 0.f, gpp = 0.f, gaa = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int t = t0 + tw * 64 + tb * 32 + col;
+        const bool ok = t < alen && t < S;
+        float num = 0.f, pp = 0.f, aa = 0.f;
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          uint2 av = make_uint2(0, 0);
+          if (ok) av = *reinterpret_cast<const uint2*>(Aa + (int64_t)t * r + 8 * jg + 4 * hi);
+          const float a4[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
+                               __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = acc[x][tb][4 * jg + i];
+            num = fmaf(pv, a4[i], num);
+            pp = fmaf(pv, pv, pp);
+            aa = fmaf(a4[i], a4[i], aa);
+          }
+        }
+        const float qm = (gate && ok && t < p.k_gate) ? 1.f : 0.f;
+        gnum = fmaf(num, qm, gnum);
+        gpp = fmaf(pp, qm, gpp);
+        gaa = fmaf(aa, qm, gaa);
+        num += __shfl_xor(num, 32);
+        pp += __shfl_xor(pp, 32);
+        aa += __shfl_xor(aa, 32);
+        const float den = sqrtf(pp) * sqrtf(aa);
+        const float cval = den > 0.f ? num / den : 0.f;
+        if (hi == 0 && t < S && tt * (kTok / kCosTile) + tw < p.n_tiles) p.scores[(((int64_t)side * p.n_layers + layer) * S + t) * p.N + a] = cval;
+      }
+      const int tile = tt * (kTok / kCosTile) + tw;
+      if (gate && tile < p.n_tiles) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          gnum += __shfl_xor(gnum, o);
+          gpp += __shfl_xor(gpp, o);
+          gaa += __shfl_xor(gaa, o);
+        }
+        if (lane == 0) {
+          const int64_t plane = (int64_t)p.n_layers * p.n_tiles * p.N;
+          const int64_t o = ((int64_t)layer * p.n_tiles + tile) * p.N + a;
+          p.partials[o] = gnum;
+          p.partials[plane + o] = gpp;
+          p.partials[2 * plane + o] = gaa;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t cos_gemm_lds() { return (size_t)kRing * kSlot; }
+
+size_t cos_gemm_packed_elems(int n_layers, int n_use, int D) { return (size_t)2 * n_layers * n_use * 32 * D; }
+
+hipError_t launch_pack_cos(const CosGemmArgs& a, uint16_t* dst, hipStream_t st) {
+  if (a.n_use < 1) return hipSuccess;
+  const int64_t n = (int64_t)2 * a.n_layers * a.n_use * 32 * (a.D / 2);
+  pack_cos<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(a, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_cos_gemm(const CosGemmArgs& a, hipStream_t st) {
+  if (a.n_use < 1) return hipSuccess;
+  if (a.D % kKc || (a.head_dim != 64 && a.head_dim != 128)) return hipErrorInvalidValue;
+  const size_t lds = cos_gemm_lds();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(score_cos_gemm),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t nblk = (int64_t)((a.n_tiles * kCosTile + kTok - 1) / kTok) * a.n_layers * 2;
+  if (nblk == 0) return hipSuccess;
+  score_cos_gemm<<<dim3((unsigned)nblk), kThreads, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -209,6 +209,15 @@ bool cos_mfma_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
   return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
 }
 
+// The second mode's GEMM scoring: rank 32, bf16, unless a single-pass kernel is asked for
+// (option bit 1 keeps the older per-anchor-group kernel); a layer must fit a 32-bit buffer.
+bool cos_gemm_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) {
+  if (p.dtype != KVC_BF16 || (prm.options & 3) || p.rank_base != 32) return false;
+  const int D = D_of(sh);
+  if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 32) return false;
+  return (uint64_t)sh.seq_len * D * 2 < (1ull << 31);
+}
+
 // The two-pass bf16 path: 128-token x 256-channel work-groups (D a multiple of 256), ranks
 // 16/32 (larger ranks would not fit the register budget; the apply also takes rank 8, padded
 // to the MFMA's 16 on chip), within the LDS budget.
@@ -235,6 +244,8 @@ struct Plan {
   bool fused_match = false;   // PAGES scores inside the fused kernel
   bool fused_apply = false;   // apply inside the fused kernel
   bool cos_mfma = false;
+  bool cos_gemm = false;        // second-mode scores as one GEMM per layer-side
+  size_t off_pack_cos = 0;
   int tile = 0, n_tiles = 0, s_work = 0, generic_tt = 0;
   size_t off_scores = 0, off_w = 0, off_partials = 0, off_pack_base = 0, off_pack_delta = 0, off_mpart = 0;
   size_t off_wa = 0;            // anchor-major token weights of the two-pass path
@@ -279,8 +290,13 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
       pl.tile = kFusedTile;
       pl.n_tiles = (S + kFusedTile - 1) / kFusedTile;
     } else {
-      pl.cos_mfma = !pages && cos_mfma_ok(sh, p, P);
-      if (pl.cos_mfma) {
+      pl.cos_gemm = !pages && cos_gemm_ok(sh, p, P);
+      pl.cos_mfma = !pages && !pl.cos_gemm && cos_mfma_ok(sh, p, P);
+      if (pl.cos_gemm) {
+        pl.tile = kCosTile;
+        pl.off_pack_cos = off;
+        off += up256(sizeof(uint16_t) * cos_gemm_packed_elems(L, std::max(n_use, 1), D));
+      } else if (pl.cos_mfma) {
         pl.tile = kCosTile;
       } else {
         pl.generic_tt = std::max(1, 256 / std::max(n_use, 1));
@@ -521,7 +537,29 @@ kvc_status run_scores(const void* k_src, const void* v_src, const kvc_shape& sh,
   kvc_status s2 = make_tab(a.can, -p_src, sh.head_dim, rope);
   if (s2 != KVC_OK) return s2;
   hipError_t e;
-  if (pl.cos_mfma) {
+  if (pl.cos_gemm) {
+    CosGemmArgs c;
+    memset(&c, 0, sizeof c);
+    c.z[0] = (const uint16_t*)k_src; c.z[1] = (const uint16_t*)v_src;
+    c.A[0] = (const uint16_t*)p.baseA_k; c.A[1] = (const uint16_t*)p.baseA_v;
+    c.B[0] = (const uint16_t*)p.baseB_k; c.B[1] = (const uint16_t*)p.baseB_v;
+    uint16_t* packed = reinterpret_cast<uint16_t*>(ws + pl.off_pack_cos);
+    c.packed = packed;
+    c.scores = a.scores; c.partials = a.partials;
+    c.a_layer_stride = a.g.a_layer_stride; c.b_layer_stride = a.g.b_layer_stride;
+    c.n_layers = a.n_layers; c.S = a.S; c.D = a.D; c.head_dim = a.head_dim; c.N = p.n_anchors;
+    c.k_gate = a.k_gate; c.n_tiles = a.n_tiles; c.mask_gate = a.mask_gate;
+    c.n_use = n_use;
+    for (int i = 0; i < n_use; ++i) c.use[i] = s.use_list[i];
+    for (int i = 0; i < p.n_anchors; ++i) { c.off[i] = a.g.off[i]; c.len[i] = a.g.len[i]; }
+    c.can = a.can;
+    tr.begin(KVC_K_PACK_COS);
+    e = launch_pack_cos(c, packed, st);
+    tr.end();
+    if (e != hipSuccess) return hip_fail(e, "pack kernel");
+    tr.begin(KVC_K_SCORE_COS_GEMM);
+    e = launch_score_cos_gemm(c, st);
+  } else if (pl.cos_mfma) {
     tr.begin(KVC_K_SCORE_COS);
     e = launch_score_cos_mfma(a, st);
   } else {

@@ -66,7 +66,7 @@ class PoolStateC(C.Structure):
 TRACE_MAX = 64
 KERNEL_NAMES = {1: "pack_base", 3: "score_cos_mfma", 4: "score_generic", 5: "gate_finalize", 6: "softmax",
                 7: "pack_delta", 8: "fused_hop", 9: "apply_generic", 10: "split_score", 11: "split_apply",
-                12: "split_weights"}
+                12: "split_weights", 13: "score_cos_gemm", 14: "pack_cos"}
 
 
 class Trace(C.Structure):

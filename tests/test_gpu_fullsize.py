@@ -12,7 +12,7 @@ import pytest
 from oracle import kvc_oracle as O
 from rank_kv_cache_layer_amd import workload as W
 
-from hop_helpers import TOL_BF16, W_ATOL, make, run_gpu
+from hop_helpers import TOL_BF16, make, run_gpu, w_atol
 
 pytestmark = pytest.mark.gpu
 
@@ -40,13 +40,24 @@ def _check_sampled(spec, layers, seed):
             bound = TOL_BF16 * np.max(np.abs(want))
             assert np.max(np.abs(got - want)) <= bound, (spec.name, l, side)
             wg = gpu[f"w_{side}"][l][rows][:, :N]
-            assert np.max(np.abs(wg - ref[f"w_{side}"])) <= W_ATOL[W.BF16], (spec.name, l, side)
-        # per-layer gate row: distances and the decision, bit-exact flags
-        d, h, f = O.gate_decide_pages(np.asarray(ref["q"]), spec.tau, spec.temp_gate, spec.cap(), N)
-        assert np.allclose(gpu["dist"][1 + l][:N], d, rtol=1e-4), (spec.name, l)
+            tol_w = w_atol(W.BF16, spec.mode, spec.temp_weight)
+            assert np.max(np.abs(wg - ref[f"w_{side}"])) <= tol_w, (spec.name, l, side)
+        # per-layer gate row: distances (segment cosines) and the decision, bit-exact flags
+        if spec.mode == W.SCORE_COS_R:
+            d, h, f = O.gate_decide_cos(*[np.asarray(x) for x in ref["cos_sums"]], spec.tau, spec.cap(), N)
+            assert np.allclose(gpu["dist"][1 + l][:N], d, rtol=1e-4, atol=1e-5), (spec.name, l)
+        else:
+            d, h, f = O.gate_decide_pages(np.asarray(ref["q"]), spec.tau, spec.temp_gate, spec.cap(), N)
+            assert np.allclose(gpu["dist"][1 + l][:N], d, rtol=1e-4), (spec.name, l)
         assert gpu["flags"][1 + l] == f, (spec.name, l, gpu["flags"][1 + l], f)
         assert abs(gpu["stat"][1 + l] - h) < 2e-3
         assert abs(h - spec.tau) >= 0.05, "oracle statistic within 0.05 of tau"
+    if spec.mode == W.SCORE_COS_R:
+        # hop row: the best segment cosine over all layers decides, by the same rule
+        best = float(np.max(gpu["dist"][0][:N]))
+        assert gpu["flags"][0] == (O.FLAG_COS_BELOW if best < spec.tau else 0)
+        assert abs(best - spec.tau) >= 0.05
+        return gpu
     # hop row: d_hop^2 = sum over layers of d_layer^2, decided by the same rule
     d_hop = gpu["dist"][0][:N]
     assert np.allclose(d_hop ** 2, np.sum(gpu["dist"][1:, :N] ** 2, axis=0), rtol=1e-5)
@@ -61,6 +72,13 @@ def test_32k_hop_sampled():
     gpu = _check_sampled(spec, layers=[0, 2, 17, 31], seed=1)
     # layers with a source no anchor holds are flagged, the others accepted
     assert [int(x) for x in gpu["flags"][1:]] == [O.FLAG_ENTROPY if l % 3 == 2 else 0 for l in range(32)]
+
+
+@pytest.mark.timeout(900)
+def test_32k_hop_sampled_cosine_mode():
+    spec = W.llama8b_long(p_src=512, p_tgt=812, mode=W.SCORE_COS_R)
+    gpu = _check_sampled(spec, layers=[0, 2, 17, 31], seed=3)
+    assert [int(x) for x in gpu["flags"][1:]] == [O.FLAG_COS_BELOW if l % 3 == 2 else 0 for l in range(32)]
 
 
 @pytest.mark.timeout(900)

@@ -25,7 +25,7 @@ def _check_hop(spec, options=0, label=""):
     assert gpu["s_cov"] == ref["s_cov"]
     assert_outputs_close(gpu, ref, spec.dtype, label)
     assert_gate_equal(gpu, ref, spec.n_anchors, label, tau=spec.tau)
-    assert_weights_close(gpu, ref, spec.dtype, label)
+    assert_weights_close(gpu, ref, spec.dtype, label, spec.mode, spec.temp_weight)
     return data, ref, gpu
 
 
@@ -128,6 +128,24 @@ def test_preconstructed_rank8_delta_weight_one():
 def test_head_dim_64_bf16():
     sp = W.llama8b_hop(n_layers=2, seq_len=200, n_kv_heads=4, head_dim=64, n_anchors=5)
     _check_hop(sp, label="hd64")
+
+
+# second scoring mode on its two MFMA kernels (option 0: one GEMM per layer-side over 128-token
+# work-groups, anchors in passes of 20; option 2: the per-anchor-group kernel): head_dim 64,
+# ragged anchors with a gate prefix, more than 20 anchors, a ragged token tail
+COS_CASES = {
+    "hd64": dict(n_layers=2, seq_len=200, n_kv_heads=4, head_dim=64, n_anchors=5),
+    "ragged": dict(n_layers=2, seq_len=400, n_kv_heads=2, n_anchors=5,
+                   anchor_len=[330, 400, 250, 400, 390], gate_len=250),
+    "two_passes": dict(n_layers=2, seq_len=330, n_kv_heads=2, n_anchors=23),
+}
+
+
+@pytest.mark.parametrize("case", sorted(COS_CASES))
+@pytest.mark.parametrize("options", [0, 2])
+def test_cosine_mode_mfma_kernels(case, options):
+    sp = W.llama8b_hop(mode=W.SCORE_COS_R, tau=0.5, **COS_CASES[case])
+    _check_hop(sp, options=options, label=f"cos-{case}-{options}")
 
 
 def test_odd_shape_bf16_generic_path():
