@@ -31,7 +31,7 @@ import statistics
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-HOT = ("split_score", "split_apply", "score_cos_mfma", "fused_hop")
+HOT = ("split_score", "split_apply", "score_cos_mfma", "score_cos_gemm", "fused_hop")
 N_SE, N_SIMD = 32, 1024   # MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
 
 
