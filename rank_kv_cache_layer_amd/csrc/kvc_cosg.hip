@@ -86,15 +86,15 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t off) {
 // B' rows of the scored anchors, in scoring order u, chunked by 32 channels:
 // dst[side][layer][chunk][u][k][32] bf16 (each row 64 contiguous bytes).  Key rows are turned
 // by the transpose of the canonical rotation (cs, sn of R(-p_src)): b'_c = b_c cs + b_{c+h} sn,
-// b'_{c+h} = b_{c+h} cs - b_c sn.  One thread per (side, layer, u, k, rotary pair).
+// b'_{c+h} = b_{c+h} cs - b_c sn.  One thread per (side, layer, u, k) row and 8 rotary pairs:
+// 16-byte loads of the 8 lower and the 8 upper channels, 16-byte stores of each.
 __global__ void __launch_bounds__(256) pack_cos(CosGemmArgs p, uint16_t* __restrict__ dst) {
   const int D = p.D, h = p.head_dim / 2, r = 32;
-  const int pairs = D / 2;
-  const int64_t per_row = pairs;
+  const int per_row = D / 16;   // groups of 8 pairs
   const int64_t rows = (int64_t)2 * p.n_layers * p.n_use * r;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * per_row) return;
-  const int pr = (int)(i % per_row);
+  const int g = (int)(i % per_row);
   int64_t row = i / per_row;
   const int k = (int)(row % r);
   row /= r;
@@ -102,21 +102,34 @@ __global__ void __launch_bounds__(256) pack_cos(CosGemmArgs p, uint16_t* __restr
   row /= p.n_use;
   const int layer = (int)(row % p.n_layers);
   const int side = (int)(row / p.n_layers);
-  const int head = pr / h, c = pr % h;
-  const int dl = head * p.head_dim + c, du = dl + h;
+  const int gph = h / 8;                            // groups per head
+  const int head = g / gph, c0 = (g % gph) * 8;
+  const int dl = head * p.head_dim + c0, du = dl + h;
   const int a = p.use[u];
   const uint16_t* b = p.B[side] + (int64_t)layer * p.b_layer_stride + ((int64_t)a * r + k) * D;
-  float x = bf2f(b[dl]), y = bf2f(b[du]);
+  uint4 xv = *reinterpret_cast<const uint4*>(b + dl), yv = *reinterpret_cast<const uint4*>(b + du);
   if (side == 0 && p.can.active) {
-    const float cs = p.can.cs[c], sn = p.can.sn[c];
-    const float ox = fmaf(x, cs, y * sn), oy = fmaf(y, cs, -(x * sn));
-    x = ox;
-    y = oy;
+    uint32_t* xw = &xv.x;
+    uint32_t* yw = &yv.x;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float x[2] = {__uint_as_float(xw[w] << 16), __uint_as_float(xw[w] & 0xffff0000u)};
+      float y[2] = {__uint_as_float(yw[w] << 16), __uint_as_float(yw[w] & 0xffff0000u)};
+      uint16_t ox[2], oy[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float cs = p.can.cs[c0 + 2 * w + e], sn = p.can.sn[c0 + 2 * w + e];
+        ox[e] = f2bf(fmaf(x[e], cs, y[e] * sn));
+        oy[e] = f2bf(fmaf(y[e], cs, -(x[e] * sn)));
+      }
+      xw[w] = (uint32_t)ox[0] | ((uint32_t)ox[1] << 16);
+      yw[w] = (uint32_t)oy[0] | ((uint32_t)oy[1] << 16);
+    }
   }
   const int nkc = D / kKc;
   uint16_t* o = dst + ((((int64_t)side * p.n_layers + layer) * nkc) * p.n_use) * r * kKc;
-  o[(((int64_t)(dl / kKc) * p.n_use + u) * r + k) * kKc + dl % kKc] = f2bf(x);
-  o[(((int64_t)(du / kKc) * p.n_use + u) * r + k) * kKc + du % kKc] = f2bf(y);
+  *reinterpret_cast<uint4*>(o + (((int64_t)(dl / kKc) * p.n_use + u) * r + k) * kKc + dl % kKc) = xv;
+  *reinterpret_cast<uint4*>(o + (((int64_t)(du / kKc) * p.n_use + u) * r + k) * kKc + du % kKc) = yv;
 }
 
 // --------------------------------------------------------------------- the GEMM and cosines
@@ -270,7 +283,8 @@ size_t cos_gemm_packed_elems(int n_layers, int n_use, int D) { return (size_t)2 
 
 hipError_t launch_pack_cos(const CosGemmArgs& a, uint16_t* dst, hipStream_t st) {
   if (a.n_use < 1) return hipSuccess;
-  const int64_t n = (int64_t)2 * a.n_layers * a.n_use * 32 * (a.D / 2);
+  if (a.head_dim % 16) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)2 * a.n_layers * a.n_use * 32 * (a.D / 16);
   pack_cos<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(a, dst);
   return hipGetLastError();
 }

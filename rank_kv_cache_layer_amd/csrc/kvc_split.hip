@@ -540,22 +540,40 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
   const int S = p.S, N = p.N, L = p.n_layers, nc = p.n_corr;
   const bool in = t < S, cov = t < p.s_cov;
   float mx = -INFINITY;
-  for (int j = 0; j < nc; ++j) {
-    const int a = p.corr[j];
-    float x = 0.f;
+  // four anchors at a time, every load issued before the values are used (the channel-tile
+  // partials are still summed in ascending order)
+  const int64_t plane = (int64_t)2 * L * N * S;
+  const float* mp0 = p.mpart + (((int64_t)side * L + layer) * N) * S + t;
+  const float* wi = wmode == SPLIT_W_PARTIALS ? nullptr : p.w_in[side] + ((int64_t)layer * S + t) * N;
+  for (int j0 = 0; j0 < nc; j0 += 4) {
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
     if (cov) {
       if (wmode == SPLIT_W_PARTIALS) {
-        float m = 0.f;
-        for (int q = 0; q < p.nct; ++q) m += p.mpart[((((int64_t)q * 2 + side) * L + layer) * N + a) * S + t];
-        x = -(m * p.inv_d) * p.inv_temp;
-      } else if (wmode == SPLIT_W_SCORES) {
-        x = p.w_in[side][((int64_t)layer * S + t) * N + a] * p.inv_temp;
+#pragma unroll 4
+        for (int q = 0; q < p.nct; ++q) {
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = j0 + u < nc ? mp0[q * plane + (int64_t)p.corr[j0 + u] * S] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] += v[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = -(x[u] * p.inv_d) * p.inv_temp;
       } else {
-        x = p.w_in[side][((int64_t)layer * S + t) * N + a];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = j0 + u < nc ? wi[p.corr[j0 + u]] : 0.f;
+        if (wmode == SPLIT_W_SCORES) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] *= p.inv_temp;
+        }
       }
     }
-    xs[j * 256 + tid] = x;
-    mx = fmaxf(mx, x);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (j0 + u >= nc) break;
+      xs[(j0 + u) * 256 + tid] = x[u];
+      mx = fmaxf(mx, x[u]);
+    }
   }
   if (wmode != SPLIT_W_GIVEN) {
     float sum = 0.f;
