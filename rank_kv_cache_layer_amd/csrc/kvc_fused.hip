@@ -628,6 +628,64 @@ hipError_t fused_dispatch(const FusedArgs& a, int mode, hipStream_t st) {
 
 }  // namespace
 
+// The same packing with 16-byte row reads: a work-group takes one 16-row rank slice (ks) of one
+// factor matrix, stages it in LDS row-major (rows past the rank as zeros), and every thread then
+// gathers its chunk lanes' 8 rank values of one channel (and of its rotary partner) from LDS and
+// writes them as one 16-byte store.  Output identical to pack_b.
+constexpr int kPackPad = 8;   // LDS row padding (elements)
+__global__ void __launch_bounds__(256) pack_b_rows(PackArgs p) {
+  extern __shared__ uint16_t rows_s[];   // [16][D + kPackPad]
+  __shared__ float cs[kFusedHalf], sn[kFusedHalf];
+  const int D = p.D, hd = p.head_dim, h = hd >> 1, RK = (p.r + 15) >> 4, NCB = D >> 5, ld = D + kPackPad;
+  const int tid = threadIdx.x;
+  int64_t blk = blockIdx.x;
+  const int ks = (int)(blk % RK);
+  blk /= RK;
+  const int64_t mats = (int64_t)p.n_layers * p.n_anchors;
+  const int64_t mat = blk % mats;
+  const int arr = (int)(blk / mats);
+  for (int i = tid; i < h; i += blockDim.x) { cs[i] = p.tab.cs[i]; sn[i] = p.tab.sn[i]; }
+  const uint16_t* B = p.src[arr] + mat * p.r * D;
+  const int units = 16 * (D >> 3);   // 16-byte units of the slice
+  for (int u = tid; u < units; u += blockDim.x) {
+    const int row = u / (D >> 3), c8 = (u - row * (D >> 3)) * 8;
+    const int k = ks * 16 + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k < p.r) v = *reinterpret_cast<const uint4*>(B + (int64_t)k * D + c8);
+    *reinterpret_cast<uint4*>(rows_s + row * ld + c8) = v;
+  }
+  __syncthreads();
+  const bool rot = p.rotate[arr] && p.tab.active;
+  const bool neg = p.negate[arr];
+  for (int o = tid; o < NCB * 64; o += blockDim.x) {
+    const int cb = o >> 6, lane = o & 63;
+    const int d = cb * 32 + (lane & 31);
+    const int r0 = 8 * (lane >> 5);
+    const int c = d % hd;
+    const int partner = c < h ? d + h : d - h;
+    float out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = bf2f(rows_s[(r0 + i) * ld + d]);
+      float val = x;
+      if (rot) {
+        const float y = bf2f(rows_s[(r0 + i) * ld + partner]);
+        float lo, up;
+        if (c < h) {
+          rot_pair(x, y, cs[c], sn[c], lo, up);
+          val = lo;
+        } else {
+          rot_pair(y, x, cs[c - h], sn[c - h], lo, up);
+          val = up;
+        }
+      }
+      out[i] = neg ? -val : val;
+    }
+    const uint4 w = make_uint4(pack2(out[0], out[1]), pack2(out[2], out[3]), pack2(out[4], out[5]), pack2(out[6], out[7]));
+    *reinterpret_cast<uint4*>(p.dst[arr] + (mat * NCB * RK + (int64_t)cb * RK + ks) * kChunk + lane * 8) = w;
+  }
+}
+
 hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const int* negate,
                          const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors, int r, int D,
                          int head_dim, hipStream_t st) {
@@ -643,6 +701,12 @@ hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const
     if (tabs[i]) a.tab = *tabs[i];   // at most one distinct rotation per launch
   }
   a.n_arrays = n_arrays; a.n_layers = n_layers; a.n_anchors = n_anchors; a.r = r; a.D = D; a.head_dim = head_dim;
+  const size_t lds = sizeof(uint16_t) * 16 * (size_t)(D + kPackPad);
+  if (lds <= 64 * 1024) {   // rows up to 2040 channels: staged through LDS
+    const int64_t blocks = (int64_t)n_arrays * n_layers * n_anchors * ((r + 15) / 16);
+    pack_b_rows<<<(unsigned)blocks, 256, lds, st>>>(a);
+    return hipGetLastError();
+  }
   const int64_t units = (int64_t)n_arrays * n_layers * n_anchors * (D / 32) * ((r + 15) / 16) * 64;
   int64_t blocks = (units + 255) / 256;
   if (blocks > 1 << 20) blocks = 1 << 20;
