@@ -148,6 +148,15 @@ def test_cosine_mode_mfma_kernels(case, options):
     _check_hop(sp, options=options, label=f"cos-{case}-{options}")
 
 
+@pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
+def test_wide_rows_bf16(mode):
+    # D = 2048: eight channel tiles per token tile, 64 contraction chunks in the second mode, and
+    # the per-column operand packing (rows too wide to stage in LDS)
+    sp = W.llama8b_hop(n_layers=1, seq_len=200, n_kv_heads=16, n_anchors=3, mode=mode,
+                       tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+    _check_hop(sp, label=f"wide-{mode}")
+
+
 def test_odd_shape_bf16_generic_path():
     sp = W.llama8b_hop(n_layers=2, seq_len=70, n_kv_heads=3, head_dim=32, n_anchors=3, rank_base=8,
                        rank_delta=8, true_delta_rank=4)
