@@ -90,11 +90,13 @@ def test_unrelated_layers_flagged_bf16():
     assert list(gpu["flags"]) == [0, 0, 0, O.FLAG_ENTROPY]
 
 
+@pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
 @pytest.mark.parametrize("rank", [16, 64, 128])
-def test_ranks_bf16(rank):
+def test_ranks_bf16(rank, mode):
+    # second mode: rank 16 on the generic scores, ranks 64 / 128 on the per-anchor-group kernel
     sp = W.llama8b_hop(n_layers=2, seq_len=300, n_anchors=6, rank_base=rank, rank_delta=rank,
-                       n_kv_heads=4)
-    _check_hop(sp, label=f"rank{rank}")
+                       n_kv_heads=4, mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+    _check_hop(sp, label=f"rank{rank}-{mode}")
 
 
 def test_rank8_delta_two_pass_bf16():
