@@ -200,6 +200,9 @@ __device__ __forceinline__ void rotate_tile(f32x16 (&z)[2][4], const float* cs, 
         z[tb][db][j] = ox;
         z[tb][du][j] = oy;
       }
+      // four table entries at a time: the compiler would otherwise load all 32 of a block pair
+      // up front, which pushes the apply kernel (168 VGPRs) into spilling
+      if ((j & 3) == 3) asm volatile("" ::: "memory");
     }
   }
 }
@@ -621,7 +624,7 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
     tab[1][i] = p.shift.sn[i];
   }
   const int nc = (t0 < p.s_cov) ? p.n_corr : 0;
-  const Slots sl = load_slots(p.corr, p.n_corr, p.off, p.len, min(S, p.s_cov), lane);
+  Slots sl;   // loaded after the tile's rotation (below), so it holds no registers through it
   const uint16_t* Al = p.Ad[id.side] + id.layer * p.ad_layer;
   const uint16_t* Bl = p.Bd[id.side] + (((int64_t)id.layer * N) * NCB + id.cq * kNCBW) * RKD * kC;
   const float* Wl = p.wa + ((int64_t)id.side * p.n_layers + id.layer) * N * S;
@@ -639,11 +642,16 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
               make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
               t0, wv, lane);
   };
+  // A fragment offsets: the second token block's rows lie 32 rows further with the same
+  // swizzle (the swizzle depends on the row through row / (16 / U) mod U, and 32 rows are a
+  // multiple of 16 / U x U), so they are an immediate offset from the first block's and take
+  // no registers of their own
   uint32_t aoff[2][RKD];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int ks = 0; ks < RKD; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
+  for (int ks = 0; ks < RKD; ++ks) {
+    aoff[0][ks] = RG::a_unit(tw * 64 + col, ks * 2 + hi) * 16;
+    aoff[1][ks] = aoff[0][ks] + 32 * RG::U * 16;
+  }
   const uint32_t boff = RG::A_BYTES + cw * 4 * RKD * 1024 + lane * 16;
   const uint32_t woff = RG::A_BYTES + RG::B_BYTES + (tw * 64 + col) * 4;
   uint16_t* stage = reinterpret_cast<uint16_t*>(ring) + wave * kStage;   // over the ring, before anchor 0
@@ -654,6 +662,11 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   const uint32_t layer_bytes = (uint32_t)S * D * 2;
   load_tile(acc, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, stage, lane, col, hi);
   if (keys && p.shift.active) rotate_tile<HD>(acc, tab[0], tab[1], hi);
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    sl = load_slots(p.corr, p.n_corr, p.off, p.len, min(S, p.s_cov), ln);
+  }
   if (nc > 0) {
     wait_vm_barrier<63>();   // every wave is done with the staging area
     fetch(0);
