@@ -500,10 +500,10 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
       }
     }
   };
+  __syncthreads();   // rotation table (before any transfer: the barrier's fence would wait for them)
   if (nl > 0) {
     f32x16 z[2][4];
-    fetch(0);
-    __syncthreads();   // rotation table
+    fetch(0);   // in flight together with the source tile's loads
     // staging (wave-private) in the ring past slot 0, free until anchor 1 is fetched
     load_tile(z, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, (uint32_t)S * D * 2), tw0, D, d0,
               reinterpret_cast<uint16_t*>(ring + RG::SLOT) + wave * kStage, lane, col, hi);
