@@ -33,6 +33,15 @@ def test_library_exports_every_declared_symbol():
     assert L.kvc_abi_version() == 2
 
 
+def test_trace_kernel_ids_named_by_the_binding():
+    # every kernel id the header defines for the optional trace has a name in the binding, and
+    # the binding names no id the header lacks
+    txt = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    ids = {int(v) for v in re.findall(r"#define KVC_K_[A-Z0-9_]+\s+(\d+)", txt)}
+    assert ids and ids == set(kvc.KERNEL_NAMES)
+    assert len(set(kvc.KERNEL_NAMES.values())) == len(kvc.KERNEL_NAMES)
+
+
 def test_status_strings():
     L = kvc.lib()
     for s in range(10):
