@@ -19,6 +19,8 @@
 
 #include <type_traits>
 
+#include <utility>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -805,13 +807,14 @@ SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
   return w;
 }
 
-// Y [b][rows][l] (fp32) <- orthonormal (or zero) columns spanning it: CholeskyQR2 with dropping.
-// `tmp` receives the intermediate pass.
-hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, int l, hipStream_t st) {
+// Y [b][rows][l] (fp32) <- orthonormal (or zero) columns spanning it: `passes` rounds of
+// CholeskyQR with pivot dropping (two = CholeskyQR2).  Rounds alternate between Y and `tmp`; with
+// an odd number the result is in `tmp` and the caller swaps the two.
+hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, int l, int passes, hipStream_t st) {
   hipError_t e;
   float* src = Y;
   float* dst = tmp;
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
     // G = Y^T Y (fp64)
     if ((e = run_gemm<float, float, double, double, true, false>(src, src, G, l, l, rows, l, l, l, (int64_t)rows * l,
                                                                   (int64_t)rows * l, (int64_t)l * l, b, st)))
@@ -836,7 +839,7 @@ hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, in
     src = dst;
     dst = t;
   }
-  return hipSuccess;   // two passes: the result is back in Y
+  return hipSuccess;
 }
 
 }  // namespace
@@ -871,16 +874,25 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   const int64_t cnt = (int64_t)b * n * l;
   sketch<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(om, cnt, seed);
   if ((e = hipGetLastError())) return e;
-  // Y = Z Omega, orthonormalised
+  // Y = Z Omega, orthonormalised; the bases between power iterations take one CholeskyQR round
+  // (their Gram is formed in fp64, so one round leaves them orthonormal to the fp32 storage
+  // precision, and the next product only needs their span), the final basis Q two
   if ((e = gemm_f32<false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
-  if ((e = orth(y0, y1, G, Li, b, m, l, st))) return e;
+  auto orth_swap = [&](float*& X, float*& Xt, int rows_, int passes) -> hipError_t {
+    hipError_t r = orth(X, Xt, G, Li, b, rows_, l, passes, st);
+    if (passes & 1) std::swap(X, Xt);
+    return r;
+  };
+  float *Y = y0, *Yt = y1, *Wb = w0, *Wt = w1;
+  if ((e = orth_swap(Y, Yt, m, power_iters > 0 ? 1 : 2))) return e;
   for (int it = 0; it < power_iters; ++it) {
     // W = Z^T Y, orthonormalised; Y = Z W, orthonormalised
-    if ((e = gemm_f32<true>(z, y0, w0, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
-    if ((e = orth(w0, w1, G, Li, b, n, l, st))) return e;
-    if ((e = gemm_f32<false>(z, w0, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
-    if ((e = orth(y0, y1, G, Li, b, m, l, st))) return e;
+    if ((e = gemm_f32<true>(z, Y, Wb, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
+    if ((e = orth_swap(Wb, Wt, n, 1))) return e;
+    if ((e = gemm_f32<false>(z, Wb, Y, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+    if ((e = orth_swap(Y, Yt, m, it + 1 < power_iters ? 1 : 2))) return e;
   }
+  y0 = Y;
   // Bsk = Q^T Z (fp64), its Gram Bsk Bsk^T, eigenpairs
   if ((e = run_gemm<float, float, double, double, true, false>(y0, z, bsk, l, n, m, l, n, n, sY, sZ, (int64_t)l * n, b,
                                                                 st)))
