@@ -606,6 +606,20 @@ __global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l,
   }
   for (int e = tid; e < l * l; e += nt) VT[e] = (e / l == e % l) ? 1.0 : 0.0;
   const int nblk = half * (half + 1) / 2;
+  // this thread's rotation-pair blocks (K1, K2), K2 <= K1, decoded once: with 1024 threads and
+  // half <= kJacobiLdsMax / 2, at most 5 per thread
+  constexpr int kMaxBlk = 5;
+  static_assert((kJacobiLdsMax / 2) * (kJacobiLdsMax / 2 + 1) / 2 <= kMaxBlk * 1024, "blocks per thread");
+  int bk1[kMaxBlk], bk2[kMaxBlk];
+#pragma unroll
+  for (int c = 0; c < kMaxBlk; ++c) {
+    const int e = tid + c * nt;
+    int k1 = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+    while (k1 * (k1 + 1) / 2 > e) --k1;
+    while ((k1 + 1) * (k1 + 2) / 2 <= e) ++k1;
+    bk1[c] = e < nblk ? k1 : -1;
+    bk2[c] = e - k1 * (k1 + 1) / 2;
+  }
   __syncthreads();
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
     double off = 0.0, tot = 0.0;
@@ -658,11 +672,10 @@ __global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l,
         sn[tid] = s;
       }
       __syncthreads();
-      for (int e = tid; e < nblk; e += nt) {   // block (K1, K2), K1 <= K2
-        int k1 = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
-        while (k1 * (k1 + 1) / 2 > e) --k1;
-        while ((k1 + 1) * (k1 + 2) / 2 <= e) ++k1;
-        const int k2 = e - k1 * (k1 + 1) / 2;   // k2 <= k1
+#pragma unroll
+      for (int c = 0; c < kMaxBlk; ++c) {   // block (K1, K2), K2 <= K1
+        const int k1 = bk1[c], k2 = bk2[c];
+        if (k1 < 0) continue;
         const int p1 = pp[k1], q1 = qq[k1], p2 = pp[k2], q2 = qq[k2];
         const double c1 = cs[k1], s1 = sn[k1], c2 = cs[k2], s2 = sn[k2];
         if (k1 == k2) {
