@@ -751,47 +751,64 @@ __global__ void __launch_bounds__(256) select_top(const double* E, const double*
 // Component c of matrix b: if the largest-magnitude entry of A[:, c] (first on ties) is
 // negative, negate A[:, c] and B[c, :].  One work-group per (component, matrix).
 template <typename T>
+__device__ __forceinline__ double sign_val(T v) {
+  if constexpr (sizeof(T) == 2) return (double)__builtin_bit_cast(__bf16, (uint16_t)v);
+  else return (double)v;
+}
+template <typename T>
+__device__ __forceinline__ T negated(T v) {
+  if constexpr (sizeof(T) == 2) return (T)(v ^ 0x8000u);
+  else return -v;
+}
+
+// Sign convention: for each column c of A (rows x r, row-major) the entry of largest magnitude
+// (the lowest row among equals) is made positive by negating column c of A and row c of B.
+// A work-group takes 64 columns of one matrix; its threads read rows of those columns (64
+// consecutive entries per row, coalesced), four row phases per column, and the phases are
+// merged by the same rule.
+template <typename T>
 __global__ void __launch_bounds__(256) fix_signs(T* Aout, T* Bout, int rows, int cols, int r) {
-  __shared__ double bv[256];
-  __shared__ int bi[256];
-  const int tid = threadIdx.x, c = blockIdx.x;
+  __shared__ double bv[4][64], sv[4][64];
+  __shared__ int bi[4][64];
+  __shared__ int neg[64];
+  const int tid = threadIdx.x, cl = tid & 63, ph = tid >> 6;
+  const int c = blockIdx.x * 64 + cl;
   Aout += (int64_t)blockIdx.y * rows * r;
   Bout += (int64_t)blockIdx.y * r * cols;
-  double best = -1.0;
+  double best = -1.0, bval = 0.0;
   int bidx = 0;
-  double bval = 0.0;
-  for (int i = tid; i < rows; i += 256) {
-    double x;
-    if constexpr (sizeof(T) == 2) x = (double)__builtin_bit_cast(__bf16, (uint16_t)Aout[(int64_t)i * r + c]);
-    else x = (double)Aout[(int64_t)i * r + c];
-    if (fabs(x) > best) { best = fabs(x); bidx = i; bval = x; }
+  if (c < r) {
+    for (int i = ph; i < rows; i += 4) {
+      const double x = sign_val(Aout[(int64_t)i * r + c]);
+      if (fabs(x) > best) { best = fabs(x); bidx = i; bval = x; }
+    }
   }
-  bv[tid] = best;
-  bi[tid] = bidx;
-  __shared__ double sval[256];
-  sval[tid] = bval;
+  bv[ph][cl] = best;
+  bi[ph][cl] = bidx;
+  sv[ph][cl] = bval;
   __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
-    if (tid < o) {
-      const bool take = bv[tid + o] > bv[tid] || (bv[tid + o] == bv[tid] && bi[tid + o] < bi[tid]);
-      if (take) {
-        bv[tid] = bv[tid + o];
-        bi[tid] = bi[tid + o];
-        sval[tid] = sval[tid + o];
+  if (ph == 0) {
+    for (int q = 1; q < 4; ++q) {
+      if (bv[q][cl] > best || (bv[q][cl] == best && bi[q][cl] < bidx)) {
+        best = bv[q][cl];
+        bidx = bi[q][cl];
+        bval = sv[q][cl];
       }
     }
-    __syncthreads();
+    neg[cl] = c < r && bval < 0.0;
   }
-  if (!(sval[0] < 0.0)) return;
-  for (int i = tid; i < rows; i += 256) {
-    T& x = Aout[(int64_t)i * r + c];
-    if constexpr (sizeof(T) == 2) x = (T)(x ^ 0x8000u);
-    else x = -x;
+  __syncthreads();
+  if (c < r && neg[cl]) {
+    for (int i = ph; i < rows; i += 4) {
+      T& x = Aout[(int64_t)i * r + c];
+      x = negated(x);
+    }
   }
-  for (int j = tid; j < cols; j += 256) {
-    T& x = Bout[(int64_t)c * cols + j];
-    if constexpr (sizeof(T) == 2) x = (T)(x ^ 0x8000u);
-    else x = -x;
+  const int nc = min(64, r - blockIdx.x * 64);
+  for (int k = 0; k < nc; ++k) {
+    if (!neg[k]) continue;
+    T* row = Bout + (int64_t)(blockIdx.x * 64 + k) * cols;
+    for (int j = tid; j < cols; j += 256) row[j] = negated(row[j]);
   }
 }
 
@@ -938,7 +955,7 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
     if ((e = run_gemm<double, double, bf16_bits, double, false, false>(m2, bsk, Bo, r, n, l, l, n, n, (int64_t)r * l,
                                                                         (int64_t)l * n, (int64_t)r * n, b, st)))
       return e;
-    fix_signs<bf16_bits><<<dim3(r, b), 256, 0, st>>>(A, Bo, m, n, r);
+    fix_signs<bf16_bits><<<dim3((r + 63) / 64, b), 256, 0, st>>>(A, Bo, m, n, r);
   } else {
     float* A = static_cast<float*>(a_out);
     float* Bo = static_cast<float*>(b_out);
@@ -948,7 +965,7 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
     if ((e = run_gemm<double, double, float, double, false, false>(m2, bsk, Bo, r, n, l, l, n, n, (int64_t)r * l,
                                                                     (int64_t)l * n, (int64_t)r * n, b, st)))
       return e;
-    fix_signs<float><<<dim3(r, b), 256, 0, st>>>(A, Bo, m, n, r);
+    fix_signs<float><<<dim3((r + 63) / 64, b), 256, 0, st>>>(A, Bo, m, n, r);
   }
   return hipGetLastError();
 }
