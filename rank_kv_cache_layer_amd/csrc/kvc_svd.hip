@@ -149,10 +149,11 @@ __device__ __forceinline__ void load4(const T* p, int k, int K, double (&x)[4]) 
 template <typename TA, typename TB, typename TC, bool TRA, bool TRB>
 __global__ void __launch_bounds__(256) gemm_f64(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ C,
                                                 int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA,
-                                                int64_t sB, int64_t sC) {
+                                                int64_t sB, int64_t sC, int lower) {
   __shared__ double red[3][16][64];   // partial tiles of waves 1..3
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
   const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  if (lower && j0 >= i0 + 32) return;   // tile strictly above the diagonal of a Gram nobody reads
   A += (int64_t)blockIdx.z * sA;
   B += (int64_t)blockIdx.z * sB;
   C += (int64_t)blockIdx.z * sC;
@@ -220,12 +221,15 @@ __global__ void __launch_bounds__(256) gemm_f64(const TA* __restrict__ A, const 
       }
 }
 
+// lower_only: C is a symmetric Gram whose consumers read only its lower triangle (fp64 path):
+// tiles strictly above the diagonal are skipped
 template <typename TA, typename TB, typename TC, typename ACC, bool TRA, bool TRB>
 hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
-                    int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st) {
+                    int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st, bool lower_only = false) {
   if constexpr (std::is_same<ACC, double>::value) {
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32), (unsigned)batch);
-    gemm_f64<TA, TB, TC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+    gemm_f64<TA, TB, TC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC,
+                                                         lower_only ? 1 : 0);
   } else {
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
     gemm<TA, TB, TC, ACC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
@@ -846,8 +850,9 @@ hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, in
   float* dst = tmp;
   for (int pass = 0; pass < passes; ++pass) {
     // G = Y^T Y (fp64)
+    // both Cholesky kernels read only the lower triangle of G
     if ((e = run_gemm<float, float, double, double, true, false>(src, src, G, l, l, rows, l, l, l, (int64_t)rows * l,
-                                                                  (int64_t)rows * l, (int64_t)l * l, b, st)))
+                                                                  (int64_t)rows * l, (int64_t)l * l, b, st, true)))
       return e;
     const double tolr = pass == 0 ? 1e-12 : 1e-10;
     const size_t tri_bytes = sizeof(double) * (size_t)l * (l + 1) / 2;
@@ -927,12 +932,13 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   if ((e = run_gemm<float, float, double, double, true, false>(y0, z, bsk, l, n, m, l, n, n, sY, sZ, (int64_t)l * n, b,
                                                                 st)))
     return e;
-  if ((e = run_gemm<double, double, double, double, false, true>(bsk, bsk, g2, l, l, n, n, n, l, (int64_t)l * n,
-                                                                  (int64_t)l * n, sLL, b, st)))
-    return e;
   const int lp = (l + 1) & ~1;
   const size_t tri_bytes = sizeof(double) * (size_t)lp * (lp + 1) / 2;
   const bool in_lds = lp <= kJacobiLdsMax;
+  // the LDS eigensolver reads only the lower triangle of the Gram; the global one all of it
+  if ((e = run_gemm<double, double, double, double, false, true>(bsk, bsk, g2, l, l, n, n, n, l, (int64_t)l * n,
+                                                                  (int64_t)l * n, sLL, b, st, in_lds)))
+    return e;
   if (in_lds) {
     if (tri_bytes > 64 * 1024 &&
         (e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_lds), hipFuncAttributeMaxDynamicSharedMemorySize,
