@@ -230,6 +230,30 @@ def measure_pool_insert(kvc, torch, L=32, S=4096, H=8, hd=128, r=32, V=20, p=16,
     return out
 
 
+def measure_rank128(kvc, torch, W, steps=5):
+    """Rank-128 correction (32 layers x 4096 tokens x 8x128 bf16, 10 anchors at rank 128 for base
+    and delta), both scoring modes, through the library's default path for that rank."""
+    sp = W.llama8b_rank128()
+    data = W.make_hop(sp)
+    k, v = data.k_src.to("cuda"), data.v_src.to("cuda")
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    pool = kvc.pool_from(data, "cuda")
+    shp = kvc.shape_of(sp.n_layers, sp.seq_len, sp.n_kv_heads, sp.head_dim)
+    L, S, D, N, r = sp.n_layers, sp.seq_len, sp.d_model, sp.n_anchors, sp.rank_base
+    flops = 4 * L * S * D * N * (r + sp.rank_delta)
+    nbytes = 2 * L * S * D * (2 + 2) + 2 * L * N * (r + sp.rank_delta) * (S + D) * 2
+    out = {"workload": f"{L} layers x {S} tokens x {sp.n_kv_heads}x{sp.head_dim} bf16, {N} anchors at rank {r}",
+           "mfma_flops": flops, "algorithmic_bytes": nbytes}
+    for name, mode in (("pages", W.SCORE_PAGES), ("cos_r", W.SCORE_COS_R)):
+        prm_fn = lambda tr, m=mode: kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, m, 0, tr)
+        ws = torch.empty((kvc.correct_hop_workspace(shp, pool, prm_fn(None)),), dtype=torch.uint8, device="cuda")
+        ms, _, per_kernel, _ = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn, ws, steps, 2)
+        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(S / (ms / 1e3), 1),
+                     "mfma_frac": round(flops / (ms / 1e3) / PEAK_MFMA_BF16, 4),
+                     "kernels_ms": {n: round(statistics.median(t), 4) for n, t in per_kernel.items()}}
+    return out
+
+
 def measure_pf_delta(kvc, torch, L=32, S=32768, H=8, hd=128, r=8, reps=10):
     """App. A.2: a recurring relation's correction, profiled once and stored at rank 8, reused
     with weight 1 and re-alignment and no matching (kvc_apply_lowrank_delta with one anchor),
@@ -526,7 +550,7 @@ def main():
                   "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
         log(f"[bench] second mode {second['mode']}: {ms2:.3f} ms/hop")
 
-    refresh = chain = pool_ins = pf = study_out = None
+    refresh = chain = pool_ins = pf = study_out = r128 = None
     if not args.no_extra:
         log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
         refresh = measure_refresh(kvc, torch, oracle=not args.no_cpu_baseline)
@@ -538,6 +562,9 @@ def main():
         log(f"[bench] chain: {chain['ms']} ms, {chain['tokens_per_s']} tokens/s")
         log("[bench] preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens) ...")
         pf = measure_pf_delta(kvc, torch)
+        log("[bench] rank-128 correction (32 layers x 4096 tokens, 10 anchors) ...")
+        r128 = measure_rank128(kvc, torch, W)
+        log(f"[bench] rank 128: pages {r128['pages']['ms']} ms, cos_r {r128['cos_r']['ms']} ms")
         log(f"[bench] pf delta: {pf['ms']} ms, {pf['achieved_GBps']} GB/s")
         log("[bench] chained vs non-chained correction error along A0 -> A3 (8 layers x 4096 x 1024) ...")
         study_out = measure_study(torch)
@@ -562,7 +589,7 @@ def main():
                    "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
         "roofline": dominant, "cpu_baseline": cpu,
         "hop": hop, "protocol": protocol, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
-        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf, "chain_study": study_out,
+        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf, "rank128_hop": r128, "chain_study": study_out,
         "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
     }
     print(json.dumps(out), flush=True)
