@@ -218,9 +218,9 @@ bool cos_gemm_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
   return (uint64_t)sh.seq_len * D * 2 < (1ull << 31);
 }
 
-// The two-pass bf16 path: 128-token x 256-channel work-groups (D a multiple of 256), ranks
-// 16/32 (larger ranks would not fit the register budget; the apply also takes rank 8, padded
-// to the MFMA's 16 on chip), within the LDS budget.
+// The two-pass bf16 path: 128-token x 256-channel work-groups (D a multiple of 256), scoring
+// ranks 16/32 (larger ranks would not fit the register budget), apply ranks 8 (padded to the
+// MFMA's 16 on chip), 16, 32 and 64/128/256 (as slices of 32), within the LDS budget.
 constexpr size_t kLdsBudget = 160 * 1024;
 bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, bool pages_scores, bool apply) {
   if (p.dtype != KVC_BF16 || (prm.options & 3)) return false;
@@ -231,7 +231,8 @@ bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, boo
     if (split_score_lds(p.rank_base) + 8 * 1024 > kLdsBudget) return false;
   }
   if (apply) {
-    if (p.rank_delta != 8 && p.rank_delta != 16 && p.rank_delta != 32) return false;
+    const int rd = p.rank_delta;
+    if (rd != 8 && rd != 16 && rd != 32 && split_apply_slices(rd) == 1) return false;
     if (split_apply_lds(p.rank_delta) + 2 * 1024 > kLdsBudget) return false;
   }
   return true;
@@ -243,6 +244,7 @@ struct Plan {
   bool split_apply = false;   // apply in the two-pass path
   bool fused_match = false;   // PAGES scores inside the fused kernel
   bool fused_apply = false;   // apply inside the fused kernel
+  bool fused_split = false;   // PAGES scores in the fused kernel, weights through the workspace to the two-pass apply
   bool cos_mfma = false;
   bool cos_gemm = false;        // second-mode scores as one GEMM per layer-side
   size_t off_pack_cos = 0;
@@ -275,11 +277,19 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
     pl.s_work = s.n_gate ? std::max(s.s_cov, s.k) : s.s_cov;
     pl.split_match = pages && split_ok(sh, p, P, true, do_apply);
     if (pl.split_match && do_apply && !pl.split_apply) pl.split_match = false;
-    if (do_apply && pages && !pl.split_match && pl.split_apply) {   // keep the pair on one path
-      pl.split_apply = false;
-      pl.fused_apply = fused_ok(sh, p, P, false, true);
+    if (do_apply && pages && !pl.split_match && pl.split_apply) {
+      // scores from the fused kernel: the two-pass apply only where it takes the rank in slices
+      // (at ranks 64 and up the fused apply is the slower half); otherwise the pair stays on
+      // the fused kernel
+      if (split_apply_slices(p.rank_delta) > 1 && fused_ok(sh, p, P, true, false)) {
+        pl.fused_split = true;
+      } else {
+        pl.split_apply = false;
+        pl.fused_apply = fused_ok(sh, p, P, false, true);
+      }
     }
-    pl.fused_match = !pl.split_match && pages && fused_ok(sh, p, P, true, false) && (!do_apply || pl.fused_apply);
+    pl.fused_match = !pl.split_match && pages && fused_ok(sh, p, P, true, false) &&
+                     (!do_apply || pl.fused_apply || pl.fused_split);
     if (pl.split_match) {
       const int ntt = (S + kScoreTile - 1) / kScoreTile, nct = D / kSplitWidth;
       pl.tile = kScoreTile;
@@ -289,6 +299,10 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
     } else if (pl.fused_match) {
       pl.tile = kFusedTile;
       pl.n_tiles = (S + kFusedTile - 1) / kFusedTile;
+      if (pl.fused_split) {
+        pl.off_w = off;
+        off += up256(sizeof(float) * 2 * (size_t)L * S * N);
+      }
     } else {
       pl.cos_gemm = !pages && cos_gemm_ok(sh, p, P);
       pl.cos_mfma = !pages && !pl.cos_gemm && cos_mfma_ok(sh, p, P);
@@ -378,8 +392,12 @@ kvc_status fused_tab(FusedTab& ft, int64_t dp, int head_dim, const kvc_rope* rop
 }
 
 // Packs B factors of both sides into MFMA operand chunks.
+// slices > 1: each anchor's r x D factor packs as `slices` matrices of r / slices rows (the
+// rows of one slice are contiguous, so the factor array is read as slices x n_anchors matrices);
+// the packed size is the same.
 kvc_status pack_pair(const void* bk, const void* bv, uint16_t* dst, int r, int negate, const FusedTab* key_tab,
-                     const kvc_shape& sh, const kvc_pool& p, Tracer& tr, int trace_id, hipStream_t st) {
+                     const kvc_shape& sh, const kvc_pool& p, Tracer& tr, int trace_id, hipStream_t st,
+                     int slices = 1) {
   if (p.n_anchors == 0) return KVC_OK;
   const size_t per = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(r);
   const uint16_t* src[2] = {(const uint16_t*)bk, (const uint16_t*)bv};
@@ -387,7 +405,8 @@ kvc_status pack_pair(const void* bk, const void* bv, uint16_t* dst, int r, int n
   const int neg[2] = {negate, negate};
   const FusedTab* tabs[2] = {key_tab, nullptr};
   tr.begin(trace_id);
-  hipError_t e = launch_pack_b(src, dsts, neg, tabs, 2, sh.n_layers, p.n_anchors, r, D_of(sh), sh.head_dim, st);
+  hipError_t e = launch_pack_b(src, dsts, neg, tabs, 2, sh.n_layers, p.n_anchors * slices, r / slices, D_of(sh),
+                               sh.head_dim, st);
   tr.end();
   if (e != hipSuccess) return hip_fail(e, "pack factors");
   return KVC_OK;
@@ -467,7 +486,8 @@ kvc_status split_apply_fields(SplitArgs& f, void* k_out, void* v_out, const kvc_
   kvc_status r;
   if ((r = fused_tab(tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return r;
   uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
-  if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st)) != KVC_OK)
+  if ((r = pack_pair(p.deltaB_k, p.deltaB_v, pd, p.rank_delta, 0, &tgt, sh, p, tr, KVC_K_PACK_DELTA, st,
+                     split_apply_slices(p.rank_delta))) != KVC_OK)
     return r;
   const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D_of(sh) * rpad16(p.rank_delta);
   f.out[0] = (uint16_t*)k_out; f.out[1] = (uint16_t*)v_out;
@@ -663,7 +683,12 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
     f.Bb[0] = pb; f.Bb[1] = pb + per_b;
     f.w_out[0] = out->w_k; f.w_out[1] = out->w_v;
     f.partials = partials;
-    if (apply) {
+    const size_t plane = (size_t)sh.n_layers * sh.seq_len * std::max(p.n_anchors, 1);
+    float* wts = reinterpret_cast<float*>(ws + pl.off_w);
+    if (apply && pl.fused_split) {   // token weights to the workspace; the caller's copy comes from the apply's pass
+      f.w_out[0] = wts;
+      f.w_out[1] = wts + plane;
+    } else if (apply) {
       FusedTab tgt;
       if ((r = fused_tab(tgt, p_tgt, sh.head_dim, rope)) != KVC_OK) return r;
       uint16_t* pd = reinterpret_cast<uint16_t*>(ws + pl.off_pack_delta);
@@ -680,6 +705,15 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
     tr.end();
     if (e != hipSuccess) return hip_fail(e, "fused kernel");
     if ((r = run_gate(sh, p, prm, s, partials, reinterpret_cast<double*>(ws + pl.off_gsum), pl.n_tiles, out, pred_flags, tr, st)) != KVC_OK) return r;
+    if (apply && pl.fused_split) {
+      SplitArgs g;
+      if ((r = split_args(g, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;
+      if ((r = split_apply_fields(g, k_out, v_out, sh, p_tgt, rope, p, ws, pl, tr, st)) != KVC_OK) return r;
+      g.w_in[0] = wts; g.w_in[1] = wts + plane;
+      g.w_out[0] = out->w_k; g.w_out[1] = out->w_v;
+      if ((r = run_split_weights(g, SPLIT_W_GIVEN, ws, pl, tr, st)) != KVC_OK) return r;
+      if ((r = run_split_apply(g, sh, tr, st)) != KVC_OK) return r;
+    }
     if (out->s_cov) *out->s_cov = s.s_cov;
     return KVC_OK;
   }

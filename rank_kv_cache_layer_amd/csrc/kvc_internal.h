@@ -244,6 +244,9 @@ hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st);
 hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st);
 size_t split_score_lds(int r_b);                   // dynamic LDS bytes
 size_t split_apply_lds(int r_d);
+// rank slices of 32 the apply takes per anchor: ranks 64, 128 and 256 run as 2, 4 and 8 slices
+// (their packed delta B is then one matrix per slice); ranks 8, 16 and 32 in one step
+inline int split_apply_slices(int r_d) { return r_d == 64 ? 2 : r_d == 128 ? 4 : r_d == 256 ? 8 : 1; }
 
 // SVD refresh
 hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank, void* a_out,

@@ -363,11 +363,12 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // Slot layout for rank 16 RK, TT tokens, NW waves: A rows (TT x R bf16, 16-byte units
 // swizzled so the fragment reads of 16 consecutive rows hit distinct banks), the B slice
 // (kNCBW x RK packed 1 KiB chunks), the TT token weights (fp32, apply only).  RA = the rank
-// of the A rows in memory (<= R): the units of an LDS row past it are filled with zeros.
-template <int RK, int TT, int NW, bool W, int RA = RK * 16>
+// of the A rows taken (<= R): the units of an LDS row past it are filled with zeros; RS = the
+// A rows' stride in memory (elements, >= RA: a slice of the columns of wider rows).
+template <int RK, int TT, int NW, bool W, int RA = RK * 16, int RS = RA>
 struct Ring {
   static constexpr int R = RK * 16;
-  static_assert(RA % 8 == 0 && RA <= R, "A row rank");
+  static_assert(RA % 8 == 0 && RA <= R && RS >= RA && RS % 8 == 0, "A row rank");
   static constexpr int U = R / 8;                       // 16-byte units per A row
   static constexpr int A_BYTES = TT * R * 2;
   static constexpr int B_BYTES = kNCBW * RK * 1024;
@@ -394,7 +395,7 @@ struct Ring {
       const int row = u / U, cpos = u % U;
       const int c = cpos ^ ((row / (16 / U)) & (U - 1));     // global unit stored there
       // units past the stored rank read out of range: the transfer writes zeros there
-      const uint32_t voff = c * 8 < RA ? (uint32_t)(((t0 + row) * RA + c * 8) * 2) : 0x80000000u;
+      const uint32_t voff = c * 8 < RA ? (uint32_t)(((t0 + row) * RS + c * 8) * 2) : 0x80000000u;
       dma16(Ar, slot + (wave * A_PER_WAVE + i) * 1024, voff);
     }
 #pragma unroll
@@ -604,10 +605,15 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
 // Three work-groups share a CU (at most 168 VGPRs per lane, a two-slot ring of ~49 KB): the
 // extra waves cover the tile's load and store phases and the operand waits, which pays more
 // than a third slot or operands held in registers across a step.
-template <int HD, int RKD, int RA>
+// NS > 1: a delta of rank NS x RA runs as NS steps of rank RA per anchor (the contraction over
+// the rank splits into column slices of A and row slices of B): step j takes slice j % NS of
+// correction anchor j / NS, the same ring slot size as rank RA.  The packed B operand then holds
+// each slice as its own matrix (rows RA k .. RA k + RA - 1 of anchor a at index a NS + k).
+template <int HD, int RKD, int RA, int NS = 1>
 __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
-  using RG = Ring<RKD, kST, kNW, true, RA>;
+  constexpr int RS = RA * NS;   // stored rank of the A rows
+  using RG = Ring<RKD, kST, kNW, true, RA, RS>;
   extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
   __shared__ float tab[2][kFusedHalf];
 
@@ -623,10 +629,10 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
     tab[0][i] = p.shift.cs[i];
     tab[1][i] = p.shift.sn[i];
   }
-  const int nc = (t0 < p.s_cov) ? p.n_corr : 0;
+  const int nc = (t0 < p.s_cov) ? p.n_corr * NS : 0;   // steps
   Slots sl;   // loaded after the tile's rotation (below), so it holds no registers through it
   const uint16_t* Al = p.Ad[id.side] + id.layer * p.ad_layer;
-  const uint16_t* Bl = p.Bd[id.side] + (((int64_t)id.layer * N) * NCB + id.cq * kNCBW) * RKD * kC;
+  const uint16_t* Bl = p.Bd[id.side] + (((int64_t)id.layer * N * NS) * NCB + id.cq * kNCBW) * RKD * kC;
   const float* Wl = p.wa + ((int64_t)id.side * p.n_layers + id.layer) * N * S;
   const int64_t bstride = (int64_t)NCB * RKD * kC;
   // zero-size descriptors past the correction set (see split_score)
@@ -634,13 +640,16 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   const int wv = uni(wave);
   auto fetch = [&](int j) {
     const bool live = j < nc;
-    const int js = live ? j : 0;
+    const int js = live ? j / NS : 0, ks = live ? j % NS : 0;   // anchor, rank slice
     const int a = lane_get(sl.a, js);
     const int lim = live ? lane_get(sl.lim, js) : 0;
+    // the slice's rows end RA (NS - 1 - ks) elements before the stored rows do (a live anchor
+    // has lim >= 1 rows, so this is positive; past the list lim = ks = 0)
+    const int a_elems = lim * RS - ks * RA;
     RG::fetch(ring0 + (uint32_t)(j % kApplySlots) * RG::SLOT,
-              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * RA, (uint32_t)lim * RA * 2),
-              make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4),
-              t0, wv, lane);
+              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * RS + ks * RA, (uint32_t)a_elems * 2),
+              make_rsrc(Bl + (a * NS + ks) * bstride, live ? RG::B_BYTES : 0),
+              make_rsrc(Wl + (int64_t)a * S, (uint32_t)lim * 4), t0, wv, lane);
   };
   // A fragment offsets: the second token block's rows lie 32 rows further with the same
   // swizzle (the swizzle depends on the row through row / (16 / U) mod U, and 32 rows are a
@@ -725,6 +734,9 @@ hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
     case 8: return go(split_apply<HD, 1, 8>, a, kApplyTile, kApplyThreads, lds, st);
     case 16: return go(split_apply<HD, 1, 16>, a, kApplyTile, kApplyThreads, lds, st);
     case 32: return go(split_apply<HD, 2, 32>, a, kApplyTile, kApplyThreads, lds, st);
+    case 64: return go(split_apply<HD, 2, 32, 2>, a, kApplyTile, kApplyThreads, lds, st);
+    case 128: return go(split_apply<HD, 2, 32, 4>, a, kApplyTile, kApplyThreads, lds, st);
+    case 256: return go(split_apply<HD, 2, 32, 8>, a, kApplyTile, kApplyThreads, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -740,7 +752,7 @@ size_t split_score_lds(int r_b) {
 }
 
 size_t split_apply_lds(int r_d) {
-  const int rp = (r_d + 15) & ~15;   // on chip the rank is padded to 16
+  const int rp = split_apply_slices(r_d) > 1 ? 32 : (r_d + 15) & ~15;   // on chip: padded to 16, or slices of 32
   const size_t slot = (size_t)kApplyTile * rp * 2 + (size_t)kNCBW * (rp / 16) * 1024 + (size_t)kApplyTile * 4;
   return std::max((size_t)kApplySlots * slot, sizeof(uint16_t) * (kApplyThreads / 64) * kStage);
 }

@@ -93,10 +93,44 @@ def test_unrelated_layers_flagged_bf16():
 @pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
 @pytest.mark.parametrize("rank", [16, 64, 128])
 def test_ranks_bf16(rank, mode):
-    # second mode: rank 16 on the generic scores, ranks 64 / 128 on the per-anchor-group kernel
+    # second mode: rank 16 on the generic scores, ranks 64 / 128 on the per-anchor-group kernel;
+    # ranks 64 / 128: the delta goes through the two-pass apply in rank slices of 32 (first mode:
+    # scores and weights from the fused kernel)
     sp = W.llama8b_hop(n_layers=2, seq_len=300, n_anchors=6, rank_base=rank, rank_delta=rank,
                        n_kv_heads=4, mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
     _check_hop(sp, label=f"rank{rank}-{mode}")
+
+
+@pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
+def test_rank_sliced_delta_ragged_bf16(mode):
+    # a rank-128 delta in four slices of 32 behind rank-32 scores, anchors of unequal length (the
+    # covered prefix ends inside the second token tile; a slice's A rows past an anchor's length
+    # read as zeros), a ragged tail tile
+    sp = W.llama8b_hop(n_layers=2, seq_len=333, n_anchors=5, rank_base=32, rank_delta=128, n_kv_heads=2,
+                       anchor_len=[333, 250, 180, 333, 201], mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+    _check_hop(sp, label=f"rank-delta-128-ragged-{mode}")
+
+
+def test_rank256_delta_two_pass_bf16():
+    # rank-256 deltas: eight slices per anchor through the two-pass apply, rank-16 two-pass scores
+    sp = W.llama8b_hop(n_layers=2, seq_len=260, n_anchors=3, rank_base=16, rank_delta=256, n_kv_heads=2)
+    _check_hop(sp, label="rank-delta-256")
+
+
+def test_apply_rank128_given_weights_matches_correct_hop():
+    # the explicit apply at rank 128 (slices) with the weights the match returned reproduces the
+    # corrected hop bit for bit (same kernels, same operands)
+    sp = W.llama8b_hop(n_layers=2, seq_len=260, n_kv_heads=2, n_anchors=4, rank_base=128, rank_delta=128)
+    print(f"[parity] apply-r128 L=2 S=260 D={sp.d_model}", flush=True)
+    data = make(sp)
+    full = run_gpu(data)
+    k, v = data.k_src.to(DEV), data.v_src.to(DEV)
+    pool = kvc.pool_from(data, DEV)
+    m = kvc.match_anchors(k, v, shape(sp), sp.p_src, pool, params(sp))
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    kvc.apply_lowrank_delta(k, v, ko, vo, shape(sp), sp.p_src, sp.p_tgt, pool, m.w_k, m.w_v, m.s_cov)
+    torch.cuda.synchronize()
+    assert torch.equal(ko, full["raw_k"]) and torch.equal(vo, full["raw_v"])
 
 
 def test_rank8_delta_two_pass_bf16():
