@@ -89,7 +89,7 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t off) {
 // b'_{c+h} = b_{c+h} cs - b_c sn.  One thread per (side, layer, u, k) row and 8 rotary pairs:
 // 16-byte loads of the 8 lower and the 8 upper channels, 16-byte stores of each.
 __global__ void __launch_bounds__(256) pack_cos(CosGemmArgs p, uint16_t* __restrict__ dst) {
-  const int D = p.D, h = p.head_dim / 2, r = 32;
+  const int D = p.D, h = p.head_dim / 2, r = p.r;
   const int per_row = D / 16;   // groups of 8 pairs
   const int64_t rows = (int64_t)2 * p.n_layers * p.n_use * r;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -132,7 +132,98 @@ __global__ void __launch_bounds__(256) pack_cos(CosGemmArgs p, uint16_t* __restr
   *reinterpret_cast<uint4*>(o + (((int64_t)(du / kKc) * p.n_use + u) * r + k) * kKc + du % kKc) = yv;
 }
 
+// Cosines at rank 32 NS from slice sums (NS > 1).  Each wave forms, per token of its 64 and per
+// column group of its five, the slice's sums <P, A>, |P|^2, |A|^2 and stores them in LDS
+// (red[tw][group][3][64], 30 KiB over the ring, free once every transfer has drained); after a
+// barrier, wave (tw, ag) finishes anchors ag, ag + 4, ... of the pass for its 64 tokens: the
+// sums over the slices, the cosine, and the value-side gate sums of its 64-token tile.  Ends
+// with a barrier, so the next pass may refill the ring.
+template <int NS>
+__device__ __forceinline__ void slice_cosines(const CosGemmArgs& p, const f32x16 (&acc)[kAnch][2], float* red,
+                                              int u0, int np, int side, int layer, int tt, int t0, int tw, int ag,
+                                              int lane, int col, int hi) {
+  constexpr int R = 32 * NS;
+  const int S = p.S;
+#pragma unroll
+  for (int x = 0; x < kAnch; ++x) {
+    const int qp = ag * kAnch + x;   // column group within the pass
+    if (qp >= np) break;
+    const int q = u0 + qp, a = p.use[q / NS], sl = q % NS;
+    const int alen = p.len[a];
+    const uint16_t* Aa = p.A[side] + layer * p.a_layer_stride + (int64_t)p.off[a] * R + sl * 32;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = t0 + tw * 64 + tb * 32 + col;
+      const bool ok = t < alen && t < S;
+      float num = 0.f, pp = 0.f, aa = 0.f;
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        uint2 av = make_uint2(0, 0);
+        if (ok) av = *reinterpret_cast<const uint2*>(Aa + (int64_t)t * R + 8 * jg + 4 * hi);
+        const float a4[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
+                             __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = acc[x][tb][4 * jg + i];
+          num = fmaf(pv, a4[i], num);
+          pp = fmaf(pv, pv, pp);
+          aa = fmaf(a4[i], a4[i], aa);
+        }
+      }
+      num += __shfl_xor(num, 32);
+      pp += __shfl_xor(pp, 32);
+      aa += __shfl_xor(aa, 32);
+      if (hi == 0) {
+        float* o = red + ((tw * kPass + qp) * 3) * 64 + tb * 32 + col;
+        o[0] = num;
+        o[64] = pp;
+        o[128] = aa;
+      }
+    }
+  }
+  __syncthreads();
+  const int t = t0 + tw * 64 + lane;
+  const int tile = tt * (kTok / kCosTile) + tw;
+  for (int ap = ag; ap < np / NS; ap += 4) {
+    const int a = p.use[u0 / NS + ap];
+    float num = 0.f, pp = 0.f, aa = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const float* o = red + ((tw * kPass + ap * NS + sl) * 3) * 64 + lane;
+      num += o[0];
+      pp += o[64];
+      aa += o[128];
+    }
+    const float den = sqrtf(pp) * sqrtf(aa);
+    const float cval = den > 0.f ? num / den : 0.f;
+    if (t < S && tile < p.n_tiles) p.scores[(((int64_t)side * p.n_layers + layer) * S + t) * p.N + a] = cval;
+    if (side == 1 && ((p.mask_gate >> a) & 1) && tile < p.n_tiles) {
+      const float qm = (t < p.len[a] && t < S && t < p.k_gate) ? 1.f : 0.f;
+      float gnum = num * qm, gpp = pp * qm, gaa = aa * qm;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        gnum += __shfl_xor(gnum, o);
+        gpp += __shfl_xor(gpp, o);
+        gaa += __shfl_xor(gaa, o);
+      }
+      if (lane == 0) {
+        const int64_t plane = (int64_t)p.n_layers * p.n_tiles * p.N;
+        const int64_t o = ((int64_t)layer * p.n_tiles + tile) * p.N + a;
+        p.partials[o] = gnum;
+        p.partials[plane + o] = gpp;
+        p.partials[2 * plane + o] = gaa;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // --------------------------------------------------------------------- the GEMM and cosines
+// NS = rank / 32: GEMM column group q = u NS + s is slice s (rows 32 s .. 32 s + 31 of B',
+// columns of A) of scored anchor u; the packed rows [u][r] are the same memory as [u NS + s][32].
+// At NS > 1 the cosine's three sums are formed per slice, summed over the slices through LDS
+// (the slices of one anchor sit in different waves), then finished per (token, anchor).
+template <int NS>
 __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char ring[];   // kRing x kSlot
   const int nwg = (p.n_tiles * kCosTile + kTok - 1) / kTok;   // token range of the scored tiles
@@ -143,13 +234,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int tw = wave >> 2, ag = wave & 3;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int D = p.D, S = p.S, nkc = D / kKc, r = 32;
+  const int D = p.D, S = p.S, nkc = D / kKc, r = 32, R = 32 * NS;
+  const int nq = p.n_use * NS;   // GEMM column groups of 32
   const int t0 = tt * kTok;
   const uint32_t ring0 = lds_off(ring);
 
   const uint16_t* zl = p.z[side] + (int64_t)layer * S * D;
   const rsrc_t zr = make_rsrc(zl, (uint32_t)S * D * 2);
-  const uint16_t* bside = p.packed + (((int64_t)side * p.n_layers + layer) * nkc) * p.n_use * r * kKc;
+  const uint16_t* bside = p.packed + (((int64_t)side * p.n_layers + layer) * nkc) * nq * r * kKc;
 
   // fragment offsets inside a slot: token rows (operand B) and rank rows (operand A)
   uint32_t zoff[2][2], boff[kAnch][2];
@@ -162,8 +254,9 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) boff[x][s] = kZBytes + unit_of((ag * kAnch + x) * 32 + col, s * 2 + hi) * 16;
 
-  for (int u0 = 0; u0 < p.n_use; u0 += kPass) {
-    const int np = min(kPass, p.n_use - u0);
+  static_assert(kPass % NS == 0, "a pass holds whole anchors");
+  for (int u0 = 0; u0 < nq; u0 += kPass) {
+    const int np = min(kPass, nq - u0);
     // chunk kc of this pass into slot kc % kRing; past the last chunk the descriptors have
     // size 0 (zeros written, nothing fetched), so every step issues the same transfers
     auto fetch = [&](int kc) {
@@ -177,7 +270,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
         dma16(zs, slot + (uint32_t)(wv * kZDma + i) * 1024,
               (uint32_t)(((int64_t)(t0 + row) * D + kc * kKc + c * 8) * 2));
       }
-      const uint16_t* bc = bside + ((int64_t)(live ? kc : 0) * p.n_use + u0) * r * kKc;
+      const uint16_t* bc = bside + ((int64_t)(live ? kc : 0) * nq + u0) * r * kKc;
       const rsrc_t bs = make_rsrc(bc, live ? (uint32_t)np * r * kRowB : 0u);
 #pragma unroll
       for (int i = 0; i < kBDma; ++i) {
@@ -214,6 +307,10 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
       }
     }
     wait_vm_barrier<0>();   // trailing (empty) transfers drained; every wave past the last chunk
+    if constexpr (NS > 1) {
+      slice_cosines<NS>(p, acc, reinterpret_cast<float*>(ring), u0, np, side, layer, tt, t0, tw, ag, lane, col, hi);
+      continue;
+    }
 
     // cosines of P with A per token, and the value-side gate sums over the prefix
 #pragma unroll
@@ -279,12 +376,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
 
 size_t cos_gemm_lds() { return (size_t)kRing * kSlot; }
 
-size_t cos_gemm_packed_elems(int n_layers, int n_use, int D) { return (size_t)2 * n_layers * n_use * 32 * D; }
+size_t cos_gemm_packed_elems(int n_layers, int n_use, int r, int D) { return (size_t)2 * n_layers * n_use * r * D; }
 
 hipError_t launch_pack_cos(const CosGemmArgs& a, uint16_t* dst, hipStream_t st) {
   if (a.n_use < 1) return hipSuccess;
-  if (a.head_dim % 16) return hipErrorInvalidValue;
-  const int64_t n = (int64_t)2 * a.n_layers * a.n_use * 32 * (a.D / 16);
+  if (a.head_dim % 16 || (a.r != 32 && a.r != 64 && a.r != 128)) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)2 * a.n_layers * a.n_use * a.r * (a.D / 16);
   pack_cos<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(a, dst);
   return hipGetLastError();
 }
@@ -292,13 +389,19 @@ hipError_t launch_pack_cos(const CosGemmArgs& a, uint16_t* dst, hipStream_t st) 
 hipError_t launch_score_cos_gemm(const CosGemmArgs& a, hipStream_t st) {
   if (a.n_use < 1) return hipSuccess;
   if (a.D % kKc || (a.head_dim != 64 && a.head_dim != 128)) return hipErrorInvalidValue;
+  const void* k = a.r == 32    ? reinterpret_cast<const void*>(score_cos_gemm<1>)
+                  : a.r == 64  ? reinterpret_cast<const void*>(score_cos_gemm<2>)
+                  : a.r == 128 ? reinterpret_cast<const void*>(score_cos_gemm<4>)
+                               : nullptr;
+  if (!k) return hipErrorInvalidValue;
   const size_t lds = cos_gemm_lds();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(score_cos_gemm),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t nblk = (int64_t)((a.n_tiles * kCosTile + kTok - 1) / kTok) * a.n_layers * 2;
   if (nblk == 0) return hipSuccess;
-  score_cos_gemm<<<dim3((unsigned)nblk), kThreads, lds, st>>>(a);
+  if (a.r == 32) score_cos_gemm<1><<<dim3((unsigned)nblk), kThreads, lds, st>>>(a);
+  else if (a.r == 64) score_cos_gemm<2><<<dim3((unsigned)nblk), kThreads, lds, st>>>(a);
+  else score_cos_gemm<4><<<dim3((unsigned)nblk), kThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 

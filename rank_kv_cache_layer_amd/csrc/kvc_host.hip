@@ -209,10 +209,12 @@ bool cos_mfma_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
   return p.rank_base == 32 || p.rank_base == 64 || p.rank_base == 128;
 }
 
-// The second mode's GEMM scoring: rank 32, bf16, unless a single-pass kernel is asked for
-// (option bit 1 keeps the older per-anchor-group kernel); a layer must fit a 32-bit buffer.
+// The second mode's GEMM scoring: ranks 32, 64 and 128, bf16, unless a single-pass kernel is
+// asked for (option bit 1 keeps the older per-anchor-group kernel); a layer must fit a 32-bit
+// buffer.
 bool cos_gemm_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) {
-  if (p.dtype != KVC_BF16 || (prm.options & 3) || p.rank_base != 32) return false;
+  const int r = p.rank_base;
+  if (p.dtype != KVC_BF16 || (prm.options & 3) || (r != 32 && r != 64 && r != 128)) return false;
   const int D = D_of(sh);
   if ((sh.head_dim != 64 && sh.head_dim != 128) || D % 32) return false;
   return (uint64_t)sh.seq_len * D * 2 < (1ull << 31);
@@ -309,7 +311,7 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
       if (pl.cos_gemm) {
         pl.tile = kCosTile;
         pl.off_pack_cos = off;
-        off += up256(sizeof(uint16_t) * cos_gemm_packed_elems(L, std::max(n_use, 1), D));
+        off += up256(sizeof(uint16_t) * cos_gemm_packed_elems(L, std::max(n_use, 1), p.rank_base, D));
       } else if (pl.cos_mfma) {
         pl.tile = kCosTile;
       } else {
@@ -569,6 +571,7 @@ kvc_status run_scores(const void* k_src, const void* v_src, const kvc_shape& sh,
     c.a_layer_stride = a.g.a_layer_stride; c.b_layer_stride = a.g.b_layer_stride;
     c.n_layers = a.n_layers; c.S = a.S; c.D = a.D; c.head_dim = a.head_dim; c.N = p.n_anchors;
     c.k_gate = a.k_gate; c.n_tiles = a.n_tiles; c.mask_gate = a.mask_gate;
+    c.r = p.rank_base;
     c.n_use = n_use;
     for (int i = 0; i < n_use; ++i) c.use[i] = s.use_list[i];
     for (int i = 0; i < p.n_anchors; ++i) { c.off[i] = a.g.off[i]; c.len[i] = a.g.len[i]; }

@@ -131,9 +131,9 @@ constexpr int kCosTile = 64;      // tokens per work-group (and per gate partial
 constexpr int kCosGemmTile = 128; // tokens per work-group (two gate partial tiles)
 struct CosGemmArgs {
   const uint16_t* z[2];      // source K, V   [N_l][S][D] bf16
-  const uint16_t* A[2];      // base A (K, V) packed [N_l][sum len][32]
-  const uint16_t* B[2];      // base B (K, V) [N_l][N][32][D] (read by the packing kernel)
-  const uint16_t* packed;    // B' rows [2][N_l][D / 32][n_use][32][32] (workspace)
+  const uint16_t* A[2];      // base A (K, V) packed [N_l][sum len][r]
+  const uint16_t* B[2];      // base B (K, V) [N_l][N][r][D] (read by the packing kernel)
+  const uint16_t* packed;    // B' rows [2][N_l][D / 32][n_use][r][32] (workspace)
   float* scores;             // [2][N_l][S][N]
   float* partials;           // [3][N_l][n_tiles][N], tiles of kCosTile tokens
   int64_t a_layer_stride;    // elements per layer of A (sum len * 32)
@@ -141,6 +141,7 @@ struct CosGemmArgs {
   int32_t n_layers, S, D, head_dim, N;
   int32_t k_gate, n_tiles;
   uint64_t mask_gate;
+  int32_t r;                 // base rank: 32, 64 or 128 (slices of 32 GEMM columns)
   int32_t n_use;             // scored anchors (corr U gate), ascending
   int32_t use[kMaxAnchors];
   int32_t off[kMaxAnchors];  // first packed A row of each anchor
@@ -148,7 +149,7 @@ struct CosGemmArgs {
   RopeTab can;               // R(-p_src): keys' B rows are turned by its transpose
 };
 size_t cos_gemm_lds();
-size_t cos_gemm_packed_elems(int n_layers, int n_use, int D);
+size_t cos_gemm_packed_elems(int n_layers, int n_use, int r, int D);
 hipError_t launch_pack_cos(const CosGemmArgs& a, uint16_t* dst, hipStream_t st);
 hipError_t launch_score_cos_gemm(const CosGemmArgs& a, hipStream_t st);
 

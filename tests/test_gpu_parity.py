@@ -93,7 +93,7 @@ def test_unrelated_layers_flagged_bf16():
 @pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
 @pytest.mark.parametrize("rank", [16, 64, 128])
 def test_ranks_bf16(rank, mode):
-    # second mode: rank 16 on the generic scores, ranks 64 / 128 on the per-anchor-group kernel;
+    # second mode: rank 16 on the generic scores, ranks 64 / 128 on the GEMM in column groups of 32;
     # ranks 64 / 128: the delta goes through the two-pass apply in rank slices of 32 (first mode:
     # scores and weights from the fused kernel)
     sp = W.llama8b_hop(n_layers=2, seq_len=300, n_anchors=6, rank_base=rank, rank_delta=rank,
@@ -167,13 +167,19 @@ def test_head_dim_64_bf16():
 
 
 # second scoring mode on its two MFMA kernels (option 0: one GEMM per layer-side over 128-token
-# work-groups, anchors in passes of 20; option 2: the per-anchor-group kernel): head_dim 64,
-# ragged anchors with a gate prefix, more than 20 anchors, a ragged token tail
+# work-groups, column groups of 32 in passes of 20; option 2: the per-anchor-group kernel):
+# head_dim 64, ragged anchors with a gate prefix, more than one pass, a ragged token tail; ranks
+# 64 and 128 (two and four column groups per anchor, summed across waves before the cosine)
 COS_CASES = {
     "hd64": dict(n_layers=2, seq_len=200, n_kv_heads=4, head_dim=64, n_anchors=5),
     "ragged": dict(n_layers=2, seq_len=400, n_kv_heads=2, n_anchors=5,
                    anchor_len=[330, 400, 250, 400, 390], gate_len=250),
     "two_passes": dict(n_layers=2, seq_len=330, n_kv_heads=2, n_anchors=23),
+    "r64_ragged_two_passes": dict(n_layers=2, seq_len=333, n_kv_heads=2, n_anchors=12, rank_base=64,
+                                  rank_delta=64, gate_len=200,
+                                  anchor_len=[333, 300, 250, 333, 201, 333, 333, 290, 333, 260, 333, 333]),
+    "r128_hd64": dict(n_layers=2, seq_len=260, n_kv_heads=4, head_dim=64, n_anchors=7, rank_base=128,
+                      rank_delta=128, anchor_len=[260, 200, 260, 260, 150, 260, 230]),
 }
 
 
