@@ -312,11 +312,18 @@ def test_apply_explicit_one_hot_weights():
 
 
 @pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
-def test_batched_chain_matches_sequential_oracle(mode):
+@pytest.mark.parametrize("rank", [0, 128])
+def test_batched_chain_matches_sequential_oracle(mode, rank):
+    # rank 0: the chain specification's ranks (16 / 32); 128: every pool at rank 128 (the sliced
+    # apply behind fused scores in the first mode, four column groups per anchor and up to four
+    # passes in the second)
     reqs = W.chain_specs(n_requests=2, n_hops=3, seq_len=256, n_layers=2, n_kv_heads=2)
     for hops in reqs:
-        if mode == W.SCORE_COS_R:   # second mode: rank 16 on the generic scores, rank 32 on the GEMM
+        if rank:
+            hops = [dataclasses.replace(h, rank_base=rank, rank_delta=rank) for h in hops]
+        if mode == W.SCORE_COS_R:   # second mode: rank 16 on the generic scores, the GEMM otherwise
             hops = [dataclasses.replace(h, mode=mode, tau=0.5) for h in hops]
+        print(f"[parity] chain mode={mode} ranks={[h.rank_base for h in hops]}", flush=True)
         datas = [make(h) for h in hops]
         shp = shape(hops[0])
         k0 = datas[0].k_src.to(DEV)
