@@ -22,6 +22,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -230,11 +232,10 @@ def measure_pool_insert(kvc, torch, L=32, S=4096, H=8, hd=128, r=32, V=20, p=16,
     return out
 
 
-def measure_rank128(kvc, torch, W, steps=5):
+def measure_rank128(kvc, torch, W, data, steps=5):
     """Rank-128 correction (32 layers x 4096 tokens x 8x128 bf16, 10 anchors at rank 128 for base
     and delta), both scoring modes, through the library's default path for that rank."""
-    sp = W.llama8b_rank128()
-    data = W.make_hop(sp)
+    sp = data.spec
     k, v = data.k_src.to("cuda"), data.v_src.to("cuda")
     ko, vo = torch.empty_like(k), torch.empty_like(v)
     pool = kvc.pool_from(data, "cuda")
@@ -334,47 +335,268 @@ def measure_chain(kvc, torch, W, n_requests=8, n_hops=3, steps=3):
             hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
                               torch.empty_like(v0), h.p_src, h.p_tgt, base + i - 1 if i else -1, pool, out))
     prm = kvc.params_of(h0.tau, h0.temp_gate, h0.temp_weight, h0.gate_len, h0.mode, 0, None)
-    kvc.correct_hops_batched(hl, shp, prm)
-    torch.cuda.synchronize()
+    ws = torch.empty((kvc.hops_batched_workspace(hl, shp, prm),), dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(steps):
-        kvc.correct_hops_batched(hl, shp, prm)
-    e1.record(st)
+
+    def timed(one):
+        kvc.correct_hops_batched(hl, shp, prm, workspace=ws, one_at_a_time=one)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            kvc.correct_hops_batched(hl, shp, prm, workspace=ws, one_at_a_time=one)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(False)
+    ms_one = timed(True)
+    tr = kvc.KernelTrace(32)
+    kvc.correct_hops_batched(hl, shp, kvc.params_of(h0.tau, h0.temp_gate, h0.temp_weight, h0.gate_len, h0.mode, 0, tr),
+                             workspace=ws)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    per_kernel = {}
+    for name, t in tr.results():
+        per_kernel[name] = per_kernel.get(name, 0.0) + t
+    tr.close()
     toks = sum(h.seq_len for hops in reqs for h in hops)
     nbytes = sum(int(t.numel()) * 2 for h in hl for t in (h.k_out, h.v_out))
     nbytes += sum(int(t.numel()) * 2 for h in hl if h.k_src is not None for t in (h.k_src, h.v_src))
     nbytes += sum(int(t.numel()) * 2 for h in hl for t in (h.pool.baseA_k, h.pool.baseB_k, h.pool.baseA_v,
                                                             h.pool.baseB_v, h.pool.deltaA_k, h.pool.deltaB_k,
                                                             h.pool.deltaA_v, h.pool.deltaB_v))
+    flops = sum(4 * L * S * D * h.n_anchors * (h.rank_base + h.rank_delta) for hops in reqs for h in hops)
+    floor_ms = max(nbytes / PEAK_HBM, flops / PEAK_MFMA_BF16) * 1e3
     out = {"workload": f"{n_requests} requests x {n_hops} chained hops, {L} layers x {S} tokens, "
                        f"{h0.n_kv_heads}x{h0.head_dim} KV heads, bf16, pools of 10-20 anchors at rank 16/32 "
-                       f"(seeded chain specification, values drawn on the device)",
+                       f"(seeded chain specification, values drawn on the device); each chain level one grid "
+                       f"per kernel",
            "ms": round(ms, 3), "tokens_per_s": round(toks / (ms / 1e3), 1),
-           "algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms / 1e3) / 1e9, 1)}
-    del hl
+           "ms_one_hop_per_call": round(ms_one, 3),
+           "algorithmic_bytes": nbytes, "mfma_flops": flops, "achieved_GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+           "achieved_TFLOPs": round(flops / (ms / 1e3) / 1e12, 1), "roofline_floor_ms": round(floor_ms, 3),
+           "frac_of_floor": round(floor_ms / ms, 4),
+           "kernels_ms_per_batch": {n: round(t, 4) for n, t in per_kernel.items()}}
+    del hl, ws
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(data, n_layers):
-    """The fp64 oracle on layer 0 of the same hop (all tokens, keys and values)."""
-    from oracle import kvc_oracle as O
+def host_info():
+    """The host the oracle runs on: CPU model, logical CPUs, BLAS threads."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        blas = 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "sched_affinity": affinity, "blas_threads": int(blas)}
+
+
+def _layers_of(data, layers, **repl):
+    """The hop's inputs restricted to `layers` (the oracle then sees layer i of the list as layer i)."""
+    import torch
+    idx = torch.tensor(layers)
+    t = {k: v.index_select(0, idx) for k, v in data.tensors().items()}
+    t.update(repl)
+    return dataclasses.replace(data, spec=dataclasses.replace(data.spec, n_layers=len(layers)), **t)
+
+
+def hop_quality(O, W, data, gpu, layers, exact=True):
+    """Parity and correction quality on sampled layers, all tokens (the oracle on the GPU's own
+    inputs): max |gpu - oracle| / max |oracle| per side, per-layer flag agreement, the oracle's and
+    the GPU's normalised error against the exact target (KVCMAS App. A.1 / Fig. 3: ||C_hat - C|| /
+    ||C||) and that of the uncorrected re-aligned source, on matched layers."""
+    sp = data.spec
+    fr = O.inv_freq(sp.head_dim, sp.theta)
+    err = {"k": 0.0, "v": 0.0}
+    agree, n_flag = 0, 0
+    m02, m02_oracle, m02_none = [], [], []
+    t0 = time.perf_counter()
+    for i, l in enumerate(layers):
+        ref = O.correct_layer(data, i)
+        for side in ("k", "v"):
+            want = O.round_to(ref[f"{side}_out"], sp.dtype)
+            got = gpu[f"{side}_out"][i]
+            err[side] = max(err[side], float(np.max(np.abs(got - want)) / np.max(np.abs(want))))
+        if sp.mode == W.SCORE_PAGES:
+            _, _, f = O.gate_decide_pages(np.asarray(ref["q"]), sp.tau, sp.temp_gate, sp.cap(), sp.n_anchors)
+        else:
+            _, _, f = O.gate_decide_cos(*[np.asarray(x) for x in ref["cos_sums"]], sp.tau, sp.cap(), sp.n_anchors)
+        agree += int(f == int(gpu["flags"][1 + l]))
+        n_flag += 1
+        unrelated = sp.unrelated_layers is not None and gpu["orig_layer"][i] in sp.unrelated_layers
+        if not exact or unrelated:
+            continue
+        for side in ("k", "v"):
+            A, B = O.layer_factors(data, i, side, "delta", [0])
+            corr = A[0] @ B[0] + W.target_noise(sp, gpu["orig_layer"][i], 0 if side == "k" else 1)
+            src = O._np(getattr(data, f"{side}_src")[i])
+            if side == "k":
+                aligned = O.rope(src, sp.shift, sp.head_dim, fr)
+                target = aligned + O.rope(corr, sp.p_tgt, sp.head_dim, fr)
+            else:
+                aligned = src
+                target = src + corr
+            m02.append(O.normalized_error(gpu[f"{side}_out"][i], target))
+            m02_oracle.append(O.normalized_error(ref[f"{side}_out"], target))
+            m02_none.append(O.normalized_error(aligned, target))
+    out = {"layers": [int(gpu["orig_layer"][i]) for i in range(len(layers))],
+           "max_abs_err_over_max_x": {"k": round(err["k"], 6), "v": round(err["v"], 6), "bound": 2.0 ** -7},
+           "layer_flags_agree": f"{agree}/{n_flag}",
+           "oracle_s": round(time.perf_counter() - t0, 2)}
+    if m02:
+        out["normalised_error_vs_exact_target"] = {"gpu": round(float(np.mean(m02)), 5),
+                                                   "oracle": round(float(np.mean(m02_oracle)), 5),
+                                                   "uncorrected": round(float(np.mean(m02_none)), 5)}
+    return out
+
+
+def cpu_baseline(O, data, n_layers, layers):
+    """The fp64 oracle (as it stands) on `layers` of the same hop, all tokens, keys and values;
+    tokens/s scaled to all layers."""
+    info = host_info()
     S = data.spec.seq_len
     t0 = time.perf_counter()
-    O.correct_layer(data, 0)
+    for i in range(len(layers)):
+        O.correct_layer(data, i)
     dt = time.perf_counter() - t0
-    return {"value": round(S / (dt * n_layers), 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer 0 of {n_layers}: {S} tokens x (K, V), scores + weights + gate sums + delta in fp64; "
-                      f"{dt:.1f} s, scaled to all layers"}
+    return {"value": round(S / (dt * n_layers / len(layers)), 2), "unit": "tokens/s", "cores": info["blas_threads"],
+            "kind": "oracle", "host": info,
+            "sample": f"layers {layers} of {n_layers}: {S} tokens x (K, V), scores + weights + gate sums + delta "
+                      f"in fp64; {dt:.1f} s, scaled to all layers"}
+
+
+def cpu_median(O, data, n_layers, layers, runs=3, threads=None):
+    """Median of `runs` oracle runs on `layers` (optionally with the BLAS pool limited)."""
+    from contextlib import nullcontext
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(threads) if threads else nullcontext()
+    except Exception:
+        ctx = nullcontext()
+    ts = []
+    with ctx:
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            for i in range(len(layers)):
+                O.correct_layer(data, i)
+            ts.append(time.perf_counter() - t0)
+    dt = statistics.median(ts)
+    S = data.spec.seq_len
+    return {"value": round(S / (dt * n_layers / len(layers)), 2), "unit": "tokens/s",
+            "median_s": round(dt, 3), "runs": runs, "layers": layers, "threads": threads or host_info()["blas_threads"]}
+
+
+def measure_c2(kvc, torch, W, data, steps=10, warmup=2):
+    """The 4096-token Llama-3.1-8B-shaped hop (32 layers x 8x128, 20 anchors at rank 32, start
+    position and shift from the seeded specification), keys placed at p_src on the device by the
+    library's re-alignment.  Returns the timing and the GPU's inputs / outputs of sampled layers
+    for the oracle leg."""
+    sp = data.spec
+    k, v = data.k_src.to("cuda"), data.v_src.to("cuda")
+    shp = kvc.shape_of(sp.n_layers, sp.seq_len, sp.n_kv_heads, sp.head_dim)
+    kvc.align_rope(k, k, shp, 0, sp.p_src)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    pool = kvc.pool_from(data, "cuda")
+    prm_fn = lambda tr: kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, sp.mode, 0, tr)
+    ws = torch.empty((kvc.correct_hop_workspace(shp, pool, prm_fn(None)),), dtype=torch.uint8, device="cuda")
+    ms, _, per_kernel, res = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn, ws, steps, warmup)
+    L, S, D, N, r = sp.n_layers, sp.seq_len, sp.d_model, sp.n_anchors, sp.rank_base
+    nbytes = 2 * L * S * D * (2 + 2) + 2 * L * N * (2 * r) * (S + D) * 2
+    flops = 8 * L * S * D * N * r
+    flags = res.flags.cpu().tolist()
+    out = {"workload": f"{L} layers x {S} tokens x {sp.n_kv_heads}x{sp.head_dim} bf16, {N} anchors at rank {r}, "
+                       f"p_src {sp.p_src}, shift {sp.shift}",
+           "ms": round(ms, 4), "tokens_per_s": round(S / (ms / 1e3), 1), "algorithmic_bytes": nbytes,
+           "mfma_flops": flops, "hbm_frac": round(nbytes / (ms / 1e3) / PEAK_HBM, 4),
+           "mfma_frac": round(flops / (ms / 1e3) / PEAK_MFMA_BF16, 4),
+           "kernels_ms": {n: round(statistics.median(t), 4) for n, t in per_kernel.items()},
+           "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)}}
+    # the flagged fraction over the per-layer gates (reuse ratio of this hop's layers)
+    out["accepted_layer_fraction"] = round(sum(1 for f in flags[1:] if not f) / L, 4)
+    res2 = kvc.correct_hop(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, prm_fn(None), workspace=ws,
+                           want_weights=True)
+    torch.cuda.synchronize()
+    layers = [0, 15, 31]
+    idx = torch.tensor(layers, device="cuda")
+    art = {"layers": layers, "k_src": k.index_select(0, idx).cpu(),
+           "gpu": {"k_out": ko.index_select(0, idx).double().cpu().numpy(),
+                   "v_out": vo.index_select(0, idx).double().cpu().numpy(),
+                   "flags": res2.flags.cpu().numpy(), "orig_layer": layers}}
+    del k, v, ko, vo, pool, ws
+    torch.cuda.empty_cache()
+    return out, art
+
+
+def measure_c5(kvc, torch, W, data, p=32, q=3, steps=5):
+    """KVCMAS Sec. 3.3 Eq. 7 then Eq. 8 at the rank-128 configuration: dense fp32 deltas
+    (4096 x 1024 per layer and side, Gaussian factors with i^-1.5 column scales, drawn on the
+    device) factorised at rank 128 by the refresh, written as anchor 0's delta factors (bf16) of a
+    10-anchor pool, then the rank-128 correction of the 32-layer 4096-token hop.  Timed as one
+    pipeline: refresh, the factor copies into the pool, the correction."""
+    sp = data.spec
+    L, S, D, r = sp.n_layers, sp.seq_len, sp.d_model, sp.rank_delta
+    k, v = data.k_src.to("cuda"), data.v_src.to("cuda")
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    pool = kvc.pool_from(data, "cuda")
+    shp = kvc.shape_of(L, S, sp.n_kv_heads, sp.head_dim)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    sc = torch.arange(1, D + 1, device="cuda", dtype=torch.float32) ** -1.5
+    z = torch.empty((2 * L, S, D), device="cuda")
+    for m in range(2 * L):
+        a = torch.randn((S, D), device="cuda", generator=g) * sc[None, :]
+        z[m] = a @ (torch.randn((D, D), device="cuda", generator=g) / D ** 0.5)
+    ws_svd = torch.empty((kvc.svd_workspace_size(2 * L, S, D, r, p),), dtype=torch.uint8, device="cuda")
+    a_out = torch.empty((2 * L, S, r), dtype=torch.bfloat16, device="cuda")
+    b_out = torch.empty((2 * L, r, D), dtype=torch.bfloat16, device="cuda")
+    prm = kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, sp.mode, 0, None)
+    ws = torch.empty((kvc.correct_hop_workspace(shp, pool, prm),), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def pipeline():
+        kvc.anchor_refresh_svd(z, r, oversample=p, power_iters=q, workspace=ws_svd, a_out=a_out, b_out=b_out)
+        pool.deltaA_k[:, :S].copy_(a_out[0::2])
+        pool.deltaB_k[:, 0].copy_(b_out[0::2])
+        pool.deltaA_v[:, :S].copy_(a_out[1::2])
+        pool.deltaB_v[:, 0].copy_(b_out[1::2])
+        kvc.correct_hop(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, prm, workspace=ws)
+
+    pipeline()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(st)
+        kvc.anchor_refresh_svd(z, r, oversample=p, power_iters=q, workspace=ws_svd, a_out=a_out, b_out=b_out)
+        e[1].record(st)
+        pool.deltaA_k[:, :S].copy_(a_out[0::2])
+        pool.deltaB_k[:, 0].copy_(b_out[0::2])
+        pool.deltaA_v[:, :S].copy_(a_out[1::2])
+        pool.deltaB_v[:, 0].copy_(b_out[1::2])
+        e[2].record(st)
+        kvc.correct_hop(k, v, ko, vo, shp, sp.p_src, sp.p_tgt, pool, prm, workspace=ws)
+        e[3].record(st)
+    torch.cuda.synchronize()
+    med = lambda i, j: statistics.median(e[i].elapsed_time(e[j]) for e in evs)
+    t_svd, t_copy, t_cor, t_all = med(0, 1), med(1, 2), med(2, 3), med(0, 3)
+    del z, ws_svd, a_out, b_out, k, v, ko, vo, pool, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"refresh of {2 * L} fp32 deltas {S}x{D} at rank {r} (oversample {p}, {q} power "
+                        f"iterations) into anchor 0, then the rank-{r} correction with {sp.n_anchors} anchors "
+                        f"({L} layers x {S} tokens x {sp.n_kv_heads}x{sp.head_dim} bf16)",
+            "ms": round(t_all, 3), "refresh_ms": round(t_svd, 3), "factor_copy_ms": round(t_copy, 3),
+            "correction_ms": round(t_cor, 3), "tokens_per_s_correction": round(S / (t_cor / 1e3), 1)}
 
 
 def time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn, ws, steps, warmup, trace=True):
@@ -460,6 +682,9 @@ def measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool, prm, reps=20, warm
     return out
 
 
+SECTIONS = ("peaks", "hop", "protocol", "second", "c2", "refresh", "chain", "pf", "r128", "c5", "study", "pool", "cpu")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,7 +696,8 @@ def main():
     ap.add_argument("--p-src", type=int, default=512, help="start position of the segment in the source agent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-mode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the refresh and chained-batch sections")
+    ap.add_argument("--no-extra", action="store_true", help="skip the refresh, chained-batch and other sections")
+    ap.add_argument("--only", default="", help="comma-separated sections to run (profiling): " + ",".join(SECTIONS))
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -479,6 +705,17 @@ def main():
         print(f"bench.py: this build runs the per-hop correction on one GPU only; --gpus {args.gpus} "
               f"(WORLD_SIZE={world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    want = set(args.only.split(",")) if args.only else set(SECTIONS)
+    bad = want - set(SECTIONS)
+    if bad:
+        print(f"bench.py: unknown sections {sorted(bad)}", file=sys.stderr)
+        sys.exit(2)
+    if args.no_extra:
+        want -= {"refresh", "chain", "pf", "r128", "c5", "study", "pool", "c2"}
+    if args.no_second_mode:
+        want.discard("second")
+    if args.no_cpu_baseline:
+        want.discard("cpu")
 
     import numpy as np  # noqa: F401
     import torch
@@ -486,112 +723,181 @@ def main():
     from rank_kv_cache_layer_amd import kvc
     from rank_kv_cache_layer_amd import workload as W
 
+    # host-side inputs first: the seeded generator forks worker processes only before the GPU is
+    # initialised in this process
     mode = W.SCORE_PAGES if args.mode == "pages" else W.SCORE_COS_R
     sp = W.llama8b_long(n_layers=args.layers, seq_len=args.seq_len, mode=mode)
-    t0 = time.perf_counter()
-    data = W.make_hop(sp)
-    log(f"[bench] generated {sp.name}: L={sp.n_layers} S={sp.seq_len} D={sp.d_model} N={sp.n_anchors} "
-        f"r={sp.rank_base} in {time.perf_counter() - t0:.1f} s")
+    data = data_c2 = data_c5 = None
+    need_hop = bool(want & {"hop", "protocol", "second", "cpu"})
+    if need_hop:
+        t0 = time.perf_counter()
+        data = W.make_hop(sp)
+        log(f"[bench] generated {sp.name}: L={sp.n_layers} S={sp.seq_len} D={sp.d_model} N={sp.n_anchors} "
+            f"r={sp.rank_base} in {time.perf_counter() - t0:.1f} s")
+    if "c2" in want:
+        sp2 = W.llama8b_hop()
+        data_c2 = W.make_hop(dataclasses.replace(sp2, p_src=0, p_tgt=sp2.shift))
+        data_c2 = dataclasses.replace(data_c2, spec=sp2)   # keys placed at p_src on the device
+        log(f"[bench] generated {sp2.name}")
+    if want & {"c5", "r128"}:
+        data_c5 = W.make_hop(W.llama8b_rank128())
+        log("[bench] generated llama8b_r128")
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     kvc.lib()
     dev = "cuda:0"
-    k = data.k_src.to(dev)
-    v = data.v_src.to(dev)
-    ko, vo = torch.empty_like(k), torch.empty_like(v)
-    pool = kvc.pool_from(data, dev)
-    shp = kvc.shape_of(sp.n_layers, sp.seq_len, sp.n_kv_heads, sp.head_dim)
-    # keys are drawn in the canonical frame; place the segment at start position 512 (target 812)
-    # with the library's own re-alignment, in place
-    kvc.align_rope(k, k, shp, 0, args.p_src)
-    sp = dataclasses.replace(sp, p_src=args.p_src, p_tgt=args.p_src + sp.shift)
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"llama8b_hop_{sp.seq_len}tok" if sp.seq_len != 32768 or sp.n_layers != 32
+                      else "llama8b_32k_hop", "n_layers": sp.n_layers, "seq_len": sp.seq_len,
+                      "n_kv_heads": sp.n_kv_heads, "head_dim": sp.head_dim, "n_anchors": sp.n_anchors,
+                      "rank": sp.rank_base, "shift": sp.shift, "score_mode": args.mode,
+                      "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
+           "roofline": None, "cpu_baseline": None}
 
-    def prm_fn(mode_):
-        return lambda tr: kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, mode_, 0, tr)
+    if "peaks" in want:
+        out["measured_peaks"] = measure_peaks(kvc, torch)
+        log(f"[bench] measured ceilings: {out['measured_peaks']}")
 
-    ws_bytes = max(kvc.correct_hop_workspace(shp, pool, prm_fn(m)(None)) for m in (W.SCORE_PAGES, W.SCORE_COS_R))
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    log(f"[bench] inputs resident on {torch.cuda.get_device_name(0)}; workspace {ws_bytes / 2**20:.0f} MiB")
+    art3 = None
+    if need_hop:
+        k = data.k_src.to(dev)
+        v = data.v_src.to(dev)
+        ko, vo = torch.empty_like(k), torch.empty_like(v)
+        pool = kvc.pool_from(data, dev)
+        shp = kvc.shape_of(sp.n_layers, sp.seq_len, sp.n_kv_heads, sp.head_dim)
+        # keys are drawn in the canonical frame; place the segment at start position 512 (target
+        # 812) with the library's own re-alignment, in place
+        kvc.align_rope(k, k, shp, 0, args.p_src)
+        sp = dataclasses.replace(sp, p_src=args.p_src, p_tgt=args.p_src + sp.shift)
 
-    peaks = measure_peaks(kvc, torch)
-    log(f"[bench] measured ceilings: {peaks}")
+        def prm_fn(mode_):
+            return lambda tr: kvc.params_of(sp.tau, sp.temp_gate, sp.temp_weight, sp.gate_len, mode_, 0, tr)
 
-    ms, wall, per_kernel, res = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode), ws, args.steps,
-                                         args.warmup)
-    flags = res.flags.cpu().tolist()
-    log(f"[bench] {args.mode}: {ms:.3f} ms/hop (wall {wall / args.steps * 1e3:.3f} ms), flags hop={flags[0]} "
-        f"layers={sum(1 for f in flags[1:] if f)} flagged")
-    S, L, D, N, r = sp.seq_len, sp.n_layers, sp.d_model, sp.n_anchors, sp.rank_base
-    kernels = {}
-    for name, ts in per_kernel.items():
-        med = statistics.median(ts)
-        kernels[name] = roofline(name, med, kernel_work(name, L, S, D, N, r, r, args.mode), measured_traffic(name))
-    dominant = max(kernels.values(), key=lambda x: x["ms"]) if kernels else None
-
-    hop_bytes = 2 * L * S * D * (2 + 2) + 2 * L * N * (2 * r) * (S + D) * 2
-    hop_flops = 8 * L * S * D * N * r
-    hop = {"ms": round(ms, 4), "algorithmic_bytes": hop_bytes, "mfma_flops": hop_flops,
-           "hbm_frac": round(hop_bytes / (ms / 1e3) / PEAK_HBM, 4),
-           "mfma_frac": round(hop_flops / (ms / 1e3) / PEAK_MFMA_BF16, 4)}
-
-    protocol = measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode)(None))
-    log(f"[bench] per-repetition protocol (cache flushed): {protocol}")
-
-    second = None
-    if not args.no_second_mode:
-        m2 = W.SCORE_COS_R if mode == W.SCORE_PAGES else W.SCORE_PAGES
-        ms2, _, pk2, _ = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(m2), ws, max(3, args.steps // 4),
-                                  1)
-        second = {"mode": "cos_r" if m2 == W.SCORE_COS_R else "pages", "ms_per_hop": round(ms2, 4),
-                  "tokens_per_s": round(S / (ms2 / 1e3), 1),
-                  "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
-        log(f"[bench] second mode {second['mode']}: {ms2:.3f} ms/hop")
-
-    refresh = chain = pool_ins = pf = study_out = r128 = None
-    if not args.no_extra:
-        log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
-        refresh = measure_refresh(kvc, torch, oracle=not args.no_cpu_baseline)
-        log(f"[bench] refresh: {refresh['ms']} ms, {refresh['achieved_TFLOPs']} TFLOP/s")
+        ws_bytes = max(kvc.correct_hop_workspace(shp, pool, prm_fn(m)(None)) for m in (W.SCORE_PAGES, W.SCORE_COS_R))
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        log(f"[bench] inputs resident on {torch.cuda.get_device_name(0)}; workspace {ws_bytes / 2**20:.0f} MiB")
+        S, L, D, N, r = sp.seq_len, sp.n_layers, sp.d_model, sp.n_anchors, sp.rank_base
+        if "hop" in want or "cpu" in want:
+            ms, wall, per_kernel, res = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode), ws,
+                                                 args.steps, args.warmup)
+            flags = res.flags.cpu().tolist()
+            log(f"[bench] {args.mode}: {ms:.3f} ms/hop (wall {wall / args.steps * 1e3:.3f} ms), flags hop={flags[0]} "
+                f"layers={sum(1 for f in flags[1:] if f)} flagged")
+            kernels = {}
+            for name, ts in per_kernel.items():
+                med = statistics.median(ts)
+                kernels[name] = roofline(name, med, kernel_work(name, L, S, D, N, r, r, args.mode),
+                                         measured_traffic(name))
+            dominant = max(kernels.values(), key=lambda x: x["ms"]) if kernels else None
+            hop_bytes = 2 * L * S * D * (2 + 2) + 2 * L * N * (2 * r) * (S + D) * 2
+            hop_flops = 8 * L * S * D * N * r
+            out.update({"value": round(S / (ms / 1e3), 1), "ms_per_step": round(ms, 4), "roofline": dominant,
+                        "kernels": kernels,
+                        "hop": {"ms": round(ms, 4), "algorithmic_bytes": hop_bytes, "mfma_flops": hop_flops,
+                                "hbm_frac": round(hop_bytes / (ms / 1e3) / PEAK_HBM, 4),
+                                "mfma_frac": round(hop_flops / (ms / 1e3) / PEAK_MFMA_BF16, 4)},
+                        "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f),
+                                  "accepted_layer_fraction": round(sum(1 for f in flags[1:] if not f) / L, 4)}})
+            if "cpu" in want:
+                # the GPU's inputs and outputs of sampled layers, for the oracle leg
+                lay = [0, 1, 2]
+                idx = torch.tensor(lay, device=dev)
+                art3 = {"layers": lay, "k_src": k.index_select(0, idx).cpu(),
+                        "gpu": {"k_out": ko.index_select(0, idx).double().cpu().numpy(),
+                                "v_out": vo.index_select(0, idx).double().cpu().numpy(),
+                                "flags": res.flags.cpu().numpy(), "orig_layer": lay}}
+        if "protocol" in want:
+            out["protocol"] = measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode)(None))
+            log(f"[bench] per-repetition protocol (cache flushed): {out['protocol']}")
+        if "second" in want:
+            m2 = W.SCORE_COS_R if mode == W.SCORE_PAGES else W.SCORE_PAGES
+            ms2, _, pk2, _ = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(m2), ws,
+                                      max(3, args.steps // 4), 1)
+            out["second_mode"] = {"mode": "cos_r" if m2 == W.SCORE_COS_R else "pages", "ms_per_hop": round(ms2, 4),
+                                  "tokens_per_s": round(S / (ms2 / 1e3), 1),
+                                  "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
+            log(f"[bench] second mode {out['second_mode']['mode']}: {ms2:.3f} ms/hop")
         del k, v, ko, vo, pool, ws
         torch.cuda.empty_cache()
+
+    art2 = None
+    if "c2" in want:
+        log("[bench] 4096-token hop (32 layers, 20 anchors at rank 32) ...")
+        out["c2_hop"], art2 = measure_c2(kvc, torch, W, data_c2)
+        log(f"[bench] c2: {out['c2_hop']['ms']} ms, {out['c2_hop']['tokens_per_s']} tokens/s")
+    if "refresh" in want:
+        log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
+        out["refresh"] = measure_refresh(kvc, torch, oracle="cpu" in want)
+        log(f"[bench] refresh: {out['refresh']['ms']} ms, {out['refresh']['achieved_TFLOPs']} TFLOP/s")
+    if "chain" in want:
         log("[bench] chained batch (8 requests x 3 hops, 8192 tokens) ...")
-        chain = measure_chain(kvc, torch, W)
-        log(f"[bench] chain: {chain['ms']} ms, {chain['tokens_per_s']} tokens/s")
+        out["chained_batch"] = measure_chain(kvc, torch, W)
+        log(f"[bench] chain: {out['chained_batch']}")
+    if "pf" in want:
         log("[bench] preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens) ...")
-        pf = measure_pf_delta(kvc, torch)
+        out["pf_delta"] = measure_pf_delta(kvc, torch)
+        log(f"[bench] pf delta: {out['pf_delta']['ms']} ms, {out['pf_delta']['achieved_GBps']} GB/s")
+    if "r128" in want:
         log("[bench] rank-128 correction (32 layers x 4096 tokens, 10 anchors) ...")
-        r128 = measure_rank128(kvc, torch, W)
-        log(f"[bench] rank 128: pages {r128['pages']['ms']} ms, cos_r {r128['cos_r']['ms']} ms")
-        log(f"[bench] pf delta: {pf['ms']} ms, {pf['achieved_GBps']} GB/s")
+        out["rank128_hop"] = measure_rank128(kvc, torch, W, data_c5)
+        log(f"[bench] rank 128: pages {out['rank128_hop']['pages']['ms']} ms, "
+            f"cos_r {out['rank128_hop']['cos_r']['ms']} ms")
+    if "c5" in want:
+        log("[bench] refresh into anchor 0, then the rank-128 correction ...")
+        out["c5_pipeline"] = measure_c5(kvc, torch, W, data_c5)
+        log(f"[bench] c5 pipeline: {out['c5_pipeline']}")
+    if "study" in want:
         log("[bench] chained vs non-chained correction error along A0 -> A3 (8 layers x 4096 x 1024) ...")
-        study_out = measure_study(torch)
-        log(f"[bench] study: {study_out}")
+        out["chain_study"] = measure_study(torch)
+        log(f"[bench] study: {out['chain_study']}")
+    if "pool" in want:
         log("[bench] pool update after a fallback (32 layers x 4096 tokens, rank 32) ...")
-        pool_ins = measure_pool_insert(kvc, torch, oracle=not args.no_cpu_baseline)
-        log(f"[bench] pool insert: {pool_ins['ms']} ms; Eq. 12 kernels {pool_ins['eq12_kernels']}")
+        out["pool_insert"] = measure_pool_insert(kvc, torch, oracle="cpu" in want)
+        log(f"[bench] pool insert: {out['pool_insert']['ms']} ms; Eq. 12 kernels {out['pool_insert']['eq12_kernels']}")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on a bounded sample ...")
-        cpu = cpu_baseline(data, L)
-        log(f"[bench] oracle: {cpu['value']} tokens/s ({cpu['sample']})")
+    if "cpu" in want:
+        from oracle import kvc_oracle as O
+        log("[bench] timing the fp64 oracle on bounded samples, and parity / quality on sampled layers ...")
+        d3 = _layers_of(data, art3["layers"], k_src=art3["k_src"])
+        d3 = dataclasses.replace(d3, spec=dataclasses.replace(d3.spec, p_src=sp.p_src, p_tgt=sp.p_tgt,
+                                                              n_layers=len(art3["layers"]),
+                                                              unrelated_layers=sp.unrelated_layers))
+        out["cpu_baseline"] = cpu_baseline(O, d3, sp.n_layers, art3["layers"])
+        log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s ({out['cpu_baseline']['sample']})")
+        base = {"c3": dict(out["cpu_baseline"])}
+        quality = {"c3": hop_quality(O, W, d3, art3["gpu"], art3["layers"])}
+        if art2 is not None:
+            sp2 = data_c2.spec
+            d2 = _layers_of(data_c2, art2["layers"], k_src=art2["k_src"])
+            base["c2"] = cpu_median(O, d2, sp2.n_layers, art2["layers"])
+            quality["c2"] = hop_quality(O, W, d2, art2["gpu"], art2["layers"])
+            quality["c2"]["accepted_layer_fraction"] = out["c2_hop"]["accepted_layer_fraction"]
+        # the tiny fp32 workload: whole hop, median of 3, also on one thread; GPU parity beside it
+        dt1 = W.make_hop(W.tiny(), place_keys=lambda x, p_: O.rope(x, p_, 64))
+        sp1 = dt1.spec
+        base["c1"] = cpu_median(O, dt1, sp1.n_layers, list(range(sp1.n_layers)))
+        base["c1_single_thread"] = cpu_median(O, dt1, sp1.n_layers, list(range(sp1.n_layers)), threads=1)
+        k1, v1 = dt1.k_src.to(dev), dt1.v_src.to(dev)
+        ko1, vo1 = torch.empty_like(k1), torch.empty_like(v1)
+        shp1 = kvc.shape_of(sp1.n_layers, sp1.seq_len, sp1.n_kv_heads, sp1.head_dim)
+        res1 = kvc.correct_hop(k1, v1, ko1, vo1, shp1, sp1.p_src, sp1.p_tgt, kvc.pool_from(dt1, dev),
+                               kvc.params_of(sp1.tau, sp1.temp_gate, sp1.temp_weight, sp1.gate_len, sp1.mode))
+        torch.cuda.synchronize()
+        ref1 = O.correct_hop(dt1)
+        quality["c1"] = {"max_abs_err_over_max_x": {
+            s_: round(float(np.max(np.abs(t.double().cpu().numpy() - ref1[f"{s_}_out"])) /
+                            np.max(np.abs(ref1[f"{s_}_out"]))), 9) for s_, t in (("k", ko1), ("v", vo1))},
+            "bound": 1e-5, "flags_equal": bool(np.array_equal(res1.flags.cpu().numpy(), ref1["flags"]))}
+        out["cpu_baselines"] = base
+        out["quality"] = quality
+        log(f"[bench] oracle baselines: {base}")
+        log(f"[bench] quality: {quality}")
 
-    out = {
-        "metric": METRIC, "value": round(S / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"llama8b_hop_{S}tok" if S != 32768 or L != 32 else "llama8b_32k_hop",
-                   "n_layers": L, "seq_len": S, "n_kv_heads": sp.n_kv_heads, "head_dim": sp.head_dim,
-                   "n_anchors": N, "rank": r, "shift": sp.shift, "score_mode": args.mode,
-                   "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
-        "roofline": dominant, "cpu_baseline": cpu,
-        "hop": hop, "protocol": protocol, "kernels": kernels, "second_mode": second, "measured_peaks": peaks,
-        "refresh": refresh, "chained_batch": chain, "pool_insert": pool_ins, "pf_delta": pf, "rank128_hop": r128, "chain_study": study_out,
-        "flags": {"hop": flags[0], "layers_flagged": sum(1 for f in flags[1:] if f)},
-    }
     print(json.dumps(out), flush=True)
 
 

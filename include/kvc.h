@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 #define KVC_MAX_ANCHORS 64
 #define KVC_MAX_HEAD_DIM 256
 
@@ -243,9 +243,20 @@ typedef struct {
   kvc_match_out out;   /* s_cov may be NULL                                                 */
 } kvc_hop_desc;
 
-/* Runs n_hops corrections in dependency order on one stream.  A hop whose predecessor is
- * flagged is still computed and gets KVC_FLAG_PRED_FLAGGED.  Workspace: the maximum of
- * kvc_workspace_size(KVC_CALL_CORRECT, ...) over the hops. */
+/* Runs n_hops corrections on one stream (KVCMAS Sec. 3.2 Eq. 6; App. A.3 "Cache
+ * Materialization and Pool Updates": a materialised target is the next edge's source; App. B.1
+ * "Workflow Structures": chains of agents and fan-in).  Hops are grouped by their depth in the
+ * chains (a hop with chain_prev = -1 is at depth 0, otherwise one deeper than chain_prev); the
+ * levels run in order, and the hops of one level that take the two-pass bf16 path (first
+ * scoring mode, base rank 16 or 32, at least one correcting anchor) run together, one launch of
+ * each kernel for the whole level (up to 64 hops per launch) with per-hop descriptors (ragged
+ * pools, ranks and positions) in the workspace.  Other hops run one call at a time.  A hop whose
+ * predecessor is flagged is still computed and gets KVC_FLAG_PRED_FLAGGED.
+ * Workspace: kvc_hops_batched_workspace_size(); given only the largest one-hop workspace
+ * (kvc_workspace_size(KVC_CALL_CORRECT, ...) over the hops) every hop runs on its own; less
+ * returns KVC_E_WORKSPACE.  Outputs are the same either way. */
+size_t kvc_hops_batched_workspace_size(const kvc_hop_desc* hops, int32_t n_hops, kvc_dtype dtype,
+                                       kvc_shape shape, const kvc_params* params);
 kvc_status kvc_correct_hops_batched(const kvc_hop_desc* hops, int32_t n_hops, kvc_dtype dtype,
                                     kvc_shape shape, const kvc_rope* rope,
                                     const kvc_params* params, void* workspace, size_t ws_bytes,

@@ -121,7 +121,20 @@ hipError_t go(const void* in, void* out, int64_t n_rows, int n_heads, int head_d
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(256) fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  fill_f32<<<(unsigned)blocks, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_align(const void* in, void* out, int in_bf16, int out_bf16, int64_t n_rows, int n_heads,
                         int head_dim, const RopeTab& tab, hipStream_t st) {

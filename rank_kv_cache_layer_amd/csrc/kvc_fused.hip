@@ -542,14 +542,6 @@ __global__ void __launch_bounds__(512) fused_hop(FusedArgs p) {
 }
 
 // ------------------------------------------------------------------------ B packing
-struct PackArgs {
-  const uint16_t* src[4];
-  uint16_t* dst[4];
-  int32_t negate[4];
-  int32_t rotate[4];
-  FusedTab tab;
-  int32_t n_arrays, n_layers, n_anchors, r, D, head_dim;
-};
 
 __global__ void __launch_bounds__(256) pack_b(PackArgs p) {
   __shared__ float cs[kFusedHalf], sn[kFusedHalf];
@@ -633,12 +625,9 @@ hipError_t fused_dispatch(const FusedArgs& a, int mode, hipStream_t st) {
 // gathers its chunk lanes' 8 rank values of one channel (and of its rotary partner) from LDS and
 // writes them as one 16-byte store.  Output identical to pack_b.
 constexpr int kPackPad = 8;   // LDS row padding (elements)
-__global__ void __launch_bounds__(256) pack_b_rows(PackArgs p) {
-  extern __shared__ uint16_t rows_s[];   // [16][D + kPackPad]
-  __shared__ float cs[kFusedHalf], sn[kFusedHalf];
+__device__ __forceinline__ void pack_rows(const PackArgs& p, int64_t blk, uint16_t* rows_s, float* cs, float* sn) {
   const int D = p.D, hd = p.head_dim, h = hd >> 1, RK = (p.r + 15) >> 4, NCB = D >> 5, ld = D + kPackPad;
   const int tid = threadIdx.x;
-  int64_t blk = blockIdx.x;
   const int ks = (int)(blk % RK);
   blk /= RK;
   const int64_t mats = (int64_t)p.n_layers * p.n_anchors;
@@ -686,25 +675,69 @@ __global__ void __launch_bounds__(256) pack_b_rows(PackArgs p) {
   }
 }
 
-hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const int* negate,
-                         const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors, int r, int D,
-                         int head_dim, hipStream_t st) {
-  if (n_arrays < 1 || n_arrays > 4 || r < 1 || (D & 31) || n_anchors < 1 || head_dim > 2 * kFusedHalf)
-    return hipErrorInvalidValue;
-  PackArgs a;
+__global__ void __launch_bounds__(256) pack_b_rows(PackArgs p) {
+  extern __shared__ uint16_t rows_s[];   // [16][D + kPackPad]
+  __shared__ float cs[kFusedHalf], sn[kFusedHalf];
+  pack_rows(p, blockIdx.x, rows_s, cs, sn);
+}
+
+// batched: descriptor h owns blocks [start[h], start[h + 1])
+__global__ void __launch_bounds__(256) pack_b_rows_batch(const PackArgs* __restrict__ d, BatchTab bt) {
+  extern __shared__ uint16_t rows_s[];
+  __shared__ float cs[kFusedHalf], sn[kFusedHalf];
+  const int64_t b = blockIdx.x;
+  int h = 0;
+  while (h + 1 < bt.n && b >= bt.start[h + 1]) ++h;
+  pack_rows(d[h], b - bt.start[h], rows_s, cs, sn);
+}
+
+static int64_t pack_blocks(const PackArgs& a) {
+  return (int64_t)a.n_arrays * a.n_layers * a.n_anchors * ((a.r + 15) / 16);
+}
+
+bool make_pack_args(PackArgs& a, const uint16_t* const* src, uint16_t* const* dst, const int* negate,
+                    const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors, int r, int D,
+                    int head_dim) {
+  if (n_arrays < 1 || n_arrays > 4 || r < 1 || (D & 31) || n_anchors < 1 || head_dim > 2 * kFusedHalf) return false;
   memset(&a, 0, sizeof a);
   for (int i = 0; i < n_arrays; ++i) {
     a.src[i] = src[i];
     a.dst[i] = dst[i];
     a.negate[i] = negate[i];
     a.rotate[i] = tabs[i] != nullptr;
-    if (tabs[i]) a.tab = *tabs[i];   // at most one distinct rotation per launch
+    if (tabs[i]) a.tab = *tabs[i];   // at most one distinct rotation per descriptor
   }
   a.n_arrays = n_arrays; a.n_layers = n_layers; a.n_anchors = n_anchors; a.r = r; a.D = D; a.head_dim = head_dim;
+  return true;
+}
+
+hipError_t launch_pack_b_batch(const PackArgs* d, const PackArgs* h, int n, hipStream_t st) {
+  if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+  BatchTab bt;
+  bt.n = n;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (h[i].D != h[0].D) return hipErrorInvalidValue;
+    bt.start[i] = (int32_t)total;
+    total += pack_blocks(h[i]);
+  }
+  bt.start[n] = (int32_t)total;
+  const size_t lds = sizeof(uint16_t) * 16 * (size_t)(h[0].D + kPackPad);
+  if (lds > 64 * 1024 || total >= (1ll << 31)) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
+  pack_b_rows_batch<<<(unsigned)total, 256, lds, st>>>(d, bt);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const int* negate,
+                         const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors, int r, int D,
+                         int head_dim, hipStream_t st) {
+  PackArgs a;
+  if (!make_pack_args(a, src, dst, negate, tabs, n_arrays, n_layers, n_anchors, r, D, head_dim))
+    return hipErrorInvalidValue;
   const size_t lds = sizeof(uint16_t) * 16 * (size_t)(D + kPackPad);
   if (lds <= 64 * 1024) {   // rows up to 2040 channels: staged through LDS
-    const int64_t blocks = (int64_t)n_arrays * n_layers * n_anchors * ((r + 15) / 16);
-    pack_b_rows<<<(unsigned)blocks, 256, lds, st>>>(a);
+    pack_b_rows<<<(unsigned)pack_blocks(a), 256, lds, st>>>(a);
     return hipGetLastError();
   }
   const int64_t units = (int64_t)n_arrays * n_layers * n_anchors * (D / 32) * ((r + 15) / 16) * 64;

@@ -20,9 +20,8 @@ namespace {
 constexpr int kMaxLayersGate = 256;
 
 // gsum [3][1 + N_l][N] (row 1 + l): layer l's sums over all tiles, fp64
-__global__ void __launch_bounds__(1024) gate_layer_sums(GateArgs p) {
-  __shared__ double wsum[16][kMaxAnchors];
-  const int N = p.N, L = p.n_layers, l = blockIdx.x;
+__device__ __forceinline__ void layer_sums(const GateArgs& p, int l, double (*wsum)[kMaxAnchors]) {
+  const int N = p.N, L = p.n_layers;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int64_t plane_in = (int64_t)L * p.n_tiles * N;
   const int planes = p.mode == KVC_SCORE_PAGES ? 1 : 3;
@@ -45,8 +44,19 @@ __global__ void __launch_bounds__(1024) gate_layer_sums(GateArgs p) {
   }
 }
 
-__global__ void __launch_bounds__(1024) gate_finalize(GateArgs p) {
-  extern __shared__ double sh[];            // [3][1 + N_l][N]
+__global__ void __launch_bounds__(1024) gate_layer_sums(GateArgs p) {
+  __shared__ double wsum[16][kMaxAnchors];
+  layer_sums(p, blockIdx.x, wsum);
+}
+
+// batched: blockIdx.y = hop (layers past a hop's count have nothing to do)
+__global__ void __launch_bounds__(1024) gate_layer_sums_batch(const GateArgs* __restrict__ d) {
+  __shared__ double wsum[16][kMaxAnchors];
+  const GateArgs& p = d[blockIdx.y];
+  if ((int)blockIdx.x < p.n_layers) layer_sums(p, blockIdx.x, wsum);
+}
+
+__device__ __forceinline__ void finalize(const GateArgs& p, double* sh) {   // sh: [3][1 + N_l][N]
   const int N = p.N, L = p.n_layers;
   const int rows = 1 + L;
   const int planes = p.mode == KVC_SCORE_PAGES ? 1 : 3;
@@ -125,6 +135,16 @@ __global__ void __launch_bounds__(1024) gate_finalize(GateArgs p) {
   }
 }
 
+__global__ void __launch_bounds__(1024) gate_finalize(GateArgs p) {
+  extern __shared__ double sh[];
+  finalize(p, sh);
+}
+
+__global__ void __launch_bounds__(1024) gate_finalize_batch(const GateArgs* __restrict__ d) {
+  extern __shared__ double sh[];
+  finalize(d[blockIdx.x], sh);
+}
+
 }  // namespace
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t st) {
@@ -139,4 +159,26 @@ hipError_t launch_gate(const GateArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+}  // namespace kvc
+
+namespace kvc {
+hipError_t launch_gate_batch(const GateArgs* d, const GateArgs* h, int n, hipStream_t st) {
+  if (n < 1 || n > 65535) return hipErrorInvalidValue;
+  int lmax = 0;
+  size_t shmem = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t b = sizeof(double) * 3 * (1 + h[i].n_layers) * (h[i].N > 0 ? h[i].N : 1);
+    if (h[i].n_layers > kMaxLayersGate || b > 160 * 1024 || h[i].N > kMaxAnchors || !h[i].gsum)
+      return hipErrorInvalidValue;
+    lmax = lmax > h[i].n_layers ? lmax : h[i].n_layers;
+    shmem = shmem > b ? shmem : b;
+  }
+  if (lmax > 0) {
+    gate_layer_sums_batch<<<dim3((unsigned)lmax, (unsigned)n), 1024, 0, st>>>(d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  gate_finalize_batch<<<(unsigned)n, 1024, shmem, st>>>(d);
+  return hipGetLastError();
+}
 }  // namespace kvc

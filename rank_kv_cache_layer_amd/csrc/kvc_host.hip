@@ -502,7 +502,15 @@ kvc_status split_apply_fields(SplitArgs& f, void* k_out, void* v_out, const kvc_
 // Anchor-major token weights for the two-pass apply (and the caller's copy, if requested).
 kvc_status run_split_weights(SplitArgs& f, int wmode, char* ws, const Plan& pl, Tracer& tr, hipStream_t st) {
   f.wa = reinterpret_cast<float*>(ws + pl.off_wa);
-  if (f.n_corr < 1) return KVC_OK;
+  if (f.n_corr < 1) {   // no correcting anchor (e.g. every arena slot empty): the caller's weights are 0
+    const int64_t n = (int64_t)f.n_layers * f.S * f.N;   // [n_layers][seq_len][n_anchors]
+    for (int s = 0; s < 2; ++s)
+      if (f.w_out[s]) {
+        hipError_t e = launch_fill(f.w_out[s], n, 0.f, st);
+        if (e != hipSuccess) return hip_fail(e, "weights fill");
+      }
+    return KVC_OK;
+  }
   tr.begin(KVC_K_WEIGHTS_SPLIT);
   hipError_t e = launch_split_weights(f, wmode, st);
   tr.end();
@@ -817,6 +825,208 @@ kvc_status validate_hop(const HopReq& h, kvc_dtype dt, const kvc_shape& sh, cons
   return KVC_OK;
 }
 
+// ----------------------------------------------------------------- batched chain levels
+// KVCMAS Sec. 3.2 Eq. 6 and App. A.3 "Cache Materialization": a materialised target is the next
+// edge's source, so hop h of every request depends only on hop h - 1 of the same request.  The
+// hops of one level (the same depth in their chains) are independent and run as one grid per
+// kernel: descriptors of every hop in device memory, each hop with its own workspace region.
+struct LevelHop {
+  int idx;   // index in the caller's hop array
+  HopReq h;
+  Sets sets;
+  Plan pl;
+  const int32_t* pred;
+};
+
+// a hop the batched kernels take: the two-pass path end to end, with at least one anchor to apply
+bool batchable(const Plan& pl, const Sets& s, const kvc_pool& p) {
+  return pl.split_match && pl.split_apply && !pl.fused_split && p.n_anchors > 0 && !s.corr_list.empty() &&
+         (p.rank_base == 16 || p.rank_base == 32);
+}
+
+size_t level_desc_bytes(int n) {
+  return up256(sizeof(SplitArgs) * n) + up256(sizeof(GateArgs) * n) + up256(sizeof(PackArgs) * 2 * n);
+}
+
+// per-hop regions of a level run batched: one plan-sized region per hop
+size_t level_region_bytes(const std::vector<LevelHop>& v) {
+  size_t t = 0;
+  for (const LevelHop& x : v) t += up256(x.pl.total);
+  return t;
+}
+
+// Host descriptors of one batched group; `region` = its hops' workspace regions.
+struct LevelArgs {
+  std::vector<SplitArgs> sa;
+  std::vector<GateArgs> ga;
+  std::vector<PackArgs> pa;
+};
+
+kvc_status level_args(LevelArgs& la, const std::vector<LevelHop>& v, const kvc_shape& sh, const kvc_rope* rope,
+                      const kvc_params& prm, char* region) {
+  const int n = (int)v.size();
+  la.sa.resize(n);
+  la.ga.resize(n);
+  la.pa.resize(2 * n);
+  const float inv_temp = (float)(1.0 / prm.temp_weight);
+  const int D = D_of(sh);
+  for (int i = 0; i < n; ++i) {
+    const LevelHop& x = v[i];
+    const kvc_pool& p = *x.h.pool;
+    char* w = region;
+    region += up256(x.pl.total);
+    kvc_status r;
+    SplitArgs& f = la.sa[i];
+    if ((r = split_args(f, x.h.k_src, x.h.v_src, sh, x.h.p_src, x.h.p_tgt, rope, p, x.sets, inv_temp)) != KVC_OK)
+      return r;
+    // operands: base B negated (scores E = Z - A B), delta B with key rows turned by R(p_tgt)
+    uint16_t* pb = reinterpret_cast<uint16_t*>(w + x.pl.off_pack_base);
+    uint16_t* pd = reinterpret_cast<uint16_t*>(w + x.pl.off_pack_delta);
+    const size_t per_b = (size_t)sh.n_layers * p.n_anchors * D * rpad16(p.rank_base);
+    const size_t per_d = (size_t)sh.n_layers * p.n_anchors * D * rpad16(p.rank_delta);
+    FusedTab tgt;
+    if ((r = fused_tab(tgt, x.h.p_tgt, sh.head_dim, rope)) != KVC_OK) return r;
+    {
+      const uint16_t* src[2] = {(const uint16_t*)p.baseB_k, (const uint16_t*)p.baseB_v};
+      uint16_t* dst[2] = {pb, pb + per_b};
+      const int neg[2] = {1, 1};
+      const FusedTab* tabs[2] = {nullptr, nullptr};
+      if (!make_pack_args(la.pa[2 * i], src, dst, neg, tabs, 2, sh.n_layers, p.n_anchors, p.rank_base, D,
+                          sh.head_dim))
+        return fail(KVC_E_PARAM, "batched hop: base factors cannot be packed");
+    }
+    {
+      const int sl = split_apply_slices(p.rank_delta);
+      const uint16_t* src[2] = {(const uint16_t*)p.deltaB_k, (const uint16_t*)p.deltaB_v};
+      uint16_t* dst[2] = {pd, pd + per_d};
+      const int neg[2] = {0, 0};
+      const FusedTab* tabs[2] = {&tgt, nullptr};
+      if (!make_pack_args(la.pa[2 * i + 1], src, dst, neg, tabs, 2, sh.n_layers, p.n_anchors * sl,
+                          p.rank_delta / sl, D, sh.head_dim))
+        return fail(KVC_E_PARAM, "batched hop: delta factors cannot be packed");
+    }
+    f.Ab[0] = (const uint16_t*)p.baseA_k; f.Ab[1] = (const uint16_t*)p.baseA_v;
+    f.Bb[0] = pb; f.Bb[1] = pb + per_b;
+    f.mpart = reinterpret_cast<float*>(w + x.pl.off_mpart);
+    f.partials = reinterpret_cast<float*>(w + x.pl.off_partials);
+    f.w_out[0] = x.h.out->w_k; f.w_out[1] = x.h.out->w_v;
+    f.wa = reinterpret_cast<float*>(w + x.pl.off_wa);
+    f.out[0] = (uint16_t*)x.h.k_out; f.out[1] = (uint16_t*)x.h.v_out;
+    f.Ad[0] = (const uint16_t*)p.deltaA_k; f.Ad[1] = (const uint16_t*)p.deltaA_v;
+    f.Bd[0] = pd; f.Bd[1] = pd + per_d;
+    f.apply = 1;
+    GateArgs& g = la.ga[i];
+    memset(&g, 0, sizeof g);
+    g.partials = f.partials;
+    g.gsum = reinterpret_cast<double*>(w + x.pl.off_gsum);
+    g.dist = x.h.out->dist; g.stat = x.h.out->stat; g.flags = x.h.out->flags;
+    g.pred_flags = x.pred;
+    g.n_layers = sh.n_layers; g.n_tiles = x.pl.n_tiles; g.N = p.n_anchors; g.mode = prm.mode;
+    g.capacity = p.capacity == 0 ? p.n_anchors : p.capacity;
+    g.mask_gate = x.sets.gate; g.tau = prm.tau; g.temp_gate = prm.temp_gate;
+  }
+  return KVC_OK;
+}
+
+// device copies of a group's descriptors at `d` (level_desc_bytes(n) bytes, uploaded already)
+kvc_status launch_level(const LevelArgs& la, const char* d, const kvc_shape& sh, const kvc_params& prm,
+                        hipStream_t st) {
+  const int n = (int)la.sa.size();
+  Tracer tr{prm.trace, st};
+  const SplitArgs* ds = reinterpret_cast<const SplitArgs*>(d);
+  const GateArgs* dg = reinterpret_cast<const GateArgs*>(d + up256(sizeof(SplitArgs) * n));
+  const PackArgs* dp = reinterpret_cast<const PackArgs*>(d + up256(sizeof(SplitArgs) * n) + up256(sizeof(GateArgs) * n));
+  tr.begin(KVC_K_PACK_BASE);
+  hipError_t e = launch_pack_b_batch(dp, la.pa.data(), 2 * n, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "batched pack kernel");
+  tr.begin(KVC_K_SCORE_SPLIT);
+  e = launch_split_score_batch(ds, la.sa.data(), n, sh.head_dim, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "batched score kernel");
+  tr.begin(KVC_K_GATE);
+  e = launch_gate_batch(dg, la.ga.data(), n, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "batched gate kernels");
+  tr.begin(KVC_K_WEIGHTS_SPLIT);
+  e = launch_split_weights_batch(ds, la.sa.data(), n, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "batched weights kernel");
+  tr.begin(KVC_K_APPLY_SPLIT);
+  e = launch_split_apply_batch(ds, la.sa.data(), n, sh.head_dim, st);
+  tr.end();
+  if (e != hipSuccess) return hip_fail(e, "batched apply kernel");
+  return KVC_OK;
+}
+
+// Chain depth of every hop (0 = reads a given source) and the hops of each level in index order.
+std::vector<std::vector<int>> chain_levels(const kvc_hop_desc* hops, int n) {
+  std::vector<int> lev(n, 0);
+  int top = 0;
+  for (int i = 0; i < n; ++i) {
+    lev[i] = hops[i].chain_prev >= 0 ? lev[hops[i].chain_prev] + 1 : 0;
+    top = std::max(top, lev[i]);
+  }
+  std::vector<std::vector<int>> out(n ? top + 1 : 0);
+  for (int i = 0; i < n; ++i) out[lev[i]].push_back(i);
+  return out;
+}
+
+HopReq hop_req(const kvc_hop_desc* hops, int i) {
+  const kvc_hop_desc& d = hops[i];
+  return HopReq{d.chain_prev >= 0 ? hops[d.chain_prev].k_out : d.k_src,
+                d.chain_prev >= 0 ? hops[d.chain_prev].v_out : d.v_src,
+                d.k_out, d.v_out, d.p_src, d.p_tgt, &d.pool, const_cast<kvc_match_out*>(&d.out)};
+}
+
+// The hops of each level: groups launched as one grid per kernel (at most kMaxBatch hops each),
+// and hops that take another path, run one call at a time.
+struct BatchLevel {
+  std::vector<std::vector<LevelHop>> groups;
+  std::vector<int> single;
+};
+struct BatchPlan {
+  std::vector<BatchLevel> levels;
+  size_t ws_desc = 0;      // descriptors of every group, uploaded once at the start
+  size_t ws_region = 0;    // largest group's per-hop regions (reused level after level)
+  size_t ws_batched = 0;   // ws_desc + ws_region
+  size_t ws_single = 0;    // largest one-hop workspace
+};
+
+BatchPlan batch_plan(const kvc_hop_desc* hops, int n, kvc_dtype dt, const kvc_shape& sh, const kvc_params& prm) {
+  BatchPlan bp;
+  const bool mode_ok = dt == KVC_BF16 && prm.mode == KVC_SCORE_PAGES && prm.options == 0;
+  for (const std::vector<int>& ids : chain_levels(hops, n)) {
+    BatchLevel lv;
+    std::vector<LevelHop> cur;
+    for (int i : ids) {
+      const kvc_hop_desc& d = hops[i];
+      LevelHop x{i, hop_req(hops, i), anchor_sets(d.pool, sh.seq_len, prm.gate_len), Plan(), nullptr};
+      x.pl = plan(KVC_CALL_CORRECT, sh, d.pool, &prm, x.sets);
+      x.pred = d.chain_prev >= 0 ? hops[d.chain_prev].out.flags : nullptr;
+      bp.ws_single = std::max(bp.ws_single, x.pl.total);
+      if (mode_ok && batchable(x.pl, x.sets, d.pool)) {
+        cur.push_back(x);
+        if ((int)cur.size() == kMaxBatch) {
+          lv.groups.push_back(cur);
+          cur.clear();
+        }
+      } else {
+        lv.single.push_back(i);
+      }
+    }
+    if (!cur.empty()) lv.groups.push_back(cur);
+    for (const auto& g : lv.groups) {
+      bp.ws_desc += level_desc_bytes((int)g.size());
+      bp.ws_region = std::max(bp.ws_region, level_region_bytes(g));
+    }
+    bp.levels.push_back(lv);
+  }
+  // one-hop calls of a batched run use the space after the descriptors too
+  bp.ws_batched = bp.ws_desc ? bp.ws_desc + std::max(bp.ws_region, bp.ws_single) : 0;
+  return bp;
+}
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -1003,6 +1213,20 @@ kvc_status kvc_correct_hop(const void* k_src, const void* v_src, void* k_out, vo
   return s == KVC_OK ? ok() : s;
 }
 
+size_t kvc_hops_batched_workspace_size(const kvc_hop_desc* hops, int32_t n_hops, kvc_dtype dtype, kvc_shape shape,
+                                       const kvc_params* params) {
+  if (!hops || n_hops < 1 || !params || check_shape(shape) != KVC_OK) return 0;
+  for (int i = 0; i < n_hops; ++i) {
+    const kvc_pool& p = hops[i].pool;
+    if (hops[i].chain_prev >= i || p.n_anchors < 0 || p.n_anchors > KVC_MAX_ANCHORS || (p.n_anchors && !p.anchor_len))
+      return 0;
+    for (int a = 0; a < p.n_anchors; ++a)
+      if (is_live(p, a) && p.anchor_len[a] < 1) return 0;
+  }
+  const BatchPlan bp = batch_plan(hops, n_hops, dtype, shape, *params);
+  return std::max(bp.ws_batched, bp.ws_single);
+}
+
 kvc_status kvc_correct_hops_batched(const kvc_hop_desc* hops, int32_t n_hops, kvc_dtype dtype, kvc_shape shape,
                                     const kvc_rope* rope, const kvc_params* params, void* workspace, size_t ws_bytes,
                                     void* stream) {
@@ -1014,29 +1238,69 @@ kvc_status kvc_correct_hops_batched(const kvc_hop_desc* hops, int32_t n_hops, kv
   for (int i = 0; i < n_hops; ++i) {
     const kvc_hop_desc& d = hops[i];
     if (d.chain_prev >= i) return fail(KVC_E_PARAM, "hop %d: chain_prev must precede the hop", i);
-    HopReq h{d.chain_prev >= 0 ? hops[d.chain_prev].k_out : d.k_src,
-             d.chain_prev >= 0 ? hops[d.chain_prev].v_out : d.v_src,
-             d.k_out, d.v_out, d.p_src, d.p_tgt, &d.pool, const_cast<kvc_match_out*>(&d.out)};
-    kvc_status s = validate_hop(h, dtype, shape, rope, params, true);
+    kvc_status s = validate_hop(hop_req(hops, i), dtype, shape, rope, params, true);
     if (s != KVC_OK) {
       char buf[512];
       snprintf(buf, sizeof buf, "hop %d: %s", i, g_err);
       return fail(s, "%s", buf);
     }
-    Sets sets = anchor_sets(d.pool, shape.seq_len, params->gate_len);
-    const size_t need = plan(KVC_CALL_CORRECT, shape, d.pool, params, sets).total;
-    if (need && (!workspace || ws_bytes < need))
-      return fail(KVC_E_WORKSPACE, "hop %d: workspace needs %zu bytes, got %zu", i, need, workspace ? ws_bytes : (size_t)0);
   }
+  const BatchPlan bp = batch_plan(hops, n_hops, dtype, shape, *params);
+  if (bp.ws_single && (!workspace || ws_bytes < bp.ws_single))
+    return fail(KVC_E_WORKSPACE, "workspace needs %zu bytes (one hop at a time) or %zu (batched), got %zu",
+                bp.ws_single, std::max(bp.ws_single, bp.ws_batched), workspace ? ws_bytes : (size_t)0);
+  // batched levels when the workspace holds the descriptors and the largest group; otherwise
+  // every hop on its own
+  const bool batched = bp.ws_desc && workspace && ws_bytes >= bp.ws_batched;
   hipStream_t st = (hipStream_t)stream;
-  for (int i = 0; i < n_hops; ++i) {
-    const kvc_hop_desc& d = hops[i];
-    HopReq h{d.chain_prev >= 0 ? hops[d.chain_prev].k_out : d.k_src,
-             d.chain_prev >= 0 ? hops[d.chain_prev].v_out : d.v_src,
-             d.k_out, d.v_out, d.p_src, d.p_tgt, &d.pool, const_cast<kvc_match_out*>(&d.out)};
-    const int32_t* pred = d.chain_prev >= 0 ? hops[d.chain_prev].out.flags : nullptr;
-    kvc_status s = correct_one(h, dtype, shape, rope, params, (char*)workspace, ws_bytes, pred, st);
-    if (s != KVC_OK) return s;
+  char* ws = (char*)workspace;
+  std::vector<LevelArgs> args;
+  if (batched) {
+    // every group's descriptors (per-hop regions after the descriptor area), one upload
+    std::vector<char> host(bp.ws_desc);
+    size_t off = 0;
+    for (const BatchLevel& lv : bp.levels)
+      for (const auto& g : lv.groups) {
+        args.emplace_back();
+        kvc_status s = level_args(args.back(), g, shape, rope, *params, ws + bp.ws_desc);
+        if (s != KVC_OK) return s;
+        const int n = (int)g.size();
+        const LevelArgs& la = args.back();
+        memcpy(host.data() + off, la.sa.data(), sizeof(SplitArgs) * n);
+        memcpy(host.data() + off + up256(sizeof(SplitArgs) * n), la.ga.data(), sizeof(GateArgs) * n);
+        memcpy(host.data() + off + up256(sizeof(SplitArgs) * n) + up256(sizeof(GateArgs) * n), la.pa.data(),
+               sizeof(PackArgs) * 2 * n);
+        off += level_desc_bytes(n);
+      }
+    hipError_t e = hipMemcpyAsync(ws, host.data(), bp.ws_desc, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "batched hops: descriptor upload");
+  }
+  size_t doff = 0;
+  size_t gi = 0;
+  for (const BatchLevel& lv : bp.levels) {
+    std::vector<int> one = lv.single;
+    if (batched) {
+      for (const auto& g : lv.groups) {
+        kvc_status s = launch_level(args[gi++], ws + doff, shape, *params, st);
+        if (s != KVC_OK) return s;
+        for (const LevelHop& x : g)
+          if (x.h.out->s_cov) *x.h.out->s_cov = x.sets.s_cov;
+        doff += level_desc_bytes((int)g.size());
+      }
+    } else {
+      for (const auto& g : lv.groups)
+        for (const LevelHop& x : g) one.push_back(x.idx);
+      std::sort(one.begin(), one.end());
+    }
+    // past the descriptor area when batched (later groups' descriptors are already there)
+    char* ws1 = batched ? ws + bp.ws_desc : ws;
+    const size_t ws1_bytes = batched ? ws_bytes - bp.ws_desc : ws_bytes;
+    for (int i : one) {
+      const kvc_hop_desc& d = hops[i];
+      const int32_t* pred = d.chain_prev >= 0 ? hops[d.chain_prev].out.flags : nullptr;
+      kvc_status s = correct_one(hop_req(hops, i), dtype, shape, rope, params, ws1, ws1_bytes, pred, st);
+      if (s != KVC_OK) return s;
+    }
   }
   return ok();
 }

@@ -65,6 +65,8 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
 
 hipError_t launch_align(const void* in, void* out, int in_bf16, int out_bf16, int64_t n_rows,
                         int n_heads, int head_dim, const RopeTab& tab, hipStream_t st);
+// p[0 .. n) = v (a kernel, so it also records as a kernel node under graph capture)
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
 // out (fp32) = R(tt) tgt - R(ts) src per rotate-half pair (Eq. 12's observed correction)
 hipError_t launch_observed_delta(const void* tgt, const void* src, int bf16, float* out, int64_t n_rows,
                                  int n_heads, int head_dim, const RopeTab& tt, const RopeTab& ts, hipStream_t st);
@@ -122,6 +124,8 @@ hipError_t launch_score_generic(const ScoreArgs& a, int bf16, int mode, int tile
 hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_apply_generic(const ApplyArgs& a, int bf16, hipStream_t st);
 hipError_t launch_gate(const GateArgs& a, hipStream_t st);
+// `n` hops' gates in two launches; d = device copies of the host descriptors h
+hipError_t launch_gate_batch(const GateArgs* d, const GateArgs* h, int n, hipStream_t st);
 
 // second scoring mode, bf16 MFMA
 hipError_t launch_score_cos_mfma(const ScoreArgs& a, hipStream_t st);
@@ -202,6 +206,21 @@ hipError_t launch_pack_b(const uint16_t* const* src, uint16_t* const* dst, const
                          int r, int D, int head_dim, hipStream_t st);
 hipError_t launch_fused(const FusedArgs& a, int mode, int head_dim, hipStream_t st);
 
+// B packing of several factor sets in one launch (each as launch_pack_b would pack it).
+struct PackArgs {
+  const uint16_t* src[4];
+  uint16_t* dst[4];
+  int32_t negate[4];
+  int32_t rotate[4];
+  FusedTab tab;
+  int32_t n_arrays, n_layers, n_anchors, r, D, head_dim;
+};
+// fills one descriptor (what launch_pack_b would launch); false for an unsupported request
+bool make_pack_args(PackArgs& a, const uint16_t* const* src, uint16_t* const* dst, const int* negate,
+                    const FusedTab* const* tabs, int n_arrays, int n_layers, int n_anchors, int r, int D,
+                    int head_dim);
+hipError_t launch_pack_b_batch(const PackArgs* d, const PackArgs* h, int n, hipStream_t st);
+
 // ------------------------------------------------------------ two-pass path (bf16)
 // Score work-group = 256 tokens x 256 channels of one (layer, side), 8 waves of 64 x 128 (one
 // per CU).  Apply work-group = 128 tokens x 256 channels, 4 waves of 64 x 128; two share a CU
@@ -240,7 +259,20 @@ struct SplitArgs {
   int32_t layer0, n_grp;            // layers [layer0, layer0 + n_grp) in this launch
 };
 
+// Several independent hops in one launch: descriptors in device memory, hop h owning the
+// logical blocks [start[h], start[h + 1]) of the grid.
+constexpr int kMaxBatch = 64;
+struct BatchTab {
+  int32_t n;
+  int32_t start[kMaxBatch + 1];
+};
+
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st);
+// batched forms: `d` = device array of `n` descriptors whose host copies are `h` (read for
+// the grid and LDS sizes); the two-pass path's ranks, one shape
+hipError_t launch_split_score_batch(const SplitArgs* d, const SplitArgs* h, int n, int head_dim, hipStream_t st);
+hipError_t launch_split_weights_batch(const SplitArgs* d, const SplitArgs* h, int n, hipStream_t st);
+hipError_t launch_split_apply_batch(const SplitArgs* d, const SplitArgs* h, int n, int head_dim, hipStream_t st);
 hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st);
 hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st);
 size_t split_score_lds(int r_b);                   // dynamic LDS bytes

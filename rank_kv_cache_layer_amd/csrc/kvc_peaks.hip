@@ -10,10 +10,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// one 16-byte unit per thread over a grid that covers the buffer: on the device this sustains
+// more than grid-stride loops with 1-8 loads in flight per lane (measured 6.5 vs 4.2-5.4 TB/s at
+// 1 GiB with 2048-16384 work-groups); non-temporal, streamed once
 __global__ void __launch_bounds__(256) peak_copy(u32x4* __restrict__ dst, const u32x4* __restrict__ src, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 __global__ void __launch_bounds__(256) peak_mfma(float* sink, int iters) {
@@ -79,10 +81,10 @@ __global__ void __launch_bounds__(256) peak_valu(float* sink, int iters) {
 
 hipError_t launch_peak_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
   const size_t n = bytes / 16;
-  // 8 work-groups of 256 threads per CU, grid-stride over the rest
-  const size_t want = (n + 255) / 256;
-  const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-  peak_copy<<<grid, 256, 0, st>>>(static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n);
+  const size_t grid = (n + 255) / 256;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffffu) return hipErrorInvalidValue;
+  peak_copy<<<(unsigned)grid, 256, 0, st>>>(static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n);
   return hipGetLastError();
 }
 

@@ -238,8 +238,7 @@ struct TileId {
   int cq, tt, layer, side;
 };
 template <bool side_first = false>
-__device__ __forceinline__ TileId tile_id(const SplitArgs& p) {
-  int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ TileId tile_id(const SplitArgs& p, int64_t lb) {
   TileId t;
   if constexpr (side_first) {
     t.side = (int)(lb & 1);
@@ -410,17 +409,24 @@ struct Ring {
   }
 };
 
+// Static LDS of a scoring work-group (the operand ring is dynamic LDS).
+struct ScoreShared {
+  float mp[2][2][kScoreTile];                    // |E| sums of two anchors, both channel halves
+  float qp[kScoreThreads / 64][kMaxAnchors];     // per-wave gate sums
+  float tab[2][kFusedHalf];                      // R(-p_src) table
+};
+
+// One scoring tile (logical block `lb` of the hop described by `p`).
 template <int HD, int RK>
-__global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
+__device__ __forceinline__ void score_tile(const SplitArgs& p, int64_t lb, char* ring, ScoreShared& sh) {
   constexpr int kST = kScoreTile, kNT = kScoreThreads, kNW = kNT / 64;
   using RG = Ring<RK, kST, kNW, false>;
   constexpr int R = RK * 16;
-  extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
-  __shared__ float mp[2][2][kST];
-  __shared__ float qp[kNW][kMaxAnchors];
-  __shared__ float tab[2][kFusedHalf];
+  auto& mp = sh.mp;
+  auto& qp = sh.qp;
+  auto& tab = sh.tab;
 
-  const TileId id = tile_id<true>(p);
+  const TileId id = tile_id<true>(p, lb);
   const bool keys = id.side == 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int tw = wave >> 1, cw = wave & 1;
@@ -530,17 +536,45 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
   }
 }
 
+template <int HD, int RK>
+__global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x slot | staging
+  __shared__ ScoreShared sh;
+  score_tile<HD, RK>(p, xcd_remap(blockIdx.x, gridDim.x), ring, sh);
+}
+
+// Hop of logical block `lb` in a batched launch: the hops' block ranges are consecutive.
+__device__ __forceinline__ int batch_hop(const BatchTab& bt, int64_t lb) {
+  int h = 0;
+  while (h + 1 < bt.n && lb >= bt.start[h + 1]) ++h;
+  return h;
+}
+
+// Several independent hops (ragged pools, base ranks 16 or 32) in one grid; descriptors in
+// device memory.  The XCD remap runs over the whole grid, so each hop's tiles stay grouped.
+template <int HD>
+__global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const SplitArgs* __restrict__ d, BatchTab bt) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  __shared__ ScoreShared sh;
+  const int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = batch_hop(bt, lb);
+  const SplitArgs& p = d[h];
+  if (p.r_b == 16)
+    score_tile<HD, 1>(p, lb - bt.start[h], ring, sh);
+  else
+    score_tile<HD, 2>(p, lb - bt.start[h], ring, sh);
+}
+
 // ================================================================== token weights
 // App. A.3 "Correction Weighting": per token and side, softmax over the correction set of
 // -m / T_w (first mode, m = mean |Z_can - A B| from the per-channel-tile partials) or of
 // cosine / T_w (second mode), or the caller's weights as given; 0 past S_cov.  Written
 // anchor-major (w[side][layer][a][t], the apply kernel's operand order) and, if requested,
 // token-major for the caller (w_out[side][layer][t][a], 0 outside the correction set).
-__global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
-  extern __shared__ float xs[];   // [n_corr][256]
+__device__ __forceinline__ void weights_rows(const SplitArgs& p, int wmode, int bx, int by, int side, float* xs) {
   const int tid = threadIdx.x;
-  const int t = blockIdx.x * 256 + tid;
-  const int layer = p.layer0 + blockIdx.y, side = blockIdx.z;
+  const int t = bx * 256 + tid;
+  const int layer = p.layer0 + by;
   const int S = p.S, N = p.N, L = p.n_layers, nc = p.n_corr;
   const bool in = t < S, cov = t < p.s_cov;
   float mx = -INFINITY;
@@ -599,6 +633,19 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
   }
 }
 
+__global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
+  extern __shared__ float xs[];   // [n_corr][256]
+  weights_rows(p, wmode, blockIdx.x, blockIdx.y, blockIdx.z, xs);
+}
+
+// batched: blockIdx.z = 2 hop + side; every hop's weights come from its distance partials
+__global__ void __launch_bounds__(256) split_weights_batch(const SplitArgs* __restrict__ d) {
+  extern __shared__ float xs[];
+  const SplitArgs& p = d[blockIdx.z >> 1];
+  if ((int)blockIdx.x * 256 >= p.S || p.n_corr < 1) return;
+  weights_rows(p, SPLIT_W_PARTIALS, blockIdx.x, blockIdx.y, blockIdx.z & 1, xs);
+}
+
 // ================================================================== pass 2: apply
 // Sec. 3.3 Eq. 8 / App. A.3 Eq. 12: out = R(s) Z + sum_a w_a A_a B'_a, the token weights read
 // anchor-major (split_weights) and folded into the A fragments after they leave LDS.
@@ -610,14 +657,12 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
 // correction anchor j / NS, the same ring slot size as rank RA.  The packed B operand then holds
 // each slice as its own matrix (rows RA k .. RA k + RA - 1 of anchor a at index a NS + k).
 template <int HD, int RKD, int RA, int NS = 1>
-__global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
+__device__ __forceinline__ void apply_tile(const SplitArgs& p, int64_t lb, char* ring, float (*tab)[kFusedHalf]) {
   constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
   constexpr int RS = RA * NS;   // stored rank of the A rows
   using RG = Ring<RKD, kST, kNW, true, RA, RS>;
-  extern __shared__ __attribute__((aligned(16))) char ring[];   // kSlots x RG::SLOT | staging
-  __shared__ float tab[2][kFusedHalf];
 
-  const TileId id = tile_id<true>(p);
+  const TileId id = tile_id<true>(p, lb);
   const bool keys = id.side == 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int tw = wave >> 1, cw = wave & 1;
@@ -704,6 +749,32 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   store_tile(acc, make_rsrc(p.out[id.side] + (int64_t)id.layer * S * D, layer_bytes), tw0, D, d0, stage, lane, col, hi);
 }
 
+template <int HD, int RKD, int RA, int NS = 1>
+__global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];   // kApplySlots x slot | staging
+  __shared__ float tab[2][kFusedHalf];
+  apply_tile<HD, RKD, RA, NS>(p, xcd_remap(blockIdx.x, gridDim.x), ring, tab);
+}
+
+// Several independent hops in one grid (delta ranks 8 to 256, one code path per rank).
+template <int HD>
+__global__ void __launch_bounds__(kApplyThreads, 3) split_apply_batch(const SplitArgs* __restrict__ d, BatchTab bt) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  __shared__ float tab[2][kFusedHalf];
+  const int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = batch_hop(bt, lb);
+  const SplitArgs& p = d[h];
+  const int64_t b = lb - bt.start[h];
+  switch (p.r_d) {
+    case 8: apply_tile<HD, 1, 8>(p, b, ring, tab); break;
+    case 16: apply_tile<HD, 1, 16>(p, b, ring, tab); break;
+    case 32: apply_tile<HD, 2, 32>(p, b, ring, tab); break;
+    case 64: apply_tile<HD, 2, 32, 2>(p, b, ring, tab); break;
+    case 128: apply_tile<HD, 2, 32, 4>(p, b, ring, tab); break;
+    default: apply_tile<HD, 2, 32, 8>(p, b, ring, tab); break;
+  }
+}
+
 template <typename K>
 hipError_t go(K kernel, const SplitArgs& args, int tile, int threads, size_t shmem, hipStream_t st) {
   if (shmem > 64 * 1024) {
@@ -769,6 +840,78 @@ hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st) 
   if (head_dim == 128) return apply_dispatch<128>(a, st);
   if (head_dim == 64) return apply_dispatch<64>(a, st);
   return hipErrorInvalidValue;
+}
+
+namespace {
+// block ranges of the hops of a batched two-pass launch (128-token x 256-channel tiles, both sides)
+bool batch_tab(BatchTab& bt, const SplitArgs* h, int n, int64_t& total) {
+  if (n < 1 || n > kMaxBatch) return false;
+  bt.n = n;
+  total = 0;
+  for (int i = 0; i < n; ++i) {
+    bt.start[i] = (int32_t)total;
+    const int64_t ntt = (h[i].S + kScoreTile - 1) / kScoreTile;
+    total += (int64_t)h[i].nct * ntt * h[i].n_grp * 2;
+    if (h[i].D % kSW || h[i].N > kMaxAnchors) return false;
+  }
+  bt.start[n] = (int32_t)total;
+  return total < (1ll << 31);
+}
+
+template <typename K>
+hipError_t go_batch(K kernel, const SplitArgs* d, const BatchTab& bt, int64_t total, size_t shmem, hipStream_t st) {
+  if (shmem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  kernel<<<dim3((unsigned)total), dim3(kScoreThreads), shmem, st>>>(d, bt);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_split_score_batch(const SplitArgs* d, const SplitArgs* h, int n, int head_dim, hipStream_t st) {
+  static_assert(kScoreThreads == kApplyThreads && kScoreTile == kApplyTile, "one tile grid for both passes");
+  BatchTab bt;
+  int64_t total;
+  if (!batch_tab(bt, h, n, total)) return hipErrorInvalidValue;
+  size_t lds = 0;
+  for (int i = 0; i < n; ++i) {
+    if (h[i].r_b != 16 && h[i].r_b != 32) return hipErrorInvalidValue;
+    lds = std::max(lds, split_score_lds(h[i].r_b));
+  }
+  if (total == 0) return hipSuccess;
+  if (head_dim == 128) return go_batch(split_score_batch<128>, d, bt, total, lds, st);
+  if (head_dim == 64) return go_batch(split_score_batch<64>, d, bt, total, lds, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_apply_batch(const SplitArgs* d, const SplitArgs* h, int n, int head_dim, hipStream_t st) {
+  BatchTab bt;
+  int64_t total;
+  if (!batch_tab(bt, h, n, total)) return hipErrorInvalidValue;
+  size_t lds = 0;
+  for (int i = 0; i < n; ++i) {
+    const int r = h[i].r_d;
+    if ((r != 8 && r != 16 && r != 32 && split_apply_slices(r) == 1) || !h[i].wa) return hipErrorInvalidValue;
+    lds = std::max(lds, split_apply_lds(r));
+  }
+  if (total == 0) return hipSuccess;
+  if (head_dim == 128) return go_batch(split_apply_batch<128>, d, bt, total, lds, st);
+  if (head_dim == 64) return go_batch(split_apply_batch<64>, d, bt, total, lds, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_weights_batch(const SplitArgs* d, const SplitArgs* h, int n, hipStream_t st) {
+  if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+  int nc = 1;
+  for (int i = 0; i < n; ++i) {
+    if (h[i].N > kMaxAnchors || !h[i].wa || h[i].S != h[0].S || h[i].n_grp != h[0].n_grp) return hipErrorInvalidValue;
+    nc = std::max(nc, h[i].n_corr);
+  }
+  const dim3 grid((unsigned)((h[0].S + 255) / 256), (unsigned)h[0].n_grp, 2u * n);
+  split_weights_batch<<<grid, 256, sizeof(float) * 256 * (size_t)nc, st>>>(d);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st) {

@@ -26,7 +26,7 @@ STATUS = {0: "KVC_OK", 1: "KVC_E_NULL", 2: "KVC_E_SHAPE", 3: "KVC_E_DTYPE", 4: "
 
 EXPORTS = ["kvc_abi_version", "kvc_status_str", "kvc_last_error", "kvc_workspace_size",
            "kvc_align_rope", "kvc_match_anchors", "kvc_apply_lowrank_delta", "kvc_correct_hop",
-           "kvc_correct_hops_batched", "kvc_svd_workspace_size", "kvc_anchor_refresh_svd",
+           "kvc_correct_hops_batched", "kvc_hops_batched_workspace_size", "kvc_svd_workspace_size", "kvc_anchor_refresh_svd",
            "kvc_peak_copy", "kvc_peak_mfma_bf16", "kvc_peak_lds_read", "kvc_peak_valu",
            "kvc_observed_delta", "kvc_pool_state_init", "kvc_pool_record_hop", "kvc_pool_view",
            "kvc_pool_insert_workspace_size", "kvc_pool_insert"]
@@ -124,6 +124,8 @@ def lib(path: Optional[str] = None):
     L.kvc_correct_hop.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, Shape, C.c_int64,
                                   C.c_int64, C.POINTER(Rope), C.POINTER(Pool), C.POINTER(Params),
                                   C.POINTER(MatchOut), C.c_void_p, C.c_size_t, C.c_void_p]
+    L.kvc_hops_batched_workspace_size.restype = C.c_size_t
+    L.kvc_hops_batched_workspace_size.argtypes = [C.POINTER(HopDesc), C.c_int32, C.c_int, Shape, C.POINTER(Params)]
     L.kvc_correct_hops_batched.restype = C.c_int
     L.kvc_correct_hops_batched.argtypes = [C.POINTER(HopDesc), C.c_int32, C.c_int, Shape, C.POINTER(Rope),
                                            C.POINTER(Params), C.c_void_p, C.c_size_t, C.c_void_p]
@@ -381,13 +383,25 @@ class Hop:
     out: MatchResult
 
 
+def hops_batched_workspace(hops: Sequence[Hop], shape: Shape, params: Params) -> int:
+    """Workspace bytes kvc_correct_hops_batched needs to run each chain level as one batch."""
+    n = len(hops)
+    arr = (HopDesc * max(n, 1))()
+    keep = []
+    for i, h in enumerate(hops):
+        p, lens = h.pool.c()
+        keep.append(lens)
+        arr[i] = HopDesc(_ptr(h.k_src), _ptr(h.v_src), _ptr(h.k_out), _ptr(h.v_out), h.p_src, h.p_tgt,
+                         h.chain_prev, 0, p, MatchOut())
+    return int(lib().kvc_hops_batched_workspace_size(arr, n, _dt(hops[0].k_out), shape, C.byref(params)))
+
+
 def correct_hops_batched(hops: Sequence[Hop], shape: Shape, params: Params, theta=10000.0, workspace=None,
-                         stream=None):
+                         stream=None, one_at_a_time: bool = False):
     L = lib()
     n = len(hops)
     arr = (HopDesc * max(n, 1))()
     keep = []
-    need = 0
     for i, h in enumerate(hops):
         p, lens = h.pool.c()
         keep.append(lens)
@@ -395,11 +409,16 @@ def correct_hops_batched(hops: Sequence[Hop], shape: Shape, params: Params, thet
                       None)
         arr[i] = HopDesc(_ptr(h.k_src), _ptr(h.v_src), _ptr(h.k_out), _ptr(h.v_out), h.p_src, h.p_tgt,
                          h.chain_prev, 0, p, mo)
-        need = max(need, L.kvc_workspace_size(CALL_CORRECT, shape, C.byref(p), C.byref(params)))
+    dt = _dt(hops[0].k_out)
+    if one_at_a_time:   # the largest one-hop workspace: the library then runs the hops one by one
+        need = max(int(L.kvc_workspace_size(CALL_CORRECT, shape, C.byref(arr[i].pool), C.byref(params)))
+                   for i in range(n))
+    else:
+        need = int(L.kvc_hops_batched_workspace_size(arr, n, dt, shape, C.byref(params)))
     dev = hops[0].k_out.device
     ws = _ws(need, dev, workspace)
     rope, _k2 = rope_of(theta)
-    _check(L.kvc_correct_hops_batched(arr, n, _dt(hops[0].k_out), shape, C.byref(rope), C.byref(params), _ptr(ws),
+    _check(L.kvc_correct_hops_batched(arr, n, dt, shape, C.byref(rope), C.byref(params), _ptr(ws),
                                       ws.numel() if ws is not None else 0, _stream(stream)))
 
 
@@ -408,13 +427,18 @@ def svd_workspace_size(n_mats, rows, cols, rank, oversample) -> int:
 
 
 def anchor_refresh_svd(z: torch.Tensor, rank: int, out_dtype=torch.float32, oversample: int = 16,
-                       power_iters: int = 2, seed: int = 0, workspace=None, stream=None):
-    """z: float32 [n_mats, rows, cols] -> (A [n, rows, rank], B [n, rank, cols], sigma [n, rank])."""
+                       power_iters: int = 2, seed: int = 0, workspace=None, stream=None, a_out=None, b_out=None,
+                       sigma_out=None):
+    """z: float32 [n_mats, rows, cols] -> (A [n, rows, rank], B [n, rank, cols], sigma [n, rank]);
+    a_out / b_out / sigma_out: optional preallocated results (their dtype then sets out_dtype)."""
     L = lib()
     n, m, k = z.shape
-    a = torch.empty((n, m, rank), dtype=out_dtype, device=z.device)
-    b = torch.empty((n, rank, k), dtype=out_dtype, device=z.device)
-    s = torch.empty((n, rank), dtype=torch.float32, device=z.device)
+    if a_out is not None:
+        out_dtype = a_out.dtype
+    a = a_out if a_out is not None else torch.empty((n, m, rank), dtype=out_dtype, device=z.device)
+    b = b_out if b_out is not None else torch.empty((n, rank, k), dtype=out_dtype, device=z.device)
+    s = sigma_out if sigma_out is not None else torch.empty((n, rank), dtype=torch.float32, device=z.device)
+    assert a.shape == (n, m, rank) and b.shape == (n, rank, k) and a.dtype == b.dtype and s.shape == (n, rank)
     need = L.kvc_svd_workspace_size(n, m, k, rank, oversample)
     ws = _ws(need, z.device, workspace)
     _check(L.kvc_anchor_refresh_svd(_ptr(z), n, m, k, rank, _ptr(a), _ptr(b), _dt(a), _ptr(s), oversample,

@@ -46,7 +46,7 @@ SCORE_COS_R = 1
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
 # stream tags for the seeded generators
-_T_SCALE, _T_E, _T_SRCLR, _T_BASE, _T_DELTA, _T_MISC = 1, 2, 3, 4, 5, 6
+_T_SCALE, _T_E, _T_SRCLR, _T_BASE, _T_DELTA, _T_MISC, _T_NOISE = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass
@@ -74,6 +74,7 @@ class HopSpec:
     scaled: bool = True          # per-channel U(0.5, 2) scale
     true_delta_rank: int = 24    # 0 -> plain Gaussian delta factors (tiny workload)
     delta_rms_ratio: float = 0.1
+    noise_ratio: float = 0.01    # exact target: rank-24 correction + this fraction of its rms as noise
     seed: int = 0
     source_seed: int = -1        # seed of the source slab (-1 -> seed); a chain shares A0's
 
@@ -156,8 +157,9 @@ def _delta_factors(spec: HopSpec, rng, s, r, d, rms_src):
     return a, w[:r].copy()
 
 
-def _slab(spec: HopSpec, layer: int, side: int, place_keys):
-    """One (layer, side): returns source [S, D] and per-anchor base/delta factors (fp64)."""
+def _slab(spec: HopSpec, layer: int, side: int, place_keys, with_source: bool = True):
+    """One (layer, side): returns source [S, D] (None without it) and per-anchor base/delta
+    factors (fp64).  The factors are the same with or without the source."""
     S, D, N = spec.seq_len, spec.d_model, spec.n_anchors
     rC, rD = spec.rank_base, spec.rank_delta
     seed = spec.seed
@@ -169,7 +171,6 @@ def _slab(spec: HopSpec, layer: int, side: int, place_keys):
         scale = np.ones(D)
     rms_scale = float(np.sqrt(np.mean(scale ** 2)))
     sigma_b = np.sqrt(2.0) * rms_scale
-    e = _rng(sseed, layer, side, _T_E).standard_normal((S, D)) * scale[None, :]
     # the source's rank-r component; a matched layer's anchor 0 holds exactly these factors
     a_s, b_s = _lowrank(_rng(sseed, layer, side, _T_SRCLR), S, rC, D, sigma_b)
     unrelated = spec.unrelated_layers is not None and layer in spec.unrelated_layers
@@ -179,17 +180,42 @@ def _slab(spec: HopSpec, layer: int, side: int, place_keys):
             base.append((a_s[: lens[0]].copy(), b_s.copy()))
         else:
             base.append(_lowrank(_rng(seed, layer, side, _T_BASE, a), lens[a], rC, D, sigma_b))
-    z = e + a_s @ b_s
-    rms_src = float(np.sqrt(np.mean(z ** 2)))
+    # the source's expected rms (E has variance scale^2 per channel; B_s has orthonormal rows, so
+    # the low-rank part's mean square is ||A_s||^2 / (S D)): the deltas are sized from it, so they
+    # do not depend on whether the source itself is drawn
+    rms_src = float(np.sqrt(np.mean(scale ** 2) + np.sum(a_s ** 2) / (S * D)))
+    z = None
+    if with_source:
+        e = _rng(sseed, layer, side, _T_E).standard_normal((S, D)) * scale[None, :]
+        z = e + a_s @ b_s
     delta = []
     for a in range(N):
         rng = _rng(seed, layer, side, _T_DELTA, a)
         delta.append(_delta_factors(spec, rng, lens[a], rD, D, rms_src))
+    if z is None:
+        return z, base, delta
     if side == 0 and spec.p_src != 0:
         if place_keys is None:
             raise ValueError("p_src != 0 needs a place_keys callable for the key source")
         z = place_keys(z, spec.p_src)
     return z, base, delta
+
+
+def target_noise(spec: HopSpec, layer: int, side: int, rows=None) -> np.ndarray:
+    """The full-rank part of a matched layer's exact target correction: the relation's correction
+    is the rank-24 matrix anchor 0 stores (Delta_true) plus Gaussian noise of rms
+    noise_ratio x rms(Delta_true), which no rank-r anchor holds.  Rows `rows` (default all) of the
+    [S, D] noise, fp64.  Only measurements use it (the normalised error against the exact target);
+    the hop's inputs do not contain it."""
+    S, D = spec.seq_len, spec.d_model
+    sseed = spec.seed if spec.source_seed < 0 else spec.source_seed
+    scale = _rng(sseed, layer, side, _T_SCALE).uniform(0.5, 2.0, size=D) if spec.scaled else np.ones(D)
+    sigma_b = np.sqrt(2.0) * float(np.sqrt(np.mean(scale ** 2)))
+    a_s, _ = _lowrank(_rng(sseed, layer, side, _T_SRCLR), S, spec.rank_base, D, sigma_b)
+    rms_src = float(np.sqrt(np.mean(scale ** 2) + np.sum(a_s ** 2) / (S * D)))
+    std = spec.noise_ratio * spec.delta_rms_ratio * rms_src
+    z = _rng(spec.seed, layer, side, _T_NOISE).standard_normal((S, D)) * std
+    return z if rows is None else z[np.asarray(rows)]
 
 
 def _shared_empty(shape, dt: torch.dtype) -> torch.Tensor:
@@ -214,11 +240,12 @@ def _one_blas_thread() -> None:
 
 
 def _fill(layer_side) -> None:
-    spec, place_keys, out, offs, lens = (_JOB[k] for k in ("spec", "place", "out", "offs", "lens"))
+    spec, place_keys, out, offs, lens, ws = (_JOB[k] for k in ("spec", "place", "out", "offs", "lens", "ws"))
     layer, side = layer_side
     tag = "kv"[side]
-    z, base, delta = _slab(spec, layer, side, place_keys)
-    out[f"{tag}_src"][layer].copy_(torch.from_numpy(z.astype(np.float32)))
+    z, base, delta = _slab(spec, layer, side, place_keys, ws)
+    if ws:
+        out[f"{tag}_src"][layer].copy_(torch.from_numpy(z.astype(np.float32)))
     for a in range(spec.n_anchors):
         o, n = offs[a], lens[a]
         out[f"baseA_{tag}"][layer, o:o + n].copy_(torch.from_numpy(base[a][0].astype(np.float32)))
@@ -227,11 +254,14 @@ def _fill(layer_side) -> None:
         out[f"deltaB_{tag}"][layer, a].copy_(torch.from_numpy(delta[a][1].astype(np.float32)))
 
 
-def make_hop(spec: HopSpec, place_keys: Optional[Callable] = None, workers: Optional[int] = None) -> HopData:
+def make_hop(spec: HopSpec, place_keys: Optional[Callable] = None, workers: Optional[int] = None,
+             with_source: bool = True) -> HopData:
     """Build one hop's inputs; bit-identical for a given spec regardless of worker count.
 
     Large hops are filled by forked worker processes (each (layer, side) slab has its own
-    seeded stream); that path is taken only while no GPU context exists in this process."""
+    seeded stream); that path is taken only while no GPU context exists in this process.
+    with_source=False leaves k_src / v_src as zeros (a chained hop whose source is the previous
+    hop's output); the anchor factors are the same either way."""
     S, D, N, L = spec.seq_len, spec.d_model, spec.n_anchors, spec.n_layers
     rC, rD = spec.rank_base, spec.rank_delta
     lens = spec.lens()
@@ -244,12 +274,12 @@ def make_hop(spec: HopSpec, place_keys: Optional[Callable] = None, workers: Opti
     alloc = _shared_empty if use_procs else (lambda shp, d: torch.empty(shp, dtype=d))
     out = {}
     for side, tag in ((0, "k"), (1, "v")):
-        out[f"{tag}_src"] = alloc((L, S, D), dt)
+        out[f"{tag}_src"] = alloc((L, S, D), dt) if with_source else torch.zeros((L, S, D), dtype=dt)
         out[f"baseA_{tag}"] = alloc((L, tot, rC), dt)
         out[f"baseB_{tag}"] = alloc((L, N, rC, D), dt)
         out[f"deltaA_{tag}"] = alloc((L, tot, rD), dt)
         out[f"deltaB_{tag}"] = alloc((L, N, rD, D), dt)
-    _JOB.update(spec=spec, place=place_keys, out=out, offs=offs, lens=lens)
+    _JOB.update(spec=spec, place=place_keys, out=out, offs=offs, lens=lens, ws=with_source)
     jobs = [(l, s) for l in range(L) for s in (0, 1)]
     try:
         if nw == 1 or len(jobs) == 1:
@@ -343,14 +373,30 @@ def chain_specs(n_requests: int = 8, n_hops: int = 3, seq_len: int = 8192, n_lay
 
 
 def decaying_matrices(n_mats: int, rows: int, cols: int, seed: int = 5, power: float = 1.5,
-                      dtype=torch.float32) -> torch.Tensor:
-    """Z = U diag(i^-power) W^T with U, W orthonormal (QR of Gaussians), one per matrix."""
+                      dtype=torch.float32, reflections: int = 0) -> torch.Tensor:
+    """Z = U diag(i^-power) W^T with U, W orthonormal, one per matrix.
+
+    reflections = 0: U, W from QR of Gaussians (Haar).  reflections = h > 0: U and W are each a
+    product of h random Householder reflections, applied to the diagonal matrix as rank-one
+    updates (the singular values are the same; far cheaper at 4096 x 1024)."""
     out = torch.empty((n_mats, rows, cols), dtype=dtype)
     k = min(rows, cols)
     sig = np.arange(1, k + 1, dtype=np.float64) ** (-power)
 
     def job(m):
         rng = _rng(seed, m, _T_MISC)
+        if reflections > 0:
+            z = np.zeros((rows, cols))
+            z[np.arange(k), np.arange(k)] = sig
+            for _ in range(reflections):
+                u = rng.standard_normal(rows)
+                u /= np.linalg.norm(u)
+                z -= 2.0 * np.outer(u, u @ z)
+                w = rng.standard_normal(cols)
+                w /= np.linalg.norm(w)
+                z -= 2.0 * np.outer(z @ w, w)
+            out[m].copy_(torch.from_numpy(z.astype(np.float32)))
+            return
         u, _ = np.linalg.qr(rng.standard_normal((rows, k)))
         w, _ = np.linalg.qr(rng.standard_normal((cols, k)))
         out[m].copy_(torch.from_numpy(((u * sig[None, :]) @ w.T).astype(np.float32)))

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for name in header_functions():
         assert hasattr(L, name), name
     assert sorted(header_functions()) == sorted(kvc.EXPORTS)
-    assert L.kvc_abi_version() == 2
+    assert L.kvc_abi_version() == 3
 
 
 def test_trace_kernel_ids_named_by_the_binding():

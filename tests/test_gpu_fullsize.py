@@ -1,18 +1,23 @@
-"""Parity at full size, in the launch configuration the benchmark times: the 32768-token
+"""Parity at full size, in the launch configurations the benchmark times: the 32768-token
 Llama-3.1-8B-shaped hop (32 layers, 8 x 128 KV heads, 20 anchors at rank 32, keys at start
-position 512, shift 300, one third of the layers unrelated) and the 4096-token hop corrected
-with 10 anchors at rank 128.  The GPU runs the whole hop; the oracle computes sampled layers
-completely for the gate and sampled tokens of those layers for weights and outputs (the
-oracle takes them one by one, so any sample is exact), and the hop-level gate row is checked
-through the property that ties it to the per-layer rows (Eq. 9 sums the layers' squared
-distances)."""
+position 512, shift 300, one third of the layers unrelated), the 4096-token hop (20 anchors at
+rank 32, shift drawn in 16..512), the 4096-token hop corrected with 10 anchors at rank 128 (also
+behind the anchor refresh: the factorised dense delta is anchor 0), and the concurrent batch of
+8 chains of 3 hops at 8192 tokens.  The GPU runs everything; the oracle computes sampled layers
+completely for the gate and sampled tokens of those layers for weights and outputs (the oracle
+takes them one by one, so any sample is exact), and the hop-level gate row is checked through
+the property that ties it to the per-layer rows (Eq. 9 sums the layers' squared distances)."""
+import dataclasses
+
 import numpy as np
 import pytest
+import torch
 
 from oracle import kvc_oracle as O
+from rank_kv_cache_layer_amd import kvc
 from rank_kv_cache_layer_amd import workload as W
 
-from hop_helpers import TOL_BF16, make, run_gpu, w_atol
+from hop_helpers import DEV, TOL_BF16, make, params, run_gpu, shape, w_atol
 
 pytestmark = pytest.mark.gpu
 
@@ -23,10 +28,10 @@ def _sample_rows(S, seed):
     return np.unique(np.concatenate([np.array([e for e in edges if 0 <= e < S]), rng.integers(0, S, 200)]))
 
 
-def _check_sampled(spec, layers, seed):
+def _check_sampled(spec, layers, seed, data=None):
     print(f"[fullsize] {spec.name} L={spec.n_layers} S={spec.seq_len} N={spec.n_anchors} "
           f"r={spec.rank_base} layers={layers}", flush=True)
-    data = make(spec)
+    data = make(spec) if data is None else data
     gpu = run_gpu(data)
     rows = _sample_rows(spec.seq_len, seed)
     N = spec.n_anchors
@@ -85,3 +90,119 @@ def test_32k_hop_sampled_cosine_mode():
 def test_rank128_hop_sampled():
     spec = W.llama8b_rank128()
     _check_sampled(spec, layers=[0, 13, 31], seed=2)
+
+
+@pytest.mark.timeout(900)
+def test_4k_hop_sampled():
+    # the 4096-token Llama-3.1-8B-shaped hop: 20 anchors at rank 32, every layer matched
+    spec = W.llama8b_hop()
+    gpu = _check_sampled(spec, layers=[0, 11, 31], seed=4)
+    assert [int(x) for x in gpu["flags"]] == [0] * 33
+
+
+@pytest.mark.timeout(900)
+def test_rank128_refresh_then_correction_sampled():
+    # KVCMAS Sec. 3.3 Eq. 7 then Eq. 8: dense fp32 deltas (4096 x 1024 per layer and side, singular
+    # values i^-1.5) factorised at rank 128 by the library's refresh become anchor 0's delta
+    # factors (bf16) of the rank-128 correction with 10 anchors; the oracle corrects with exactly
+    # those factors (the refresh's outputs are its inputs)
+    spec = W.llama8b_rank128()
+    data = make(spec)
+    L, S, D, r = spec.n_layers, spec.seq_len, spec.d_model, spec.rank_delta
+    print(f"[fullsize] refresh: {2 * L} decaying matrices {S}x{D} at rank {r}", flush=True)
+    z = W.decaying_matrices(2 * L, S, D, seed=5, reflections=8)
+    a, b, sig = kvc.anchor_refresh_svd(z.to(DEV), r, out_dtype=torch.bfloat16, oversample=32, power_iters=3)
+    torch.cuda.synchronize()
+    ac, bc = a.cpu(), b.cpu()
+    for side, j in (("k", 0), ("v", 1)):
+        getattr(data, f"deltaA_{side}")[:, :S] = ac[j::2]
+        getattr(data, f"deltaB_{side}")[:, 0] = bc[j::2]
+    # the refreshed anchor reproduces its dense delta to the truncation error (diagnostic: the
+    # Eckart-Young optimum is 4.979e-3 for this spectrum; bf16 factors add their rounding)
+    m = 7
+    err = np.linalg.norm(ac[m].double().numpy() @ bc[m].double().numpy() - z[m].double().numpy()) / \
+        np.linalg.norm(z[m].double().numpy())
+    print(f"[fullsize] refreshed anchor, matrix {m}: relative error {err:.4e}", flush=True)
+    assert err < 2 * 4.979e-3
+    del z, a, b
+    _check_sampled(spec, layers=[0, 13, 31], seed=5, data=data)
+
+
+def _layers_of(d, layers):
+    idx = torch.tensor(layers)
+    t = {k: v.index_select(0, idx) for k, v in d.tensors().items()}
+    return dataclasses.replace(d, spec=dataclasses.replace(d.spec, n_layers=len(layers)), **t)
+
+
+@pytest.mark.timeout(1500)
+def test_chain_batch_full_size_sampled():
+    # the concurrent batch at full size: 8 requests x 3 chained hops (A0 -> A3), 32 layers x 8192
+    # tokens x 8x128, per hop 10-20 anchors at rank 16 or 32 and shifts 0..1024 (seeded chain
+    # specification), each chain level one grid per kernel.  The first three requests carry the
+    # specification's seeded values and are checked on sampled layers and tokens of every hop
+    # against the oracle on the same inputs (hop h's source = the GPU's bf16 output of hop h - 1),
+    # with every layer's flag; the other five carry device-drawn values of the same shapes (the
+    # host generator costs ~30 CPU-seconds per hop) and are checked for finite outputs.
+    reqs = W.chain_specs()
+    n_seeded = 3
+    layers = [0, 17, 31]
+    h0 = reqs[0][0]
+    L, S, D = h0.n_layers, h0.seq_len, h0.d_model
+    g = torch.Generator(device=DEV).manual_seed(4)
+    rnd = lambda *sh, sc=1.0: (torch.randn(sh, device=DEV, generator=g) * sc).to(torch.bfloat16)
+    hl, kept = [], []
+    for q, hops in enumerate(reqs):
+        base = len(hl)
+        for i, h in enumerate(hops):
+            if q < n_seeded:
+                d = W.make_hop(h, place_keys=lambda x, p: O.rope(x, p, h.head_dim), with_source=i == 0)
+                if i == 0:
+                    k0, v0 = d.k_src.to(DEV), d.v_src.to(DEV)
+                pool = kvc.pool_from(d, DEV)
+                kept.append(_layers_of(d, layers))
+                del d
+            else:
+                if i == 0:
+                    k0, v0 = rnd(L, S, D), rnd(L, S, D)
+                N, r = h.n_anchors, h.rank_base
+                f = lambda rr: (rnd(L, N * S, rr, sc=0.2), rnd(L, N, rr, D, sc=0.2))
+                (bAk, bBk), (bAv, bBv), (dAk, dBk), (dAv, dBv) = f(r), f(r), f(r), f(r)
+                pool = kvc.PoolTensors([S] * N, r, r, bAk, bBk, bAv, bBv, dAk, dBk, dAv, dBv)
+            hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
+                              torch.empty_like(v0), h.p_src, h.p_tgt, base + i - 1 if i else -1, pool,
+                              kvc.alloc_match(h.n_layers, h.seq_len, h.n_anchors, DEV)))
+            print(f"[fullsize] chain request {q} hop {i}: N={h.n_anchors} r={h.rank_base} p_src={h.p_src} "
+                  f"p_tgt={h.p_tgt} {'seeded' if q < n_seeded else 'device-drawn'}", flush=True)
+    shp, prm = shape(h0), params(h0)
+    assert kvc.hops_batched_workspace(hl, shp, prm) > max(kvc.correct_hop_workspace(shp, x.pool, prm) for x in hl)
+    kvc.correct_hops_batched(hl, shp, prm)
+    torch.cuda.synchronize()
+    print("[fullsize] chain batch done on the GPU", flush=True)
+    for x in hl[3 * n_seeded:]:
+        assert torch.isfinite(x.k_out).all() and torch.isfinite(x.v_out).all()
+    idx = torch.tensor(layers, device=DEV)
+    rows = _sample_rows(S, 7)
+    rows_d = torch.from_numpy(rows).to(DEV)
+    for j in range(3 * n_seeded):
+        q, i = divmod(j, 3)
+        h = reqs[q][i]
+        d = kept[j]
+        if i > 0:   # the GPU's materialised output of the previous hop is this hop's source
+            d = dataclasses.replace(d, k_src=hl[j - 1].k_out.index_select(0, idx).cpu(),
+                                    v_src=hl[j - 1].v_out.index_select(0, idx).cpu())
+        gh = hl[j]
+        flags = gh.out.flags.cpu().numpy()
+        assert list(flags) == [0] * (1 + L), (q, i, flags)
+        N = h.n_anchors
+        for li, l in enumerate(layers):
+            ref = O.correct_layer(d, li, rows=rows)
+            for side in ("k", "v"):
+                want = O.round_to(ref[f"{side}_out"], "bf16")
+                got = getattr(gh, f"{side}_out")[l].index_select(0, rows_d).double().cpu().numpy()
+                assert np.max(np.abs(got - want)) <= TOL_BF16 * np.max(np.abs(want)), (q, i, l, side)
+                wg = getattr(gh.out, f"w_{side}")[l].index_select(0, rows_d)[:, :N].double().cpu().numpy()
+                assert np.max(np.abs(wg - ref[f"w_{side}"])) <= w_atol(W.BF16), (q, i, l, side)
+            dd, hh, ff = O.gate_decide_pages(np.asarray(ref["q"]), h.tau, h.temp_gate, h.cap(), N)
+            assert ff == 0 and abs(hh - h.tau) >= 0.05, (q, i, l, hh)
+            assert np.allclose(gh.out.dist[1 + l][:N].cpu().numpy(), dd, rtol=1e-4), (q, i, l)
+        print(f"[fullsize] chain request {q} hop {i}: sampled layers {layers} match the oracle", flush=True)

@@ -103,12 +103,56 @@ def test_ranks_bf16(rank, mode):
 
 @pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
 def test_rank_sliced_delta_ragged_bf16(mode):
-    # a rank-128 delta in four slices of 32 behind rank-32 scores, anchors of unequal length (the
-    # covered prefix ends inside the second token tile; a slice's A rows past an anchor's length
-    # read as zeros), a ragged tail tile
+    # a rank-128 delta in four slices of 32 behind rank-32 scores, anchors of unequal length, a
+    # ragged tail tile: every anchor covers the segment's first 180 rows (gate prefix), the
+    # longest covers 333 = S, so the correction set is anchors 0 and 3
     sp = W.llama8b_hop(n_layers=2, seq_len=333, n_anchors=5, rank_base=32, rank_delta=128, n_kv_heads=2,
-                       anchor_len=[333, 250, 180, 333, 201], mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+                       anchor_len=[333, 250, 180, 333, 201], gate_len=180, mode=mode,
+                       tau=0.3 if mode == W.SCORE_PAGES else 0.5)
     _check_hop(sp, label=f"rank-delta-128-ragged-{mode}")
+
+
+@pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
+@pytest.mark.parametrize("rank", [64, 128, 256])
+def test_rank_sliced_partial_coverage(rank, mode):
+    # App. A.3 "Variable Segment Lengths" at the sliced delta ranks: the longest anchor (250 rows)
+    # is shorter than the segment (333), so S_cov = 250 ends inside the second 128-token tile, rows
+    # 250.. keep R(s) K / V exactly, and the correction set is the anchors of length 250 (0, 1, 3);
+    # a slice's A rows past an anchor's length read as zeros.  Gate prefix 180 (all five anchors)
+    rb = 32 if rank == 256 else rank
+    sp = W.llama8b_hop(n_layers=2, seq_len=333, n_anchors=5, rank_base=rb, rank_delta=rank, n_kv_heads=2,
+                       anchor_len=[250, 250, 180, 250, 201], gate_len=180, mode=mode,
+                       tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+    data, ref, gpu = _check_hop(sp, label=f"rank{rank}-partial-{mode}")
+    assert ref["s_cov"] == 250
+    # rows past coverage keep the source: values bit for bit, keys re-aligned (within the bound above)
+    assert np.array_equal(gpu["v_out"][:, 250:], O._np(data.v_src)[:, 250:])
+
+
+@pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
+@pytest.mark.parametrize("rank", [32, 128])
+def test_no_live_anchor_writes_zero_weights(rank, mode):
+    # an arena whose slots are all empty: no anchor scores, corrects or gates; the hop is flagged
+    # (fewer than two compatible anchors), the output is the re-aligned source and every token
+    # weight the caller asked for is written as 0 (the buffers start as NaN here)
+    sp = W.llama8b_hop(n_layers=2, seq_len=200, n_anchors=4, rank_base=rank, rank_delta=rank, n_kv_heads=2,
+                       mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5)
+    data = make(sp)
+    k, v = data.k_src.to(DEV), data.v_src.to(DEV)
+    pool = kvc.pool_from(data, DEV)
+    pool.live = [0] * sp.n_anchors
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    out = kvc.alloc_match(sp.n_layers, sp.seq_len, sp.n_anchors, DEV)
+    out.w_k.fill_(float("nan"))
+    out.w_v.fill_(float("nan"))
+    kvc.correct_hop(k, v, ko, vo, shape(sp), sp.p_src, sp.p_tgt, pool, params(sp), out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out.w_k).item() == 0 and torch.count_nonzero(out.w_v).item() == 0
+    assert out.s_cov == 0
+    assert np.all(out.flags.cpu().numpy() & O.FLAG_FEW_ANCHORS)
+    exp_k = O.round_to(O.rope(O._np(data.k_src), sp.shift, sp.head_dim), "bf16")
+    assert np.max(np.abs(ko.double().cpu().numpy() - exp_k)) <= 2.0 ** -7 * np.max(np.abs(exp_k))
+    assert torch.equal(vo, v)
 
 
 def test_rank256_delta_two_pass_bf16():
@@ -180,6 +224,11 @@ COS_CASES = {
                                   anchor_len=[333, 300, 250, 333, 201, 333, 333, 290, 333, 260, 333, 333]),
     "r128_hd64": dict(n_layers=2, seq_len=260, n_kv_heads=4, head_dim=64, n_anchors=7, rank_base=128,
                       rank_delta=128, anchor_len=[260, 200, 260, 260, 150, 260, 230]),
+    # the longest anchor shorter than the segment: S_cov < S at the sliced ranks
+    "r64_partial": dict(n_layers=2, seq_len=333, n_kv_heads=2, n_anchors=6, rank_base=64, rank_delta=64,
+                        gate_len=200, anchor_len=[300, 300, 250, 300, 201, 290]),
+    "r128_partial": dict(n_layers=2, seq_len=260, n_kv_heads=2, n_anchors=5, rank_base=128, rank_delta=128,
+                         gate_len=150, anchor_len=[230, 200, 230, 150, 230]),
 }
 
 
@@ -311,47 +360,85 @@ def test_apply_explicit_one_hot_weights():
         assert np.max(np.abs(gv - exp_v)) <= 2.0 ** -7 * np.max(np.abs(exp_v))
 
 
+def _run_chain(reqs, one_at_a_time=False):
+    """All requests' hops through one kvc_correct_hops_batched call (each chain level batched
+    unless one_at_a_time); returns the per-request hop data and the library's hop records."""
+    datas, hl = [], []
+    for hops in reqs:
+        ds = [make(h) for h in hops]
+        base = len(hl)
+        k0, v0 = ds[0].k_src.to(DEV), ds[0].v_src.to(DEV)
+        for i, (h, d) in enumerate(zip(hops, ds)):
+            hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
+                              torch.empty_like(v0), h.p_src, h.p_tgt, base + i - 1 if i else -1,
+                              kvc.pool_from(d, DEV), kvc.alloc_match(h.n_layers, h.seq_len, h.n_anchors, DEV)))
+        datas.append(ds)
+    kvc.correct_hops_batched(hl, shape(reqs[0][0]), params(reqs[0][0]), one_at_a_time=one_at_a_time)
+    torch.cuda.synchronize()
+    return datas, hl
+
+
+def _check_chain_identical_inputs(reqs, datas, hl, label):
+    """Each hop against the oracle on the same inputs: hop h's source is the GPU's materialised
+    (bf16) output of hop h - 1 (KVCMAS Sec. 3.2 Eq. 6; App. A.3 "Cache Materialization"), so every
+    hop is held to the bf16 bound 2^-7 max|x| and bit-exact flags.  The drift of a chain the oracle
+    runs on its own outputs is printed as a diagnostic only."""
+    base = 0
+    for q, (hops, ds) in enumerate(zip(reqs, datas)):
+        src_k, src_v = ds[0].k_src, ds[0].v_src
+        own_k, own_v = src_k, src_v
+        for i, (h, d) in enumerate(zip(hops, ds)):
+            gh = hl[base + i]
+            ref = O.correct_hop(dataclasses.replace(d, k_src=src_k, v_src=src_v))
+            gpu = dict(k_out=gh.k_out.double().cpu().numpy(), v_out=gh.v_out.double().cpu().numpy())
+            assert_outputs_close(gpu, ref, h.dtype, f"{label} request {q} hop {i}")
+            pred = i > 0 and hl[base + i - 1].out.flags[0].item() != 0
+            flags = gh.out.flags.cpu().numpy()
+            assert np.array_equal(flags, ref["flags"] | (kvc.FLAG_PRED_FLAGGED if pred else 0)), (label, q, i, flags)
+            assert np.all(ref["flags"] == 0), "chain workload: every hop should match its anchor 0"
+            own = O.correct_hop(dataclasses.replace(d, k_src=own_k, v_src=own_v))
+            drift = max(np.max(np.abs(own[s] - gpu[s])) / np.max(np.abs(own[s])) for s in ("k_out", "v_out"))
+            print(f"[parity] {label} request {q} hop {i}: N={h.n_anchors} r={h.rank_base}; oracle-only chain "
+                  f"drift {drift:.2e} of max|x| (diagnostic)", flush=True)
+            # the next hop's source: the GPU's bf16 output (the oracle's own, for the diagnostic)
+            src_k, src_v = gh.k_out.cpu(), gh.v_out.cpu()
+            own_k = torch.from_numpy(own["k_out"]).to(torch.bfloat16)
+            own_v = torch.from_numpy(own["v_out"]).to(torch.bfloat16)
+        base += len(hops)
+
+
 @pytest.mark.parametrize("mode", [W.SCORE_PAGES, W.SCORE_COS_R])
 @pytest.mark.parametrize("rank", [0, 128])
-def test_batched_chain_matches_sequential_oracle(mode, rank):
-    # rank 0: the chain specification's ranks (16 / 32); 128: every pool at rank 128 (the sliced
-    # apply behind fused scores in the first mode, four column groups per anchor and up to four
-    # passes in the second)
+def test_batched_chain_matches_oracle_hop_by_hop(mode, rank):
+    # rank 0: the chain specification's ranks (16 / 32); 128: every pool at rank 128 (first mode:
+    # the sliced apply behind fused scores, so those hops run one call at a time; second mode: four
+    # column groups per anchor and up to four passes)
     reqs = W.chain_specs(n_requests=2, n_hops=3, seq_len=256, n_layers=2, n_kv_heads=2)
-    for hops in reqs:
-        if rank:
-            hops = [dataclasses.replace(h, rank_base=rank, rank_delta=rank) for h in hops]
-        if mode == W.SCORE_COS_R:   # second mode: rank 16 on the generic scores, the GEMM otherwise
-            hops = [dataclasses.replace(h, mode=mode, tau=0.5) for h in hops]
-        print(f"[parity] chain mode={mode} ranks={[h.rank_base for h in hops]}", flush=True)
-        datas = [make(h) for h in hops]
-        shp = shape(hops[0])
-        k0 = datas[0].k_src.to(DEV)
-        v0 = datas[0].v_src.to(DEV)
-        hl = []
-        for i, (h, d) in enumerate(zip(hops, datas)):
-            pool = kvc.pool_from(d, DEV)
-            out = kvc.alloc_match(h.n_layers, h.seq_len, h.n_anchors, DEV)
-            hl.append(kvc.Hop(k0 if i == 0 else None, v0 if i == 0 else None, torch.empty_like(k0),
-                              torch.empty_like(v0), h.p_src, h.p_tgt, i - 1, pool, out))
-        kvc.correct_hops_batched(hl, shp, params(hops[0]))
-        torch.cuda.synchronize()
-        # oracle: hop by hop, rounding to bf16 between hops (materialisation)
-        src_k, src_v = datas[0].k_src, datas[0].v_src
-        for i, (h, d) in enumerate(zip(hops, datas)):
-            d = dataclasses.replace(d, k_src=src_k, v_src=src_v)
-            ref = O.correct_hop(d)
-            gk = hl[i].k_out.double().cpu().numpy()
-            gv = hl[i].v_out.double().cpu().numpy()
-            assert np.max(np.abs(gk - ref["k_out"])) <= 2.0 ** -7 * np.max(np.abs(ref["k_out"])) * (i + 1)
-            assert np.max(np.abs(gv - ref["v_out"])) <= 2.0 ** -7 * np.max(np.abs(ref["v_out"])) * (i + 1)
-            flags = hl[i].out.flags.cpu().numpy()
-            pred = i > 0 and hl[i - 1].out.flags[0].item() != 0
-            assert np.array_equal(flags, ref["flags"] | (8 if pred else 0))   # 8: predecessor flagged
-            assert np.all(ref["flags"] == 0), "chain workload: every hop should match its anchor 0"
-            # the oracle chains its own materialised (bf16-rounded) output into the next hop
-            src_k = torch.from_numpy(ref["k_out"]).to(torch.bfloat16)
-            src_v = torch.from_numpy(ref["v_out"]).to(torch.bfloat16)
+    reqs = [[dataclasses.replace(h, rank_base=rank or h.rank_base, rank_delta=rank or h.rank_delta,
+                                 mode=mode, tau=0.3 if mode == W.SCORE_PAGES else 0.5) for h in hops]
+            for hops in reqs]
+    print(f"[parity] chain mode={mode} ranks={[h.rank_base for hops in reqs for h in hops]}", flush=True)
+    datas, hl = _run_chain(reqs)
+    _check_chain_identical_inputs(reqs, datas, hl, f"chain-{mode}-{rank}")
+
+
+def test_batched_chain_8b_heads_levels_batched():
+    # the chain specification at the 8B head layout (8 x 128, D = 1024), 4 layers, 1024 tokens,
+    # 3 requests x 3 hops, pools of 10-20 anchors at ranks 16 / 32: each level runs as one grid per
+    # kernel; the outputs, weights and gate rows equal those of one call per hop bit for bit (the
+    # same tile code), and every hop matches the oracle on the GPU's own chained inputs
+    reqs = W.chain_specs(n_requests=3, n_hops=3, seq_len=1024, n_layers=4, n_kv_heads=8)
+    print(f"[parity] chain 8x128: N={[h.n_anchors for hops in reqs for h in hops]} "
+          f"r={[h.rank_base for hops in reqs for h in hops]}", flush=True)
+    assert {h.rank_base for hops in reqs for h in hops} == {16, 32}
+    datas, hl = _run_chain(reqs)
+    _, hl1 = _run_chain(reqs, one_at_a_time=True)
+    for a, b in zip(hl, hl1):
+        assert torch.equal(a.k_out, b.k_out) and torch.equal(a.v_out, b.v_out)
+        assert torch.equal(a.out.flags, b.out.flags)
+        assert torch.equal(a.out.dist.nan_to_num(-1.0), b.out.dist.nan_to_num(-1.0))
+        assert torch.equal(a.out.w_k, b.out.w_k) and torch.equal(a.out.w_v, b.out.w_v)
+    _check_chain_identical_inputs(reqs, datas, hl, "chain-8x128")
 
 
 def test_fan_in_ragged_pools_in_one_batched_call():
