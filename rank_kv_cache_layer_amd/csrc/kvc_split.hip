@@ -64,8 +64,8 @@ __device__ __forceinline__ int lane_get(int v, int j) { return __builtin_amdgcn_
 struct Slots {
   int a, off, lim;
 };
-__device__ __forceinline__ Slots load_slots(const uint8_t* list, int n, const int32_t* off, const int32_t* len,
-                                            int row_cap, int lane) {
+template <typename L8, typename L32>
+__device__ __forceinline__ Slots load_slots(L8 list, int n, L32 off, L32 len, int row_cap, int lane) {
   Slots s{0, 0, 0};
   if (lane < n) {
     s.a = list[lane];
@@ -237,8 +237,8 @@ __device__ __forceinline__ float xor32_sum(float v) {
 struct TileId {
   int cq, tt, layer, side;
 };
-template <bool side_first = false>
-__device__ __forceinline__ TileId tile_id(const SplitArgs& p, int64_t lb) {
+template <bool side_first = false, typename P>
+__device__ __forceinline__ TileId tile_id(P& p, int64_t lb) {
   TileId t;
   if constexpr (side_first) {
     t.side = (int)(lb & 1);
@@ -417,8 +417,8 @@ struct ScoreShared {
 };
 
 // One scoring tile (logical block `lb` of the hop described by `p`).
-template <int HD, int RK>
-__device__ __forceinline__ void score_tile(const SplitArgs& p, int64_t lb, char* ring, ScoreShared& sh) {
+template <int HD, int RK, typename P>
+__device__ __forceinline__ void score_tile(P& p, int64_t lb, char* ring, ScoreShared& sh) {
   constexpr int kST = kScoreTile, kNT = kScoreThreads, kNW = kNT / 64;
   using RG = Ring<RK, kST, kNW, false>;
   constexpr int R = RK * 16;
@@ -434,7 +434,7 @@ __device__ __forceinline__ void score_tile(const SplitArgs& p, int64_t lb, char*
   const int t0 = id.tt * kST, tw0 = t0 + tw * 64;
   const int d0 = id.cq * kSW + cw * 128;
 
-  const uint8_t* list = keys ? p.corr : p.use;
+  const auto list = keys ? p.corr : p.use;
   int nl = keys ? p.n_corr : p.n_use;
   const int s_work = keys ? (p.n_corr ? p.s_cov : 0) : max(p.n_corr ? p.s_cov : 0, p.mask_gate ? p.k_gate : 0);
   if (t0 >= s_work) nl = 0;
@@ -543,6 +543,13 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score(SplitArgs p) {
   score_tile<HD, RK>(p, xcd_remap(blockIdx.x, gridDim.x), ring, sh);
 }
 
+// A batched launch's descriptor, read through the constant address space: like a kernel argument
+// it is known not to change during the kernel, so its fields stay in scalar registers (or are
+// re-read at will) across the operand transfers' memory clobbers instead of being re-read
+// after each of them.
+typedef const __attribute__((address_space(4))) SplitArgs CSplitArgs;
+__device__ __forceinline__ CSplitArgs& desc_of(const SplitArgs* d, int h) { return *(CSplitArgs*)(d + h); }
+
 // Hop of logical block `lb` in a batched launch: the hops' block ranges are consecutive.
 __device__ __forceinline__ int batch_hop(const BatchTab& bt, int64_t lb) {
   int h = 0;
@@ -550,19 +557,33 @@ __device__ __forceinline__ int batch_hop(const BatchTab& bt, int64_t lb) {
   return h;
 }
 
+// Logical tile of hardware block `b` in a batched launch, or -1 for a padding block.  The hops'
+// block ranges follow one another in dispatch order, each starting at a multiple of the XCD
+// count, and the XCD remap runs inside each hop: every hop is spread over all XCDs (hops of
+// unequal cost per tile would otherwise leave whole XCDs idle at the end of the launch), and a
+// hop's tiles that share operands stay on one XCD, as in a launch of that hop alone.
+template <typename P>
+__device__ __forceinline__ int64_t batch_tile(P& p, const BatchTab& bt, int h, int64_t b) {
+  const int64_t n = bt.start[h + 1] - bt.start[h];
+  const int64_t lb = xcd_remap(b - bt.start[h], n);
+  const int64_t real = (int64_t)p.nct * ((p.S + kScoreTile - 1) / kScoreTile) * p.n_grp * 2;
+  return lb < real ? lb : -1;
+}
+
 // Several independent hops (ragged pools, base ranks 16 or 32) in one grid; descriptors in
-// device memory.  The XCD remap runs over the whole grid, so each hop's tiles stay grouped.
+// device memory.
 template <int HD>
 __global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const SplitArgs* __restrict__ d, BatchTab bt) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   __shared__ ScoreShared sh;
-  const int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = batch_hop(bt, lb);
-  const SplitArgs& p = d[h];
+  const int h = batch_hop(bt, blockIdx.x);
+  CSplitArgs& p = desc_of(d, h);
+  const int64_t lb = batch_tile(p, bt, h, blockIdx.x);
+  if (lb < 0) return;
   if (p.r_b == 16)
-    score_tile<HD, 1>(p, lb - bt.start[h], ring, sh);
+    score_tile<HD, 1>(p, lb, ring, sh);
   else
-    score_tile<HD, 2>(p, lb - bt.start[h], ring, sh);
+    score_tile<HD, 2>(p, lb, ring, sh);
 }
 
 // ================================================================== token weights
@@ -571,7 +592,8 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const Spli
 // cosine / T_w (second mode), or the caller's weights as given; 0 past S_cov.  Written
 // anchor-major (w[side][layer][a][t], the apply kernel's operand order) and, if requested,
 // token-major for the caller (w_out[side][layer][t][a], 0 outside the correction set).
-__device__ __forceinline__ void weights_rows(const SplitArgs& p, int wmode, int bx, int by, int side, float* xs) {
+template <typename P>
+__device__ __forceinline__ void weights_rows(P& p, int wmode, int bx, int by, int side, float* xs) {
   const int tid = threadIdx.x;
   const int t = bx * 256 + tid;
   const int layer = p.layer0 + by;
@@ -641,7 +663,7 @@ __global__ void __launch_bounds__(256) split_weights(SplitArgs p, int wmode) {
 // batched: blockIdx.z = 2 hop + side; every hop's weights come from its distance partials
 __global__ void __launch_bounds__(256) split_weights_batch(const SplitArgs* __restrict__ d) {
   extern __shared__ float xs[];
-  const SplitArgs& p = d[blockIdx.z >> 1];
+  CSplitArgs& p = desc_of(d, blockIdx.z >> 1);
   if ((int)blockIdx.x * 256 >= p.S || p.n_corr < 1) return;
   weights_rows(p, SPLIT_W_PARTIALS, blockIdx.x, blockIdx.y, blockIdx.z & 1, xs);
 }
@@ -656,8 +678,8 @@ __global__ void __launch_bounds__(256) split_weights_batch(const SplitArgs* __re
 // the rank splits into column slices of A and row slices of B): step j takes slice j % NS of
 // correction anchor j / NS, the same ring slot size as rank RA.  The packed B operand then holds
 // each slice as its own matrix (rows RA k .. RA k + RA - 1 of anchor a at index a NS + k).
-template <int HD, int RKD, int RA, int NS = 1>
-__device__ __forceinline__ void apply_tile(const SplitArgs& p, int64_t lb, char* ring, float (*tab)[kFusedHalf]) {
+template <int HD, int RKD, int RA, int NS = 1, typename P>
+__device__ __forceinline__ void apply_tile(P& p, int64_t lb, char* ring, float (*tab)[kFusedHalf]) {
   constexpr int kST = kApplyTile, kNT = kApplyThreads, kNW = kNT / 64;
   constexpr int RS = RA * NS;   // stored rank of the A rows
   using RG = Ring<RKD, kST, kNW, true, RA, RS>;
@@ -761,10 +783,10 @@ template <int HD>
 __global__ void __launch_bounds__(kApplyThreads, 3) split_apply_batch(const SplitArgs* __restrict__ d, BatchTab bt) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   __shared__ float tab[2][kFusedHalf];
-  const int64_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = batch_hop(bt, lb);
-  const SplitArgs& p = d[h];
-  const int64_t b = lb - bt.start[h];
+  const int h = batch_hop(bt, blockIdx.x);
+  CSplitArgs& p = desc_of(d, h);
+  const int64_t b = batch_tile(p, bt, h, blockIdx.x);
+  if (b < 0) return;
   switch (p.r_d) {
     case 8: apply_tile<HD, 1, 8>(p, b, ring, tab); break;
     case 16: apply_tile<HD, 1, 16>(p, b, ring, tab); break;
@@ -851,7 +873,8 @@ bool batch_tab(BatchTab& bt, const SplitArgs* h, int n, int64_t& total) {
   for (int i = 0; i < n; ++i) {
     bt.start[i] = (int32_t)total;
     const int64_t ntt = (h[i].S + kScoreTile - 1) / kScoreTile;
-    total += (int64_t)h[i].nct * ntt * h[i].n_grp * 2;
+    const int64_t blocks = (int64_t)h[i].nct * ntt * h[i].n_grp * 2;
+    total += (blocks + 7) / 8 * 8;   // each hop starts on XCD 0 (blocks are dealt round-robin over 8)
     if (h[i].D % kSW || h[i].N > kMaxAnchors) return false;
   }
   bt.start[n] = (int32_t)total;

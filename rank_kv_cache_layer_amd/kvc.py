@@ -418,8 +418,10 @@ def correct_hops_batched(hops: Sequence[Hop], shape: Shape, params: Params, thet
     dev = hops[0].k_out.device
     ws = _ws(need, dev, workspace)
     rope, _k2 = rope_of(theta)
-    _check(L.kvc_correct_hops_batched(arr, n, dt, shape, C.byref(rope), C.byref(params), _ptr(ws),
-                                      ws.numel() if ws is not None else 0, _stream(stream)))
+    # one hop at a time: announce only the one-hop size, so the library does not batch the levels
+    nbytes = (min(ws.numel(), need) if one_at_a_time else ws.numel()) if ws is not None else 0
+    _check(L.kvc_correct_hops_batched(arr, n, dt, shape, C.byref(rope), C.byref(params), _ptr(ws), nbytes,
+                                      _stream(stream)))
 
 
 def svd_workspace_size(n_mats, rows, cols, rank, oversample) -> int:

@@ -2,8 +2,8 @@
 
 Inputs (directories written by rocprofv3 --output-format csv -o run):
   --kt     kernel trace + stats run        (run_kernel_stats.csv, run_kernel_trace.csv)
-  --fetch  --pmc FETCH_SIZE run            (run_counter_collection.csv)
-  --write  --pmc WRITE_SIZE run            (run_counter_collection.csv)
+  --fetch  optional --pmc FETCH_SIZE run   (run_counter_collection.csv)
+  --write  optional --pmc WRITE_SIZE run   (run_counter_collection.csv)
   --sq     optional --pmc SQ_* run         (run_counter_collection.csv)
   --bench  optional bench.py JSON line of the same workload (algorithmic bytes per kernel)
 
@@ -79,11 +79,11 @@ def kernel_stats(d: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--kt", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--sq")
     ap.add_argument("--bench")
-    ap.add_argument("--copy-bytes", type=int, required=True, help="size of one peak_copy dispatch")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="size of one peak_copy dispatch")
     ap.add_argument("--cmd", required=True, help="the profiled command, for the record")
     ap.add_argument("--title", default="per-hop correction, 32768-token Llama-3.1-8B-shaped hop")
     ap.add_argument("--out", required=True)
@@ -93,28 +93,36 @@ def main():
     a = ap.parse_args()
 
     ks = kernel_stats(a.kt)
-    fe, wr = counters(a.fetch), counters(a.write)
+    counted = bool(a.fetch and a.write)
+    fe, wr = (counters(a.fetch), counters(a.write)) if counted else ({}, {})
     sq = counters(a.sq) if a.sq else {}
     bench = json.loads(open(a.bench).read().strip().splitlines()[-1]) if a.bench else None
 
-    copy_f = statistics.median(fe["peak_copy"]["FETCH_SIZE"]) * 1024
-    copy_w = statistics.median(wr["peak_copy"]["WRITE_SIZE"]) * 1024
-    cal_f, cal_w = a.copy_bytes / copy_f, a.copy_bytes / copy_w
+    cal_f = cal_w = None
+    if counted:
+        copy_f = statistics.median(fe["peak_copy"]["FETCH_SIZE"]) * 1024
+        copy_w = statistics.median(wr["peak_copy"]["WRITE_SIZE"]) * 1024
+        cal_f, cal_w = a.copy_bytes / copy_f, a.copy_bytes / copy_w
 
     lines = [f"# rocprofv3 profile: {a.title}", "",
              "Commands (run from the repository root on one MI355X, `export TMPDIR=/tmp`):", "",
-             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <kt> -o run -- {a.cmd}",
-             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {a.cmd}",
-             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {a.cmd}"]
+             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <kt> -o run -- {a.cmd}"]
+    if counted:
+        lines += [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {a.cmd}",
+                  f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {a.cmd}"]
     if a.sq:
         names = sorted({c for k in sq.values() for c in k})
         lines.append(f"rocprofv3 --pmc {' '.join(names)} --output-format csv -d <sq> -o run -- {a.cmd}")
-    lines += ["python -m rank_kv_cache_layer_amd.profsum --kt <kt> --fetch <fetch> --write <write> "
-              f"{'--sq <sq> ' if a.sq else ''}--copy-bytes {a.copy_bytes} ...", "```", "",
-              f"Counter calibration from the streaming copy kernel ({a.copy_bytes} bytes read and written per "
-              f"dispatch): FETCH_SIZE x {cal_f:.3f}, WRITE_SIZE x {cal_w:.3f}.", "",
-              "| kernel | calls | avg ms | % time | HBM read GB/launch | HBM write GB/launch | algorithmic GB/launch |",
-              "|---|---|---|---|---|---|---|"]
+    if counted:
+        lines += ["python -m rank_kv_cache_layer_amd.profsum --kt <kt> --fetch <fetch> --write <write> "
+                  f"{'--sq <sq> ' if a.sq else ''}--copy-bytes {a.copy_bytes} ...", "```", "",
+                  f"Counter calibration from the streaming copy kernel ({a.copy_bytes} bytes read and written per "
+                  f"dispatch): FETCH_SIZE x {cal_f:.3f}, WRITE_SIZE x {cal_w:.3f}.", "",
+                  "| kernel | calls | avg ms | % time | HBM read GB/launch | HBM write GB/launch | algorithmic GB/launch |",
+                  "|---|---|---|---|---|---|---|"]
+    else:
+        lines += ["python -m rank_kv_cache_layer_amd.profsum --kt <kt> ...", "```", "",
+                  "| kernel | calls | avg ms | % time |", "|---|---|---|---|"]
     traffic = {}
     algo = (bench or {}).get("kernels", {})
     for name, (calls, avg_ns, pct) in sorted(ks.items(), key=lambda x: -x[1][2]):
@@ -124,7 +132,10 @@ def main():
             traffic[name] = {"bytes": int(f + w), "source_hash": kernel_source_hash(name)}
         alg = algo.get(name, {}).get("algorithmic_bytes")
         fmt = lambda x: "" if x is None else f"{x / 1e9:.3f}"
-        lines.append(f"| {name} | {calls} | {avg_ns / 1e6:.4f} | {pct:.1f} | {fmt(f)} | {fmt(w)} | {fmt(alg)} |")
+        if counted:
+            lines.append(f"| {name} | {calls} | {avg_ns / 1e6:.4f} | {pct:.1f} | {fmt(f)} | {fmt(w)} | {fmt(alg)} |")
+        else:
+            lines.append(f"| {name} | {calls} | {avg_ns / 1e6:.4f} | {pct:.1f} |")
     if sq:
         lines += ["", "SQ counters (per dispatch, median):", "", "| kernel | counter | value |", "|---|---|---|"]
         for name in HOT:
@@ -143,14 +154,14 @@ def main():
                           f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (matrix-core cycles summed over SIMDs) / "
                           f"({N_SIMD} SIMDs x clock x duration).", "",
                       "| kernel | clock GHz | MFMA busy |", "|---|---|---|", *derived]
-    if bench:
+    if bench and bench.get("roofline"):
         lines += ["", f"bench.py line of the same workload: {bench['ms_per_step']} ms/hop, {bench['value']} tokens/s; "
                       f"dominant kernel {bench['roofline']['kernel']}: {bench['roofline']['achieved']} "
                       f"{bench['roofline']['unit']} of {bench['roofline']['peak']} "
                       f"({bench['roofline']['bound']} bound, frac {bench['roofline']['frac']})."]
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     open(a.out, "w").write("\n".join(lines) + "\n")
-    if a.traffic:
+    if a.traffic and counted:
         if a.merge and os.path.exists(a.traffic):
             old = json.load(open(a.traffic)).get("kernels", {})
             traffic = {**{k: v for k, v in old.items() if isinstance(v, dict)}, **traffic}
