@@ -229,6 +229,23 @@ kvc_status kvc_correct_hop(const void* k_src, const void* v_src, void* k_out, vo
                            const kvc_params* params, kvc_match_out* out, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* kvc_correct_hop without a workspace argument, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation).  Scratch
+ * is a library-owned device array of KVC_NOALLOC_SCRATCH_BYTES per GPU (one copy per device the
+ * library runs on, kept until the process ends; its address is taken on the first call on each
+ * device).  Requests whose kvc_workspace_size(KVC_CALL_CORRECT, ...) exceeds it return
+ * KVC_E_WORKSPACE before any launch: up to about the 4096-token, 32-layer, 8x128 hop with 20
+ * anchors at rank 32, or 10 at rank 128.  Arguments, results and errors are those of
+ * kvc_correct_hop.  The call allocates no device memory and copies nothing from the host.
+ * Every call on a GPU uses that GPU's one scratch array, so calls that overlap on one GPU
+ * (different streams or threads) race; serialise them.  The kernels write every scratch word
+ * they read, so nothing left by an earlier call is used. */
+#define KVC_NOALLOC_SCRATCH_BYTES (384 << 20)
+kvc_status kvc_correct_hop_noalloc(const void* k_src, const void* v_src, void* k_out, void* v_out,
+                                   kvc_dtype dtype, kvc_shape shape, int64_t p_src, int64_t p_tgt,
+                                   const kvc_rope* rope, const kvc_pool* pool,
+                                   const kvc_params* params, kvc_match_out* out, void* stream);
+
 /* One hop of a batch (chained corrections, Eq. 6 and App. A.3 "Cache Materialization"). */
 typedef struct {
   const void* k_src;   /* ignored when chain_prev >= 0                                     */

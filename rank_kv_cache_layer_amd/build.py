@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libkvc.so")
 
 SOURCES = ["kvc_align.hip", "kvc_generic.hip", "kvc_gate.hip", "kvc_mfma.hip", "kvc_cosg.hip", "kvc_fused.hip", "kvc_split.hip",
            "kvc_svd.hip",
-           "kvc_peaks.hip", "kvc_pool.hip", "kvc_host.hip"]
+           "kvc_peaks.hip", "kvc_pool.hip", "kvc_host.hip", "kvc_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

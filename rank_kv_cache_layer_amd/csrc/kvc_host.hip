@@ -1029,6 +1029,14 @@ BatchPlan batch_plan(const kvc_hop_desc* hops, int n, kvc_dtype dt, const kvc_sh
 
 }  // namespace
 
+kvc_status kvc::report(kvc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
 // ================================================================== C ABI
 extern "C" {
 

@@ -60,6 +60,9 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return base + i;
 }
 
+// Sets the thread-local reason kvc_last_error() returns; returns s.
+kvc_status report(kvc_status s, const char* fmt, ...);
+
 // --------------------------------------------------------------------------- launchers
 // All launchers enqueue on `st` and return hipGetLastError() of the launch.
 

@@ -26,6 +26,7 @@ STATUS = {0: "KVC_OK", 1: "KVC_E_NULL", 2: "KVC_E_SHAPE", 3: "KVC_E_DTYPE", 4: "
 
 EXPORTS = ["kvc_abi_version", "kvc_status_str", "kvc_last_error", "kvc_workspace_size",
            "kvc_align_rope", "kvc_match_anchors", "kvc_apply_lowrank_delta", "kvc_correct_hop",
+           "kvc_correct_hop_noalloc",
            "kvc_correct_hops_batched", "kvc_hops_batched_workspace_size", "kvc_svd_workspace_size", "kvc_anchor_refresh_svd",
            "kvc_peak_copy", "kvc_peak_mfma_bf16", "kvc_peak_lds_read", "kvc_peak_valu",
            "kvc_observed_delta", "kvc_pool_state_init", "kvc_pool_record_hop", "kvc_pool_view",
@@ -124,6 +125,10 @@ def lib(path: Optional[str] = None):
     L.kvc_correct_hop.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, Shape, C.c_int64,
                                   C.c_int64, C.POINTER(Rope), C.POINTER(Pool), C.POINTER(Params),
                                   C.POINTER(MatchOut), C.c_void_p, C.c_size_t, C.c_void_p]
+    L.kvc_correct_hop_noalloc.restype = C.c_int
+    L.kvc_correct_hop_noalloc.argtypes = [C.c_void_p] * 4 + [C.c_int, Shape, C.c_int64, C.c_int64, C.POINTER(Rope),
+                                                           C.POINTER(Pool), C.POINTER(Params), C.POINTER(MatchOut),
+                                                           C.c_void_p]
     L.kvc_hops_batched_workspace_size.restype = C.c_size_t
     L.kvc_hops_batched_workspace_size.argtypes = [C.POINTER(HopDesc), C.c_int32, C.c_int, Shape, C.POINTER(Params)]
     L.kvc_correct_hops_batched.restype = C.c_int
@@ -361,6 +366,24 @@ def correct_hop(k_src, v_src, k_out, v_out, shape: Shape, p_src: int, p_tgt: int
     _check(L.kvc_correct_hop(_ptr(k_src), _ptr(v_src), _ptr(k_out), _ptr(v_out), _dt(k_src), shape, p_src, p_tgt,
                              C.byref(rope), C.byref(p), C.byref(params), C.byref(mo), _ptr(ws),
                              ws.numel() if ws is not None else 0, _stream(stream)))
+    out.s_cov = sc.value
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 384 << 20
+
+
+def correct_hop_noalloc(k_src, v_src, k_out, v_out, shape: Shape, p_src: int, p_tgt: int, pool: PoolTensors,
+                        params: Params, out: MatchResult, theta=10000.0, stream=None) -> MatchResult:
+    """kvc_correct_hop_noalloc: the whole hop with the library's own per-GPU scratch (no workspace,
+    no device allocation); `out` must be preallocated (alloc_match)."""
+    L = lib()
+    p, _keep = pool.c()
+    mo, sc = _mo(out)
+    rope, _k2 = rope_of(theta)
+    _check(L.kvc_correct_hop_noalloc(_ptr(k_src), _ptr(v_src), _ptr(k_out), _ptr(v_out), _dt(k_src), shape, p_src,
+                                     p_tgt, C.byref(rope), C.byref(p), C.byref(params), C.byref(mo),
+                                     _stream(stream)))
     out.s_cov = sc.value
     return out
 

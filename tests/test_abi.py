@@ -180,3 +180,20 @@ def test_svd_validation():
                                     4, 2, 0, FAKE + (4 << 24), 1 << 30, None) == 2
     assert L.kvc_anchor_refresh_svd(FAKE, 1, 64, 64, 8, FAKE + (1 << 24), FAKE + (2 << 24), 0, FAKE + (3 << 24),
                                     4, 99, 0, FAKE + (4 << 24), 1 << 30, None) == 8
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch():
+    # the 32768-token 8B-shaped hop needs ~968 MiB of scratch, beyond the no-alloc entry point's
+    # fixed 384 MiB: refused on the host before any device work (the pointers are never used)
+    L = kvc.lib()
+    n = 20
+    lens = (C.c_int32 * n)(*([32768] * n))
+    p = kvc.Pool(n, 32, 32, 0, C.cast(lens, C.POINTER(C.c_int32)), 1, *([FAKE] * 8), 0, 0, None)
+    prm = kvc.params_of()
+    mo = kvc.MatchOut(FAKE, FAKE, FAKE, None, None, None)
+    sh = kvc.shape_of(32, 32768, 8, 128)
+    assert L.kvc_workspace_size(3, sh, C.byref(p), C.byref(prm)) > kvc.NOALLOC_SCRATCH_BYTES
+    st = L.kvc_correct_hop_noalloc(FAKE, FAKE + (1 << 36), FAKE + (2 << 36), FAKE + (3 << 36), 1, sh, 0, 300,
+                                   C.byref(_rope()), C.byref(p), C.byref(prm), C.byref(mo), None)
+    assert st == 6   # KVC_E_WORKSPACE
+    assert b"maximum" in L.kvc_last_error()
