@@ -229,8 +229,9 @@ bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, boo
   const int D = D_of(sh);
   if ((sh.head_dim != 64 && sh.head_dim != 128) || D % kSplitWidth) return false;
   if (pages_scores) {
-    if (p.rank_base != 16 && p.rank_base != 32) return false;
-    if (split_score_lds(p.rank_base) + 8 * 1024 > kLdsBudget) return false;
+    const int rb = p.rank_base;
+    if (rb != 16 && rb != 32 && rb != 64 && rb != 128) return false;   // 64 / 128: rank slices of 32
+    if (split_score_lds(rb) + 8 * 1024 > kLdsBudget) return false;
   }
   if (apply) {
     const int rd = p.rank_delta;
@@ -293,8 +294,9 @@ Plan plan(int call, const kvc_shape& sh, const kvc_pool& p, const kvc_params* pr
     pl.fused_match = !pl.split_match && pages && fused_ok(sh, p, P, true, false) &&
                      (!do_apply || pl.fused_apply || pl.fused_split);
     if (pl.split_match) {
-      const int ntt = (S + kScoreTile - 1) / kScoreTile, nct = D / kSplitWidth;
-      pl.tile = kScoreTile;
+      const int tt = split_score_tile(p.rank_base);
+      const int ntt = (S + tt - 1) / tt, nct = D / kSplitWidth;
+      pl.tile = tt;
       pl.n_tiles = ntt * nct;
       pl.off_mpart = off;
       off += up256(sizeof(float) * (size_t)nct * 2 * L * N * S);
@@ -657,7 +659,9 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
   kvc_status r;
   if (pl.split_match) {
     uint16_t* pb = reinterpret_cast<uint16_t*>(ws + pl.off_pack_base);
-    if ((r = pack_pair(p.baseB_k, p.baseB_v, pb, p.rank_base, 1, nullptr, sh, p, tr, KVC_K_PACK_BASE, st)) != KVC_OK)
+    // base ranks 64 / 128 are scored in rank slices of 32: one packed matrix per slice
+    if ((r = pack_pair(p.baseB_k, p.baseB_v, pb, p.rank_base, 1, nullptr, sh, p, tr, KVC_K_PACK_BASE, st,
+                       split_apply_slices(p.rank_base))) != KVC_OK)
       return r;
     SplitArgs f;
     if ((r = split_args(f, k_src, v_src, sh, p_src, p_tgt, rope, p, s, inv_temp)) != KVC_OK) return r;

@@ -279,6 +279,7 @@ hipError_t launch_split_apply_batch(const SplitArgs* d, const SplitArgs* h, int 
 hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st);
 hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st);
 size_t split_score_lds(int r_b);                   // dynamic LDS bytes
+int split_score_tile(int r_b);                     // tokens per scoring tile (128; 64 at ranks 64 / 128)
 size_t split_apply_lds(int r_d);
 // rank slices of 32 the apply takes per anchor: ranks 64, 128 and 256 run as 2, 4 and 8 slices
 // (their packed delta B is then one matrix per slice); ranks 8, 16 and 32 in one step

@@ -586,6 +586,226 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const Spli
     score_tile<HD, 2>(p, lb, ring, sh);
 }
 
+// ------------------------------------------------- first-mode scores at base ranks 64 and 128
+// The contraction over an anchor's rank runs in NS slices of 32 (as the apply's), each a ring
+// step of the rank-32 slot size; the reconstruction Z - sum_s A_s B_s of an anchor is complete
+// only after its last slice, so every wave keeps its result blocks live across the slices.  To
+// fit them next to the source tile a work-group covers 64 tokens x 256 channels with 4 waves of
+// 64 tokens x 64 channels; a wave's two 32-channel blocks are the two halves of its rotary pairs
+// (head_dim 128: blocks b and b + 2 of a head, head_dim 64: one head), so the keys' rotation to
+// the canonical frame stays in registers.
+constexpr int kSlTile = 64;                    // tokens per work-group
+constexpr int kSlPitch = 72;                   // staging row pitch (elements): 64 channels + 8
+
+struct ScoreShared64 {
+  float mp[2][4][kSlTile];                      // |E| sums of two anchors, per wave (64 channels)
+  float qp[4][kMaxAnchors];                     // per-wave gate sums
+  float tab[2][kFusedHalf];                     // R(-p_src) table
+};
+
+// channel offset (within the 256-channel tile) of wave w's lower and upper 32-channel blocks
+template <int HD> __device__ __forceinline__ int sl_block(int w) { return HD == 128 ? 4 * (w >> 1) + (w & 1) : 2 * w; }
+
+// 64 tokens x the wave's two 32-channel blocks (channels c0 .. c0 + 31 and c1 .. c1 + 31 of the
+// layer's rows), through wave-private staging, into accumulator layout (fp32); rows >= S read 0
+__device__ __forceinline__ void load_tile2(f32x16 (&z)[2][2], rsrc_t zr, int t0, int D, int c0, int c1,
+                                           uint16_t* stage, int lane, int col, int hi) {
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // 32 rows x 2 blocks x 64 bytes: 8 lanes per row
+      const int row = i * 8 + (lane >> 3), u = lane & 7, ch = (u >> 2 ? c1 : c0) + (u & 3) * 8;
+      v[i] = bload16<kStream>(zr, (uint32_t)((t0 + tb * 32 + row) * D + ch) * 2u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 8 + (lane >> 3), u = lane & 7;
+      *reinterpret_cast<uint4*>(stage + row * kSlPitch + u * 8) = v[i];
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const uint2 x = *reinterpret_cast<const uint2*>(stage + col * kSlPitch + db * 32 + 8 * jg + 4 * hi);
+        z[tb][db][4 * jg + 0] = lo16(x.x);
+        z[tb][db][4 * jg + 1] = hi16(x.x);
+        z[tb][db][4 * jg + 2] = lo16(x.y);
+        z[tb][db][4 * jg + 3] = hi16(x.y);
+      }
+  }
+}
+
+// keys: the pairs (block 0 row, block 1 row) turned by the table's angles; `pc` = pair index of
+// the lower block's first row
+__device__ __forceinline__ void rotate_tile2(f32x16 (&z)[2][2], const float* cs, const float* sn, int pc, int hi) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int c = pc + 8 * (j >> 2) + 4 * hi + (j & 3);
+    const float cv = cs[c], sv = sn[c];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float ox, oy;
+      rot_pair(z[tb][0][j], z[tb][1][j], cv, sv, ox, oy);
+      z[tb][0][j] = ox;
+      z[tb][1][j] = oy;
+    }
+  }
+}
+
+template <int HD, int NS, typename P>
+__device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, ScoreShared64& sh) {
+  constexpr int kST = kSlTile, kNT = kScoreThreads, kNW = kNT / 64, RS = 32 * NS;
+  using RG = Ring<2, kST, kNW, false, 32, RS>;
+  auto& mp = sh.mp;
+  auto& qp = sh.qp;
+  auto& tab = sh.tab;
+
+  const TileId id = tile_id<true>(p, lb);
+  const bool keys = id.side == 0;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
+  const int D = p.D, S = p.S, N = p.N, NCB = D >> 5;
+  const int t0 = id.tt * kST;
+  const int blk0 = sl_block<HD>(wave), blk1 = blk0 + HD / 64;
+  const int c0 = id.cq * kSW + blk0 * 32, c1 = id.cq * kSW + blk1 * 32;
+
+  const auto list = keys ? p.corr : p.use;
+  int nl = keys ? p.n_corr : p.n_use;
+  const int s_work = keys ? (p.n_corr ? p.s_cov : 0) : max(p.n_corr ? p.s_cov : 0, p.mask_gate ? p.k_gate : 0);
+  if (t0 >= s_work) nl = 0;
+  const int steps = nl * NS;
+
+  for (int i = tid; i < HD / 2; i += kNT) {
+    tab[0][i] = p.can.cs[i];
+    tab[1][i] = p.can.sn[i];
+  }
+  const Slots sl = load_slots(list, keys ? p.n_corr : p.n_use, p.off, p.len, S, lane);
+
+  const uint16_t* Al = p.Ab[id.side] + id.layer * p.ab_layer;
+  // the packed base B holds each rank slice as a matrix of its own: index a NS + ks
+  const uint16_t* Bl = p.Bb[id.side] + (((int64_t)id.layer * N * NS) * NCB + id.cq * kNCBW) * 2 * kC;
+  const int64_t bstride = (int64_t)NCB * 2 * kC;
+  const uint32_t ring0 = lds_off(ring);
+  const int wv = uni(wave);
+  auto fetch = [&](int j) {   // slice j % NS of scored anchor j / NS into slot j % 3
+    const bool live = j < steps;
+    const int js = live ? j / NS : 0, ks = live ? j % NS : 0;
+    const int a = lane_get(sl.a, js);
+    const int lim = live ? lane_get(sl.lim, js) : 0;
+    const int a_elems = lim * RS - ks * 32;   // the slice's rows end where the stored rows do
+    RG::fetch(ring0 + (uint32_t)(j % kSlots) * RG::SLOT,
+              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * RS + ks * 32, (uint32_t)(live ? a_elems : 0) * 2),
+              make_rsrc(Bl + (a * NS + ks) * bstride, live ? RG::B_BYTES : 0), make_rsrc(nullptr, 0), t0, wv, lane);
+  };
+  uint32_t aoff[2][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) aoff[tb][ks] = RG::a_unit(tb * 32 + col, ks * 2 + hi) * 16;
+  const uint32_t boff0 = RG::A_BYTES + blk0 * 2 * 1024 + lane * 16, boff1 = RG::A_BYTES + blk1 * 2 * 1024 + lane * 16;
+
+  const float qm0 = (t0 + col < p.k_gate && t0 + col < S) ? 1.f : 0.f;
+  const float qm1 = (t0 + 32 + col < p.k_gate && t0 + 32 + col < S) ? 1.f : 0.f;
+  float* mpart = p.mpart + (((int64_t)id.cq * 2 + id.side) * p.n_layers + id.layer) * N * S;
+  auto store_m = [&](int ja) {   // partial |E| sums of anchor ja over the tile's 256 channels
+    const int a = lane_get(sl.a, ja);
+    if (((p.mask_corr >> a) & 1) && tid < kST) {
+      const int t = t0 + tid, b = ja & 1;
+      if (t < S) mpart[(int64_t)a * S + t] = (mp[b][0][tid] + mp[b][1][tid]) + (mp[b][2][tid] + mp[b][3][tid]);
+    }
+  };
+
+  auto run = [&](const f32x16 (&z)[2][2], auto values) {
+    constexpr bool Q = decltype(values)::value;
+#pragma nounroll
+    for (int ja = 0; ja < nl; ++ja) {
+      f32x16 e[2][2];
+#pragma unroll
+      for (int ks = 0; ks < NS; ++ks) {
+        const int j = ja * NS + ks;
+        wait_vm_barrier<RG::DMA_PER_WAVE>();   // slice j landed for every wave; slot (j + 2) % 3 is free
+        if (ks == 0 && ja > 0) store_m(ja - 1);
+        fetch(j + 2);
+        const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));
+        bf16x8 av[2][2], bv[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) av[tb][kk] = as_bf8(lds_u4(slot + aoff[tb][kk]));
+          bv[0][kk] = as_bf8(lds_u4(slot + boff0 + kk * 1024));
+          bv[1][kk] = as_bf8(lds_u4(slot + boff1 + kk * 1024));
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            e[tb][db] = mfma(bv[db][1], av[tb][1], mfma(bv[db][0], av[tb][0], ks == 0 ? z[tb][db] : e[tb][db]));
+      }
+      // E = Z_can - A B complete: |E| per token column, E^2 for the gate
+      float m0 = 0.f, m1 = 0.f, q0 = 0.f, q1 = 0.f;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          m0 += fabsf(e[0][db][jj]);
+          m1 += fabsf(e[1][db][jj]);
+          if (Q) {
+            q0 = fmaf(e[0][db][jj], e[0][db][jj], q0);
+            q1 = fmaf(e[1][db][jj], e[1][db][jj], q1);
+          }
+        }
+      const int a = lane_get(sl.a, ja);
+      if ((p.mask_corr >> a) & 1) {
+        m0 = xor32_sum(m0);
+        m1 = xor32_sum(m1);
+        if (hi == 0) {
+          mp[ja & 1][wave][col] = m0;
+          mp[ja & 1][wave][32 + col] = m1;
+        }
+      }
+      if (Q && ((p.mask_gate >> a) & 1)) {
+        float qs = fmaf(q0, qm0, q1 * qm1);
+        qs = wave_sum63(qs);
+        if (lane == 63) qp[wave][a] = qs;
+      }
+    }
+  };
+  __syncthreads();   // rotation table
+  if (nl > 0) {
+    f32x16 z[2][2];
+    fetch(0);
+    // staging (wave-private) in the ring past slot 0, free until step 1 is fetched
+    load_tile2(z, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, (uint32_t)S * D * 2), t0, D, c0, c1,
+               reinterpret_cast<uint16_t*>(ring + RG::SLOT) + wave * 32 * kSlPitch, lane, col, hi);
+    if (keys && p.can.active) rotate_tile2(z, tab[0], tab[1], (blk0 * 32) % HD, hi);
+    wait_vm_barrier<63>();   // every wave is done with the staging area
+    fetch(1);
+    if (keys)
+      run(z, std::false_type{});
+    else
+      run(z, std::true_type{});
+  }
+  wait_vm_barrier<0>();
+  if (nl > 0) store_m(nl - 1);
+  if (!keys && p.partials) {
+    float* part = p.partials + ((int64_t)id.layer * p.ntt * p.nct + (int64_t)id.tt * p.nct + id.cq) * N;
+    for (int a = tid; a < N; a += kNT) {
+      if (!((p.mask_gate >> a) & 1)) continue;
+      float s = 0.f;
+      if (t0 < p.k_gate && nl > 0)
+        for (int w = 0; w < kNW; ++w) s += qp[w][a];
+      part[a] = s;
+    }
+  }
+}
+
+template <int HD, int NS>
+__global__ void __launch_bounds__(kScoreThreads, 2) split_score_sliced(SplitArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  __shared__ ScoreShared64 sh;
+  score_tile_sliced<HD, NS>(p, xcd_remap(blockIdx.x, gridDim.x), ring, sh);
+}
+
 // ================================================================== token weights
 // App. A.3 "Correction Weighting": per token and side, softmax over the correction set of
 // -m / T_w (first mode, m = mean |Z_can - A B| from the per-channel-tile partials) or of
@@ -816,6 +1036,8 @@ hipError_t score_dispatch(const SplitArgs& a, hipStream_t st) {
   switch (a.r_b) {
     case 16: return go(split_score<HD, 1>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
     case 32: return go(split_score<HD, 2>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
+    case 64: return go(split_score_sliced<HD, 2>, a, kSlTile, kScoreThreads, split_score_lds(a.r_b), st);
+    case 128: return go(split_score_sliced<HD, 4>, a, kSlTile, kScoreThreads, split_score_lds(a.r_b), st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -840,9 +1062,15 @@ hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
 // filled during the tile load; apply: from the start, before anchor 0 is fetched), whichever
 // is larger
 size_t split_score_lds(int r_b) {
+  if (r_b == 64 || r_b == 128) {   // rank slices of 32 over 64-token tiles
+    const size_t slot = (size_t)kSlTile * 32 * 2 + (size_t)kNCBW * 2 * 1024;
+    return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kScoreThreads / 64) * 32 * kSlPitch);
+  }
   const size_t slot = (size_t)kScoreTile * r_b * 2 + (size_t)kNCBW * (r_b / 16) * 1024;
   return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kScoreThreads / 64) * kStage);
 }
+
+int split_score_tile(int r_b) { return r_b == 64 || r_b == 128 ? kSlTile : kScoreTile; }
 
 size_t split_apply_lds(int r_d) {
   const int rp = split_apply_slices(r_d) > 1 ? 32 : (r_d + 15) & ~15;   // on chip: padded to 16, or slices of 32
