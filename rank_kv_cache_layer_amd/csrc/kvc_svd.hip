@@ -221,11 +221,98 @@ __global__ void __launch_bounds__(256) gemm_f64(const TA* __restrict__ A, const 
       }
 }
 
+// four consecutive floats at p + base, of which `avail` exist (the rest read as 0)
+__device__ __forceinline__ float4 ld4_guard(const float* p, int64_t base, int avail) {
+  if (avail >= 4) return *reinterpret_cast<const float4*>(p + base);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (avail > 0) v.x = p[base];
+  if (avail > 1) v.y = p[base + 1];
+  if (avail > 2) v.z = p[base + 2];
+  return v;
+}
+
+// C (M x N, fp64) = A^T B with A stored [K][M] and B stored [K][N], both fp32 (exact in fp64),
+// for M <= 160 (the sketch width: Gram matrices Y^T Y and the projection Q^T Z): one work-group
+// holds all M rows x 64 columns, each wave one 16-column block against the ten 16-row blocks, K
+// in chunks of 16 through double-buffered LDS.  Every operand is read once per 64 columns
+// (the 32 x 32 tiles of gemm_f64 read A once per 32 columns and B once per 32 rows).
+constexpr int kTnRows = 160;
+__global__ void __launch_bounds__(256) gemm_f64_tn(const float* __restrict__ A, const float* __restrict__ B,
+                                                   double* __restrict__ C, int M, int N, int K, int64_t lda,
+                                                   int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC) {
+  constexpr int AQ = kTnRows / 4, NAV = (16 * AQ + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float As[2][16][kTnRows + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[2][16][64 + 4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, kq = lane >> 4;
+  const int j0 = blockIdx.x * 64;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  float4 ra[NAV], rb;
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < NAV; ++u) {
+      const int idx = tid + 256 * u, k = idx / AQ, m4 = (idx % AQ) * 4;
+      ra[u] = (idx < 16 * AQ && k0 + k < K) ? ld4_guard(A, (int64_t)(k0 + k) * lda + m4, M - m4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int k = tid >> 4, n4 = (tid & 15) * 4;
+    rb = (k0 + k < K) ? ld4_guard(B, (int64_t)(k0 + k) * ldb + j0 + n4, N - j0 - n4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NAV; ++u) {
+      const int idx = tid + 256 * u, k = idx / AQ, m4 = (idx % AQ) * 4;
+      if (idx < 16 * AQ) *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[u];
+    }
+    *reinterpret_cast<float4*>(&Bs[buf][tid >> 4][(tid & 15) * 4]) = rb;
+  };
+  f64x4 acc[kTnRows / 16];
+#pragma unroll
+  for (int t = 0; t < kTnRows / 16; ++t) acc[t] = (f64x4){0.0, 0.0, 0.0, 0.0};
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const bool more = k0 + 16 < K;
+    if (more) load(k0 + 16);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = 4 * s + kq;
+      const double b = (double)Bs[buf][k][wave * 16 + r16];
+#pragma unroll
+      for (int t = 0; t < kTnRows / 16; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)As[buf][k][16 * t + r16], b, acc[t], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  const int j = j0 + wave * 16 + r16;
+  if (j >= N) return;
+#pragma unroll
+  for (int t = 0; t < kTnRows / 16; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = 16 * t + 4 * v + kq;
+      if (i < M) C[(int64_t)i * ldc + j] = acc[t][v];
+    }
+}
+
 // lower_only: C is a symmetric Gram whose consumers read only its lower triangle (fp64 path):
 // tiles strictly above the diagonal are skipped
 template <typename TA, typename TB, typename TC, typename ACC, bool TRA, bool TRB>
 hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
                     int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st, bool lower_only = false) {
+  if constexpr (std::is_same<ACC, double>::value && std::is_same<TA, float>::value &&
+                std::is_same<TB, float>::value && std::is_same<TC, double>::value && TRA && !TRB) {
+    if (M <= kTnRows && lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0) {
+      const dim3 grid((unsigned)((N + 63) / 64), 1u, (unsigned)batch);
+      gemm_f64_tn<<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+      return hipGetLastError();
+    }
+  }
   if constexpr (std::is_same<ACC, double>::value) {
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32), (unsigned)batch);
     gemm_f64<TA, TB, TC, TRA, TRB><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC,
@@ -246,14 +333,6 @@ hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_
 // tails in M, N, K are bounds-checked.
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ float4 ld4_guard(const float* p, int64_t base, int avail) {
-  if (avail >= 4) return *reinterpret_cast<const float4*>(p + base);
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (avail > 0) v.x = p[base];
-  if (avail > 1) v.y = p[base + 1];
-  if (avail > 2) v.z = p[base + 2];
-  return v;
-}
 
 template <bool TRA>
 __global__ void __launch_bounds__(256) gemm_f32_mfma(const float* __restrict__ A, const float* __restrict__ B,
@@ -350,10 +429,118 @@ __global__ void __launch_bounds__(256) gemm_f32_mfma(const float* __restrict__ A
     }
 }
 
+// The same product for narrow N (the sketch width l = r + p, at most 160): a 128 x 32 NB tile per
+// work-group, each wave 32 rows x all NB column blocks, so no matrix-core work is spent on
+// columns past N (a 128 x 128 tile at N = 160 computes 256 columns).
+template <bool TRA, int NB>
+__global__ void __launch_bounds__(256) gemm_f32_mfma_wide(const float* __restrict__ A, const float* __restrict__ B,
+                                                          float* __restrict__ C, int M, int N, int K, int64_t lda,
+                                                          int64_t ldb, int64_t ldc, int64_t sA, int64_t sB,
+                                                          int64_t sC) {
+  constexpr int BN = 32 * NB, BQ = BN / 4, NBV = (16 * BQ + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float As[2][16][128 + 4];   // [buffer][k][m]
+  __shared__ __attribute__((aligned(16))) float Bs[2][16][BN + 4];    // [buffer][k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int i0 = blockIdx.y * 128, j0 = blockIdx.x * BN;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  float4 ra[2], rb[NBV];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u;
+      if (TRA) {   // A stored [k][m]: 16 rows of 32 float4 along m
+        const int k = idx >> 5, m4 = (idx & 31) * 4;
+        ra[u] = (k0 + k < K) ? ld4_guard(A, (int64_t)(k0 + k) * lda + i0 + m4, M - i0 - m4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {     // A stored [m][k]: 128 rows of 4 float4 along k
+        const int m = idx >> 2, k4 = (idx & 3) * 4;
+        ra[u] = (i0 + m < M) ? ld4_guard(A, (int64_t)(i0 + m) * lda + k0 + k4, K - k0 - k4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NBV; ++u) {
+      const int idx = tid + 256 * u, k = idx / BQ, n4 = (idx % BQ) * 4;
+      rb[u] = (idx < 16 * BQ && k0 + k < K) ? ld4_guard(B, (int64_t)(k0 + k) * ldb + j0 + n4, N - j0 - n4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u;
+      if (TRA) {
+        const int k = idx >> 5, m4 = (idx & 31) * 4;
+        *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[u];
+      } else {
+        const int m = idx >> 2, k4 = (idx & 3) * 4;
+        As[buf][k4 + 0][m] = ra[u].x;
+        As[buf][k4 + 1][m] = ra[u].y;
+        As[buf][k4 + 2][m] = ra[u].z;
+        As[buf][k4 + 3][m] = ra[u].w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NBV; ++u) {
+      const int idx = tid + 256 * u, k = idx / BQ, n4 = (idx % BQ) * 4;
+      if (idx < 16 * BQ) *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = rb[u];
+    }
+  };
+  f32x16v acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const bool more = k0 + 16 < K;
+    if (more) load(k0 + 16);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = 2 * kk + kh;
+      const float a = As[buf][k][wave * 32 + l32];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bs[buf][k][nb * 32 + l32], acc[nb], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = j0 + nb * 32 + l32;
+    if (j >= N) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + wave * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (i < M) C[(int64_t)i * ldc + j] = acc[nb][r];
+    }
+  }
+}
+
 // fp32 products: matrix cores when every leading dimension allows 16-byte loads, else VALU
 template <bool TRA>
 hipError_t gemm_f32(const float* A, const float* B, float* C, int M, int N, int K, int64_t lda, int64_t ldb,
                     int64_t ldc, int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st) {
+  if (lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0 && N <= 160) {
+    // narrow products (the sketch and power iterations): one column tile of 32 ceil(N / 32)
+    const dim3 grid(1u, (unsigned)((M + 127) / 128), (unsigned)batch);
+    switch ((N + 31) / 32) {
+      case 1: gemm_f32_mfma_wide<TRA, 1><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+      case 2: gemm_f32_mfma_wide<TRA, 2><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+      case 3: gemm_f32_mfma_wide<TRA, 3><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+      case 4: gemm_f32_mfma_wide<TRA, 4><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+      default: gemm_f32_mfma_wide<TRA, 5><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+    }
+    return hipGetLastError();
+  }
   if (lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0) {
     const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128), (unsigned)batch);
     gemm_f32_mfma<TRA><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
