@@ -680,6 +680,118 @@ __global__ void __launch_bounds__(1024) chol_inv_lds(const double* G, double* Li
   }
 }
 
+// The same factorisation and inverse for l <= kCholRegMax with both L (as the trailing Gram
+// block) and X = L^-1 in registers: thread (a, b) of 16 x 32 holds entries (a + 16 u, b + 32 v),
+// u < 10, v < 5, of the full symmetric T and of X, so a step moves only one column of L and one
+// row of X through LDS.  Step k: the sixteen threads holding column k of T take the pivot
+// (dropped below rel_tol times the largest diagonal entry of G) and publish
+// L[:, k] = T[:, k] / L_kk below the diagonal and L_kk (0 when dropped); the threads holding
+// row k of X publish it unscaled.  After one barrier every thread applies the trailing update
+// T_ij -= L_ik L_jk (i, j > k) and the forward elimination X_i. -= L_ik X_k. / L_kk (i > k), and
+// row k of X is divided by L_kk (zeroed for a dropped pivot, which also leaves its column of X
+// zero).  The buffers alternate between steps, so one barrier per step suffices.  The steps
+// run in blocks of 16 with the block index a template argument, so every register index is a
+// constant and the register blocks wholly before the step are skipped at compile time.
+// Writes LiT [l][l] (fp32) = (L^-1)^T, the right operand of Y (L^-1)^T.
+constexpr int kCholRegMax = 160;
+constexpr int kCholNU = kCholRegMax / 16, kCholNV = kCholRegMax / 32;
+struct CholShared {
+  double colb[2][kCholRegMax], rowb[2][kCholRegMax], lkk[2];
+};
+
+template <int KU>
+__device__ __forceinline__ void chol_steps(double (&T)[kCholNU][kCholNV], double (&X)[kCholNU][kCholNV],
+                                           CholShared& sh, int l, double tol, int a, int b, int lane) {
+  constexpr int KV = KU >> 1;
+  for (int kk = 0; kk < 16; ++kk) {
+    const int k = 16 * KU + kk, buf = k & 1;
+    if (k >= l) return;
+    // pivot from lane a == kk of this thread's 16-lane group (the group shares b)
+    const double d = __shfl(T[KU][KV], (lane & 48) | kk, 64);
+    if (b == (k & 31)) {
+      const bool drop = !(d > tol);
+      const double piv = drop ? 0.0 : sqrt(d);
+      const double rp = drop ? 0.0 : 1.0 / piv;
+#pragma unroll
+      for (int u = KU; u < kCholNU; ++u) {
+        const int i = a + 16 * u;
+        if (i > k && i < l) sh.colb[buf][i] = T[u][KV] * rp;
+      }
+      if (a == kk) sh.lkk[buf] = piv;
+    }
+    if (a == kk) {
+#pragma unroll
+      for (int v = 0; v < kCholNV; ++v) {
+        const int j = b + 32 * v;
+        if (j < l) sh.rowb[buf][j] = X[KU][v];
+      }
+    }
+    __syncthreads();
+    const double lk = sh.lkk[buf];
+    const double inv = lk > 0.0 ? 1.0 / lk : 0.0;
+    double cc[kCholNV], rw[kCholNV];
+#pragma unroll
+    for (int v = 0; v < kCholNV; ++v) {
+      const int j = b + 32 * v;
+      cc[v] = (v >= KV && j > k && j < l) ? sh.colb[buf][j] : 0.0;
+      rw[v] = (v <= KV && j <= k) ? sh.rowb[buf][j] * inv : 0.0;
+    }
+#pragma unroll
+    for (int u = KU; u < kCholNU; ++u) {
+      const int i = a + 16 * u;
+      const double cr = (i > k && i < l) ? sh.colb[buf][i] : 0.0;
+#pragma unroll
+      for (int v = KV; v < kCholNV; ++v) T[u][v] -= cr * cc[v];
+#pragma unroll
+      for (int v = 0; v <= KV; ++v) X[u][v] -= cr * rw[v];
+    }
+    if (a == kk) {
+#pragma unroll
+      for (int v = 0; v <= KV; ++v) X[KU][v] = rw[v];
+    }
+  }
+}
+
+template <int... KU>
+__device__ __forceinline__ void chol_all(double (&T)[kCholNU][kCholNV], double (&X)[kCholNU][kCholNV],
+                                         CholShared& sh, int l, double tol, int a, int b, int lane,
+                                         std::integer_sequence<int, KU...>) {
+  (chol_steps<KU>(T, X, sh, l, tol, a, b, lane), ...);
+}
+
+__global__ void __launch_bounds__(512) chol_inv_reg(const double* G, float* LiT, int l, double rel_tol) {
+  __shared__ CholShared sh;
+  __shared__ double diag_max;
+  const int tid = threadIdx.x, a = tid & 15, b = tid >> 4, lane = tid & 63;
+  G += (int64_t)blockIdx.x * l * l;
+  LiT += (int64_t)blockIdx.x * l * l;
+  double T[kCholNU][kCholNV], X[kCholNU][kCholNV];
+#pragma unroll
+  for (int u = 0; u < kCholNU; ++u)
+#pragma unroll
+    for (int v = 0; v < kCholNV; ++v) {
+      const int i = a + 16 * u, j = b + 32 * v;
+      const bool in = i < l && j < l;
+      T[u][v] = in ? (i >= j ? G[(int64_t)i * l + j] : G[(int64_t)j * l + i]) : 0.0;   // lower triangle
+      X[u][v] = (in && i == j) ? 1.0 : 0.0;
+    }
+  if (tid < 64) {
+    double m = 0.0;
+    for (int i = lane; i < l; i += 64) m = fmax(m, G[(int64_t)i * l + i]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+    if (lane == 0) diag_max = m;
+  }
+  __syncthreads();
+  chol_all(T, X, sh, l, rel_tol * diag_max, a, b, lane, std::make_integer_sequence<int, kCholNU>());
+#pragma unroll
+  for (int u = 0; u < kCholNU; ++u)
+#pragma unroll
+    for (int v = 0; v < kCholNV; ++v) {
+      const int i = a + 16 * u, j = b + 32 * v;
+      if (i < l && j < l) LiT[(int64_t)j * l + i] = (float)X[u][v];
+    }
+}
+
 // ------------------------------------------------------------------ Jacobi eigensolver
 // Symmetric A [l][l] (fp64, overwritten; its diagonal ends as the eigenvalues) and V [l][l]
 // (out: eigenvectors as columns).  Parallel cyclic Jacobi with round-robin pairing: each round
@@ -770,32 +882,76 @@ __global__ void __launch_bounds__(1024) jacobi(double* A, double* V, int l, int 
 }
 
 // Same eigenproblem with the matrix resident in LDS as its packed lower triangle (index
-// i (i + 1) / 2 + j, j <= i; fp64), for l up to kJacobiLdsMax.  A round rotates the l/2
-// disjoint pairs at once: each 2 x 2 block between two pairs P, Q (stored once, P <= Q) becomes
-// J_P^T B J_Q, a diagonal block diag(a'_pp, a'_qq) with a'_pq = 0.  The eigenvectors accumulate
-// in VT [l][l] (global, row k = eigenvector k), V <- V J applied to rows p, q of VT.  An odd l
-// is padded with a zero row that is never rotated.
+// i (i + 1) / 2 + j, j <= i; fp64), for l up to kJacobiLdsMax, split in two kernels so that the
+// eigenvector accumulation does not serialise on the one work-group that owns a matrix:
+//  - jacobi_chunk (one 1024-thread work-group per matrix) runs up to kJacobiChunkSweeps sweeps
+//    on the triangle.  A round rotates the l/2 disjoint pairs at once: each 2 x 2 block between
+//    two pairs P, Q (stored once, P <= Q) becomes J_P^T B J_Q, a diagonal block
+//    diag(a'_pp, a'_qq) with a'_pq = 0.  Every round's (c, s) are written to a rotation log;
+//    the triangle is kept in global memory between chunks.
+//  - jacobi_apply replays the chunk's log on VT (row k = eigenvector k): V <- V J acts on rows p
+//    and q of VT independently in every column, so a work-group takes kApplyCols columns of one
+//    matrix into LDS and applies all logged rounds to them.
+// The host launches the pair ceil(max_sweeps / kJacobiChunkSweeps) times; chunks after
+// convergence return at once.  Per-matrix state: [0] converged (or out of sweeps), [1] rounds
+// logged by the last chunk, [2] sweeps done.  An odd l is padded with a zero row that is never
+// rotated.
 constexpr int kJacobiLdsMax = 192;
+constexpr int kJacobiChunkSweeps = 4;
+constexpr int kApplyCols = 16, kApplyPitch = kApplyCols + 1, kApplyGroups = 256 / kApplyCols;
 __device__ __forceinline__ int tri(int i, int j) { return i >= j ? i * (i + 1) / 2 + j : j * (j + 1) / 2 + i; }
 
-__global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l, int max_sweeps, double tol) {
+// Round-robin pairing (lp even): position 0 stays, positions 1 .. lp-1 advance by one each
+// round; round `round` (0 .. lp-2) pairs position k with position lp-1-k.  Returns p < q.
+__device__ __forceinline__ void jacobi_pair(int k, int round, int lp, int& p, int& q) {
+  auto pos = [&](int x) {
+    if (x == 0) return 0;
+    int v = x - 1 + round;   // < 2 (lp - 1)
+    if (v >= lp - 1) v -= lp - 1;
+    return 1 + v;
+  };
+  p = pos(k);
+  q = pos(lp - 1 - k);
+  if (p > q) {
+    const int t = p;
+    p = q;
+    q = t;
+  }
+}
+
+__device__ __forceinline__ int tri_row(int e) {   // i with i (i + 1) / 2 <= e < (i + 1) (i + 2) / 2
+  int i = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+  while (i * (i + 1) / 2 > e) --i;
+  while ((i + 1) * (i + 2) / 2 <= e) ++i;
+  return i;
+}
+
+__global__ void __launch_bounds__(1024) jacobi_chunk(double* A, double* Tg, double2* rot, int* state, int l,
+                                                     int first, int max_sweeps, double tol) {
   extern __shared__ double T[];   // packed lower triangle, lp (lp + 1) / 2 entries
   __shared__ double cs[kJacobiLdsMax / 2], sn[kJacobiLdsMax / 2];
   __shared__ int pp[kJacobiLdsMax / 2], qq[kJacobiLdsMax / 2];
   __shared__ double red[2][32];
   __shared__ int done;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 31, warp = tid >> 5;
-  A += (int64_t)blockIdx.x * l * l;
-  VT += (int64_t)blockIdx.x * l * l;
   const int lp = (l + 1) & ~1, half = lp / 2, ntri = lp * (lp + 1) / 2;
-  for (int e = tid; e < ntri; e += nt) {
-    int i = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
-    while (i * (i + 1) / 2 > e) --i;
-    while ((i + 1) * (i + 2) / 2 <= e) ++i;
-    const int j = e - i * (i + 1) / 2;
-    T[e] = (i < l && j < l) ? A[(int64_t)i * l + j] : 0.0;
+  int* stt = state + 4 * blockIdx.x;
+  if (!first && stt[0]) {
+    if (tid == 0) stt[1] = 0;
+    return;
   }
-  for (int e = tid; e < l * l; e += nt) VT[e] = (e / l == e % l) ? 1.0 : 0.0;
+  const int swept = first ? 0 : stt[2];
+  A += (int64_t)blockIdx.x * l * l;
+  Tg += (int64_t)blockIdx.x * ntri;
+  rot += (int64_t)blockIdx.x * kJacobiChunkSweeps * (lp - 1) * half;
+  for (int e = tid; e < ntri; e += nt) {
+    if (first) {
+      const int i = tri_row(e), j = e - i * (i + 1) / 2;
+      T[e] = (i < l && j < l) ? A[(int64_t)i * l + j] : 0.0;
+    } else {
+      T[e] = Tg[e];
+    }
+  }
   const int nblk = half * (half + 1) / 2;
   // this thread's rotation-pair blocks (K1, K2), K2 <= K1, decoded once: with 1024 threads and
   // half <= kJacobiLdsMax / 2, at most 5 per thread
@@ -805,20 +961,17 @@ __global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l,
 #pragma unroll
   for (int c = 0; c < kMaxBlk; ++c) {
     const int e = tid + c * nt;
-    int k1 = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
-    while (k1 * (k1 + 1) / 2 > e) --k1;
-    while ((k1 + 1) * (k1 + 2) / 2 <= e) ++k1;
+    const int k1 = tri_row(e);
     bk1[c] = e < nblk ? k1 : -1;
     bk2[c] = e - k1 * (k1 + 1) / 2;
   }
   __syncthreads();
-  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+  int sweeps = 0, logged = 0;
+  bool conv = false;
+  for (; sweeps < kJacobiChunkSweeps && swept + sweeps < max_sweeps; ++sweeps) {
     double off = 0.0, tot = 0.0;
     for (int e = tid; e < ntri; e += nt) {
-      int i = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
-      while (i * (i + 1) / 2 > e) --i;
-      while ((i + 1) * (i + 2) / 2 <= e) ++i;
-      const int j = e - i * (i + 1) / 2;
+      const int i = tri_row(e), j = e - i * (i + 1) / 2;
       const double x = T[e] * T[e];
       if (i == j) tot += x;
       else { off += 2.0 * x; tot += 2.0 * x; }
@@ -841,12 +994,14 @@ __global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l,
       done = !(o > tol * tol * t);
     }
     __syncthreads();
-    if (done) break;
-    for (int round = 0; round < lp - 1; ++round) {
+    if (done) {
+      conv = true;
+      break;
+    }
+    for (int round = 0; round < lp - 1; ++round, ++logged) {
       if (tid < half) {
-        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (lp - 1); };
-        int p = pos(tid), q = pos(lp - 1 - tid);
-        if (p > q) { const int t = p; p = q; q = t; }
+        int p, q;
+        jacobi_pair(tid, round, lp, p, q);
         double c = 1.0, s = 0.0;
         if (q < l) {
           const double apq = T[tri(q, p)];
@@ -861,42 +1016,130 @@ __global__ void __launch_bounds__(1024) jacobi_lds(double* A, double* VT, int l,
         qq[tid] = q;
         cs[tid] = c;
         sn[tid] = s;
+        rot[(int64_t)logged * half + tid] = make_double2(c, s);
       }
       __syncthreads();
+      // the blocks of one round are disjoint: read a group of blocks first, then write them
+      auto blocks = [&](auto c0_, auto c1_) {
+        constexpr int c0 = decltype(c0_)::value, c1 = decltype(c1_)::value;
+        double b[c1 - c0][4];
+        int ix[c1 - c0][4];
 #pragma unroll
-      for (int c = 0; c < kMaxBlk; ++c) {   // block (K1, K2), K2 <= K1
-        const int k1 = bk1[c], k2 = bk2[c];
-        if (k1 < 0) continue;
-        const int p1 = pp[k1], q1 = qq[k1], p2 = pp[k2], q2 = qq[k2];
-        const double c1 = cs[k1], s1 = sn[k1], c2 = cs[k2], s2 = sn[k2];
-        if (k1 == k2) {
-          const double app = T[tri(p1, p1)], aqq = T[tri(q1, q1)], apq = T[tri(q1, p1)];
-          T[tri(p1, p1)] = c1 * c1 * app - 2.0 * c1 * s1 * apq + s1 * s1 * aqq;
-          T[tri(q1, q1)] = s1 * s1 * app + 2.0 * c1 * s1 * apq + c1 * c1 * aqq;
-          T[tri(q1, p1)] = 0.0;
-        } else {
-          // B rows {p1, q1}, columns {p2, q2}; B' = J1^T B J2
-          const double b00 = T[tri(p1, p2)], b01 = T[tri(p1, q2)], b10 = T[tri(q1, p2)], b11 = T[tri(q1, q2)];
-          const double r00 = c1 * b00 - s1 * b10, r01 = c1 * b01 - s1 * b11;
-          const double r10 = s1 * b00 + c1 * b10, r11 = s1 * b01 + c1 * b11;
-          T[tri(p1, p2)] = c2 * r00 - s2 * r01;
-          T[tri(p1, q2)] = s2 * r00 + c2 * r01;
-          T[tri(q1, p2)] = c2 * r10 - s2 * r11;
-          T[tri(q1, q2)] = s2 * r10 + c2 * r11;
+        for (int c = c0; c < c1; ++c) {   // block (K1, K2), K2 <= K1
+          const int k1 = bk1[c], k2 = bk2[c];
+          if (k1 < 0) continue;
+          const int p1 = pp[k1], q1 = qq[k1], p2 = pp[k2], q2 = qq[k2];
+          int* x = ix[c - c0];
+          if (k1 == k2) {
+            x[0] = tri(p1, p1);
+            x[1] = tri(q1, q1);
+            x[2] = tri(q1, p1);
+            x[3] = x[2];
+          } else {
+            x[0] = tri(p1, p2);
+            x[1] = tri(p1, q2);
+            x[2] = tri(q1, p2);
+            x[3] = tri(q1, q2);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) b[c - c0][u] = T[x[u]];
         }
-      }
-      for (int e = tid; e < half * l; e += nt) {   // V <- V J: rows p, q of VT
-        const int k = e / l, i = e % l, p = pp[k], q = qq[k];
-        if (q >= l) continue;
-        const double c = cs[k], s = sn[k];
-        const double x = VT[(int64_t)p * l + i], y = VT[(int64_t)q * l + i];
-        VT[(int64_t)p * l + i] = c * x - s * y;
-        VT[(int64_t)q * l + i] = s * x + c * y;
-      }
+#pragma unroll
+        for (int c = c0; c < c1; ++c) {
+          const int k1 = bk1[c], k2 = bk2[c];
+          if (k1 < 0) continue;
+          const int* x = ix[c - c0];
+          const double* v = b[c - c0];
+          const double c1v = cs[k1], s1 = sn[k1], c2 = cs[k2], s2 = sn[k2];
+          if (k1 == k2) {
+            const double app = v[0], aqq = v[1], apq = v[2];
+            T[x[0]] = c1v * c1v * app - 2.0 * c1v * s1 * apq + s1 * s1 * aqq;
+            T[x[1]] = s1 * s1 * app + 2.0 * c1v * s1 * apq + c1v * c1v * aqq;
+            T[x[2]] = 0.0;
+          } else {
+            // B rows {p1, q1}, columns {p2, q2}; B' = J1^T B J2
+            const double r00 = c1v * v[0] - s1 * v[2], r01 = c1v * v[1] - s1 * v[3];
+            const double r10 = s1 * v[0] + c1v * v[2], r11 = s1 * v[1] + c1v * v[3];
+            T[x[0]] = c2 * r00 - s2 * r01;
+            T[x[1]] = s2 * r00 + c2 * r01;
+            T[x[2]] = c2 * r10 - s2 * r11;
+            T[x[3]] = s2 * r10 + c2 * r11;
+          }
+        }
+      };
+      blocks(std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
+      blocks(std::integral_constant<int, 3>(), std::integral_constant<int, kMaxBlk>());
       __syncthreads();
     }
   }
+  for (int e = tid; e < ntri; e += nt) Tg[e] = T[e];
   for (int i = tid; i < l; i += nt) A[(int64_t)i * l + i] = T[tri(i, i)];
+  if (tid == 0) {
+    stt[0] = conv || swept + sweeps >= max_sweeps;
+    stt[1] = logged;
+    stt[2] = swept + sweeps;
+  }
+}
+
+// Replays the rotation log of the last chunk on kApplyCols columns of VT (identity before the
+// first chunk): thread (column, group g) applies the rotations of pairs g, g + kApplyGroups, ...
+// of every round, the round's rows read first (its pairs are disjoint), then written; the next
+// round's (c, s) are loaded while this one is applied.
+__global__ void __launch_bounds__(256) jacobi_apply(double* VT, const double2* __restrict__ rot,
+                                                    const int* __restrict__ state, int l, int first) {
+  extern __shared__ double Vs[];   // [l][kApplyPitch]
+  const int rounds = state[4 * blockIdx.y + 1];
+  if (!first && rounds == 0) return;
+  const int tid = threadIdx.x, col = tid % kApplyCols, g = tid / kApplyCols;
+  const int lp = (l + 1) & ~1, half = lp / 2, ncyc = lp - 1;
+  const int gc = blockIdx.x * kApplyCols + col;
+  VT += (int64_t)blockIdx.y * l * l;
+  rot += (int64_t)blockIdx.y * kJacobiChunkSweeps * ncyc * half;
+  for (int i = g; i < l; i += kApplyGroups)
+    Vs[i * kApplyPitch + col] = first ? (i == gc ? 1.0 : 0.0) : (gc < l ? VT[(int64_t)i * l + gc] : 0.0);
+  constexpr int kMaxPairs = (kJacobiLdsMax / 2 + kApplyGroups - 1) / kApplyGroups;
+  double2 nxt[kMaxPairs];
+  auto fetch = [&](int r) {
+#pragma unroll
+    for (int u = 0; u < kMaxPairs; ++u) {
+      const int k = g + u * kApplyGroups;
+      nxt[u] = (r < rounds && k < half) ? rot[(int64_t)r * half + k] : make_double2(1.0, 0.0);
+    }
+  };
+  fetch(0);
+  __syncthreads();
+  int round = 0;
+  for (int r = 0; r < rounds; ++r) {
+    double2 cur[kMaxPairs];
+#pragma unroll
+    for (int u = 0; u < kMaxPairs; ++u) cur[u] = nxt[u];
+    fetch(r + 1);
+    int pi[kMaxPairs], qi[kMaxPairs];
+    double x[kMaxPairs], y[kMaxPairs];
+#pragma unroll
+    for (int u = 0; u < kMaxPairs; ++u) {
+      const int k = g + u * kApplyGroups;
+      int p = 0, q = l;
+      if (k < half) jacobi_pair(k, round, lp, p, q);
+      pi[u] = p;
+      qi[u] = q;
+      if (q < l) {
+        x[u] = Vs[p * kApplyPitch + col];
+        y[u] = Vs[q * kApplyPitch + col];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxPairs; ++u) {
+      if (qi[u] >= l) continue;
+      const double c = cur[u].x, s = cur[u].y;
+      Vs[pi[u] * kApplyPitch + col] = c * x[u] - s * y[u];
+      Vs[qi[u] * kApplyPitch + col] = s * x[u] + c * y[u];
+    }
+    __syncthreads();
+    if (++round == ncyc) round = 0;
+  }
+  if (gc < l)
+    for (int i = g; i < l; i += kApplyGroups) VT[(int64_t)i * l + gc] = Vs[i * kApplyPitch + col];
 }
 
 // ------------------------------------------------------------------ top-r selection
@@ -1005,7 +1248,7 @@ __global__ void __launch_bounds__(256) fix_signs(T* Aout, T* Bout, int rows, int
 
 // ------------------------------------------------------------------ workspace layout
 struct SvdWs {
-  size_t om, y0, y1, w0, w1, g, li, bsk, g2, v, m1, m2, total;
+  size_t om, y0, y1, w0, w1, g, li, bsk, g2, v, m1, m2, jt, jr, js, total;
 };
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
@@ -1024,6 +1267,10 @@ SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
   w.v = o;   o += al(b * l * l * 8);
   w.m1 = o;  o += al(b * l * r * 8);
   w.m2 = o;  o += al(b * r * l * 8);
+  const size_t lp = (l + 1) & ~(size_t)1;
+  w.jt = o;  o += al(b * lp * (lp + 1) / 2 * 8);                       // Jacobi triangles
+  w.jr = o;  o += al(b * kJacobiChunkSweeps * (lp - 1) * (lp / 2) * 16);  // rotation log
+  w.js = o;  o += al(b * 4 * 4);                                        // Jacobi state
   w.total = o;
   return w;
 }
@@ -1042,21 +1289,32 @@ hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, in
                                                                   (int64_t)rows * l, (int64_t)l * l, b, st, true)))
       return e;
     const double tolr = pass == 0 ? 1e-12 : 1e-10;
-    const size_t tri_bytes = sizeof(double) * (size_t)l * (l + 1) / 2;
-    if (l <= kJacobiLdsMax) {
-      if (tri_bytes > 64 * 1024 &&
-          (e = hipFuncSetAttribute(reinterpret_cast<const void*>(chol_inv_lds),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)tri_bytes)))
+    if (l <= kCholRegMax) {
+      // dst = src Li^T on matrix cores; Li^T (fp32) takes the place of Li
+      float* lit = reinterpret_cast<float*>(Li);
+      chol_inv_reg<<<b, 512, 0, st>>>(G, lit, l, tolr);
+      if ((e = hipGetLastError())) return e;
+      if ((e = gemm_f32<false>(src, lit, dst, rows, l, l, l, l, l, (int64_t)rows * l, (int64_t)l * l,
+                               (int64_t)rows * l, b, st)))
         return e;
-      chol_inv_lds<<<b, 1024, tri_bytes, st>>>(G, Li, l, tolr);
     } else {
-      chol_inv<<<b, 1024, 0, st>>>(G, Li, l, tolr);
+      const size_t tri_bytes = sizeof(double) * (size_t)l * (l + 1) / 2;
+      if (l <= kJacobiLdsMax) {
+        if (tri_bytes > 64 * 1024 &&
+            (e = hipFuncSetAttribute(reinterpret_cast<const void*>(chol_inv_lds),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)tri_bytes)))
+          return e;
+        chol_inv_lds<<<b, 1024, tri_bytes, st>>>(G, Li, l, tolr);
+      } else {
+        chol_inv<<<b, 1024, 0, st>>>(G, Li, l, tolr);
+      }
+      if ((e = hipGetLastError())) return e;
+      // dst = src Li^T
+      if ((e = run_gemm<float, double, float, double, false, true>(src, Li, dst, rows, l, l, l, l, l,
+                                                                    (int64_t)rows * l, (int64_t)l * l,
+                                                                    (int64_t)rows * l, b, st)))
+        return e;
     }
-    if ((e = hipGetLastError())) return e;
-    // dst = src Li^T
-    if ((e = run_gemm<float, double, float, double, false, true>(src, Li, dst, rows, l, l, l, l, l, (int64_t)rows * l,
-                                                                  (int64_t)l * l, (int64_t)rows * l, b, st)))
-      return e;
     float* t = src;
     src = dst;
     dst = t;
@@ -1128,10 +1386,21 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
     return e;
   if (in_lds) {
     if (tri_bytes > 64 * 1024 &&
-        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_lds), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)tri_bytes)))
+        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_chunk),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)tri_bytes)))
       return e;
-    jacobi_lds<<<b, 1024, tri_bytes, st>>>(g2, V, l, 40, 1e-13);
+    double* jt = reinterpret_cast<double*>(base + L.jt);
+    double2* jr = reinterpret_cast<double2*>(base + L.jr);
+    int* js = reinterpret_cast<int*>(base + L.js);
+    const int max_sweeps = 40;
+    const dim3 agrid((unsigned)((l + kApplyCols - 1) / kApplyCols), (unsigned)b);
+    const size_t a_bytes = sizeof(double) * (size_t)l * kApplyPitch;
+    for (int c = 0; c * kJacobiChunkSweeps < max_sweeps; ++c) {
+      jacobi_chunk<<<b, 1024, tri_bytes, st>>>(g2, jt, jr, js, l, c == 0, max_sweeps, 1e-13);
+      if ((e = hipGetLastError())) return e;
+      jacobi_apply<<<agrid, 256, a_bytes, st>>>(V, jr, js, l, c == 0);
+      if ((e = hipGetLastError())) return e;
+    }
   } else {
     jacobi<<<b, 1024, 0, st>>>(g2, V, l, 40, 1e-13);
   }
