@@ -232,22 +232,27 @@ __device__ __forceinline__ float4 ld4_guard(const float* p, int64_t base, int av
 }
 
 // C (M x N, fp64) = A^T B with A stored [K][M] and B stored [K][N], both fp32 (exact in fp64),
-// for M <= 160 (the sketch width: Gram matrices Y^T Y and the projection Q^T Z): one work-group
-// holds all M rows x 64 columns, each wave one 16-column block against the ten 16-row blocks, K
-// in chunks of 16 through double-buffered LDS.  Every operand is read once per 64 columns
-// (the 32 x 32 tiles of gemm_f64 read A once per 32 columns and B once per 32 rows).
+// for M <= 160 (the sketch width: Gram matrices Y^T Y): one work-group holds all M rows x 64
+// columns, each wave one 16-column block against the ten 16-row blocks, K in chunks of 16
+// through double-buffered LDS.  Every operand is read once per 64 columns.  Split K: work-group
+// y sums rows [y kc, (y + 1) kc) of A and B into C + y sP.  With `lower` (a Gram read only below
+// its diagonal), row blocks wholly above a wave's columns are skipped and left zero.
 constexpr int kTnRows = 160;
 __global__ void __launch_bounds__(256) gemm_f64_tn(const float* __restrict__ A, const float* __restrict__ B,
                                                    double* __restrict__ C, int M, int N, int K, int64_t lda,
-                                                   int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC) {
+                                                   int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
+                                                   int kc, int64_t sP, int lower) {
   constexpr int AQ = kTnRows / 4, NAV = (16 * AQ + 255) / 256;
   __shared__ __attribute__((aligned(16))) float As[2][16][kTnRows + 4];
   __shared__ __attribute__((aligned(16))) float Bs[2][16][64 + 4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, kq = lane >> 4;
   const int j0 = blockIdx.x * 64;
-  A += (int64_t)blockIdx.z * sA;
-  B += (int64_t)blockIdx.z * sB;
-  C += (int64_t)blockIdx.z * sC;
+  const int kb = blockIdx.y * kc;
+  A += (int64_t)blockIdx.z * sA + (int64_t)kb * lda;
+  B += (int64_t)blockIdx.z * sB + (int64_t)kb * ldb;
+  C += (int64_t)blockIdx.z * sC + (int64_t)blockIdx.y * sP;
+  K = min(K - kb, kc);
+  const int t0 = lower ? (j0 + wave * 16) / 16 : 0;   // first row block that meets the lower triangle
   float4 ra[NAV], rb;
   auto load = [&](int k0) {
 #pragma unroll
@@ -283,7 +288,8 @@ __global__ void __launch_bounds__(256) gemm_f64_tn(const float* __restrict__ A, 
       const double b = (double)Bs[buf][k][wave * 16 + r16];
 #pragma unroll
       for (int t = 0; t < kTnRows / 16; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)As[buf][k][16 * t + r16], b, acc[t], 0, 0, 0);
+        if (t >= t0)
+          acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)As[buf][k][16 * t + r16], b, acc[t], 0, 0, 0);
     }
     if (more) store(buf ^ 1);
     __syncthreads();
@@ -309,7 +315,7 @@ hipError_t run_gemm(const TA* A, const TB* B, TC* C, int M, int N, int K, int64_
                 std::is_same<TB, float>::value && std::is_same<TC, double>::value && TRA && !TRB) {
     if (M <= kTnRows && lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0) {
       const dim3 grid((unsigned)((N + 63) / 64), 1u, (unsigned)batch);
-      gemm_f64_tn<<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC);
+      gemm_f64_tn<<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, K, 0, lower_only ? 1 : 0);
       return hipGetLastError();
     }
   }
@@ -547,6 +553,41 @@ hipError_t gemm_f32(const float* A, const float* B, float* C, int M, int N, int 
     return hipGetLastError();
   }
   return run_gemm<float, float, float, float, TRA, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, st);
+}
+
+// ------------------------------------------------------------------ Gram matrices
+// G (fp64, l x l) = Y^T Y for Y [rows][l] fp32; with `lower` only the lower triangle (zero above).  The rows are split
+// over `splits` work-groups per column tile so the grid covers the device; their partial sums
+// land in `part` and are added in split order (deterministic).
+constexpr int kGramSplitMax = 4;
+__global__ void __launch_bounds__(256) sum_splits(const double* __restrict__ part, double* __restrict__ G,
+                                                  int64_t n, int splits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  double s = part[i];
+  for (int y = 1; y < splits; ++y) s += part[(int64_t)y * n + i];
+  G[i] = s;
+}
+
+hipError_t gram_f64(const float* Y, double* G, double* part, int rows, int l, int b, bool lower, hipStream_t st) {
+  const int64_t sY = (int64_t)rows * l, sG = (int64_t)l * l;
+  if (l > kTnRows || l % 4)
+    return run_gemm<float, float, double, double, true, false>(Y, Y, G, l, l, rows, l, l, l, sY, sY, sG, b, st, lower);
+  const int tiles = (l + 63) / 64 * b;
+  int splits = std::min(kGramSplitMax, std::max(1, (2048 + tiles - 1) / tiles));
+  splits = std::min(splits, std::max(1, rows / 256));
+  const int kc = (rows + splits - 1) / splits;
+  const dim3 grid((unsigned)((l + 63) / 64), (unsigned)splits, (unsigned)b);
+  if (splits == 1) {
+    gemm_f64_tn<<<grid, 256, 0, st>>>(Y, Y, G, l, l, rows, l, l, l, sY, sY, sG, rows, 0, lower ? 1 : 0);
+    return hipGetLastError();
+  }
+  const int64_t n = (int64_t)b * sG;
+  gemm_f64_tn<<<grid, 256, 0, st>>>(Y, Y, part, l, l, rows, l, l, l, sY, sY, sG, kc, n, lower ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e) return e;
+  sum_splits<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, G, n, splits);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ Cholesky with dropping
@@ -1145,15 +1186,16 @@ __global__ void __launch_bounds__(256) jacobi_apply(double* VT, const double2* _
 // ------------------------------------------------------------------ top-r selection
 // From the eigenpairs (diag of E, columns of V) of matrix b: sigma_i = sqrt(lambda_(i)) for the
 // r largest eigenvalues in descending order (ties by index), M1 = V_r Sigma_r [l][r] and
-// M2 = Sigma_r^-1 V_r^T [r][l] (zero rows for sigma = 0).
+// M2 = Sigma_r^-1 V_r^T [r][l] (zero rows for sigma = 0); M1f is M1 rounded to fp32.
 __global__ void __launch_bounds__(256) select_top(const double* E, const double* V, float* sigma, double* M1,
-                                                  double* M2, int l, int r, int v_transposed) {
+                                                  float* M1f, double* M2, int l, int r, int v_transposed) {
   __shared__ int order[256];
   __shared__ double sig[256];
   const int tid = threadIdx.x;
   E += (int64_t)blockIdx.x * l * l;
   V += (int64_t)blockIdx.x * l * l;
   M1 += (int64_t)blockIdx.x * l * r;
+  M1f += (int64_t)blockIdx.x * l * r;
   M2 += (int64_t)blockIdx.x * r * l;
   sigma += (int64_t)blockIdx.x * r;
   for (int i = tid; i < l; i += blockDim.x) {
@@ -1172,7 +1214,9 @@ __global__ void __launch_bounds__(256) select_top(const double* E, const double*
   for (int i = tid; i < r; i += blockDim.x) sigma[i] = (float)sig[i];
   for (int e = tid; e < l * r; e += blockDim.x) {
     const int row = e / r, c = e % r;
-    M1[e] = (v_transposed ? V[(int64_t)order[c] * l + row] : V[(int64_t)row * l + order[c]]) * sig[c];
+    const double x = (v_transposed ? V[(int64_t)order[c] * l + row] : V[(int64_t)row * l + order[c]]) * sig[c];
+    M1[e] = x;
+    M1f[e] = (float)x;
   }
   for (int e = tid; e < r * l; e += blockDim.x) {
     const int c = e / l, col = e % l;
@@ -1182,8 +1226,11 @@ __global__ void __launch_bounds__(256) select_top(const double* E, const double*
 }
 
 // ------------------------------------------------------------------ sign convention
-// Component c of matrix b: if the largest-magnitude entry of A[:, c] (first on ties) is
-// negative, negate A[:, c] and B[c, :].  One work-group per (component, matrix).
+// Component c of matrix b: if the largest-magnitude entry of A[:, c] (the lowest row among
+// equals) is negative, A[:, c] and B[c, :] are negated.  Three passes so the row scan covers the
+// device: sign_partial reduces row slices (kSignSplits per matrix, 64 columns per work-group,
+// coalesced rows), sign_decide merges the slices in row order, sign_negate flips the flagged
+// entries of A and B.
 template <typename T>
 __device__ __forceinline__ double sign_val(T v) {
   if constexpr (sizeof(T) == 2) return (double)__builtin_bit_cast(__bf16, (uint16_t)v);
@@ -1195,60 +1242,106 @@ __device__ __forceinline__ T negated(T v) {
   else return -v;
 }
 
-// Sign convention: for each column c of A (rows x r, row-major) the entry of largest magnitude
-// (the lowest row among equals) is made positive by negating column c of A and row c of B.
-// A work-group takes 64 columns of one matrix; its threads read rows of those columns (64
-// consecutive entries per row, coalesced), four row phases per column, and the phases are
-// merged by the same rule.
+constexpr int kSignSplits = 16;
+struct SignPart {
+  double mag;
+  int idx, neg;
+};
+// (mag, idx) beats (bm, bi): larger magnitude, or equal magnitude at a lower row
+__device__ __forceinline__ bool sign_better(double mag, int idx, double bm, int bi) {
+  return mag > bm || (mag == bm && idx < bi);
+}
+
 template <typename T>
-__global__ void __launch_bounds__(256) fix_signs(T* Aout, T* Bout, int rows, int cols, int r) {
-  __shared__ double bv[4][64], sv[4][64];
-  __shared__ int bi[4][64];
-  __shared__ int neg[64];
+__global__ void __launch_bounds__(256) sign_partial(const T* __restrict__ A, SignPart* __restrict__ part, int rows,
+                                                    int r) {
+  __shared__ double bv[4][64];
+  __shared__ int bi[4][64], bn[4][64];
   const int tid = threadIdx.x, cl = tid & 63, ph = tid >> 6;
   const int c = blockIdx.x * 64 + cl;
-  Aout += (int64_t)blockIdx.y * rows * r;
-  Bout += (int64_t)blockIdx.y * r * cols;
-  double best = -1.0, bval = 0.0;
-  int bidx = 0;
+  const int rs = (rows + kSignSplits - 1) / kSignSplits, r0 = blockIdx.y * rs, r1 = min(rows, r0 + rs);
+  A += (int64_t)blockIdx.z * rows * r;
+  double best = -1.0;
+  int bidx = 0, neg = 0;
   if (c < r) {
-    for (int i = ph; i < rows; i += 4) {
-      const double x = sign_val(Aout[(int64_t)i * r + c]);
-      if (fabs(x) > best) { best = fabs(x); bidx = i; bval = x; }
+    for (int i = r0 + ph; i < r1; i += 4) {
+      const double x = sign_val(A[(int64_t)i * r + c]);
+      if (fabs(x) > best) {
+        best = fabs(x);
+        bidx = i;
+        neg = x < 0.0;
+      }
     }
   }
   bv[ph][cl] = best;
   bi[ph][cl] = bidx;
-  sv[ph][cl] = bval;
+  bn[ph][cl] = neg;
   __syncthreads();
-  if (ph == 0) {
+  if (ph == 0 && c < r) {
     for (int q = 1; q < 4; ++q) {
-      if (bv[q][cl] > best || (bv[q][cl] == best && bi[q][cl] < bidx)) {
+      if (sign_better(bv[q][cl], bi[q][cl], best, bidx)) {
         best = bv[q][cl];
         bidx = bi[q][cl];
-        bval = sv[q][cl];
+        neg = bn[q][cl];
       }
     }
-    neg[cl] = c < r && bval < 0.0;
+    SignPart o;
+    o.mag = best;
+    o.idx = bidx;
+    o.neg = neg;
+    part[((int64_t)blockIdx.z * kSignSplits + blockIdx.y) * r + c] = o;
   }
-  __syncthreads();
-  if (c < r && neg[cl]) {
-    for (int i = ph; i < rows; i += 4) {
-      T& x = Aout[(int64_t)i * r + c];
-      x = negated(x);
+}
+
+__global__ void __launch_bounds__(256) sign_decide(const SignPart* __restrict__ part, int* __restrict__ flag, int r,
+                                                   int n_mats) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_mats * r) return;
+  const int z = i / r, c = i % r;
+  double best = -1.0;
+  int bidx = 0, neg = 0;
+  for (int y = 0; y < kSignSplits; ++y) {
+    const SignPart p = part[((int64_t)z * kSignSplits + y) * r + c];
+    if (sign_better(p.mag, p.idx, best, bidx)) {
+      best = p.mag;
+      bidx = p.idx;
+      neg = p.neg;
     }
   }
-  const int nc = min(64, r - blockIdx.x * 64);
-  for (int k = 0; k < nc; ++k) {
-    if (!neg[k]) continue;
-    T* row = Bout + (int64_t)(blockIdx.x * 64 + k) * cols;
-    for (int j = tid; j < cols; j += 256) row[j] = negated(row[j]);
+  flag[i] = neg;
+}
+
+// A [b][rows][r] and B [b][r][cols]: entries of flagged components negated, one per thread
+template <typename T>
+__global__ void __launch_bounds__(256) sign_negate(T* __restrict__ A, T* __restrict__ B, const int* __restrict__ flag,
+                                                   int rows, int cols, int r, int64_t na, int64_t nb) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < na) {
+    const int64_t z = i / ((int64_t)rows * r);
+    const int c = (int)(i % r);
+    if (flag[z * r + c]) A[i] = negated(A[i]);
+  } else if (i < na + nb) {
+    const int64_t j = i - na;
+    const int64_t zc = j / cols;   // z * r + c
+    if (flag[zc]) B[j] = negated(B[j]);
   }
+}
+
+template <typename T>
+hipError_t fix_signs(T* A, T* B, SignPart* part, int* flag, int b, int rows, int cols, int r, hipStream_t st) {
+  sign_partial<T><<<dim3((r + 63) / 64, kSignSplits, b), 256, 0, st>>>(A, part, rows, r);
+  hipError_t e = hipGetLastError();
+  if (e) return e;
+  sign_decide<<<(b * r + 255) / 256, 256, 0, st>>>(part, flag, r, b);
+  if ((e = hipGetLastError())) return e;
+  const int64_t na = (int64_t)b * rows * r, nb = (int64_t)b * r * cols;
+  sign_negate<T><<<(unsigned)((na + nb + 255) / 256), 256, 0, st>>>(A, B, flag, rows, cols, r, na, nb);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ workspace layout
 struct SvdWs {
-  size_t om, y0, y1, w0, w1, g, li, bsk, g2, v, m1, m2, jt, jr, js, total;
+  size_t om, y0, y1, w0, w1, g, li, part, bskt, g2, v, m1, m1f, m2, jt, jr, js, sp, sf, total;
 };
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
@@ -1262,15 +1355,19 @@ SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
   w.w1 = o;  o += al(b * n * l * 4);
   w.g = o;   o += al(b * l * l * 8);
   w.li = o;  o += al(b * l * l * 8);
-  w.bsk = o; o += al(b * l * n * 8);
+  w.part = o; o += al(kGramSplitMax * b * l * l * 8);                 // split Gram partial sums
+  w.bskt = o; o += al(b * n * l * 4);                                  // Bsk^T = Z^T Q (fp32)
   w.g2 = o;  o += al(b * l * l * 8);
   w.v = o;   o += al(b * l * l * 8);
   w.m1 = o;  o += al(b * l * r * 8);
+  w.m1f = o; o += al(b * l * r * 4);
   w.m2 = o;  o += al(b * r * l * 8);
   const size_t lp = (l + 1) & ~(size_t)1;
   w.jt = o;  o += al(b * lp * (lp + 1) / 2 * 8);                       // Jacobi triangles
   w.jr = o;  o += al(b * kJacobiChunkSweeps * (lp - 1) * (lp / 2) * 16);  // rotation log
   w.js = o;  o += al(b * 4 * 4);                                        // Jacobi state
+  w.sp = o;  o += al(b * kSignSplits * r * sizeof(SignPart));           // sign scan partials
+  w.sf = o;  o += al(b * r * 4);                                        // sign flags
   w.total = o;
   return w;
 }
@@ -1278,16 +1375,14 @@ SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
 // Y [b][rows][l] (fp32) <- orthonormal (or zero) columns spanning it: `passes` rounds of
 // CholeskyQR with pivot dropping (two = CholeskyQR2).  Rounds alternate between Y and `tmp`; with
 // an odd number the result is in `tmp` and the caller swaps the two.
-hipError_t orth(float* Y, float* tmp, double* G, double* Li, int b, int rows, int l, int passes, hipStream_t st) {
+hipError_t orth(float* Y, float* tmp, double* G, double* Li, double* part, int b, int rows, int l, int passes,
+                hipStream_t st) {
   hipError_t e;
   float* src = Y;
   float* dst = tmp;
   for (int pass = 0; pass < passes; ++pass) {
-    // G = Y^T Y (fp64)
-    // both Cholesky kernels read only the lower triangle of G
-    if ((e = run_gemm<float, float, double, double, true, false>(src, src, G, l, l, rows, l, l, l, (int64_t)rows * l,
-                                                                  (int64_t)rows * l, (int64_t)l * l, b, st, true)))
-      return e;
+    // G = Y^T Y (fp64); the Cholesky kernels read only its lower triangle
+    if ((e = gram_f64(src, G, part, rows, l, b, true, st))) return e;
     const double tolr = pass == 0 ? 1e-12 : 1e-10;
     if (l <= kCholRegMax) {
       // dst = src Li^T on matrix cores; Li^T (fp32) takes the place of Li
@@ -1341,7 +1436,7 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   float* w1 = reinterpret_cast<float*>(base + L.w1);
   double* G = reinterpret_cast<double*>(base + L.g);
   double* Li = reinterpret_cast<double*>(base + L.li);
-  double* bsk = reinterpret_cast<double*>(base + L.bsk);
+  double* part = reinterpret_cast<double*>(base + L.part);
   double* g2 = reinterpret_cast<double*>(base + L.g2);
   double* V = reinterpret_cast<double*>(base + L.v);
   double* m1 = reinterpret_cast<double*>(base + L.m1);
@@ -1359,7 +1454,7 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   // precision, and the next product only needs their span), the final basis Q two
   if ((e = gemm_f32<false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
   auto orth_swap = [&](float*& X, float*& Xt, int rows_, int passes) -> hipError_t {
-    hipError_t r = orth(X, Xt, G, Li, b, rows_, l, passes, st);
+    hipError_t r = orth(X, Xt, G, Li, part, b, rows_, l, passes, st);
     if (passes & 1) std::swap(X, Xt);
     return r;
   };
@@ -1373,17 +1468,14 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
     if ((e = orth_swap(Y, Yt, m, it + 1 < power_iters ? 1 : 2))) return e;
   }
   y0 = Y;
-  // Bsk = Q^T Z (fp64), its Gram Bsk Bsk^T, eigenpairs
-  if ((e = run_gemm<float, float, double, double, true, false>(y0, z, bsk, l, n, m, l, n, n, sY, sZ, (int64_t)l * n, b,
-                                                                st)))
-    return e;
+  // Bsk^T = Z^T Q (fp32 matrix cores), the Gram Bsk Bsk^T in fp64, its eigenpairs
+  float* bskt = reinterpret_cast<float*>(base + L.bskt);
+  if ((e = gemm_f32<true>(z, y0, bskt, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
   const int lp = (l + 1) & ~1;
   const size_t tri_bytes = sizeof(double) * (size_t)lp * (lp + 1) / 2;
   const bool in_lds = lp <= kJacobiLdsMax;
   // the LDS eigensolver reads only the lower triangle of the Gram; the global one all of it
-  if ((e = run_gemm<double, double, double, double, false, true>(bsk, bsk, g2, l, l, n, n, n, l, (int64_t)l * n,
-                                                                  (int64_t)l * n, sLL, b, st, in_lds)))
-    return e;
+  if ((e = gram_f64(bskt, g2, part, n, l, b, in_lds, st))) return e;
   if (in_lds) {
     if (tri_bytes > 64 * 1024 &&
         (e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_chunk),
@@ -1405,31 +1497,30 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
     jacobi<<<b, 1024, 0, st>>>(g2, V, l, 40, 1e-13);
   }
   if ((e = hipGetLastError())) return e;
-  select_top<<<b, 256, 0, st>>>(g2, V, sigma_out, m1, m2, l, r, in_lds ? 1 : 0);
+  float* m1f = reinterpret_cast<float*>(base + L.m1f);
+  select_top<<<b, 256, 0, st>>>(g2, V, sigma_out, m1, m1f, m2, l, r, in_lds ? 1 : 0);
   if ((e = hipGetLastError())) return e;
   // A = Q (W_r Sigma_r), B = (Sigma_r^-1 W_r^T) Bsk, then the sign convention
+  SignPart* sp = reinterpret_cast<SignPart*>(base + L.sp);
+  int* sf = reinterpret_cast<int*>(base + L.sf);
   if (out_bf16) {
     bf16_bits* A = static_cast<bf16_bits*>(a_out);
     bf16_bits* Bo = static_cast<bf16_bits*>(b_out);
     if ((e = run_gemm<float, double, bf16_bits, double, false, false>(y0, m1, A, m, r, l, l, r, r, sY, (int64_t)l * r,
                                                                        (int64_t)m * r, b, st)))
       return e;
-    if ((e = run_gemm<double, double, bf16_bits, double, false, false>(m2, bsk, Bo, r, n, l, l, n, n, (int64_t)r * l,
-                                                                        (int64_t)l * n, (int64_t)r * n, b, st)))
+    if ((e = run_gemm<double, float, bf16_bits, double, false, true>(m2, bskt, Bo, r, n, l, l, l, n, (int64_t)r * l,
+                                                                      sW, (int64_t)r * n, b, st)))
       return e;
-    fix_signs<bf16_bits><<<dim3((r + 63) / 64, b), 256, 0, st>>>(A, Bo, m, n, r);
-  } else {
-    float* A = static_cast<float*>(a_out);
-    float* Bo = static_cast<float*>(b_out);
-    if ((e = run_gemm<float, double, float, double, false, false>(y0, m1, A, m, r, l, l, r, r, sY, (int64_t)l * r,
-                                                                   (int64_t)m * r, b, st)))
-      return e;
-    if ((e = run_gemm<double, double, float, double, false, false>(m2, bsk, Bo, r, n, l, l, n, n, (int64_t)r * l,
-                                                                    (int64_t)l * n, (int64_t)r * n, b, st)))
-      return e;
-    fix_signs<float><<<dim3((r + 63) / 64, b), 256, 0, st>>>(A, Bo, m, n, r);
+    return fix_signs<bf16_bits>(A, Bo, sp, sf, b, m, n, r, st);
   }
-  return hipGetLastError();
+  float* A = static_cast<float*>(a_out);
+  float* Bo = static_cast<float*>(b_out);
+  if ((e = gemm_f32<false>(y0, m1f, A, m, r, l, l, r, r, sY, (int64_t)l * r, (int64_t)m * r, b, st))) return e;
+  if ((e = run_gemm<double, float, float, double, false, true>(m2, bskt, Bo, r, n, l, l, l, n, (int64_t)r * l, sW,
+                                                                (int64_t)r * n, b, st)))
+    return e;
+  return fix_signs<float>(A, Bo, sp, sf, b, m, n, r, st);
 }
 
 }  // namespace kvc
