@@ -438,31 +438,31 @@ __global__ void __launch_bounds__(256) gemm_f32_mfma(const float* __restrict__ A
 // The same product for narrow N (the sketch width l = r + p, at most 160): a 128 x 32 NB tile per
 // work-group, each wave 32 rows x all NB column blocks, so no matrix-core work is spent on
 // columns past N (a 128 x 128 tile at N = 160 computes 256 columns).
-template <bool TRA, int NB>
+template <bool TRA, int NB, int KC = 16>
 __global__ void __launch_bounds__(256) gemm_f32_mfma_wide(const float* __restrict__ A, const float* __restrict__ B,
                                                           float* __restrict__ C, int M, int N, int K, int64_t lda,
                                                           int64_t ldb, int64_t ldc, int64_t sA, int64_t sB,
                                                           int64_t sC) {
-  constexpr int BN = 32 * NB, BQ = BN / 4, NBV = (16 * BQ + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float As[2][16][128 + 4];   // [buffer][k][m]
-  __shared__ __attribute__((aligned(16))) float Bs[2][16][BN + 4];    // [buffer][k][n]
+  constexpr int BN = 32 * NB, BQ = BN / 4, NBV = (KC * BQ + 255) / 256, NAV = KC / 8;
+  __shared__ __attribute__((aligned(16))) float As[2][KC][128 + 4];   // [buffer][k][m]
+  __shared__ __attribute__((aligned(16))) float Bs[2][KC][BN + 4];    // [buffer][k][n]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, kh = lane >> 5;
   const int i0 = blockIdx.y * 128, j0 = blockIdx.x * BN;
   A += (int64_t)blockIdx.z * sA;
   B += (int64_t)blockIdx.z * sB;
   C += (int64_t)blockIdx.z * sC;
-  float4 ra[2], rb[NBV];
+  float4 ra[NAV], rb[NBV];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NAV; ++u) {
       const int idx = tid + 256 * u;
-      if (TRA) {   // A stored [k][m]: 16 rows of 32 float4 along m
+      if (TRA) {   // A stored [k][m]: KC rows of 32 float4 along m
         const int k = idx >> 5, m4 = (idx & 31) * 4;
         ra[u] = (k0 + k < K) ? ld4_guard(A, (int64_t)(k0 + k) * lda + i0 + m4, M - i0 - m4)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {     // A stored [m][k]: 128 rows of 4 float4 along k
-        const int m = idx >> 2, k4 = (idx & 3) * 4;
+      } else {     // A stored [m][k]: 128 rows of KC / 4 float4 along k
+        const int m = idx / (KC / 4), k4 = (idx % (KC / 4)) * 4;
         ra[u] = (i0 + m < M) ? ld4_guard(A, (int64_t)(i0 + m) * lda + k0 + k4, K - k0 - k4)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -470,19 +470,19 @@ __global__ void __launch_bounds__(256) gemm_f32_mfma_wide(const float* __restric
 #pragma unroll
     for (int u = 0; u < NBV; ++u) {
       const int idx = tid + 256 * u, k = idx / BQ, n4 = (idx % BQ) * 4;
-      rb[u] = (idx < 16 * BQ && k0 + k < K) ? ld4_guard(B, (int64_t)(k0 + k) * ldb + j0 + n4, N - j0 - n4)
+      rb[u] = (idx < KC * BQ && k0 + k < K) ? ld4_guard(B, (int64_t)(k0 + k) * ldb + j0 + n4, N - j0 - n4)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NAV; ++u) {
       const int idx = tid + 256 * u;
       if (TRA) {
         const int k = idx >> 5, m4 = (idx & 31) * 4;
         *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[u];
       } else {
-        const int m = idx >> 2, k4 = (idx & 3) * 4;
+        const int m = idx / (KC / 4), k4 = (idx % (KC / 4)) * 4;
         As[buf][k4 + 0][m] = ra[u].x;
         As[buf][k4 + 1][m] = ra[u].y;
         As[buf][k4 + 2][m] = ra[u].z;
@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(256) gemm_f32_mfma_wide(const float* __restric
 #pragma unroll
     for (int u = 0; u < NBV; ++u) {
       const int idx = tid + 256 * u, k = idx / BQ, n4 = (idx % BQ) * 4;
-      if (idx < 16 * BQ) *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = rb[u];
+      if (idx < KC * BQ) *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = rb[u];
     }
   };
   f32x16v acc[NB];
@@ -504,16 +504,30 @@ __global__ void __launch_bounds__(256) gemm_f32_mfma_wide(const float* __restric
   store(0);
   __syncthreads();
   int buf = 0;
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const bool more = k0 + 16 < K;
-    if (more) load(k0 + 16);
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    const bool more = k0 + KC < K;
+    if (more) load(k0 + KC);
+    // operands of step kk + 1 are read from LDS before the products of step kk are issued
+    float a_cur = As[buf][kh][wave * 32 + l32], b_cur[NB];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = 2 * kk + kh;
-      const float a = As[buf][k][wave * 32 + l32];
+    for (int nb = 0; nb < NB; ++nb) b_cur[nb] = Bs[buf][kh][nb * 32 + l32];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bs[buf][k][nb * 32 + l32], acc[nb], 0, 0, 0);
+    for (int kk = 0; kk < KC / 2; ++kk) {
+      float a_nxt = 0.f, b_nxt[NB];
+      if (kk + 1 < KC / 2) {
+        const int k = 2 * kk + 2 + kh;
+        a_nxt = As[buf][k][wave * 32 + l32];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) b_nxt[nb] = Bs[buf][k][nb * 32 + l32];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a_cur, b_cur[nb], acc[nb], 0, 0, 0);
+      // keep the next step's LDS reads ahead of this step's products
+      __builtin_amdgcn_sched_group_barrier(0x100, NB + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+      a_cur = a_nxt;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) b_cur[nb] = b_nxt[nb];
     }
     if (more) store(buf ^ 1);
     __syncthreads();
@@ -553,6 +567,160 @@ hipError_t gemm_f32(const float* A, const float* B, float* C, int M, int N, int 
     return hipGetLastError();
   }
   return run_gemm<float, float, float, float, TRA, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, st);
+}
+
+// The same narrow product on bf16 matrix cores to about 16 significant bits ("bf16x3"): every
+// operand is split x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), and
+// C = Ahi Bhi + Ahi Blo + Alo Bhi with fp32 sums (v_mfma_f32_32x32x16_bf16); the dropped
+// Alo Blo and the split residues stay below about 2^-16 of |a b|.  For products whose result
+// only has to keep its span: the power-iteration bases.  A 128 x 32 NB tile per work-group,
+// each wave 32 rows x NB column blocks; K in chunks of 32 staged through LDS as bf16 [row][k]
+// (the next chunk is loaded into registers while the current one is multiplied).
+constexpr int kB3K = 32, kB3Pitch = kB3K + 8;   // 80-byte LDS rows: conflict-free 16-byte reads
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split8(const float* x, uint4& hi, uint4& lo) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 bh = (__bf16)x[i];
+    const __bf16 bl = (__bf16)(x[i] - (float)bh);
+    h[i] = __builtin_bit_cast(uint16_t, bh);
+    l[i] = __builtin_bit_cast(uint16_t, bl);
+  }
+  hi = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, h[4] | (uint32_t)h[5] << 16,
+                  h[6] | (uint32_t)h[7] << 16);
+  lo = make_uint4(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16, l[4] | (uint32_t)l[5] << 16,
+                  l[6] | (uint32_t)l[7] << 16);
+}
+
+template <bool TRA, int NB>
+__global__ void __launch_bounds__(256) gemm_bf3_wide(const float* __restrict__ A, const float* __restrict__ B,
+                                                     float* __restrict__ C, int M, int N, int K, int64_t lda,
+                                                     int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC) {
+  constexpr int BN = 32 * NB;
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[128][kB3Pitch], Al[128][kB3Pitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[BN][kB3Pitch], Bl[BN][kB3Pitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int i0 = blockIdx.y * 128, j0 = blockIdx.x * BN;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  // staging: a thread takes 8 consecutive k of one LDS row (a row of A or a column of B), so the
+  // 16-byte LDS writes of a wave go to consecutive rows; A stored [m][k] is read as two float4
+  // per item, operands stored [k][row] as eight coalesced scalars
+  constexpr int NBI = (4 * BN + 255) / 256;   // B items per thread
+  float ra[16], rb[8 * NBI];
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto put4 = [](float* d, float4 v) {
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int it = tid + 256 * u;
+      if (TRA) {   // item: row it & 127, k-octet it >> 7
+        const int m = it & 127, k = k0 + 8 * (it >> 7);
+        const bool in = i0 + m < M;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ra[8 * u + j] = (in && k + j < K) ? A[(int64_t)(k + j) * lda + i0 + m] : 0.f;
+      } else {     // item: row it >> 2, k-octet it & 3
+        const int m = it >> 2, k = k0 + 8 * (it & 3);
+        const bool in = i0 + m < M;
+        const int64_t base = (int64_t)(i0 + m) * lda + k;
+        put4(ra + 8 * u, in ? ld4_guard(A, base, K - k) : z4);
+        put4(ra + 8 * u + 4, in ? ld4_guard(A, base + 4, K - k - 4) : z4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) {   // item: column it % BN, k-octet it / BN
+      const int it = tid + 256 * u, n = it % BN, k = k0 + 8 * (it / BN);
+      const bool in = it < 4 * BN && j0 + n < N;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rb[8 * u + j] = (in && k + j < K) ? B[(int64_t)(k + j) * ldb + j0 + n] : 0.f;
+    }
+  };
+  auto store = [&]() {
+    uint4 h, l;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int it = tid + 256 * u;
+      const int m = TRA ? (it & 127) : (it >> 2), g = TRA ? (it >> 7) : (it & 3);
+      split8(ra + 8 * u, h, l);
+      *reinterpret_cast<uint4*>(&Ah[m][8 * g]) = h;
+      *reinterpret_cast<uint4*>(&Al[m][8 * g]) = l;
+    }
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) {
+      const int it = tid + 256 * u;
+      if (it < 4 * BN) {
+        split8(rb + 8 * u, h, l);
+        *reinterpret_cast<uint4*>(&Bh[it % BN][8 * (it / BN)]) = h;
+        *reinterpret_cast<uint4*>(&Bl[it % BN][8 * (it / BN)]) = l;
+      }
+    }
+  };
+  f32x16v acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += kB3K) {
+    __syncthreads();   // every wave is done with the previous chunk
+    store();
+    __syncthreads();
+    if (k0 + kB3K < K) load(k0 + kB3K);
+#pragma unroll
+    for (int s = 0; s < kB3K / 16; ++s) {
+      const int kc = 16 * s + 8 * kh;
+      const bf16x8v ah = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&Ah[wave * 32 + l32][kc]));
+      const bf16x8v al = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&Al[wave * 32 + l32][kc]));
+      bf16x8v bh[NB], bl[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        bh[nb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&Bh[nb * 32 + l32][kc]));
+        bl[nb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&Bl[nb * 32 + l32][kc]));
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh[nb], acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[nb], acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[nb], acc[nb], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = j0 + nb * 32 + l32;
+    if (j >= N) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + wave * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (i < M) C[(int64_t)i * ldc + j] = acc[nb][r];
+    }
+  }
+}
+
+// the same products through gemm_bf3_wide where the operands allow it, else fp32
+template <bool TRA>
+hipError_t gemm_bf3(const float* A, const float* B, float* C, int M, int N, int K, int64_t lda, int64_t ldb,
+                    int64_t ldc, int64_t sA, int64_t sB, int64_t sC, int batch, hipStream_t st) {
+  if (!(lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0 && N <= 160))
+    return gemm_f32<TRA>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, st);
+  const dim3 grid(1u, (unsigned)((M + 127) / 128), (unsigned)batch);
+  switch ((N + 31) / 32) {
+    case 1: gemm_bf3_wide<TRA, 1><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+    case 2: gemm_bf3_wide<TRA, 2><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+    case 3: gemm_bf3_wide<TRA, 3><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+    case 4: gemm_bf3_wide<TRA, 4><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+    default: gemm_bf3_wide<TRA, 5><<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC); break;
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ Gram matrices
@@ -1451,8 +1619,14 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   if ((e = hipGetLastError())) return e;
   // Y = Z Omega, orthonormalised; the bases between power iterations take one CholeskyQR round
   // (their Gram is formed in fp64, so one round leaves them orthonormal to the fp32 storage
-  // precision, and the next product only needs their span), the final basis Q two
-  if ((e = gemm_f32<false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+  // precision, and the next product only needs their span), the final basis Q two.  Every
+  // product but the one that forms the final basis runs in split bf16 (about 16 significant
+  // bits: it only steers the span); the final Y = Z W and Bsk^T = Z^T Q run in fp32, so error
+  // components of W outside the row space of Z are annihilated and the span of Q and the
+  // projection keep fp32 accuracy.
+  if ((e = power_iters > 0 ? gemm_bf3<false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st)
+                           : gemm_f32<false>(z, om, y0, m, l, n, n, l, l, sZ, sW, sY, b, st)))
+    return e;
   auto orth_swap = [&](float*& X, float*& Xt, int rows_, int passes) -> hipError_t {
     hipError_t r = orth(X, Xt, G, Li, part, b, rows_, l, passes, st);
     if (passes & 1) std::swap(X, Xt);
@@ -1462,9 +1636,12 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   if ((e = orth_swap(Y, Yt, m, power_iters > 0 ? 1 : 2))) return e;
   for (int it = 0; it < power_iters; ++it) {
     // W = Z^T Y, orthonormalised; Y = Z W, orthonormalised
-    if ((e = gemm_f32<true>(z, Y, Wb, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
+    const bool last = it + 1 == power_iters;
+    if ((e = gemm_bf3<true>(z, Y, Wb, n, l, m, n, l, l, sZ, sY, sW, b, st))) return e;
     if ((e = orth_swap(Wb, Wt, n, 1))) return e;
-    if ((e = gemm_f32<false>(z, Wb, Y, m, l, n, n, l, l, sZ, sW, sY, b, st))) return e;
+    if ((e = last ? gemm_f32<false>(z, Wb, Y, m, l, n, n, l, l, sZ, sW, sY, b, st)
+                  : gemm_bf3<false>(z, Wb, Y, m, l, n, n, l, l, sZ, sW, sY, b, st)))
+      return e;
     if ((e = orth_swap(Y, Yt, m, it + 1 < power_iters ? 1 : 2))) return e;
   }
   y0 = Y;
