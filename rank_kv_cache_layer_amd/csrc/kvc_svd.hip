@@ -1091,23 +1091,23 @@ __global__ void __launch_bounds__(1024) jacobi(double* A, double* V, int l, int 
 }
 
 // Same eigenproblem with the matrix resident in LDS as its packed lower triangle (index
-// i (i + 1) / 2 + j, j <= i; fp64), for l up to kJacobiLdsMax, split in two kernels so that the
-// eigenvector accumulation does not serialise on the one work-group that owns a matrix:
-//  - jacobi_chunk (one 1024-thread work-group per matrix) runs up to kJacobiChunkSweeps sweeps
+// i (i + 1) / 2 + j, j <= i; fp64), for l up to kJacobiLdsMax.  The eigenvector accumulation is
+// taken off the one work-group that owns a matrix, and overlapped with it:
+//  - sweep blocks (one 1024-thread work-group per matrix) run up to kJacobiChunkSweeps sweeps
 //    on the triangle.  A round rotates the l/2 disjoint pairs at once: each 2 x 2 block between
 //    two pairs P, Q (stored once, P <= Q) becomes J_P^T B J_Q, a diagonal block
-//    diag(a'_pp, a'_qq) with a'_pq = 0.  Every round's (c, s) are written to a rotation log;
-//    the triangle is kept in global memory between chunks.
-//  - jacobi_apply replays the chunk's log on VT (row k = eigenvector k): V <- V J acts on rows p
-//    and q of VT independently in every column, so a work-group takes kApplyCols columns of one
-//    matrix into LDS and applies all logged rounds to them.
-// The host launches the pair ceil(max_sweeps / kJacobiChunkSweeps) times; chunks after
-// convergence return at once.  Per-matrix state: [0] converged (or out of sweeps), [1] rounds
-// logged by the last chunk, [2] sweeps done.  An odd l is padded with a zero row that is never
-// rotated.
+//    diag(a'_pp, a'_qq) with a'_pq = 0.  Every round's (c, s) go to a rotation log; the
+//    triangle is kept in global memory between launches.
+//  - replay blocks replay the previous launch's log on VT (row k = eigenvector k): V <- V J acts
+//    on rows p and q of VT independently in every column, so a work-group takes kApplyCols
+//    columns of one matrix into LDS and applies all logged rounds to them.
+// Launch c runs sweep chunk c and replays chunk c - 1 (two logs alternate); the host launches
+// ceil(max_sweeps / kJacobiChunkSweeps) + 1 of them and chunks after convergence return at once.
+// Per-matrix state: [0] converged (or out of sweeps), [1 + buffer] rounds logged in that
+// buffer, [3] sweeps done.  An odd l is padded with a zero row that is never rotated.
 constexpr int kJacobiLdsMax = 192;
 constexpr int kJacobiChunkSweeps = 4;
-constexpr int kApplyCols = 16, kApplyPitch = kApplyCols + 1, kApplyGroups = 256 / kApplyCols;
+constexpr int kApplyCols = 64, kApplyPitch = kApplyCols + 1, kApplyGroups = 1024 / kApplyCols;
 __device__ __forceinline__ int tri(int i, int j) { return i >= j ? i * (i + 1) / 2 + j : j * (j + 1) / 2 + i; }
 
 // Round-robin pairing (lp even): position 0 stays, positions 1 .. lp-1 advance by one each
@@ -1135,24 +1135,24 @@ __device__ __forceinline__ int tri_row(int e) {   // i with i (i + 1) / 2 <= e <
   return i;
 }
 
-__global__ void __launch_bounds__(1024) jacobi_chunk(double* A, double* Tg, double2* rot, int* state, int l,
-                                                     int first, int max_sweeps, double tol) {
-  extern __shared__ double T[];   // packed lower triangle, lp (lp + 1) / 2 entries
-  __shared__ double cs[kJacobiLdsMax / 2], sn[kJacobiLdsMax / 2];
-  __shared__ int pp[kJacobiLdsMax / 2], qq[kJacobiLdsMax / 2];
+__host__ __device__ size_t jacobi_log_pairs(int l) {   // (c, s) entries per matrix and log buffer
+  const size_t lp = (l + 1) & ~1;
+  return (size_t)kJacobiChunkSweeps * (lp - 1) * (lp / 2);
+}
+
+__device__ void jacobi_sweeps(double* T, double* A, double* Tg, double2* rot, int* stt, int l, int first, int buf,
+                              int max_sweeps, double tol) {
+  __shared__ double2 csn[kJacobiLdsMax / 2];   // (c, s) of pair k this round
+  __shared__ int2 pq[kJacobiLdsMax / 2];       // (p, q) of pair k this round
   __shared__ double red[2][32];
   __shared__ int done;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 31, warp = tid >> 5;
   const int lp = (l + 1) & ~1, half = lp / 2, ntri = lp * (lp + 1) / 2;
-  int* stt = state + 4 * blockIdx.x;
   if (!first && stt[0]) {
-    if (tid == 0) stt[1] = 0;
+    if (tid == 0) stt[1 + buf] = 0;
     return;
   }
-  const int swept = first ? 0 : stt[2];
-  A += (int64_t)blockIdx.x * l * l;
-  Tg += (int64_t)blockIdx.x * ntri;
-  rot += (int64_t)blockIdx.x * kJacobiChunkSweeps * (lp - 1) * half;
+  const int swept = first ? 0 : stt[3];
   for (int e = tid; e < ntri; e += nt) {
     if (first) {
       const int i = tri_row(e), j = e - i * (i + 1) / 2;
@@ -1221,10 +1221,8 @@ __global__ void __launch_bounds__(1024) jacobi_chunk(double* A, double* Tg, doub
             s = t * c;
           }
         }
-        pp[tid] = p;
-        qq[tid] = q;
-        cs[tid] = c;
-        sn[tid] = s;
+        pq[tid] = make_int2(p, q);
+        csn[tid] = make_double2(c, s);
         rot[(int64_t)logged * half + tid] = make_double2(c, s);
       }
       __syncthreads();
@@ -1237,18 +1235,18 @@ __global__ void __launch_bounds__(1024) jacobi_chunk(double* A, double* Tg, doub
         for (int c = c0; c < c1; ++c) {   // block (K1, K2), K2 <= K1
           const int k1 = bk1[c], k2 = bk2[c];
           if (k1 < 0) continue;
-          const int p1 = pp[k1], q1 = qq[k1], p2 = pp[k2], q2 = qq[k2];
+          const int2 r1 = pq[k1], r2 = pq[k2];
           int* x = ix[c - c0];
           if (k1 == k2) {
-            x[0] = tri(p1, p1);
-            x[1] = tri(q1, q1);
-            x[2] = tri(q1, p1);
+            x[0] = tri(r1.x, r1.x);
+            x[1] = tri(r1.y, r1.y);
+            x[2] = tri(r1.y, r1.x);
             x[3] = x[2];
           } else {
-            x[0] = tri(p1, p2);
-            x[1] = tri(p1, q2);
-            x[2] = tri(q1, p2);
-            x[3] = tri(q1, q2);
+            x[0] = tri(r1.x, r2.x);
+            x[1] = tri(r1.x, r2.y);
+            x[2] = tri(r1.y, r2.x);
+            x[3] = tri(r1.y, r2.y);
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) b[c - c0][u] = T[x[u]];
@@ -1259,7 +1257,8 @@ __global__ void __launch_bounds__(1024) jacobi_chunk(double* A, double* Tg, doub
           if (k1 < 0) continue;
           const int* x = ix[c - c0];
           const double* v = b[c - c0];
-          const double c1v = cs[k1], s1 = sn[k1], c2 = cs[k2], s2 = sn[k2];
+          const double2 j1 = csn[k1], j2 = csn[k2];
+          const double c1v = j1.x, s1 = j1.y, c2 = j2.x, s2 = j2.y;
           if (k1 == k2) {
             const double app = v[0], aqq = v[1], apq = v[2];
             T[x[0]] = c1v * c1v * app - 2.0 * c1v * s1 * apq + s1 * s1 * aqq;
@@ -1285,25 +1284,20 @@ __global__ void __launch_bounds__(1024) jacobi_chunk(double* A, double* Tg, doub
   for (int i = tid; i < l; i += nt) A[(int64_t)i * l + i] = T[tri(i, i)];
   if (tid == 0) {
     stt[0] = conv || swept + sweeps >= max_sweeps;
-    stt[1] = logged;
-    stt[2] = swept + sweeps;
+    stt[1 + buf] = logged;
+    stt[3] = swept + sweeps;
   }
 }
 
-// Replays the rotation log of the last chunk on kApplyCols columns of VT (identity before the
-// first chunk): thread (column, group g) applies the rotations of pairs g, g + kApplyGroups, ...
-// of every round, the round's rows read first (its pairs are disjoint), then written; the next
+// Replays `rounds` logged rounds on kApplyCols columns of VT (identity before the first
+// chunk): thread (column, group g) applies the rotations of pairs g, g + kApplyGroups, ... of
+// every round, the round's rows read first (its pairs are disjoint), then written; the next
 // round's (c, s) are loaded while this one is applied.
-__global__ void __launch_bounds__(256) jacobi_apply(double* VT, const double2* __restrict__ rot,
-                                                    const int* __restrict__ state, int l, int first) {
-  extern __shared__ double Vs[];   // [l][kApplyPitch]
-  const int rounds = state[4 * blockIdx.y + 1];
-  if (!first && rounds == 0) return;
+__device__ void jacobi_replay(double* Vs, double* VT, const double2* __restrict__ rot, int rounds, int l, int c0,
+                              int first) {
   const int tid = threadIdx.x, col = tid % kApplyCols, g = tid / kApplyCols;
   const int lp = (l + 1) & ~1, half = lp / 2, ncyc = lp - 1;
-  const int gc = blockIdx.x * kApplyCols + col;
-  VT += (int64_t)blockIdx.y * l * l;
-  rot += (int64_t)blockIdx.y * kJacobiChunkSweeps * ncyc * half;
+  const int gc = c0 + col;
   for (int i = g; i < l; i += kApplyGroups)
     Vs[i * kApplyPitch + col] = first ? (i == gc ? 1.0 : 0.0) : (gc < l ? VT[(int64_t)i * l + gc] : 0.0);
   constexpr int kMaxPairs = (kJacobiLdsMax / 2 + kApplyGroups - 1) / kApplyGroups;
@@ -1349,6 +1343,28 @@ __global__ void __launch_bounds__(256) jacobi_apply(double* VT, const double2* _
   }
   if (gc < l)
     for (int i = g; i < l; i += kApplyGroups) VT[(int64_t)i * l + gc] = Vs[i * kApplyPitch + col];
+}
+
+// Launch c: work-groups [0, b) run sweep chunk c (c < n_chunks), the next b * ceil(l /
+// kApplyCols) replay chunk c - 1 (c >= 1) on their column slices.
+__global__ void __launch_bounds__(1024) jacobi_step(double* A, double* Tg, double* VT, double2* rot, int* state,
+                                                    int l, int b, int c, int n_chunks, int max_sweeps, double tol) {
+  extern __shared__ double lds[];
+  const size_t per = jacobi_log_pairs(l);
+  const int nsl = (l + kApplyCols - 1) / kApplyCols;
+  if ((int)blockIdx.x < b) {
+    if (c >= n_chunks) return;
+    const int m = blockIdx.x, lp = (l + 1) & ~1;
+    jacobi_sweeps(lds, A + (int64_t)m * l * l, Tg + (int64_t)m * (lp * (lp + 1) / 2),
+                  rot + ((size_t)(c & 1) * b + m) * per, state + 4 * m, l, c == 0, c & 1, max_sweeps, tol);
+  } else {
+    if (c == 0) return;
+    const int w = blockIdx.x - b, m = w / nsl, sl = w % nsl, pb = (c - 1) & 1;
+    const int rounds = state[4 * m + 1 + pb];
+    if (c - 1 > 0 && rounds == 0) return;
+    jacobi_replay(lds, VT + (int64_t)m * l * l, rot + ((size_t)pb * b + m) * per, rounds, l, sl * kApplyCols,
+                  c - 1 == 0);
+  }
 }
 
 // ------------------------------------------------------------------ top-r selection
@@ -1532,7 +1548,7 @@ SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
   w.m2 = o;  o += al(b * r * l * 8);
   const size_t lp = (l + 1) & ~(size_t)1;
   w.jt = o;  o += al(b * lp * (lp + 1) / 2 * 8);                       // Jacobi triangles
-  w.jr = o;  o += al(b * kJacobiChunkSweeps * (lp - 1) * (lp / 2) * 16);  // rotation log
+  w.jr = o;  o += al(2 * b * jacobi_log_pairs((int)l) * 16);            // two rotation logs
   w.js = o;  o += al(b * 4 * 4);                                        // Jacobi state
   w.sp = o;  o += al(b * kSignSplits * r * sizeof(SignPart));           // sign scan partials
   w.sf = o;  o += al(b * r * 4);                                        // sign flags
@@ -1654,20 +1670,17 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   // the LDS eigensolver reads only the lower triangle of the Gram; the global one all of it
   if ((e = gram_f64(bskt, g2, part, n, l, b, in_lds, st))) return e;
   if (in_lds) {
-    if (tri_bytes > 64 * 1024 &&
-        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_chunk),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)tri_bytes)))
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_step), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)std::max(tri_bytes, sizeof(double) * (size_t)l * kApplyPitch))))
       return e;
     double* jt = reinterpret_cast<double*>(base + L.jt);
     double2* jr = reinterpret_cast<double2*>(base + L.jr);
     int* js = reinterpret_cast<int*>(base + L.js);
-    const int max_sweeps = 40;
-    const dim3 agrid((unsigned)((l + kApplyCols - 1) / kApplyCols), (unsigned)b);
-    const size_t a_bytes = sizeof(double) * (size_t)l * kApplyPitch;
-    for (int c = 0; c * kJacobiChunkSweeps < max_sweeps; ++c) {
-      jacobi_chunk<<<b, 1024, tri_bytes, st>>>(g2, jt, jr, js, l, c == 0, max_sweeps, 1e-13);
-      if ((e = hipGetLastError())) return e;
-      jacobi_apply<<<agrid, 256, a_bytes, st>>>(V, jr, js, l, c == 0);
+    const int max_sweeps = 40, n_chunks = (max_sweeps + kJacobiChunkSweeps - 1) / kJacobiChunkSweeps;
+    const int nsl = (l + kApplyCols - 1) / kApplyCols;
+    const size_t lds = std::max(tri_bytes, sizeof(double) * (size_t)l * kApplyPitch);
+    for (int c = 0; c <= n_chunks; ++c) {
+      jacobi_step<<<b * (1 + nsl), 1024, lds, st>>>(g2, jt, V, jr, js, l, b, c, n_chunks, max_sweeps, 1e-13);
       if ((e = hipGetLastError())) return e;
     }
   } else {
