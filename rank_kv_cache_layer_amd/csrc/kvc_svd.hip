@@ -1094,9 +1094,9 @@ __global__ void __launch_bounds__(1024) jacobi(double* A, double* V, int l, int 
 // i (i + 1) / 2 + j, j <= i; fp64), for l up to kJacobiLdsMax.  The eigenvector accumulation is
 // taken off the one work-group that owns a matrix, and overlapped with it:
 //  - sweep blocks (one 1024-thread work-group per matrix) run up to kJacobiChunkSweeps sweeps
-//    on the triangle.  A round rotates the l/2 disjoint pairs at once: each 2 x 2 block between
-//    two pairs P, Q (stored once, P <= Q) becomes J_P^T B J_Q, a diagonal block
-//    diag(a'_pp, a'_qq) with a'_pq = 0.  Every round's (c, s) go to a rotation log; the
+//    on the triangle.  A round rotates the l/2 disjoint pairs at once: the thread that computes
+//    pair P's rotation turns its diagonal block into diag(a'_pp, a'_qq) (a'_pq = 0), then each
+//    2 x 2 block between two pairs P, Q (stored once, P > Q) becomes J_P^T B J_Q.  Every round's (c, s) go to a rotation log; the
 //    triangle is kept in global memory between launches.
 //  - replay blocks replay the previous launch's log on VT (row k = eigenvector k): V <- V J acts
 //    on rows p and q of VT independently in every column, so a work-group takes kApplyCols
@@ -1143,7 +1143,7 @@ __host__ __device__ size_t jacobi_log_pairs(int l) {   // (c, s) entries per mat
 __device__ void jacobi_sweeps(double* T, double* A, double* Tg, double2* rot, int* stt, int l, int first, int buf,
                               int max_sweeps, double tol) {
   __shared__ double2 csn[kJacobiLdsMax / 2];   // (c, s) of pair k this round
-  __shared__ int2 pq[kJacobiLdsMax / 2];       // (p, q) of pair k this round
+  __shared__ int4 pq[kJacobiLdsMax / 2];       // (p, q, p (p + 1) / 2, q (q + 1) / 2) of pair k this round
   __shared__ double red[2][32];
   __shared__ int done;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 31, warp = tid >> 5;
@@ -1161,18 +1161,19 @@ __device__ void jacobi_sweeps(double* T, double* A, double* Tg, double2* rot, in
       T[e] = Tg[e];
     }
   }
-  const int nblk = half * (half + 1) / 2;
-  // this thread's rotation-pair blocks (K1, K2), K2 <= K1, decoded once: with 1024 threads and
-  // half <= kJacobiLdsMax / 2, at most 5 per thread
+  const int nblk = half * (half - 1) / 2;
+  // this thread's off-diagonal rotation-pair blocks (K1, K2), K2 < K1 (index e = K1 (K1 - 1) / 2
+  // + K2), decoded once: with 1024 threads and half <= kJacobiLdsMax / 2, at most 5 per thread.
+  // The diagonal block of each pair is rotated by the thread that computes the pair's rotation.
   constexpr int kMaxBlk = 5;
-  static_assert((kJacobiLdsMax / 2) * (kJacobiLdsMax / 2 + 1) / 2 <= kMaxBlk * 1024, "blocks per thread");
+  static_assert((kJacobiLdsMax / 2) * (kJacobiLdsMax / 2 - 1) / 2 <= kMaxBlk * 1024, "blocks per thread");
   int bk1[kMaxBlk], bk2[kMaxBlk];
 #pragma unroll
   for (int c = 0; c < kMaxBlk; ++c) {
     const int e = tid + c * nt;
-    const int k1 = tri_row(e);
+    const int k1 = tri_row(e) + 1;   // K1 (K1 - 1) / 2 <= e < K1 (K1 + 1) / 2
     bk1[c] = e < nblk ? k1 : -1;
-    bk2[c] = e - k1 * (k1 + 1) / 2;
+    bk2[c] = e - k1 * (k1 - 1) / 2;
   }
   __syncthreads();
   int sweeps = 0, logged = 0;
@@ -1211,17 +1212,22 @@ __device__ void jacobi_sweeps(double* T, double* A, double* Tg, double2* rot, in
       if (tid < half) {
         int p, q;
         jacobi_pair(tid, round, lp, p, q);
+        const int rp = p * (p + 1) / 2, rq = q * (q + 1) / 2;
         double c = 1.0, s = 0.0;
         if (q < l) {
-          const double apq = T[tri(q, p)];
+          const double app = T[rp + p], aqq = T[rq + q], apq = T[rq + p];
           if (apq != 0.0) {
-            const double tau = (T[tri(q, q)] - T[tri(p, p)]) / (2.0 * apq);
+            const double tau = (aqq - app) / (2.0 * apq);
             const double t = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau)) : -1.0 / (-tau + sqrt(1.0 + tau * tau));
             c = 1.0 / sqrt(1.0 + t * t);
             s = t * c;
+            // the pair's own 2 x 2 diagonal block: J^T B J = diag(a'_pp, a'_qq)
+            T[rp + p] = c * c * app - 2.0 * c * s * apq + s * s * aqq;
+            T[rq + q] = s * s * app + 2.0 * c * s * apq + c * c * aqq;
+            T[rq + p] = 0.0;
           }
         }
-        pq[tid] = make_int2(p, q);
+        pq[tid] = make_int4(p, q, rp, rq);
         csn[tid] = make_double2(c, s);
         rot[(int64_t)logged * half + tid] = make_double2(c, s);
       }
@@ -1232,22 +1238,17 @@ __device__ void jacobi_sweeps(double* T, double* A, double* Tg, double2* rot, in
         double b[c1 - c0][4];
         int ix[c1 - c0][4];
 #pragma unroll
-        for (int c = c0; c < c1; ++c) {   // block (K1, K2), K2 <= K1
+        for (int c = c0; c < c1; ++c) {   // block (K1, K2), K2 < K1
           const int k1 = bk1[c], k2 = bk2[c];
           if (k1 < 0) continue;
-          const int2 r1 = pq[k1], r2 = pq[k2];
+          const int4 r1 = pq[k1], r2 = pq[k2];
+          // packed index of (i, j) from the row offsets: the larger index owns the row
+          auto at = [](int i, int ri, int j, int rj) { return i >= j ? ri + j : rj + i; };
           int* x = ix[c - c0];
-          if (k1 == k2) {
-            x[0] = tri(r1.x, r1.x);
-            x[1] = tri(r1.y, r1.y);
-            x[2] = tri(r1.y, r1.x);
-            x[3] = x[2];
-          } else {
-            x[0] = tri(r1.x, r2.x);
-            x[1] = tri(r1.x, r2.y);
-            x[2] = tri(r1.y, r2.x);
-            x[3] = tri(r1.y, r2.y);
-          }
+          x[0] = at(r1.x, r1.z, r2.x, r2.z);
+          x[1] = at(r1.x, r1.z, r2.y, r2.w);
+          x[2] = at(r1.y, r1.w, r2.x, r2.z);
+          x[3] = at(r1.y, r1.w, r2.y, r2.w);
 #pragma unroll
           for (int u = 0; u < 4; ++u) b[c - c0][u] = T[x[u]];
         }
@@ -1259,20 +1260,13 @@ __device__ void jacobi_sweeps(double* T, double* A, double* Tg, double2* rot, in
           const double* v = b[c - c0];
           const double2 j1 = csn[k1], j2 = csn[k2];
           const double c1v = j1.x, s1 = j1.y, c2 = j2.x, s2 = j2.y;
-          if (k1 == k2) {
-            const double app = v[0], aqq = v[1], apq = v[2];
-            T[x[0]] = c1v * c1v * app - 2.0 * c1v * s1 * apq + s1 * s1 * aqq;
-            T[x[1]] = s1 * s1 * app + 2.0 * c1v * s1 * apq + c1v * c1v * aqq;
-            T[x[2]] = 0.0;
-          } else {
-            // B rows {p1, q1}, columns {p2, q2}; B' = J1^T B J2
-            const double r00 = c1v * v[0] - s1 * v[2], r01 = c1v * v[1] - s1 * v[3];
-            const double r10 = s1 * v[0] + c1v * v[2], r11 = s1 * v[1] + c1v * v[3];
-            T[x[0]] = c2 * r00 - s2 * r01;
-            T[x[1]] = s2 * r00 + c2 * r01;
-            T[x[2]] = c2 * r10 - s2 * r11;
-            T[x[3]] = s2 * r10 + c2 * r11;
-          }
+          // B rows {p1, q1}, columns {p2, q2}; B' = J1^T B J2
+          const double r00 = c1v * v[0] - s1 * v[2], r01 = c1v * v[1] - s1 * v[3];
+          const double r10 = s1 * v[0] + c1v * v[2], r11 = s1 * v[1] + c1v * v[3];
+          T[x[0]] = c2 * r00 - s2 * r01;
+          T[x[1]] = s2 * r00 + c2 * r01;
+          T[x[2]] = c2 * r10 - s2 * r11;
+          T[x[3]] = s2 * r10 + c2 * r11;
         }
       };
       blocks(std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
@@ -1573,8 +1567,11 @@ hipError_t orth(float* Y, float* tmp, double* G, double* Li, double* part, int b
       float* lit = reinterpret_cast<float*>(Li);
       chol_inv_reg<<<b, 512, 0, st>>>(G, lit, l, tolr);
       if ((e = hipGetLastError())) return e;
-      if ((e = gemm_f32<false>(src, lit, dst, rows, l, l, l, l, l, (int64_t)rows * l, (int64_t)l * l,
-                               (int64_t)rows * l, b, st)))
+      // a one-round basis between power iterations only has to keep its span: split bf16
+      if ((e = passes == 1 ? gemm_bf3<false>(src, lit, dst, rows, l, l, l, l, l, (int64_t)rows * l, (int64_t)l * l,
+                                             (int64_t)rows * l, b, st)
+                           : gemm_f32<false>(src, lit, dst, rows, l, l, l, l, l, (int64_t)rows * l, (int64_t)l * l,
+                                             (int64_t)rows * l, b, st)))
         return e;
     } else {
       const size_t tri_bytes = sizeof(double) * (size_t)l * (l + 1) / 2;
