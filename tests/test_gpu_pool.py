@@ -94,7 +94,9 @@ def test_insert_reconstructs_writes_only_its_slot_and_round_trips():
         A = getattr(arena, Aname).double().cpu().numpy()
         B = getattr(arena, Bname).double().cpu().numpy()
         rec = np.einsum("lsr,lrd->lsd", A[:, rows], B[:, slot])
-        assert np.max(np.abs(rec - want)) <= 1e-4 * np.max(np.abs(want)), Aname
+        rel = np.max(np.abs(rec - want)) / np.max(np.abs(want))
+        print(f"[pool] {Aname} reconstruction {rel:.2e} of max|x|", flush=True)
+        assert rel <= 1e-5, Aname
         # nothing outside the slot's rows / entry was written
         assert np.all(np.delete(A, np.r_[rows], axis=1) == 7.0), Aname
         assert np.all(np.delete(B, slot, axis=1) == 7.0), Bname
@@ -107,8 +109,9 @@ def test_insert_reconstructs_writes_only_its_slot_and_round_trips():
     res = kvc.correct_hop(x["k_src"], x["v_src"], ko, vo, shp, p_src, p_tgt, arena, prm)
     torch.cuda.synchronize()
     for got, want in ((ko, x["kt"]), (vo, x["vt"])):
-        err = np.max(np.abs(got.double().cpu().numpy() - want))
-        assert err <= 1e-4 * np.max(np.abs(want)), err
+        rel = np.max(np.abs(got.double().cpu().numpy() - want)) / np.max(np.abs(want))
+        print(f"[pool] round trip {rel:.2e} of max|x|", flush=True)
+        assert rel <= 1e-5, rel
     assert int(res.flags[0].item()) & O.FLAG_FEW_ANCHORS   # one compatible anchor: dense fallback flagged
 
 

@@ -118,5 +118,6 @@ def test_eq12_round_trip_through_the_library():
     kvc.apply_lowrank_delta(k_src, v_src, ko, vo, kvc.shape_of(L, S, H, hd), p_src, p_tgt, pool, w, w, S)
     torch.cuda.synchronize()
     for got, want in ((ko, cj_k), (vo, cj_v)):
-        err = np.max(np.abs(got.double().cpu().numpy() - want))
-        assert err <= 1e-4 * np.max(np.abs(want)), err
+        rel = np.max(np.abs(got.double().cpu().numpy() - want)) / np.max(np.abs(want))
+        print(f"[svd] Eq. 12 round trip {rel:.2e} of max|x|", flush=True)
+        assert rel <= 1e-5, rel
