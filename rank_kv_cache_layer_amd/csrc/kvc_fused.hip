@@ -719,6 +719,7 @@ hipError_t launch_pack_b_batch(const PackArgs* d, const PackArgs* h, int n, hipS
   for (int i = 0; i < n; ++i) {
     if (h[i].D != h[0].D) return hipErrorInvalidValue;
     bt.start[i] = (int32_t)total;
+    bt.hop[i] = i;
     total += pack_blocks(h[i]);
   }
   bt.start[n] = (int32_t)total;

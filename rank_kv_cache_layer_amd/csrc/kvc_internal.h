@@ -268,6 +268,7 @@ constexpr int kMaxBatch = 64;
 struct BatchTab {
   int32_t n;
   int32_t start[kMaxBatch + 1];
+  int32_t hop[kMaxBatch];   // descriptor index of the grid's i-th hop
 };
 
 hipError_t launch_split_score(const SplitArgs& a, int head_dim, hipStream_t st);

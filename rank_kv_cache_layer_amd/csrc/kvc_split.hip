@@ -570,20 +570,18 @@ __device__ __forceinline__ int64_t batch_tile(P& p, const BatchTab& bt, int h, i
   return lb < real ? lb : -1;
 }
 
-// Several independent hops (ragged pools, base ranks 16 or 32) in one grid; descriptors in
-// device memory.
-template <int HD>
+// Several independent hops of one base rank (16 or 32; ragged pools) in one grid; descriptors in
+// device memory.  Hops of the other rank go to a grid of their own, so each instance keeps the
+// single-hop kernel's register allocation.
+template <int HD, int RK>
 __global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const SplitArgs* __restrict__ d, BatchTab bt) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   __shared__ ScoreShared sh;
   const int h = batch_hop(bt, blockIdx.x);
-  CSplitArgs& p = desc_of(d, h);
+  CSplitArgs& p = desc_of(d, bt.hop[h]);
   const int64_t lb = batch_tile(p, bt, h, blockIdx.x);
   if (lb < 0) return;
-  if (p.r_b == 16)
-    score_tile<HD, 1>(p, lb, ring, sh);
-  else
-    score_tile<HD, 2>(p, lb, ring, sh);
+  score_tile<HD, RK>(p, lb, ring, sh);
 }
 
 // ------------------------------------------------- first-mode scores at base ranks 64 and 128
@@ -998,23 +996,18 @@ __global__ void __launch_bounds__(kApplyThreads, 3) split_apply(SplitArgs p) {
   apply_tile<HD, RKD, RA, NS>(p, xcd_remap(blockIdx.x, gridDim.x), ring, tab);
 }
 
-// Several independent hops in one grid (delta ranks 8 to 256, one code path per rank).
-template <int HD>
+// Several independent hops of one delta rank in one grid (descriptors in device memory); hops
+// of other ranks go to grids of their own, so every instance keeps the single-hop kernel's
+// register allocation.
+template <int HD, int RKD, int RA, int NS>
 __global__ void __launch_bounds__(kApplyThreads, 3) split_apply_batch(const SplitArgs* __restrict__ d, BatchTab bt) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   __shared__ float tab[2][kFusedHalf];
   const int h = batch_hop(bt, blockIdx.x);
-  CSplitArgs& p = desc_of(d, h);
+  CSplitArgs& p = desc_of(d, bt.hop[h]);
   const int64_t b = batch_tile(p, bt, h, blockIdx.x);
   if (b < 0) return;
-  switch (p.r_d) {
-    case 8: apply_tile<HD, 1, 8>(p, b, ring, tab); break;
-    case 16: apply_tile<HD, 1, 16>(p, b, ring, tab); break;
-    case 32: apply_tile<HD, 2, 32>(p, b, ring, tab); break;
-    case 64: apply_tile<HD, 2, 32, 2>(p, b, ring, tab); break;
-    case 128: apply_tile<HD, 2, 32, 4>(p, b, ring, tab); break;
-    default: apply_tile<HD, 2, 32, 8>(p, b, ring, tab); break;
-  }
+  apply_tile<HD, RKD, RA, NS>(p, b, ring, tab);
 }
 
 template <typename K>
@@ -1094,20 +1087,27 @@ hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st) 
 
 namespace {
 // block ranges of the hops of a batched two-pass launch (128-token x 256-channel tiles, both sides)
-bool batch_tab(BatchTab& bt, const SplitArgs* h, int n, int64_t& total) {
-  if (n < 1 || n > kMaxBatch) return false;
-  bt.n = n;
+// grid of the hops idx[0..m) of h (128-token x 256-channel tiles, both sides)
+bool batch_tab(BatchTab& bt, const SplitArgs* h, const int* idx, int m, int64_t& total) {
+  if (m < 1 || m > kMaxBatch) return false;
+  bt.n = m;
   total = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < m; ++i) {
+    const SplitArgs& a = h[idx[i]];
     bt.start[i] = (int32_t)total;
-    const int64_t ntt = (h[i].S + kScoreTile - 1) / kScoreTile;
-    const int64_t blocks = (int64_t)h[i].nct * ntt * h[i].n_grp * 2;
+    bt.hop[i] = idx[i];
+    const int64_t ntt = (a.S + kScoreTile - 1) / kScoreTile;
+    const int64_t blocks = (int64_t)a.nct * ntt * a.n_grp * 2;
     total += (blocks + 7) / 8 * 8;   // each hop starts on XCD 0 (blocks are dealt round-robin over 8)
-    if (h[i].D % kSW || h[i].N > kMaxAnchors) return false;
+    if (a.D % kSW || a.N > kMaxAnchors) return false;
   }
-  bt.start[n] = (int32_t)total;
+  bt.start[m] = (int32_t)total;
   return total < (1ll << 31);
 }
+
+template <int HD>
+hipError_t apply_batch_dispatch(int r, const SplitArgs* d, const BatchTab& bt, int64_t total, size_t lds,
+                                hipStream_t st);
 
 template <typename K>
 hipError_t go_batch(K kernel, const SplitArgs* d, const BatchTab& bt, int64_t total, size_t shmem, hipStream_t st) {
@@ -1121,36 +1121,80 @@ hipError_t go_batch(K kernel, const SplitArgs* d, const BatchTab& bt, int64_t to
 }
 }  // namespace
 
+// one grid per distinct base rank among the hops, in order of first appearance
 hipError_t launch_split_score_batch(const SplitArgs* d, const SplitArgs* h, int n, int head_dim, hipStream_t st) {
   static_assert(kScoreThreads == kApplyThreads && kScoreTile == kApplyTile, "one tile grid for both passes");
-  BatchTab bt;
-  int64_t total;
-  if (!batch_tab(bt, h, n, total)) return hipErrorInvalidValue;
-  size_t lds = 0;
-  for (int i = 0; i < n; ++i) {
+  if (n < 1 || n > kMaxBatch || (head_dim != 128 && head_dim != 64)) return hipErrorInvalidValue;
+  for (int i = 0; i < n; ++i)
     if (h[i].r_b != 16 && h[i].r_b != 32) return hipErrorInvalidValue;
-    lds = std::max(lds, split_score_lds(h[i].r_b));
+  bool done[kMaxBatch] = {};
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    int idx[kMaxBatch], m = 0;
+    for (int j = i; j < n; ++j)
+      if (!done[j] && h[j].r_b == h[i].r_b) {
+        idx[m++] = j;
+        done[j] = true;
+      }
+    BatchTab bt;
+    int64_t total;
+    if (!batch_tab(bt, h, idx, m, total)) return hipErrorInvalidValue;
+    if (total == 0) continue;
+    const size_t lds = split_score_lds(h[i].r_b);
+    hipError_t e;
+    if (head_dim == 128)
+      e = h[i].r_b == 16 ? go_batch(split_score_batch<128, 1>, d, bt, total, lds, st)
+                         : go_batch(split_score_batch<128, 2>, d, bt, total, lds, st);
+    else
+      e = h[i].r_b == 16 ? go_batch(split_score_batch<64, 1>, d, bt, total, lds, st)
+                         : go_batch(split_score_batch<64, 2>, d, bt, total, lds, st);
+    if (e != hipSuccess) return e;
   }
-  if (total == 0) return hipSuccess;
-  if (head_dim == 128) return go_batch(split_score_batch<128>, d, bt, total, lds, st);
-  if (head_dim == 64) return go_batch(split_score_batch<64>, d, bt, total, lds, st);
-  return hipErrorInvalidValue;
+  return hipSuccess;
 }
 
+namespace {
+template <int HD>
+hipError_t apply_batch_dispatch(int r, const SplitArgs* d, const BatchTab& bt, int64_t total, size_t lds,
+                                hipStream_t st) {
+  switch (r) {
+    case 8: return go_batch(split_apply_batch<HD, 1, 8, 1>, d, bt, total, lds, st);
+    case 16: return go_batch(split_apply_batch<HD, 1, 16, 1>, d, bt, total, lds, st);
+    case 32: return go_batch(split_apply_batch<HD, 2, 32, 1>, d, bt, total, lds, st);
+    case 64: return go_batch(split_apply_batch<HD, 2, 32, 2>, d, bt, total, lds, st);
+    case 128: return go_batch(split_apply_batch<HD, 2, 32, 4>, d, bt, total, lds, st);
+    case 256: return go_batch(split_apply_batch<HD, 2, 32, 8>, d, bt, total, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+// one grid per distinct delta rank among the hops, in order of first appearance
 hipError_t launch_split_apply_batch(const SplitArgs* d, const SplitArgs* h, int n, int head_dim, hipStream_t st) {
-  BatchTab bt;
-  int64_t total;
-  if (!batch_tab(bt, h, n, total)) return hipErrorInvalidValue;
-  size_t lds = 0;
+  if (n < 1 || n > kMaxBatch || (head_dim != 128 && head_dim != 64)) return hipErrorInvalidValue;
   for (int i = 0; i < n; ++i) {
     const int r = h[i].r_d;
     if ((r != 8 && r != 16 && r != 32 && split_apply_slices(r) == 1) || !h[i].wa) return hipErrorInvalidValue;
-    lds = std::max(lds, split_apply_lds(r));
   }
-  if (total == 0) return hipSuccess;
-  if (head_dim == 128) return go_batch(split_apply_batch<128>, d, bt, total, lds, st);
-  if (head_dim == 64) return go_batch(split_apply_batch<64>, d, bt, total, lds, st);
-  return hipErrorInvalidValue;
+  bool done[kMaxBatch] = {};
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    int idx[kMaxBatch], m = 0;
+    for (int j = i; j < n; ++j)
+      if (!done[j] && h[j].r_d == h[i].r_d) {
+        idx[m++] = j;
+        done[j] = true;
+      }
+    BatchTab bt;
+    int64_t total;
+    if (!batch_tab(bt, h, idx, m, total)) return hipErrorInvalidValue;
+    if (total == 0) continue;
+    const size_t lds = split_apply_lds(h[i].r_d);
+    const hipError_t e = head_dim == 128 ? apply_batch_dispatch<128>(h[i].r_d, d, bt, total, lds, st)
+                                         : apply_batch_dispatch<64>(h[i].r_d, d, bt, total, lds, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_split_weights_batch(const SplitArgs* d, const SplitArgs* h, int n, hipStream_t st) {
