@@ -64,6 +64,8 @@ def kernel_work(name, L, S, D, N, rC, rD, mode="pages", b=2):
         return dict(bytes=src + out + fac_delta + scores, flops=4 * L * S * D * N * rD, alu=0)
     if name in ("score_cos_mfma", "score_cos_gemm"):
         return dict(bytes=src + fac_base + scores, flops=4 * L * S * D * N * rC, alu=6 * L * S * N * rC)
+    if name == "split_weights":                   # per-channel-tile distance partials in, weights out
+        return dict(bytes=2 * L * S * N * 4 * (D // 256 + 1), flops=0, alu=0)
     if name in ("pack_base", "pack_delta", "pack_cos"):
         r = rD if name == "pack_delta" else rC
         return dict(bytes=2 * 2 * L * N * r * D * b, flops=0, alu=0)
