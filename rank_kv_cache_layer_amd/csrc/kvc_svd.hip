@@ -1106,7 +1106,7 @@ __global__ void __launch_bounds__(1024) jacobi(double* A, double* V, int l, int 
 // Per-matrix state: [0] converged (or out of sweeps), [1 + buffer] rounds logged in that
 // buffer, [3] sweeps done.  An odd l is padded with a zero row that is never rotated.
 constexpr int kJacobiLdsMax = 192;
-constexpr int kJacobiChunkSweeps = 4;
+constexpr int kJacobiChunkSweeps = 2;
 constexpr int kApplyCols = 64, kApplyPitch = kApplyCols + 1, kApplyGroups = 1024 / kApplyCols;
 __device__ __forceinline__ int tri(int i, int j) { return i >= j ? i * (i + 1) / 2 + j : j * (j + 1) / 2 + i; }
 
