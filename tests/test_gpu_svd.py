@@ -40,7 +40,11 @@ def test_eckart_young_at_the_refresh_shape():
         assert np.max(np.abs(b[m] @ b[m].T - np.eye(128))) <= 1e-5
 
 
-@pytest.mark.parametrize("rows,cols,rank,p", [(300, 200, 16, 8), (256, 1024, 24, 16), (1000, 96, 8, 4)])
+# sketch widths l = rank + p: 24, 40, 12 (register Cholesky, split-bf16 and fp32 matrix-core
+# products), 11 (odd: the unaligned fallbacks of every product), 176 (LDS Cholesky and fp64
+# triangular product, LDS Jacobi at its largest triangle) and 200 (global Cholesky and Jacobi)
+@pytest.mark.parametrize("rows,cols,rank,p", [(300, 200, 16, 8), (256, 1024, 24, 16), (1000, 96, 8, 4),
+                                              (200, 152, 7, 4), (300, 260, 144, 32), (260, 240, 168, 32)])
 def test_exact_rank_r_is_reconstructed(rows, cols, rank, p):
     g = torch.Generator().manual_seed(rows + cols)
     z = (torch.randn((3, rows, rank), generator=g, dtype=torch.float64)
