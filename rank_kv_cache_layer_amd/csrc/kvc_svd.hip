@@ -3,18 +3,27 @@
 //
 // The pages name no method; this is randomised subspace iteration (Halko, Martinsson & Tropp,
 // "Finding structure with randomness", SIAM Review 2011, Alg. 4.4) with a Gaussian sketch of
-// l = rank + oversample columns and `power_iters` power iterations, every intermediate basis
-// re-orthonormalised by CholeskyQR2 (Fukaya et al. 2014) with a fp64 Gram matrix.  Directions
-// whose Cholesky pivot vanishes (rank-deficient sketches, e.g. an exactly rank-r Z) are dropped
-// (their basis columns set to zero).  The small problem is solved as the symmetric
-// eigenproblem of the l x l Gram matrix of Bsk = Q^T Z (fp64) by parallel cyclic Jacobi
-// (Golub & Van Loan, Matrix Computations, Sec. 8.5): Bsk Bsk^T = W Lambda W^T, sigma = sqrt(lambda),
-// A = Q W_r Sigma_r, B = Sigma_r^-1 W_r^T Bsk.  Each component is signed so that the
-// largest-magnitude entry of its left singular vector (column of A) is positive.
+// l = rank + oversample columns and `power_iters` power iterations.  The bases between power
+// iterations take one CholeskyQR round and the final basis Q two (CholeskyQR2, Fukaya et al.
+// 2014), each with an fp64 Gram matrix.  Directions whose Cholesky pivot vanishes
+// (rank-deficient sketches, e.g. an exactly rank-r Z) are dropped (their basis columns set to
+// zero).  The small problem is solved as the symmetric eigenproblem of the l x l Gram matrix of
+// Bsk = Q^T Z (fp64) by parallel cyclic Jacobi (Golub & Van Loan, Matrix Computations,
+// Sec. 8.5): Bsk Bsk^T = W Lambda W^T, sigma = sqrt(lambda), A = Q W_r Sigma_r,
+// B = Sigma_r^-1 W_r^T Bsk.  Each component is signed so that the largest-magnitude entry of its
+// left singular vector (column of A) is positive.
 //
-// Kernels: sketch (counter-based Gaussian draws), a batched tiled GEMM for every product
-// (VALU FMA in fp32 or fp64; the refresh is off the time-to-first-token path), Cholesky with
-// pivot dropping + triangular inverse, Jacobi, top-r selection, sign fix.
+// Precision: the products that only steer the sketch's span (Z Omega, every Z^T Y, every Z W
+// but the last, the one-round CholeskyQR products) run with each fp32 operand split into two
+// bf16 parts on the matrix cores (about 16 significant bits); the last Z W, the final
+// CholeskyQR2 products, Q^T Z and A run in fp32 on the matrix cores, the Grams, the Cholesky
+// factorisation and the eigensolver in fp64.
+//
+// Kernels: sketch (counter-based Gaussian draws); gemm_bf3_wide / gemm_f32_mfma_wide (narrow
+// products, N <= 160), gemm_f32_mfma (wider fp32 products), gemm_f64_tn (split-K fp64 Grams) and
+// the VALU GEMMs for the remaining shapes; chol_inv_reg (l <= 160, registers), chol_inv_lds and
+// chol_inv (wider); jacobi_step (l <= 192: sweeps in LDS, eigenvector replay spread over the
+// device) and jacobi (wider); select_top; the three sign-convention passes.
 #include <math.h>
 
 #include <type_traits>
@@ -1552,7 +1561,9 @@ SvdWs layout(int n_mats, int rows, int cols, int rank, int oversample) {
 
 // Y [b][rows][l] (fp32) <- orthonormal (or zero) columns spanning it: `passes` rounds of
 // CholeskyQR with pivot dropping (two = CholeskyQR2).  Rounds alternate between Y and `tmp`; with
-// an odd number the result is in `tmp` and the caller swaps the two.
+// an odd number the result is in `tmp` and the caller swaps the two.  A single round (a basis
+// between power iterations) multiplies Y L^-T in split bf16; two rounds (the final basis) in
+// fp32.  `part`: the Gram's split-K partial sums.
 hipError_t orth(float* Y, float* tmp, double* G, double* Li, double* part, int b, int rows, int l, int passes,
                 hipStream_t st) {
   hipError_t e;
