@@ -760,8 +760,17 @@ def main():
                       "unrelated_layers": len(sp.unrelated_layers or []), "parallelism": "single-gpu"},
            "roofline": None, "cpu_baseline": None}
 
+    def guarded(key, fn):
+        # a failing secondary measurement is recorded and must not hide the headline line
+        try:
+            return fn()
+        except Exception as e:
+            log(f"[bench] {key} failed: {type(e).__name__}: {e}")
+            out.setdefault("errors", {})[key] = f"{type(e).__name__}: {e}"
+            return None
+
     if "peaks" in want:
-        out["measured_peaks"] = measure_peaks(kvc, torch)
+        out["measured_peaks"] = guarded("peaks", lambda: measure_peaks(kvc, torch))
         log(f"[bench] measured ceilings: {out['measured_peaks']}")
 
     art3 = None
@@ -814,93 +823,98 @@ def main():
                                 "v_out": vo.index_select(0, idx).double().cpu().numpy(),
                                 "flags": res.flags.cpu().numpy(), "orig_layer": lay}}
         if "protocol" in want:
-            out["protocol"] = measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(mode)(None))
+            out["protocol"] = guarded("protocol", lambda: measure_protocol(kvc, torch, k, v, ko, vo, shp, sp, pool,
+                                                                           prm_fn(mode)(None)))
             log(f"[bench] per-repetition protocol (cache flushed): {out['protocol']}")
         if "second" in want:
-            m2 = W.SCORE_COS_R if mode == W.SCORE_PAGES else W.SCORE_PAGES
-            ms2, _, pk2, _ = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(m2), ws,
-                                      max(3, args.steps // 4), 1)
-            out["second_mode"] = {"mode": "cos_r" if m2 == W.SCORE_COS_R else "pages", "ms_per_hop": round(ms2, 4),
-                                  "tokens_per_s": round(S / (ms2 / 1e3), 1),
-                                  "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
-            log(f"[bench] second mode {out['second_mode']['mode']}: {ms2:.3f} ms/hop")
+            def second():
+                m2 = W.SCORE_COS_R if mode == W.SCORE_PAGES else W.SCORE_PAGES
+                ms2, _, pk2, _ = time_hop(kvc, torch, k, v, ko, vo, shp, sp, pool, prm_fn(m2), ws,
+                                          max(3, args.steps // 4), 1)
+                return {"mode": "cos_r" if m2 == W.SCORE_COS_R else "pages", "ms_per_hop": round(ms2, 4),
+                        "tokens_per_s": round(S / (ms2 / 1e3), 1),
+                        "kernels_ms": {n: round(statistics.median(t), 4) for n, t in pk2.items()}}
+            out["second_mode"] = guarded("second", second)
+            log(f"[bench] second mode: {out['second_mode']}")
         del k, v, ko, vo, pool, ws
         torch.cuda.empty_cache()
 
     art2 = None
     if "c2" in want:
         log("[bench] 4096-token hop (32 layers, 20 anchors at rank 32) ...")
-        out["c2_hop"], art2 = measure_c2(kvc, torch, W, data_c2)
-        log(f"[bench] c2: {out['c2_hop']['ms']} ms, {out['c2_hop']['tokens_per_s']} tokens/s")
-    if "refresh" in want:
-        log("[bench] anchor refresh (64 x 4096 x 1024, rank 128) ...")
-        out["refresh"] = measure_refresh(kvc, torch, oracle="cpu" in want)
-        log(f"[bench] refresh: {out['refresh']['ms']} ms, {out['refresh']['achieved_TFLOPs']} TFLOP/s")
-    if "chain" in want:
-        log("[bench] chained batch (8 requests x 3 hops, 8192 tokens) ...")
-        out["chained_batch"] = measure_chain(kvc, torch, W)
-        log(f"[bench] chain: {out['chained_batch']}")
-    if "pf" in want:
-        log("[bench] preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens) ...")
-        out["pf_delta"] = measure_pf_delta(kvc, torch)
-        log(f"[bench] pf delta: {out['pf_delta']['ms']} ms, {out['pf_delta']['achieved_GBps']} GB/s")
-    if "r128" in want:
-        log("[bench] rank-128 correction (32 layers x 4096 tokens, 10 anchors) ...")
-        out["rank128_hop"] = measure_rank128(kvc, torch, W, data_c5)
-        log(f"[bench] rank 128: pages {out['rank128_hop']['pages']['ms']} ms, "
-            f"cos_r {out['rank128_hop']['cos_r']['ms']} ms")
-    if "c5" in want:
-        log("[bench] refresh into anchor 0, then the rank-128 correction ...")
-        out["c5_pipeline"] = measure_c5(kvc, torch, W, data_c5)
-        log(f"[bench] c5 pipeline: {out['c5_pipeline']}")
-    if "study" in want:
-        log("[bench] chained vs non-chained correction error along A0 -> A3 (8 layers x 4096 x 1024) ...")
-        out["chain_study"] = measure_study(torch)
-        log(f"[bench] study: {out['chain_study']}")
-    if "pool" in want:
-        log("[bench] pool update after a fallback (32 layers x 4096 tokens, rank 32) ...")
-        out["pool_insert"] = measure_pool_insert(kvc, torch, oracle="cpu" in want)
-        log(f"[bench] pool insert: {out['pool_insert']['ms']} ms; Eq. 12 kernels {out['pool_insert']['eq12_kernels']}")
+        r2 = guarded("c2", lambda: measure_c2(kvc, torch, W, data_c2))
+        if r2 is not None:
+            out["c2_hop"], art2 = r2
+        log(f"[bench] c2: {out.get('c2_hop')}")
+    for key, want_key, msg, fn in (
+            ("refresh", "refresh", "anchor refresh (64 x 4096 x 1024, rank 128)",
+             lambda: measure_refresh(kvc, torch, oracle="cpu" in want)),
+            ("chained_batch", "chain", "chained batch (8 requests x 3 hops, 8192 tokens)",
+             lambda: measure_chain(kvc, torch, W)),
+            ("pf_delta", "pf", "preconstructed rank-8 correction, weight 1 (32 layers x 32768 tokens)",
+             lambda: measure_pf_delta(kvc, torch)),
+            ("rank128_hop", "r128", "rank-128 correction (32 layers x 4096 tokens, 10 anchors)",
+             lambda: measure_rank128(kvc, torch, W, data_c5)),
+            ("c5_pipeline", "c5", "refresh into anchor 0, then the rank-128 correction",
+             lambda: measure_c5(kvc, torch, W, data_c5)),
+            ("chain_study", "study", "chained vs non-chained correction error along A0 -> A3 (8 layers x 4096 x 1024)",
+             lambda: measure_study(torch)),
+            ("pool_insert", "pool", "pool update after a fallback (32 layers x 4096 tokens, rank 32)",
+             lambda: measure_pool_insert(kvc, torch, oracle="cpu" in want))):
+        if want_key in want:
+            log(f"[bench] {msg} ...")
+            out[key] = guarded(want_key, fn)
+            log(f"[bench] {want_key}: {out[key]}")
 
-    if "cpu" in want:
-        from oracle import kvc_oracle as O
-        log("[bench] timing the fp64 oracle on bounded samples, and parity / quality on sampled layers ...")
-        d3 = _layers_of(data, art3["layers"], k_src=art3["k_src"])
-        d3 = dataclasses.replace(d3, spec=dataclasses.replace(d3.spec, p_src=sp.p_src, p_tgt=sp.p_tgt,
-                                                              n_layers=len(art3["layers"]),
-                                                              unrelated_layers=sp.unrelated_layers))
-        out["cpu_baseline"] = cpu_baseline(O, d3, sp.n_layers, art3["layers"])
-        log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s ({out['cpu_baseline']['sample']})")
-        base = {"c3": dict(out["cpu_baseline"])}
-        quality = {"c3": hop_quality(O, W, d3, art3["gpu"], art3["layers"])}
-        if art2 is not None:
-            sp2 = data_c2.spec
-            d2 = _layers_of(data_c2, art2["layers"], k_src=art2["k_src"])
-            base["c2"] = cpu_median(O, d2, sp2.n_layers, art2["layers"])
-            quality["c2"] = hop_quality(O, W, d2, art2["gpu"], art2["layers"])
-            quality["c2"]["accepted_layer_fraction"] = out["c2_hop"]["accepted_layer_fraction"]
-        # the tiny fp32 workload: whole hop, median of 3, also on one thread; GPU parity beside it
-        dt1 = W.make_hop(W.tiny(), place_keys=lambda x, p_: O.rope(x, p_, 64))
-        sp1 = dt1.spec
-        base["c1"] = cpu_median(O, dt1, sp1.n_layers, list(range(sp1.n_layers)))
-        base["c1_single_thread"] = cpu_median(O, dt1, sp1.n_layers, list(range(sp1.n_layers)), threads=1)
-        k1, v1 = dt1.k_src.to(dev), dt1.v_src.to(dev)
-        ko1, vo1 = torch.empty_like(k1), torch.empty_like(v1)
-        shp1 = kvc.shape_of(sp1.n_layers, sp1.seq_len, sp1.n_kv_heads, sp1.head_dim)
-        res1 = kvc.correct_hop(k1, v1, ko1, vo1, shp1, sp1.p_src, sp1.p_tgt, kvc.pool_from(dt1, dev),
-                               kvc.params_of(sp1.tau, sp1.temp_gate, sp1.temp_weight, sp1.gate_len, sp1.mode))
-        torch.cuda.synchronize()
-        ref1 = O.correct_hop(dt1)
-        quality["c1"] = {"max_abs_err_over_max_x": {
-            s_: round(float(np.max(np.abs(t.double().cpu().numpy() - ref1[f"{s_}_out"])) /
-                            np.max(np.abs(ref1[f"{s_}_out"]))), 9) for s_, t in (("k", ko1), ("v", vo1))},
-            "bound": 1e-5, "flags_equal": bool(np.array_equal(res1.flags.cpu().numpy(), ref1["flags"]))}
-        out["cpu_baselines"] = base
-        out["quality"] = quality
-        log(f"[bench] oracle baselines: {base}")
-        log(f"[bench] quality: {quality}")
+    if "cpu" in want and art3 is not None:
+        guarded("cpu", lambda: cpu_section(O_loader(), out, data, data_c2, art2, art3, sp, dev, kvc, torch, W))
 
     print(json.dumps(out), flush=True)
+
+
+def O_loader():
+    from oracle import kvc_oracle as O
+    return O
+
+
+def cpu_section(O, out, data, data_c2, art2, art3, sp, dev, kvc, torch, W):
+    """The oracle's baselines (bounded samples of the 32768-, 4096-token and tiny hops) and the quality of the GPU's
+    outputs of sampled layers against the oracle and the exact target."""
+    log("[bench] timing the fp64 oracle on bounded samples, and parity / quality on sampled layers ...")
+    d3 = _layers_of(data, art3["layers"], k_src=art3["k_src"])
+    d3 = dataclasses.replace(d3, spec=dataclasses.replace(d3.spec, p_src=sp.p_src, p_tgt=sp.p_tgt,
+                                                          n_layers=len(art3["layers"]),
+                                                          unrelated_layers=sp.unrelated_layers))
+    out["cpu_baseline"] = cpu_baseline(O, d3, sp.n_layers, art3["layers"])
+    log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s ({out['cpu_baseline']['sample']})")
+    base = {"c3": dict(out["cpu_baseline"])}
+    quality = {"c3": hop_quality(O, W, d3, art3["gpu"], art3["layers"])}
+    if art2 is not None:
+        sp2 = data_c2.spec
+        d2 = _layers_of(data_c2, art2["layers"], k_src=art2["k_src"])
+        base["c2"] = cpu_median(O, d2, sp2.n_layers, art2["layers"])
+        quality["c2"] = hop_quality(O, W, d2, art2["gpu"], art2["layers"])
+        quality["c2"]["accepted_layer_fraction"] = out["c2_hop"]["accepted_layer_fraction"]
+    # the tiny fp32 workload: whole hop, median of 3, also on one thread; GPU parity beside it
+    dt1 = W.make_hop(W.tiny(), place_keys=lambda x, p_: O.rope(x, p_, 64))
+    sp1 = dt1.spec
+    base["c1"] = cpu_median(O, dt1, sp1.n_layers, list(range(sp1.n_layers)))
+    base["c1_single_thread"] = cpu_median(O, dt1, sp1.n_layers, list(range(sp1.n_layers)), threads=1)
+    k1, v1 = dt1.k_src.to(dev), dt1.v_src.to(dev)
+    ko1, vo1 = torch.empty_like(k1), torch.empty_like(v1)
+    shp1 = kvc.shape_of(sp1.n_layers, sp1.seq_len, sp1.n_kv_heads, sp1.head_dim)
+    res1 = kvc.correct_hop(k1, v1, ko1, vo1, shp1, sp1.p_src, sp1.p_tgt, kvc.pool_from(dt1, dev),
+                           kvc.params_of(sp1.tau, sp1.temp_gate, sp1.temp_weight, sp1.gate_len, sp1.mode))
+    torch.cuda.synchronize()
+    ref1 = O.correct_hop(dt1)
+    quality["c1"] = {"max_abs_err_over_max_x": {
+        s_: round(float(np.max(np.abs(t.double().cpu().numpy() - ref1[f"{s_}_out"])) /
+                        np.max(np.abs(ref1[f"{s_}_out"]))), 9) for s_, t in (("k", ko1), ("v", vo1))},
+        "bound": 1e-5, "flags_equal": bool(np.array_equal(res1.flags.cpu().numpy(), ref1["flags"]))}
+    out["cpu_baselines"] = base
+    out["quality"] = quality
+    log(f"[bench] oracle baselines: {base}")
+    log(f"[bench] quality: {quality}")
 
 
 if __name__ == "__main__":
