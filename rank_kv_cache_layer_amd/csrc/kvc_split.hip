@@ -256,22 +256,47 @@ __device__ __forceinline__ TileId tile_id(P& p, int64_t lb) {
 }
 
 // ================================================================== pass 1: scores
+// The operands an anchor's first products need (its A fragments and the first two channel
+// blocks' B fragments), read as soon as the anchor's slot has landed, ahead of the step's scalar
+// bookkeeping, so their latency is not paid in front of the first products.
+template <int RK>
+struct ScoreFrags {
+  bf16x8 av[2][RK], bv[RK], bn[RK];
+};
+template <int RK>
+__device__ __forceinline__ ScoreFrags<RK> score_frags(uint32_t slot, const uint32_t (&aoff)[2][RK], uint32_t boff) {
+  ScoreFrags<RK> f;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < RK; ++ks) f.av[tb][ks] = as_bf8(lds_u4(slot + aoff[tb][ks]));
+  const uint32_t bs = slot + boff;
+#pragma unroll
+  for (int ks = 0; ks < RK; ++ks) {
+    f.bv[ks] = as_bf8(lds_u4(bs + ks * 1024));
+    f.bn[ks] = as_bf8(lds_u4(bs + (RK + ks) * 1024));
+  }
+  return f;
+}
+
 // One anchor for a wave: 8 accumulator blocks (2 token x 4 channel, channel-block major), each
 // E = Z_can - A B reduced to per-lane |E| sums and (Q) E^2 sums.  Software-pipelined one block
 // deep: the MFMA chain of block b + 1 is issued before the VALU reduction of block b, and the
 // empty asm statement after each reduction "redefines" the A operands, so the compiler cannot
 // hoist the chain of block b + 2 above it (two live result blocks, not eight).
-// `slot`: LDS byte offset of the anchor's slot; `aoff[tb][ks]`: this lane's A fragment offsets
-// inside a slot; `boff`: this lane's offset of its first B chunk inside a slot.
-template <int RK, bool Q, typename RG>
-__device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t slot, const uint32_t (&aoff)[2][RK],
+// `slot`: LDS byte offset of the anchor's slot; `fr`: its first fragments (score_frags);
+// `boff`: this lane's offset of its first B chunk inside a slot; `dma(u)`: issues transfer u of
+// this wave's share of a later anchor's operands, called once per result block while u is below
+// the share's size.
+template <int RK, bool Q, typename RG, typename DMA>
+__device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], const ScoreFrags<RK>& fr, uint32_t slot,
                                              uint32_t boff, float qm0, float qm1, float& ms0, float& ms1,
-                                             float& qs) {
+                                             float& qs, DMA&& dma) {
   bf16x8 av[2][RK];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < RK; ++ks) av[tb][ks] = as_bf8(lds_u4(slot + aoff[tb][ks]));
+    for (int ks = 0; ks < RK; ++ks) av[tb][ks] = fr.av[tb][ks];
   const uint32_t bs = slot + boff;
   float m[2] = {0.f, 0.f}, q[2] = {0.f, 0.f};
   auto chain = [&](const bf16x8* bv, int tb, int db) {
@@ -293,8 +318,8 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t s
   bf16x8 bv[RK], bn[RK];
 #pragma unroll
   for (int ks = 0; ks < RK; ++ks) {
-    bv[ks] = as_bf8(lds_u4(bs + ks * 1024));
-    bn[ks] = as_bf8(lds_u4(bs + (RK + ks) * 1024));
+    bv[ks] = fr.bv[ks];
+    bn[ks] = fr.bn[ks];
   }
   f32x16 e = chain(bv, 0, 0);
 #pragma unroll
@@ -312,6 +337,7 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], uint32_t s
         for (int ks = 0; ks < RK; ++ks) bn[ks] = as_bf8(lds_u4(bs + ((db + 1) * RK + ks) * 1024));
       }
     }
+    if (b - 1 < RG::DMA_PER_WAVE) dma(b - 1);
     reduce(e, (b - 1) & 1);
     // the q sums are tied too: left free, their FMAs sink and keep every block alive
     if constexpr (RK == 1)
@@ -407,6 +433,22 @@ struct Ring {
         dma16(Wr, slot + A_BYTES + B_BYTES + wave * W_LANES * 16, (uint32_t)((t0 + (wave * W_LANES + lane) * 4) * 4));
     }
   }
+
+  // Transfer `i` (< A_PER_WAVE + B_PER_WAVE; a compile-time constant after unrolling) of this
+  // wave's share of fetch() without weights, so a step can spread its transfers over its work.
+  static __device__ __forceinline__ void fetch_unit(int i, uint32_t slot, rsrc_t Ar, rsrc_t Br, int t0, int wave,
+                                                    int lane) {
+    if (i < A_PER_WAVE) {
+      const int u = (wave * A_PER_WAVE + i) * 64 + lane;
+      const int row = u / U, cpos = u % U;
+      const int c = cpos ^ ((row / (16 / U)) & (U - 1));
+      const uint32_t voff = c * 8 < RA ? (uint32_t)(((t0 + row) * RS + c * 8) * 2) : 0x80000000u;
+      dma16(Ar, slot + (wave * A_PER_WAVE + i) * 1024, voff);
+    } else {
+      const int kc = wave * B_PER_WAVE + (i - A_PER_WAVE);
+      dma16(Br, slot + A_BYTES + kc * 1024, (uint32_t)(kc * 1024 + lane * 16));
+    }
+  }
 };
 
 // Static LDS of a scoring work-group (the operand ring is dynamic LDS).
@@ -461,6 +503,22 @@ __device__ __forceinline__ void score_tile(P& p, int64_t lb, char* ring, ScoreSh
               make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
               make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0), make_rsrc(nullptr, 0), t0, wv, lane);
   };
+  // The same transfers for the steady state, issued one per result block of the step two
+  // anchors earlier (score_anchor's `dma`), not all right after the step's barrier where every
+  // wave of the CU would queue its transfers at once in front of its first products.
+  struct Plan {
+    uint32_t slot;
+    rsrc_t Ar, Br;
+  };
+  auto plan = [&](int j) {
+    const bool live = j < nl;
+    const int js = live ? j : 0;
+    const int a = lane_get(sl.a, js);
+    const int lim = live ? lane_get(sl.lim, js) : 0;
+    return Plan{ring0 + (uint32_t)(j % kSlots) * RG::SLOT,
+                make_rsrc(Al + (int64_t)lane_get(sl.off, js) * R, (uint32_t)lim * R * 2),
+                make_rsrc(Bl + a * bstride, live ? RG::B_BYTES : 0)};
+  };
   uint32_t aoff[2][RK];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
@@ -485,14 +543,15 @@ __device__ __forceinline__ void score_tile(P& p, int64_t lb, char* ring, ScoreSh
 #pragma nounroll
     for (int j = 0; j < nl; ++j) {
       wait_vm_barrier<RG::DMA_PER_WAVE>();   // anchor j landed for every wave; slot (j + 2) % 3 is free
-      if (j > 0) store_m(j - 1);
-      fetch(j + 2);
-      const int a = lane_get(sl.a, j);
       // through a lane read the base is opaque: each operand address is then one add to it
       // plus an immediate offset, not a re-derivation of j % kSlots per access
       const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));
+      const ScoreFrags<RK> fr = score_frags<RK>(slot, aoff, boff);
+      const Plan fp = plan(j + 2);
+      const int a = lane_get(sl.a, j);
       float ms0 = 0.f, ms1 = 0.f, qs = 0.f;
-      score_anchor<RK, Q, RG>(z, slot, aoff, boff, qm0, qm1, ms0, ms1, qs);
+      score_anchor<RK, Q, RG>(z, fr, slot, boff, qm0, qm1, ms0, ms1, qs,
+                              [&](int u) { RG::fetch_unit(u, fp.slot, fp.Ar, fp.Br, t0, wv, lane); });
       if ((p.mask_corr >> a) & 1) {
         ms0 = xor32_sum(ms0);
         ms1 = xor32_sum(ms1);
@@ -505,6 +564,9 @@ __device__ __forceinline__ void score_tile(P& p, int64_t lb, char* ring, ScoreSh
         qs = wave_sum63(qs);
         if (lane == 63) qp[wave][a] = qs;
       }
+      // anchor j - 1's sums (written by every wave before this step's barrier; this step writes
+      // the other buffer, and the next step's barrier orders this read before its reuse)
+      if (j > 0) store_m(j - 1);
     }
   };
   __syncthreads();   // rotation table (before any transfer: the barrier's fence would wait for them)
@@ -722,9 +784,8 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
       for (int ks = 0; ks < NS; ++ks) {
         const int j = ja * NS + ks;
         wait_vm_barrier<RG::DMA_PER_WAVE>();   // slice j landed for every wave; slot (j + 2) % 3 is free
-        if (ks == 0 && ja > 0) store_m(ja - 1);
-        fetch(j + 2);
         const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));
+        // the slice's fragments first: their reads are in flight while the transfers issue
         bf16x8 av[2][2], bv[2][2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -733,6 +794,7 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
           bv[0][kk] = as_bf8(lds_u4(slot + boff0 + kk * 1024));
           bv[1][kk] = as_bf8(lds_u4(slot + boff1 + kk * 1024));
         }
+        fetch(j + 2);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -766,6 +828,10 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
         qs = wave_sum63(qs);
         if (lane == 63) qp[wave][a] = qs;
       }
+      // anchor ja - 1's sums (written by every wave before this anchor's first barrier; this
+      // anchor wrote the other buffer, and the next anchor's first barrier orders this read
+      // before that buffer is written again)
+      if (ja > 0) store_m(ja - 1);
     }
   };
   __syncthreads();   // rotation table
