@@ -279,6 +279,26 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
         dma16(bs, slot + kZBytes + (uint32_t)(wv * kBDma + i) * 1024, (uint32_t)(row * kRowB + c * 16));
       }
     };
+    // transfer u (< kDmaPerWave, a compile-time constant after unrolling) of fetch(kc): the
+    // steady state spreads a chunk's transfers over the previous chunk's products
+    auto fetch_unit = [&](int kc, int u) {
+      const bool live = kc < nkc;
+      const uint32_t slot = ring0 + (uint32_t)(kc % kRing) * kSlot;
+      if (u < kZDma) {
+        const rsrc_t zs = live ? zr : make_rsrc(zl, 0);
+        const int unit = (wv * kZDma + u) * 64 + lane;
+        const int row = unit >> 2, c = (unit & 3) ^ ((row >> 2) & 3);
+        dma16(zs, slot + (uint32_t)(wv * kZDma + u) * 1024,
+              (uint32_t)(((int64_t)(t0 + row) * D + kc * kKc + c * 8) * 2));
+      } else {
+        const int i = u - kZDma;
+        const uint16_t* bc = bside + ((int64_t)(live ? kc : 0) * nq + u0) * r * kKc;
+        const rsrc_t bs = make_rsrc(bc, live ? (uint32_t)np * r * kRowB : 0u);
+        const int unit = (wv * kBDma + i) * 64 + lane;
+        const int row = unit >> 2, c = (unit & 3) ^ ((row >> 2) & 3);
+        dma16(bs, slot + kZBytes + (uint32_t)(wv * kBDma + i) * 1024, (uint32_t)(row * kRowB + c * 16));
+      }
+    };
 
     f32x16 acc[kAnch][2];
 #pragma unroll
@@ -293,16 +313,21 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
 #pragma nounroll
     for (int kc = 0; kc < nkc; ++kc) {
       wait_vm_barrier<kDmaPerWave>();   // chunk kc landed everywhere; slot (kc + 2) % 3 is free
-      fetch(kc + 2);
       const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ring0 + (uint32_t)(kc % kRing) * kSlot));
+      // the first half-chunk's fragments are in flight while the next transfers issue
+      const bf16x8 f0 = lds_frag(slot + zoff[0][0]), f1 = lds_frag(slot + zoff[1][0]);
+      bf16x8 fb[kAnch];
+#pragma unroll
+      for (int x = 0; x < kAnch; ++x) fb[x] = lds_frag(slot + boff[x][0]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 z0 = lds_frag(slot + zoff[0][s]), z1 = lds_frag(slot + zoff[1][s]);
+        const bf16x8 z0 = s == 0 ? f0 : lds_frag(slot + zoff[0][s]), z1 = s == 0 ? f1 : lds_frag(slot + zoff[1][s]);
 #pragma unroll
         for (int x = 0; x < kAnch; ++x) {
-          const bf16x8 bx = lds_frag(slot + boff[x][s]);
+          const bf16x8 bx = s == 0 ? fb[x] : lds_frag(slot + boff[x][s]);
           acc[x][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx, z0, acc[x][0], 0, 0, 0);
           acc[x][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx, z1, acc[x][1], 0, 0, 0);
+          if (s * kAnch + x < kDmaPerWave) fetch_unit(kc + 2, s * kAnch + x);
         }
       }
     }
