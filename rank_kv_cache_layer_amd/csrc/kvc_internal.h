@@ -225,9 +225,10 @@ bool make_pack_args(PackArgs& a, const uint16_t* const* src, uint16_t* const* ds
 hipError_t launch_pack_b_batch(const PackArgs* d, const PackArgs* h, int n, hipStream_t st);
 
 // ------------------------------------------------------------ two-pass path (bf16)
-// Score work-group = 256 tokens x 256 channels of one (layer, side), 8 waves of 64 x 128 (one
-// per CU).  Apply work-group = 128 tokens x 256 channels, 4 waves of 64 x 128; two share a CU
-// so one's streaming phases (source in, corrected cache out) overlap the other's MFMA phases.
+// Score work-group = 128 tokens x 256 channels of one (layer, side), 4 waves of 64 x 128, two per
+// CU (64 tokens at base ranks 64 / 128).  Apply work-group = 128 tokens x 256 channels, 4 waves
+// of 64 x 128, three per CU, so one's streaming phases (source in, corrected cache out) overlap
+// the others' MFMA phases.
 constexpr int kScoreTile = 128;
 constexpr int kScoreThreads = 256;
 constexpr int kApplyTile = 128;
