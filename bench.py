@@ -704,7 +704,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs the per-hop correction on one GPU only; --gpus {args.gpus} "
+        print(f"bench.py: the per-hop correction runs on one GPU only; --gpus {args.gpus} "
               f"(WORLD_SIZE={world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     want = set(args.only.split(",")) if args.only else set(SECTIONS)

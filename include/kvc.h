@@ -58,7 +58,7 @@ typedef enum {
   KVC_E_WORKSPACE = 6,   /* workspace missing or smaller than kvc_workspace_size()   */
   KVC_E_HIP = 7,         /* the HIP runtime reported an error at launch              */
   KVC_E_PARAM = 8,       /* a scalar parameter is out of range                       */
-  KVC_E_UNSUPPORTED = 9  /* valid request this build does not implement              */
+  KVC_E_UNSUPPORTED = 9  /* valid request the kernels do not implement               */
 } kvc_status;
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
