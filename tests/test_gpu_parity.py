@@ -422,15 +422,17 @@ def test_batched_chain_matches_oracle_hop_by_hop(mode, rank):
     _check_chain_identical_inputs(reqs, datas, hl, f"chain-{mode}-{rank}")
 
 
-def test_batched_chain_8b_heads_levels_batched():
+@pytest.mark.parametrize("seed", [4, 9, 13])
+def test_batched_chain_8b_heads_levels_batched(seed):
     # the chain specification at the 8B head layout (8 x 128, D = 1024), 4 layers, 1024 tokens,
     # 3 requests x 3 hops, pools of 10-20 anchors at ranks 16 / 32: each level runs as one grid per
     # kernel; the outputs, weights and gate rows equal those of one call per hop bit for bit (the
     # same tile code), and every hop matches the oracle on the GPU's own chained inputs
-    reqs = W.chain_specs(n_requests=3, n_hops=3, seq_len=1024, n_layers=4, n_kv_heads=8)
-    print(f"[parity] chain 8x128: N={[h.n_anchors for hops in reqs for h in hops]} "
+    reqs = W.chain_specs(n_requests=3, n_hops=3, seq_len=1024, n_layers=4, n_kv_heads=8, seed=seed)
+    print(f"[parity] chain 8x128 seed {seed}: N={[h.n_anchors for hops in reqs for h in hops]} "
           f"r={[h.rank_base for hops in reqs for h in hops]}", flush=True)
-    assert {h.rank_base for hops in reqs for h in hops} == {16, 32}
+    if seed == 4:
+        assert {h.rank_base for hops in reqs for h in hops} == {16, 32}
     datas, hl = _run_chain(reqs)
     _, hl1 = _run_chain(reqs, one_at_a_time=True)
     for a, b in zip(hl, hl1):
@@ -438,7 +440,7 @@ def test_batched_chain_8b_heads_levels_batched():
         assert torch.equal(a.out.flags, b.out.flags)
         assert torch.equal(a.out.dist.nan_to_num(-1.0), b.out.dist.nan_to_num(-1.0))
         assert torch.equal(a.out.w_k, b.out.w_k) and torch.equal(a.out.w_v, b.out.w_v)
-    _check_chain_identical_inputs(reqs, datas, hl, "chain-8x128")
+    _check_chain_identical_inputs(reqs, datas, hl, f"chain-8x128-seed{seed}")
 
 
 def test_fan_in_ragged_pools_in_one_batched_call():
