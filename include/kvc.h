@@ -284,7 +284,11 @@ kvc_status kvc_correct_hops_batched(const kvc_hop_desc* hops, int32_t n_hops, kv
  * sigma_out [n_mats][rank] (device float).  Randomised subspace iteration with `oversample`
  * extra columns and `power_iters` power iterations, seeded by `seed`; each component's
  * sign is fixed so the largest-magnitude entry of its left singular vector is positive.
- * a_out/b_out dtype out_t.  Workspace: kvc_svd_workspace_size. */
+ * With power_iters >= 1 the basis comes from a last fp32 product of z with an orthonormal
+ * factor, and an exactly rank-r input is reconstructed to fp32 accuracy; with power_iters = 0
+ * it comes from the fp32 sketch z Omega itself, whose span is exact only to about the fp32
+ * unit roundoff times the sketch's condition number (1e-5 to 1e-4 relative on exactly rank-r
+ * products of Gaussian factors).  a_out/b_out dtype out_t.  Workspace: kvc_svd_workspace_size. */
 size_t kvc_svd_workspace_size(int32_t n_mats, int32_t rows, int32_t cols, int32_t rank,
                               int32_t oversample);
 kvc_status kvc_anchor_refresh_svd(const float* z, int32_t n_mats, int32_t rows, int32_t cols,
