@@ -81,6 +81,16 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t off) {
   const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)off);
   return __builtin_bit_cast(bf16x8, v);
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_u2(uint32_t off) {
+  const u32x2 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>((uintptr_t)off);
+  return make_uint2(v.x, v.y);
+}
+// s_waitcnt vmcnt <= N only
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // --------------------------------------------------------------------- operand packing
 // B' rows of the scored anchors, in scoring order u, chunked by 32 channels:
@@ -300,6 +310,32 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
       }
     };
 
+    // Rank 32: the epilogue's A rows (per wave, its 5 anchors x 64 tokens x 64 bytes, four 1 KiB
+    // units per anchor, 16-byte units swizzled as the ring's) come into LDS through the ring's
+    // transfers instead of global loads after the products: units 0-11 (anchors 0-2) take the
+    // places of the empty transfers of the last two chunks (slots nkc % 3 and (nkc + 1) % 3, six
+    // units per wave each), units 12-17 (anchor 3, half of anchor 4) the last chunk's slot once
+    // every wave is past it, units 18-19 anchor 0's first two places once this wave has read
+    // them.  Every unit is written and read by one wave only.
+    auto a_place = [&](int i) -> uint32_t {
+      int sl, pos;
+      if (i < 12) { sl = (nkc + i / 6) % kRing; pos = i % 6; }
+      else if (i < 18) { sl = (nkc + 2) % kRing; pos = i - 12; }
+      else { sl = nkc % kRing; pos = i - 18; }
+      return ring0 + (uint32_t)sl * kSlot + (uint32_t)(wv * 6 + pos) * 1024;
+    };
+    auto stage_a = [&](int i) {
+      const int x = i >> 2, k = i & 3;
+      const int u = u0 + __builtin_amdgcn_readfirstlane(ag) * kAnch + x;   // wave-uniform: the descriptor is scalar
+      const bool un = u < p.n_use;
+      const int a = un ? p.use[u] : 0;
+      const int rows = un ? min(p.len[a], S) : 0;
+      const rsrc_t ar = make_rsrc(p.A[side] + layer * p.a_layer_stride + (int64_t)p.off[a] * r, (uint32_t)rows * r * 2);
+      const int row = 16 * k + (lane >> 2), c = (lane & 3) ^ ((row >> 2) & 3);
+      dma16(ar, a_place(i), (uint32_t)(((t0 + tw * 64 + row) * r + c * 8) * 2));
+    };
+    static_assert(NS > 1 || kDmaPerWave == 6, "the last two chunks carry anchors 0-2 of the epilogue");
+
     f32x16 acc[kAnch][2];
 #pragma unroll
     for (int x = 0; x < kAnch; ++x)
@@ -327,11 +363,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
           const bf16x8 bx = s == 0 ? fb[x] : lds_frag(slot + boff[x][s]);
           acc[x][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx, z0, acc[x][0], 0, 0, 0);
           acc[x][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx, z1, acc[x][1], 0, 0, 0);
-          if (s * kAnch + x < kDmaPerWave) fetch_unit(kc + 2, s * kAnch + x);
+          if (s * kAnch + x < kDmaPerWave) {
+            if (NS == 1 && kc + 2 >= nkc) stage_a((kc + 2 - nkc) * kDmaPerWave + s * kAnch + x);
+            else fetch_unit(kc + 2, s * kAnch + x);
+          }
         }
       }
     }
-    wait_vm_barrier<0>();   // trailing (empty) transfers drained; every wave past the last chunk
+    wait_vm_barrier<0>();   // trailing transfers drained; every wave past the last chunk
     if constexpr (NS > 1) {
       slice_cosines<NS>(p, acc, reinterpret_cast<float*>(ring), u0, np, side, layer, tt, t0, tw, ag, lane, col, hi);
       continue;
@@ -339,12 +378,18 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
 
     // cosines of P with A per token, and the value-side gate sums over the prefix
 #pragma unroll
+    for (int i = 12; i < 18; ++i) stage_a(i);
+#pragma unroll
     for (int x = 0; x < kAnch; ++x) {
       const int u = u0 + ag * kAnch + x;
       if (u >= p.n_use) break;
+      if (x == 1) {   // anchor 0's reads are done (their values were used)
+        stage_a(18);
+        stage_a(19);
+      }
+      if (x == 3) wait_vm<0>();
       const int a = p.use[u];
       const int alen = p.len[a];
-      const uint16_t* Aa = p.A[side] + layer * p.a_layer_stride + (int64_t)p.off[a] * r;
       const bool gate = side == 1 && ((p.mask_gate >> a) & 1);
       float gnum = 0.f, gpp = 0.f, gaa = 0.f;
 #pragma unroll
@@ -352,10 +397,13 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
         const int t = t0 + tw * 64 + tb * 32 + col;
         const bool ok = t < alen && t < S;
         float num = 0.f, pp = 0.f, aa = 0.f;
+        // this lane's row of the wave's 64 (unit k = row / 16 of the anchor's four)
+        const int row = tb * 32 + col;
+        const uint32_t ub = (col >> 4) ? a_place(4 * x + 2 * tb + 1) : a_place(4 * x + 2 * tb);
 #pragma unroll
         for (int jg = 0; jg < 4; ++jg) {
-          uint2 av = make_uint2(0, 0);
-          if (ok) av = *reinterpret_cast<const uint2*>(Aa + (int64_t)t * r + 8 * jg + 4 * hi);
+          // rows past the anchor or the layer were transferred as zeros
+          const uint2 av = lds_u2(ub + (uint32_t)(((row & 15) * 4 + (jg ^ ((row >> 2) & 3))) * 16 + 8 * hi));
           const float a4[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
                                __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
 #pragma unroll
@@ -394,6 +442,8 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
         }
       }
     }
+    wait_vm<0>();   // no transfer into this work-group's LDS outlives the pass
+    if (u0 + kPass < nq) __syncthreads();   // every wave done with its A rows before the next pass's transfers
   }
 }
 
