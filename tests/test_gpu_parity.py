@@ -216,6 +216,11 @@ def test_head_dim_64_bf16():
 # 64 and 128 (two and four column groups per anchor, summed across waves before the cosine)
 COS_CASES = {
     "hd64": dict(n_layers=2, seq_len=200, n_kv_heads=4, head_dim=64, n_anchors=5),
+    # one head: two and four 32-channel chunks, so the epilogue's A rows ride on the first chunks'
+    # trailing transfers
+    "one_head_hd64": dict(n_layers=2, seq_len=230, n_kv_heads=1, head_dim=64, n_anchors=6,
+                          anchor_len=[230, 180, 230, 230, 99, 230]),
+    "one_head_hd128": dict(n_layers=2, seq_len=150, n_kv_heads=1, head_dim=128, n_anchors=21),
     "ragged": dict(n_layers=2, seq_len=400, n_kv_heads=2, n_anchors=5,
                    anchor_len=[330, 400, 250, 400, 390], gate_len=250),
     "two_passes": dict(n_layers=2, seq_len=330, n_kv_heads=2, n_anchors=23),
