@@ -14,7 +14,8 @@
 // Wave (tw, ag) owns tokens [64 tw, 64 tw + 64) and anchors [5 ag, 5 ag + 5) of the pass, i.e.
 // a 64 x 160 block of P in 160 accumulator registers.  The contraction runs over 32-channel
 // chunks: each chunk's source rows (128 x 64 B) and packed B' rows (20 x 32 x 64 B) are copied
-// from memory straight into a three-slot LDS ring by buffer->LDS transfers two chunks ahead.
+// from memory straight into a three-slot LDS ring by buffer->LDS transfers two chunks ahead.  At
+// rank 32 the transfers past the last chunk carry the epilogue's A rows instead of nothing.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16, operand A = 32 rank rows of B' x 16 channels, operand B =
 // 32 tokens x 16 channels; result register j of lane l holds rank row 8 (j / 4) + 4 (l / 32)
