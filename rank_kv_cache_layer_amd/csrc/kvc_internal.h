@@ -226,9 +226,9 @@ hipError_t launch_pack_b_batch(const PackArgs* d, const PackArgs* h, int n, hipS
 
 // ------------------------------------------------------------ two-pass path (bf16)
 // Score work-group = 128 tokens x 256 channels of one (layer, side), 4 waves of 64 x 128, two per
-// CU (64 tokens at base ranks 64 / 128).  Apply work-group = 128 tokens x 256 channels, 4 waves
-// of 64 x 128, three per CU, so one's streaming phases (source in, corrected cache out) overlap
-// the others' MFMA phases.
+// CU (at base ranks 64 / 128: 8 waves of 64 x 64, one per CU).  Apply work-group = 128 tokens x
+// 256 channels, 4 waves of 64 x 128, three per CU, so one's streaming phases (source in,
+// corrected cache out) overlap the others' MFMA phases.
 constexpr int kScoreTile = 128;
 constexpr int kScoreThreads = 256;
 constexpr int kApplyTile = 128;
@@ -281,7 +281,7 @@ hipError_t launch_split_apply_batch(const SplitArgs* d, const SplitArgs* h, int 
 hipError_t launch_split_weights(const SplitArgs& a, int wmode, hipStream_t st);
 hipError_t launch_split_apply(const SplitArgs& a, int head_dim, hipStream_t st);
 size_t split_score_lds(int r_b);                   // dynamic LDS bytes
-int split_score_tile(int r_b);                     // tokens per scoring tile (128; 64 at ranks 64 / 128)
+int split_score_tile(int r_b);                     // tokens per scoring tile (128 at every rank)
 size_t split_apply_lds(int r_d);
 // rank slices of 32 the apply takes per anchor: ranks 64, 128 and 256 run as 2, 4 and 8 slices
 // (their packed delta B is then one matrix per slice); ranks 8, 16 and 32 in one step

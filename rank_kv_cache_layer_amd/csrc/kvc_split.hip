@@ -650,16 +650,19 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const Spli
 // The contraction over an anchor's rank runs in NS slices of 32 (as the apply's), each a ring
 // step of the rank-32 slot size; the reconstruction Z - sum_s A_s B_s of an anchor is complete
 // only after its last slice, so every wave keeps its result blocks live across the slices.  To
-// fit them next to the source tile a work-group covers 64 tokens x 256 channels with 4 waves of
-// 64 tokens x 64 channels; a wave's two 32-channel blocks are the two halves of its rotary pairs
-// (head_dim 128: blocks b and b + 2 of a head, head_dim 64: one head), so the keys' rotation to
-// the canonical frame stays in registers.
-constexpr int kSlTile = 64;                    // tokens per work-group
+// fit them next to the source tile each wave covers 64 tokens x 64 channels; a work-group of 8
+// waves (two token halves x four channel pairs, one work-group per CU) covers 128 tokens x 256
+// channels, so a slice's A rows and B slice (24 KiB, three transfers per wave) serve twice the
+// products that a 64-token work-group's 20 KiB do.  A wave's two 32-channel blocks are the two
+// halves of its rotary pairs (head_dim 128: blocks b and b + 2 of a head, head_dim 64: one
+// head), so the keys' rotation to the canonical frame stays in registers.
+constexpr int kSlTile = 128;                   // tokens per work-group
+constexpr int kSlThreads = 512;                // 8 waves: 2 token halves x 4 channel pairs
 constexpr int kSlPitch = 72;                   // staging row pitch (elements): 64 channels + 8
 
 struct ScoreShared64 {
   float mp[2][4][kSlTile];                      // |E| sums of two anchors, per wave (64 channels)
-  float qp[4][kMaxAnchors];                     // per-wave gate sums
+  float qp[kSlThreads / 64][kMaxAnchors];       // per-wave gate sums
   float tab[2][kFusedHalf];                     // R(-p_src) table
 };
 
@@ -715,7 +718,7 @@ __device__ __forceinline__ void rotate_tile2(f32x16 (&z)[2][2], const float* cs,
 
 template <int HD, int NS, typename P>
 __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, ScoreShared64& sh) {
-  constexpr int kST = kSlTile, kNT = kScoreThreads, kNW = kNT / 64, RS = 32 * NS;
+  constexpr int kST = kSlTile, kNT = kSlThreads, kNW = kNT / 64, RS = 32 * NS;
   using RG = Ring<2, kST, kNW, false, 32, RS>;
   auto& mp = sh.mp;
   auto& qp = sh.qp;
@@ -726,7 +729,8 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int D = p.D, S = p.S, N = p.N, NCB = D >> 5;
   const int t0 = id.tt * kST;
-  const int blk0 = sl_block<HD>(wave), blk1 = blk0 + HD / 64;
+  const int tw = wave >> 2, wc = wave & 3, tw0 = t0 + tw * 64;
+  const int blk0 = sl_block<HD>(wc), blk1 = blk0 + HD / 64;
   const int c0 = id.cq * kSW + blk0 * 32, c1 = id.cq * kSW + blk1 * 32;
 
   const auto list = keys ? p.corr : p.use;
@@ -761,11 +765,11 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) aoff[tb][ks] = RG::a_unit(tb * 32 + col, ks * 2 + hi) * 16;
+    for (int ks = 0; ks < 2; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
   const uint32_t boff0 = RG::A_BYTES + blk0 * 2 * 1024 + lane * 16, boff1 = RG::A_BYTES + blk1 * 2 * 1024 + lane * 16;
 
-  const float qm0 = (t0 + col < p.k_gate && t0 + col < S) ? 1.f : 0.f;
-  const float qm1 = (t0 + 32 + col < p.k_gate && t0 + 32 + col < S) ? 1.f : 0.f;
+  const float qm0 = (tw0 + col < p.k_gate && tw0 + col < S) ? 1.f : 0.f;
+  const float qm1 = (tw0 + 32 + col < p.k_gate && tw0 + 32 + col < S) ? 1.f : 0.f;
   float* mpart = p.mpart + (((int64_t)id.cq * 2 + id.side) * p.n_layers + id.layer) * N * S;
   auto store_m = [&](int ja) {   // partial |E| sums of anchor ja over the tile's 256 channels
     const int a = lane_get(sl.a, ja);
@@ -819,8 +823,8 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
         m0 = xor32_sum(m0);
         m1 = xor32_sum(m1);
         if (hi == 0) {
-          mp[ja & 1][wave][col] = m0;
-          mp[ja & 1][wave][32 + col] = m1;
+          mp[ja & 1][wc][tw * 64 + col] = m0;
+          mp[ja & 1][wc][tw * 64 + 32 + col] = m1;
         }
       }
       if (Q && ((p.mask_gate >> a) & 1)) {
@@ -839,7 +843,7 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
     f32x16 z[2][2];
     fetch(0);
     // staging (wave-private) in the ring past slot 0, free until step 1 is fetched
-    load_tile2(z, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, (uint32_t)S * D * 2), t0, D, c0, c1,
+    load_tile2(z, make_rsrc(p.z[id.side] + (int64_t)id.layer * S * D, (uint32_t)S * D * 2), tw0, D, c0, c1,
                reinterpret_cast<uint16_t*>(ring + RG::SLOT) + wave * 32 * kSlPitch, lane, col, hi);
     if (keys && p.can.active) rotate_tile2(z, tab[0], tab[1], (blk0 * 32) % HD, hi);
     wait_vm_barrier<63>();   // every wave is done with the staging area
@@ -864,7 +868,7 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
 }
 
 template <int HD, int NS>
-__global__ void __launch_bounds__(kScoreThreads, 2) split_score_sliced(SplitArgs p) {
+__global__ void __launch_bounds__(kSlThreads, 1) split_score_sliced(SplitArgs p) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   __shared__ ScoreShared64 sh;
   score_tile_sliced<HD, NS>(p, xcd_remap(blockIdx.x, gridDim.x), ring, sh);
@@ -1095,8 +1099,8 @@ hipError_t score_dispatch(const SplitArgs& a, hipStream_t st) {
   switch (a.r_b) {
     case 16: return go(split_score<HD, 1>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
     case 32: return go(split_score<HD, 2>, a, kScoreTile, kScoreThreads, split_score_lds(a.r_b), st);
-    case 64: return go(split_score_sliced<HD, 2>, a, kSlTile, kScoreThreads, split_score_lds(a.r_b), st);
-    case 128: return go(split_score_sliced<HD, 4>, a, kSlTile, kScoreThreads, split_score_lds(a.r_b), st);
+    case 64: return go(split_score_sliced<HD, 2>, a, kSlTile, kSlThreads, split_score_lds(a.r_b), st);
+    case 128: return go(split_score_sliced<HD, 4>, a, kSlTile, kSlThreads, split_score_lds(a.r_b), st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1121,9 +1125,9 @@ hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
 // filled during the tile load; apply: from the start, before anchor 0 is fetched), whichever
 // is larger
 size_t split_score_lds(int r_b) {
-  if (r_b == 64 || r_b == 128) {   // rank slices of 32 over 64-token tiles
+  if (r_b == 64 || r_b == 128) {   // rank slices of 32, 8 waves' staging
     const size_t slot = (size_t)kSlTile * 32 * 2 + (size_t)kNCBW * 2 * 1024;
-    return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kScoreThreads / 64) * 32 * kSlPitch);
+    return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kSlThreads / 64) * 32 * kSlPitch);
   }
   const size_t slot = (size_t)kScoreTile * r_b * 2 + (size_t)kNCBW * (r_b / 16) * 1024;
   return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kScoreThreads / 64) * kStage);
