@@ -221,8 +221,9 @@ bool cos_gemm_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm) 
 }
 
 // The two-pass bf16 path: 128-token x 256-channel work-groups (D a multiple of 256), scoring
-// ranks 16/32 (larger ranks would not fit the register budget), apply ranks 8 (padded to the
-// MFMA's 16 on chip), 16, 32 and 64/128/256 (as slices of 32), within the LDS budget.
+// ranks 16/32 (and 64/128 in steps of 64 ranks with the result blocks held across them), apply
+// ranks 8 (padded to the MFMA's 16 on chip), 16, 32 and 64/128/256 (as slices of 32), within
+// the LDS budget.
 constexpr size_t kLdsBudget = 160 * 1024;
 bool split_ok(const kvc_shape& sh, const kvc_pool& p, const kvc_params& prm, bool pages_scores, bool apply) {
   if (p.dtype != KVC_BF16 || (prm.options & 3)) return false;
@@ -659,7 +660,7 @@ kvc_status run_hop(const void* k_src, const void* v_src, void* k_out, void* v_ou
   kvc_status r;
   if (pl.split_match) {
     uint16_t* pb = reinterpret_cast<uint16_t*>(ws + pl.off_pack_base);
-    // base ranks 64 / 128 are scored in rank slices of 32: one packed matrix per slice
+    // base ranks 64 / 128 are packed as one matrix per rank slice of 32 (a scoring step takes two)
     if ((r = pack_pair(p.baseB_k, p.baseB_v, pb, p.rank_base, 1, nullptr, sh, p, tr, KVC_K_PACK_BASE, st,
                        split_apply_slices(p.rank_base))) != KVC_OK)
       return r;

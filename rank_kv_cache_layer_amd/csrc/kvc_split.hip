@@ -647,15 +647,16 @@ __global__ void __launch_bounds__(kScoreThreads, 2) split_score_batch(const Spli
 }
 
 // ------------------------------------------------- first-mode scores at base ranks 64 and 128
-// The contraction over an anchor's rank runs in NS slices of 32 (as the apply's), each a ring
-// step of the rank-32 slot size; the reconstruction Z - sum_s A_s B_s of an anchor is complete
-// only after its last slice, so every wave keeps its result blocks live across the slices.  To
-// fit them next to the source tile each wave covers 64 tokens x 64 channels; a work-group of 8
-// waves (two token halves x four channel pairs, one work-group per CU) covers 128 tokens x 256
-// channels, so a slice's A rows and B slice (24 KiB, three transfers per wave) serve twice the
-// products that a 64-token work-group's 20 KiB do.  A wave's two 32-channel blocks are the two
-// halves of its rotary pairs (head_dim 128: blocks b and b + 2 of a head, head_dim 64: one
-// head), so the keys' rotation to the canonical frame stays in registers.
+// The contraction over an anchor's rank runs in ring steps of 64 ranks (two of the packed rank-32
+// slices, NS / 2 steps per anchor, the slot 48 KiB); the reconstruction Z - sum_s A_s B_s of an
+// anchor is complete only after its last step, so every wave keeps its result blocks live
+// across the steps.  To fit them next to the source tile each wave covers 64 tokens x 64
+// channels; a work-group of 8 waves (two token halves x four channel pairs, one work-group per
+// CU) covers 128 tokens x 256 channels, so a step's A rows and B slices (six transfers per wave)
+// feed 16 products per wave, and an anchor takes half the barriers of steps of 32 ranks.  A
+// wave's two 32-channel blocks are the two halves of its rotary pairs (head_dim 128: blocks b
+// and b + 2 of a head, head_dim 64: one head), so the keys' rotation to the canonical frame
+// stays in registers.
 constexpr int kSlTile = 128;                   // tokens per work-group
 constexpr int kSlThreads = 512;                // 8 waves: 2 token halves x 4 channel pairs
 constexpr int kSlPitch = 72;                   // staging row pitch (elements): 64 channels + 8
@@ -719,7 +720,8 @@ __device__ __forceinline__ void rotate_tile2(f32x16 (&z)[2][2], const float* cs,
 template <int HD, int NS, typename P>
 __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, ScoreShared64& sh) {
   constexpr int kST = kSlTile, kNT = kSlThreads, kNW = kNT / 64, RS = 32 * NS;
-  using RG = Ring<2, kST, kNW, false, 32, RS>;
+  constexpr int NS2 = NS / 2;   // ring steps per anchor, two rank-32 slices each
+  using RG = Ring<4, kST, kNW, false, 64, RS>;
   auto& mp = sh.mp;
   auto& qp = sh.qp;
   auto& tab = sh.tab;
@@ -737,7 +739,7 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
   int nl = keys ? p.n_corr : p.n_use;
   const int s_work = keys ? (p.n_corr ? p.s_cov : 0) : max(p.n_corr ? p.s_cov : 0, p.mask_gate ? p.k_gate : 0);
   if (t0 >= s_work) nl = 0;
-  const int steps = nl * NS;
+  const int steps = nl * NS2;
 
   for (int i = tid; i < HD / 2; i += kNT) {
     tab[0][i] = p.can.cs[i];
@@ -751,22 +753,37 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
   const int64_t bstride = (int64_t)NCB * 2 * kC;
   const uint32_t ring0 = lds_off(ring);
   const int wv = uni(wave);
-  auto fetch = [&](int j) {   // slice j % NS of scored anchor j / NS into slot j % 3
+  auto fetch = [&](int j) {   // slices 2 (j % NS2) and 2 (j % NS2) + 1 of scored anchor j / NS2 into slot j % 3
     const bool live = j < steps;
-    const int js = live ? j / NS : 0, ks = live ? j % NS : 0;
+    const int js = live ? j / NS2 : 0, ks = live ? j % NS2 : 0;
     const int a = lane_get(sl.a, js);
     const int lim = live ? lane_get(sl.lim, js) : 0;
-    const int a_elems = lim * RS - ks * 32;   // the slice's rows end where the stored rows do
-    RG::fetch(ring0 + (uint32_t)(j % kSlots) * RG::SLOT,
-              make_rsrc(Al + (int64_t)lane_get(sl.off, js) * RS + ks * 32, (uint32_t)(live ? a_elems : 0) * 2),
-              make_rsrc(Bl + (a * NS + ks) * bstride, live ? RG::B_BYTES : 0), make_rsrc(nullptr, 0), t0, wv, lane);
+    const int a_elems = lim * RS - ks * 64;   // the step's rows end where the stored rows do
+    const uint32_t slot = ring0 + (uint32_t)(j % kSlots) * RG::SLOT;
+    const rsrc_t Ar = make_rsrc(Al + (int64_t)lane_get(sl.off, js) * RS + ks * 64, (uint32_t)(live ? a_elems : 0) * 2);
+#pragma unroll
+    for (int i = 0; i < RG::A_PER_WAVE; ++i) {
+      const int u = (wv * RG::A_PER_WAVE + i) * 64 + lane;
+      const int row = u / RG::U, cpos = u % RG::U;
+      const int c = cpos ^ ((row / (16 / RG::U)) & (RG::U - 1));
+      dma16(Ar, slot + (wv * RG::A_PER_WAVE + i) * 1024, (uint32_t)(((t0 + row) * RS + c * 8) * 2));
+    }
+    // the two slices' packed matrices (each [block][k16] 1 KiB chunks) interleaved into the
+    // slot's [block][k16 of the step] order
+    const rsrc_t Br = make_rsrc(Bl + (a * NS + 2 * ks) * bstride, live ? (uint32_t)(2 * bstride * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < RG::B_PER_WAVE; ++i) {
+      const int kc = wv * RG::B_PER_WAVE + i, db = kc >> 2, kk = kc & 3;
+      dma16(Br, slot + RG::A_BYTES + kc * 1024,
+            (uint32_t)((((kk >> 1) * bstride + (db * 2 + (kk & 1)) * kC)) * 2 + lane * 16));
+    }
   };
-  uint32_t aoff[2][2];
+  uint32_t aoff[2][4];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
-  const uint32_t boff0 = RG::A_BYTES + blk0 * 2 * 1024 + lane * 16, boff1 = RG::A_BYTES + blk1 * 2 * 1024 + lane * 16;
+    for (int ks = 0; ks < 4; ++ks) aoff[tb][ks] = RG::a_unit(tw * 64 + tb * 32 + col, ks * 2 + hi) * 16;
+  const uint32_t boff0 = RG::A_BYTES + blk0 * 4 * 1024 + lane * 16, boff1 = RG::A_BYTES + blk1 * 4 * 1024 + lane * 16;
 
   const float qm0 = (tw0 + col < p.k_gate && tw0 + col < S) ? 1.f : 0.f;
   const float qm1 = (tw0 + 32 + col < p.k_gate && tw0 + 32 + col < S) ? 1.f : 0.f;
@@ -785,14 +802,14 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
     for (int ja = 0; ja < nl; ++ja) {
       f32x16 e[2][2];
 #pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
-        const int j = ja * NS + ks;
-        wait_vm_barrier<RG::DMA_PER_WAVE>();   // slice j landed for every wave; slot (j + 2) % 3 is free
+      for (int ks = 0; ks < NS2; ++ks) {
+        const int j = ja * NS2 + ks;
+        wait_vm_barrier<RG::DMA_PER_WAVE>();   // step j landed for every wave; slot (j + 2) % 3 is free
         const uint32_t slot = (uint32_t)uni((int)(ring0 + (uint32_t)(j % kSlots) * RG::SLOT));
-        // the slice's fragments first: their reads are in flight while the transfers issue
-        bf16x8 av[2][2], bv[2][2];
+        // the step's fragments first: their reads are in flight while the transfers issue
+        bf16x8 av[2][4], bv[2][4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) av[tb][kk] = as_bf8(lds_u4(slot + aoff[tb][kk]));
           bv[0][kk] = as_bf8(lds_u4(slot + boff0 + kk * 1024));
@@ -802,8 +819,12 @@ __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, 
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int db = 0; db < 2; ++db)
-            e[tb][db] = mfma(bv[db][1], av[tb][1], mfma(bv[db][0], av[tb][0], ks == 0 ? z[tb][db] : e[tb][db]));
+          for (int db = 0; db < 2; ++db) {
+            f32x16 acc = ks == 0 ? z[tb][db] : e[tb][db];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma(bv[db][kk], av[tb][kk], acc);
+            e[tb][db] = acc;
+          }
       }
       // E = Z_can - A B complete: |E| per token column, E^2 for the gate
       float m0 = 0.f, m1 = 0.f, q0 = 0.f, q1 = 0.f;
@@ -1125,8 +1146,8 @@ hipError_t apply_dispatch(const SplitArgs& a, hipStream_t st) {
 // filled during the tile load; apply: from the start, before anchor 0 is fetched), whichever
 // is larger
 size_t split_score_lds(int r_b) {
-  if (r_b == 64 || r_b == 128) {   // rank slices of 32, 8 waves' staging
-    const size_t slot = (size_t)kSlTile * 32 * 2 + (size_t)kNCBW * 2 * 1024;
+  if (r_b == 64 || r_b == 128) {   // steps of 64 ranks, 8 waves' staging
+    const size_t slot = (size_t)kSlTile * 64 * 2 + (size_t)kNCBW * 4 * 1024;
     return std::max((size_t)kSlots * slot, slot + sizeof(uint16_t) * (kSlThreads / 64) * 32 * kSlPitch);
   }
   const size_t slot = (size_t)kScoreTile * r_b * 2 + (size_t)kNCBW * (r_b / 16) * 1024;
