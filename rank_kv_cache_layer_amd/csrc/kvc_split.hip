@@ -721,6 +721,7 @@ template <int HD, int NS, typename P>
 __device__ __forceinline__ void score_tile_sliced(P& p, int64_t lb, char* ring, ScoreShared64& sh) {
   constexpr int kST = kSlTile, kNT = kSlThreads, kNW = kNT / 64, RS = 32 * NS;
   constexpr int NS2 = NS / 2;   // ring steps per anchor, two rank-32 slices each
+  static_assert(NS % 2 == 0, "ranks 64 and 128: whole steps of 64");
   using RG = Ring<4, kST, kNW, false, 64, RS>;
   auto& mp = sh.mp;
   auto& qp = sh.qp;
