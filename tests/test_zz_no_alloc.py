@@ -46,3 +46,15 @@ def test_noalloc_matches_correct_hop_two_calls(mode):
     _both(big)
     print(f"[noalloc] mode={mode} call 2: L={small.n_layers} S={small.seq_len} N={small.n_anchors}", flush=True)
     _both(small)
+
+
+def test_noalloc_sliced_ranks_two_calls():
+    # base and delta ranks 128, then 64: the scoring in 64-rank steps and the apply in rank
+    # slices, through the library-owned scratch, equal to the workspace entry point
+    big = W.llama8b_hop(n_layers=2, seq_len=600, n_kv_heads=4, n_anchors=6, rank_base=128, rank_delta=128,
+                        anchor_len=[600, 520, 600, 410, 600, 580], gate_len=300)
+    small = W.llama8b_hop(n_layers=2, seq_len=333, n_kv_heads=2, n_anchors=5, rank_base=64, rank_delta=64)
+    print(f"[noalloc] rank 128 call 1: L={big.n_layers} S={big.seq_len} N={big.n_anchors}", flush=True)
+    _both(big)
+    print(f"[noalloc] rank 64 call 2: L={small.n_layers} S={small.seq_len} N={small.n_anchors}", flush=True)
+    _both(small)
