@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_cos_gemm(CosGemmArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int tw = wave >> 2, ag = wave & 3;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int D = p.D, S = p.S, nkc = D / kKc, r = 32, R = 32 * NS;
+  const int D = p.D, S = p.S, nkc = D / kKc, r = 32;
   const int nq = p.n_use * NS;   // GEMM column groups of 32
   const int t0 = tt * kTok;
   const uint32_t ring0 = lds_off(ring);

@@ -371,10 +371,10 @@ struct Tracer {
     if (!t || t->count >= t->capacity || t->count >= KVC_TRACE_MAX) return;
     slot = t->count++;
     t->kernel_id[slot] = id;
-    hipEventRecord((hipEvent_t)t->start[slot], st);
+    (void)hipEventRecord((hipEvent_t)t->start[slot], st);   // best effort: a missing event reads as no time
   }
   void end() {
-    if (slot >= 0) hipEventRecord((hipEvent_t)t->stop[slot], st);
+    if (slot >= 0) (void)hipEventRecord((hipEvent_t)t->stop[slot], st);
     slot = -1;
   }
 };
@@ -1202,7 +1202,8 @@ kvc_status kvc_apply_lowrank_delta(const void* k_src, const void* v_src, void* k
   return ok();
 }
 
-static kvc_status correct_one(const HopReq& h, kvc_dtype dt, const kvc_shape& sh, const kvc_rope* rope,
+static kvc_status correct_one(const HopReq& h, kvc_dtype /* validated by the caller; the pool carries it */,
+                              const kvc_shape& sh, const kvc_rope* rope,
                               const kvc_params* prm, char* ws, size_t ws_bytes, const int32_t* pred_flags,
                               hipStream_t st) {
   const kvc_pool& p = *h.pool;

@@ -24,7 +24,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
-__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
 // Flattened block index -> logical tile, XCD-aware (consecutive tiles share an XCD L2).
 __device__ __forceinline__ int64_t logical_block() {

@@ -1634,7 +1634,7 @@ hipError_t svd_refresh(const float* z, int n_mats, int rows, int cols, int rank,
   double* m1 = reinterpret_cast<double*>(base + L.m1);
   double* m2 = reinterpret_cast<double*>(base + L.m2);
   const int m = rows, n = cols, l = rank + oversample, r = rank, b = n_mats;
-  const int64_t sZ = (int64_t)m * n, sY = (int64_t)m * l, sW = (int64_t)n * l, sLL = (int64_t)l * l;
+  const int64_t sZ = (int64_t)m * n, sY = (int64_t)m * l, sW = (int64_t)n * l;
   hipError_t e;
 
   // Omega [b][n][l] ~ N(0, 1)
