@@ -345,7 +345,7 @@ __device__ __forceinline__ void score_anchor(const f32x16 (&z)[2][4], const Scor
     else
       asm volatile("" : "+v"(av[0][0]), "+v"(av[0][1]), "+v"(av[1][0]), "+v"(av[1][1]), "+v"(m[0]), "+v"(m[1]),
                    "+v"(q[0]), "+v"(q[1]));
-    e = en;
+    if (b < 8) e = en;
   }
   ms0 += m[0];
   ms1 += m[1];
