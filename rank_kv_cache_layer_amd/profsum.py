@@ -31,7 +31,7 @@ import statistics
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-HOT = ("split_score", "split_apply", "score_cos_mfma", "score_cos_gemm", "fused_hop")
+HOT = ("split_score", "split_score_sliced", "split_apply", "score_cos_mfma", "score_cos_gemm", "fused_hop")
 N_SE, N_SIMD = 32, 1024   # MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
 
 
@@ -121,7 +121,7 @@ def main():
                   "| kernel | calls | avg ms | % time | HBM read GB/launch | HBM write GB/launch | algorithmic GB/launch |",
                   "|---|---|---|---|---|---|---|"]
     else:
-        lines += ["python -m rank_kv_cache_layer_amd.profsum --kt <kt> ...", "```", "",
+        lines += [f"python -m rank_kv_cache_layer_amd.profsum --kt <kt> {'--sq <sq> ' if a.sq else ''}...", "```", "",
                   "| kernel | calls | avg ms | % time |", "|---|---|---|---|"]
     traffic = {}
     algo = (bench or {}).get("kernels", {})
